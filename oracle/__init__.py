@@ -1,0 +1,138 @@
+"""Python face of the CPU oracle (oracle/hs2_oracle.c).
+
+TEST INFRASTRUCTURE ONLY. Only tests/, the smoke check and the benchmark's
+CPU-baseline leg use this package. It imports nothing from the HIP library
+and the HIP library imports nothing from it.
+
+Arrays are CPU torch tensors or numpy arrays in their storage formats
+(float32, bfloat16, uint8 FP8 codes + float32 per-token scales); the C code
+widens them to double itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_hs2.so")
+_lib = None
+
+F32, BF16, FP8 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i = ctypes.c_int
+_d = ctypes.c_double
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.orc_full_select.argtypes = [_p, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i,
+                                      _i, _i, _d, _p, _i64, _p, _p, _p, _p, _p]
+        L.orc_full_select.restype = _i
+        L.orc_sparse.argtypes = [_p, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _d,
+                                 _p, _i64, _p, _p]
+        L.orc_sparse.restype = _i
+        L.orc_select_scores_f32.argtypes = [_p, _i64, _i64, _p, _i, _p]
+        L.orc_select_scores_f32.restype = _i
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_value.restype = _d
+        L.orc_num_threads.restype = _i
+        L.orc_set_threads.argtypes = [_i]
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        assert t.device.type == "cpu" and t.is_contiguous()
+        return t.data_ptr()
+    assert isinstance(t, np.ndarray) and t.flags["C_CONTIGUOUS"]
+    return t.ctypes.data
+
+
+def _dt(t: torch.Tensor) -> int:
+    return _DT[t.dtype]
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(n)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(code)
+
+
+def full_select(q, k, v, k_scale, v_scale, q_pos0: int, window: int, k_global: int,
+                sm_scale: float, rows: Sequence[int], want_scores: bool = False,
+                select: bool = True):
+    """Full attention + score + selection for flat query rows `rows`.
+
+    q: [B][n_q][H][d]; k, v: [B][n_ctx][d]. Returns dict with out [n][H][d],
+    lse [n][H] (float64), idx [n][window+k_global] int32, kth [n] and, if
+    asked, scores [n][n_ctx] (-1 beyond the causal limit)."""
+    B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = len(rows_a)
+    out = np.zeros((n, H, d), np.float64)
+    lse = np.zeros((n, H), np.float64)
+    S = window + k_global
+    idx = np.zeros((n, S), np.int32) if select else None
+    kth = np.zeros((n,), np.float64)
+    sc = np.zeros((n, n_ctx), np.float64) if want_scores else None
+    rc = lib().orc_full_select(_ptr(q), _dt(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                               _dt(k), B, n_q, q_pos0, n_ctx, H, d, window, k_global, sm_scale,
+                               _ptr(rows_a), n, _ptr(out), _ptr(lse), _ptr(idx), _ptr(sc),
+                               _ptr(kth))
+    if rc != 0:
+        raise ValueError("oracle full_select: invalid arguments")
+    return {"out": out, "lse": lse, "idx": idx, "kth": kth, "scores": sc, "rows": rows_a}
+
+
+def sparse(q, k, v, k_scale, v_scale, idx, sm_scale: float, rows: Sequence[int]):
+    """Sparse attention of query rows `rows` of q ([B][n_q][H][d]) over the
+    positions in idx[r] (one index row per entry of `rows`; < 0 skipped)."""
+    B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    idx_a = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    assert idx_a.shape[0] == len(rows_a)
+    n = len(rows_a)
+    out = np.zeros((n, H, d), np.float64)
+    lse = np.zeros((n, H), np.float64)
+    rc = lib().orc_sparse(_ptr(q), _dt(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _dt(k),
+                          B, n_q, n_ctx, H, d, _ptr(idx_a), idx_a.shape[1], sm_scale,
+                          _ptr(rows_a), n, _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle sparse: invalid arguments")
+    return {"out": out, "lse": lse}
+
+
+def select_scores_f32(scores: np.ndarray, n_cand: Sequence[int], k: int) -> np.ndarray:
+    """Top-k (score desc, position asc) of each row's first n_cand[r] entries,
+    written ascending and padded with -1."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    rows, stride = s.shape
+    nc = np.ascontiguousarray(np.asarray(n_cand, dtype=np.int64))
+    out = np.zeros((rows, k), np.int32)
+    rc = lib().orc_select_scores_f32(_ptr(s), rows, stride, _ptr(nc), k, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle select: invalid arguments")
+    return out

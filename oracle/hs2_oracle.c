@@ -1,0 +1,316 @@
+/*
+ * CPU oracle for the HySparse2 attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY: this file is used by tests/, by the smoke check
+ * and by the benchmark's CPU-baseline timing. The product (the HIP library)
+ * neither links nor calls it, and it shares no code with the product.
+ *
+ * It is the plain definition of what the path computes, in double precision:
+ *
+ *  - Full attention (HySparse2 page, "어떻게 동작하나": full-attention layers
+ *    of the cross-decoder; "어떻게 쓰나": MQA with a single K/V head, NoPE, so
+ *    no positional rotation). For a query at position p and head h:
+ *      s_hj = sm_scale * <q_h, k_j>           for j = 0..p (causal)
+ *      LSE_h = log sum_j exp(s_hj)            (natural log, max-shifted)
+ *      O_h   = sum_j exp(s_hj - LSE_h) v_j
+ *  - Token score (HySparse2 page, "무엇과 다른가": the full layer's exact
+ *    attention scores act as the indexer; IndexCache page, section 3
+ *    "표기법": the aggregated attention distribution is the softmax weight
+ *    averaged over heads). This build stores the head SUM,
+ *      score_j = sum_h exp(s_hj - LSE_h),
+ *    which is H times the head mean and ranks keys identically.
+ *  - Selection ("무엇과 다른가" and "어떻게 쓰나": the 128 most recent tokens
+ *    are always taken first, then the 1,024 highest-scoring tokens outside
+ *    that window, per token):
+ *      window  = positions max(0, p-W+1) .. p
+ *      global  = the first min(K, p-W+1) candidates j in [0, p-W] ordered by
+ *                (score descending, position ascending)
+ *    Each output row holds the window ascending (padded with -1 to W), then
+ *    the global set ascending (padded with -1 to K).
+ *  - Sparse layers (KV Reuse, "어떻게 동작하나"): the same attention with a
+ *    layer's own query, restricted to the positions listed in an index row
+ *    (entries < 0 are skipped).
+ *
+ * Inputs are the already-rounded storage arrays. bf16 and FP8-E4M3 values are
+ * widened to double exactly; an FP8 value is code_value * per-token scale,
+ * which is exact in double (4-bit times 24-bit significand).
+ *
+ * Every reduction runs sequentially in index order inside one thread;
+ * OpenMP only splits independent outputs, so results do not depend on the
+ * thread count.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+
+/* bf16 is the top half of an IEEE binary32. */
+static double orc_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0 is
+ * subnormal (m * 2^-9); S.1111.111 is NaN; there is no infinity. */
+double orc_e4m3_value(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+static double orc_elem(const void* base, int dt, size_t i) {
+    switch (dt) {
+        case ORC_F32: return (double)((const float*)base)[i];
+        case ORC_BF16: return orc_bf16(((const uint16_t*)base)[i]);
+        default: return orc_e4m3_value(((const uint8_t*)base)[i]);
+    }
+}
+
+/* Row j of a [B][n_ctx][d] cache for sequence b, widened to double. */
+static void orc_kv_row(const void* x, const float* scale, int dt, int64_t b, int64_t n_ctx,
+                       int d, int64_t j, double* dst) {
+    size_t base = ((size_t)b * (size_t)n_ctx + (size_t)j) * (size_t)d;
+    double sc = (dt == ORC_FP8) ? (double)scale[(size_t)b * (size_t)n_ctx + (size_t)j] : 1.0;
+    for (int c = 0; c < d; ++c) dst[c] = orc_elem(x, dt, base + (size_t)c) * sc;
+}
+
+static int orc_dt_ok(int dt) { return dt == ORC_F32 || dt == ORC_BF16 || dt == ORC_FP8; }
+
+typedef struct {
+    double s;
+    int64_t j;
+} orc_cand;
+
+/* score descending, then position ascending */
+static int orc_cand_cmp(const void* a, const void* b) {
+    const orc_cand* x = (const orc_cand*)a;
+    const orc_cand* y = (const orc_cand*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+static int orc_i32_cmp(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Softmax attention of one query row (H heads) over the key positions pos[0..n).
+ * Writes out[H][d], lse[H]; if prob != NULL also the per-head probabilities
+ * prob[h*n + t] = exp(s_h,pos[t] - LSE_h). */
+static void orc_attend(const double* qd, int H, int d, double sm_scale, const void* k,
+                       const void* v, const float* ks, const float* vs, int kv_dt, int64_t b,
+                       int64_t n_ctx, const int64_t* pos, int64_t n, double* out, double* lse,
+                       double* prob, int parallel) {
+    double* s = (double*)malloc(sizeof(double) * (size_t)H * (size_t)(n > 0 ? n : 1));
+    /* logits */
+#pragma omp parallel for schedule(static) if (parallel)
+    for (int64_t t = 0; t < n; ++t) {
+        double kd[256];
+        orc_kv_row(k, ks, kv_dt, b, n_ctx, d, pos[t], kd);
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += qd[h * d + c] * kd[c];
+            s[(size_t)h * n + t] = sm_scale * acc;
+        }
+    }
+    /* log-sum-exp per head, then probabilities */
+    for (int h = 0; h < H; ++h) {
+        if (n == 0) {
+            lse[h] = -INFINITY;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) m = fmax(m, s[(size_t)h * n + t]);
+        double sum = 0.0;
+        for (int64_t t = 0; t < n; ++t) sum += exp(s[(size_t)h * n + t] - m);
+        lse[h] = m + log(sum);
+    }
+#pragma omp parallel for schedule(static) if (parallel)
+    for (int64_t t = 0; t < n; ++t)
+        for (int h = 0; h < H; ++h) s[(size_t)h * n + t] = exp(s[(size_t)h * n + t] - lse[h]);
+    /* O_h[c] = sum_t P_h,t v_t[c], sequential in t for every (h, c) */
+#pragma omp parallel for schedule(static) if (parallel)
+    for (int c = 0; c < d; ++c) {
+        double acc[64];
+        for (int h = 0; h < H; ++h) acc[h] = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            size_t row = (size_t)b * (size_t)n_ctx + (size_t)pos[t];
+            double vv = orc_elem(v, kv_dt, row * (size_t)d + (size_t)c);
+            if (kv_dt == ORC_FP8) vv *= (double)vs[row];
+            for (int h = 0; h < H; ++h) acc[h] += s[(size_t)h * n + t] * vv;
+        }
+        for (int h = 0; h < H; ++h) out[h * d + c] = acc[h];
+    }
+    if (prob) memcpy(prob, s, sizeof(double) * (size_t)H * (size_t)n);
+    free(s);
+}
+
+static void orc_query(const void* q, int q_dt, int64_t row, int H, int d, double* qd) {
+    size_t base = (size_t)row * (size_t)H * (size_t)d;
+    for (int t = 0; t < H * d; ++t) qd[t] = orc_elem(q, q_dt, base + (size_t)t);
+}
+
+static int orc_check_common(int q_dt, int kv_dt, int B, int64_t n_q, int64_t n_ctx, int H, int d) {
+    if (!orc_dt_ok(kv_dt) || (q_dt != ORC_F32 && q_dt != ORC_BF16)) return 1;
+    if (B <= 0 || n_q <= 0 || n_ctx <= 0 || H <= 0 || H > 64 || d <= 0 || d > 256) return 1;
+    return 0;
+}
+
+/*
+ * Full causal attention + score + window/top-K selection for the flat query
+ * rows rows[0..n_rows) (row = b*n_q + i, position p = q_pos0 + i).
+ *   out    [n_rows][H][d]           attention output
+ *   lse    [n_rows][H]              natural-log LSE
+ *   idx    [n_rows][window+k_glob]  index rows (NULL: skip selection)
+ *   scores [n_rows][n_ctx]          score_j for j <= p, -1 beyond (NULL: not stored)
+ *   kth    [n_rows]                 score of the last global element taken, -1 if none
+ * Returns 0, or 1 on invalid arguments.
+ */
+int orc_full_select(const void* q, int q_dt, const void* k, const void* v, const float* k_scale,
+                    const float* v_scale, int kv_dt, int B, int64_t n_q, int64_t q_pos0,
+                    int64_t n_ctx, int H, int d, int window, int k_global, double sm_scale,
+                    const int64_t* rows, int64_t n_rows, double* out, double* lse, int32_t* idx,
+                    double* scores, double* kth) {
+    if (orc_check_common(q_dt, kv_dt, B, n_q, n_ctx, H, d)) return 1;
+    if (q_pos0 < 0 || q_pos0 + n_q > n_ctx || window < 1 || k_global < 0) return 1;
+    if (kv_dt == ORC_FP8 && (!k_scale || !v_scale)) return 1;
+    const int S = window + k_global;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t row = rows[r];
+        if (row < 0 || row >= (int64_t)B * n_q) return 1;
+        int64_t b = row / n_q, i = row % n_q, p = q_pos0 + i, n = p + 1;
+        double* qd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)d);
+        int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+        double* prob = (double*)malloc(sizeof(double) * (size_t)H * (size_t)n);
+        orc_query(q, q_dt, row, H, d, qd);
+        for (int64_t j = 0; j < n; ++j) pos[j] = j;
+        orc_attend(qd, H, d, sm_scale, k, v, k_scale, v_scale, kv_dt, b, n_ctx, pos, n,
+                   out + (size_t)r * H * d, lse + (size_t)r * H, prob, 1);
+        /* score_j = sum over heads, heads summed in order */
+        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += prob[(size_t)h * n + j];
+            sc[j] = acc;
+        }
+        if (scores) {
+            double* dst = scores + (size_t)r * (size_t)n_ctx;
+            for (int64_t j = 0; j < n_ctx; ++j) dst[j] = (j < n) ? sc[j] : -1.0;
+        }
+        if (idx || kth) {
+            int32_t* dst = idx ? idx + (size_t)r * (size_t)S : NULL;
+            int64_t nw = (p + 1 < window) ? p + 1 : window;
+            if (dst)
+                for (int t = 0; t < window; ++t) dst[t] = (t < nw) ? (int32_t)(p - nw + 1 + t) : -1;
+            int64_t n_cand = p - window + 1;
+            if (n_cand < 0) n_cand = 0;
+            int64_t take = n_cand < k_global ? n_cand : k_global;
+            orc_cand* cand = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(n_cand > 0 ? n_cand : 1));
+            for (int64_t j = 0; j < n_cand; ++j) {
+                cand[j].s = sc[j];
+                cand[j].j = j;
+            }
+            qsort(cand, (size_t)n_cand, sizeof(orc_cand), orc_cand_cmp);
+            if (kth) kth[r] = take > 0 ? cand[take - 1].s : -1.0;
+            if (dst) {
+                int32_t* g = dst + window;
+                for (int64_t t = 0; t < take; ++t) g[t] = (int32_t)cand[t].j;
+                qsort(g, (size_t)take, sizeof(int32_t), orc_i32_cmp);
+                for (int64_t t = take; t < k_global; ++t) g[t] = -1;
+            }
+            free(cand);
+        }
+        free(sc);
+        free(prob);
+        free(pos);
+        free(qd);
+    }
+    return 0;
+}
+
+/*
+ * Sparse attention (KV Reuse): query rows rows[] of q ([B][n_q][H][d]) attend
+ * to the positions of their index row idx[r][0..n_sel) (entries < 0 skipped).
+ * idx is indexed by r (position in rows[]), not by the flat row id.
+ * An empty set gives O = 0 and LSE = -inf. Returns 0, or 1 on invalid input.
+ */
+int orc_sparse(const void* q, int q_dt, const void* k, const void* v, const float* k_scale,
+               const float* v_scale, int kv_dt, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+               const int32_t* idx, int n_sel, double sm_scale, const int64_t* rows, int64_t n_rows,
+               double* out, double* lse) {
+    if (orc_check_common(q_dt, kv_dt, B, n_q, n_ctx, H, d) || n_sel < 0) return 1;
+    if (n_sel > 65536) return 1;
+    if (kv_dt == ORC_FP8 && (!k_scale || !v_scale)) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        if (rows[r] < 0 || rows[r] >= (int64_t)B * n_q) return 1;
+        for (int t = 0; t < n_sel; ++t)
+            if (idx[(size_t)r * n_sel + t] >= n_ctx) return 1;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t row = rows[r], b = row / n_q;
+        double* qd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)d);
+        int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_sel > 0 ? n_sel : 1));
+        int64_t n = 0;
+        orc_query(q, q_dt, row, H, d, qd);
+        for (int t = 0; t < n_sel; ++t) {
+            int32_t j = idx[(size_t)r * n_sel + t];
+            if (j >= 0) pos[n++] = j;
+        }
+        double* o = out + (size_t)r * H * d;
+        double* l = lse + (size_t)r * H;
+        if (n == 0) {
+            for (int t = 0; t < H * d; ++t) o[t] = 0.0;
+            for (int h = 0; h < H; ++h) l[h] = -INFINITY;
+        } else {
+            orc_attend(qd, H, d, sm_scale, k, v, k_scale, v_scale, kv_dt, b, n_ctx, pos, n, o, l,
+                       NULL, 0);
+        }
+        free(pos);
+        free(qd);
+    }
+    return 0;
+}
+
+/*
+ * Top-k of a given fp32 score array: for every row r the first n_cand[r]
+ * entries of scores[r*stride ...] are ranked by (score descending, position
+ * ascending); the first min(k, n_cand[r]) positions are written ascending to
+ * out[r][0..k), padded with -1. Scores must not be NaN. Returns 0 or 1.
+ */
+int orc_select_scores_f32(const float* scores, int64_t n_rows, int64_t stride,
+                          const int64_t* n_cand, int k, int32_t* out) {
+    if (k < 0 || stride < 0) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (n_cand[r] < 0 || n_cand[r] > stride) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t n = n_cand[r];
+        orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(n > 0 ? n : 1));
+        for (int64_t j = 0; j < n; ++j) {
+            c[j].s = (double)scores[(size_t)r * (size_t)stride + (size_t)j];
+            c[j].j = j;
+        }
+        qsort(c, (size_t)n, sizeof(orc_cand), orc_cand_cmp);
+        int64_t take = n < k ? n : k;
+        int32_t* g = out + (size_t)r * (size_t)k;
+        for (int64_t t = 0; t < take; ++t) g[t] = (int32_t)c[t].j;
+        qsort(g, (size_t)take, sizeof(int32_t), orc_i32_cmp);
+        for (int64_t t = take; t < k; ++t) g[t] = -1;
+        free(c);
+    }
+    return 0;
+}
+
+int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
