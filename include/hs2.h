@@ -1,0 +1,179 @@
+/*
+ * hs2.h -- C ABI of the HySparse2 attention hot path for AMD MI355X (gfx950).
+ *
+ * The method (HySparse2 page, onedev.kr/papers/146):
+ *  - section "어떻게 동작하나" (KV Reuse): inside each hybrid block the sparse
+ *    layers reuse the full-attention layer's KV cache and its selected indices,
+ *    each with its own queries;
+ *  - section "무엇과 다른가": selection is per token, not per block; the most
+ *    recent tokens (a sliding window) are always selected first, then the
+ *    highest-scoring tokens outside that window; the full layer's exact
+ *    attention scores are the indexer (no separate indexer module);
+ *  - section "어떻게 쓰나": MQA (one K/V head), NoPE for the full and sparse
+ *    layers, 128 forced local tokens and 1,024 global tokens;
+ *  - section "전제와 한계": efficiency is quoted with an FP8 KV cache.
+ * The IndexCache page, section 3 ("표기법"), defines the per-query top-k set
+ * T_t = Top-k(I_t) and the aggregated attention distribution as the softmax
+ * weights averaged over heads.
+ *
+ * What the library computes, for a query token at position p with heads h:
+ *   s_hj    = sm_scale * <q_h, k_j>                 j = 0..p  (causal, no RoPE)
+ *   LSE_h   = ln sum_{j<=p} exp(s_hj)
+ *   O_h     = sum_{j<=p} exp(s_hj - LSE_h) v_j
+ *   score_j = sum_h exp(s_hj - LSE_h)               (H times the head mean)
+ *   window  = positions max(0, p-window+1) .. p
+ *   global  = the min(k_global, p-window+1) positions j <= p-window with the
+ *             largest score_j; equal scores go to the lower position.
+ * An index row has window + k_global int32 entries: the window ascending,
+ * padded with -1 up to `window` entries, then the global set ascending,
+ * padded with -1 up to `k_global` entries. A sparse layer attends, with its
+ * own queries, to the positions in an index row (entries < 0 are skipped).
+ *
+ * Conventions shared by every entry point:
+ *  - Every array pointer is a DEVICE pointer, allocated and owned by the
+ *    caller; the library never allocates, frees or keeps a pointer past the
+ *    call. Buffers must stay alive until the stream has finished the work.
+ *  - Layouts are dense, row-major, in the order given. Data pointers must be
+ *    16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work; they never synchronise. The library is stateless: concurrent
+ *    calls on different streams are safe if they use distinct workspaces.
+ *  - All arguments are validated on the host before anything is enqueued: a
+ *    call that returns an error wrote nothing. HS2_ERR_HIP reports a failed
+ *    launch; device faults surface at the caller's next synchronisation.
+ *  - Element types: (q, kv) in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3)}.
+ *    FP8 is OCP E4M3FN; an FP8 cache row j carries an fp32 scale, and its
+ *    value is code_value * scale[j]. Outputs take the query type; LSE is fp32
+ *    natural log.
+ *  - Supported shapes: H in {4, 8, 16}, d in {64, 128}, 1 <= window,
+ *    0 <= k_global <= 2048, window + k_global <= 4096, n_ctx < 2^31,
+ *    0 <= q_pos0, q_pos0 + n_q <= n_ctx (query i sits at position q_pos0+i and
+ *    its own key/value are already in the cache). Others: HS2_ERR_UNSUPPORTED.
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS2_ABI_VERSION 1
+
+typedef enum {
+    HS2_OK = 0,
+    HS2_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or range     */
+    HS2_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype pair, H, d)   */
+    HS2_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
+    HS2_ERR_HIP = 4           /* a HIP launch or runtime call failed            */
+} hs2_status;
+
+typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3 = 2 } hs2_dtype;
+
+typedef enum {
+    HS2_OP_FULL_ATTN_SELECT = 0,
+    HS2_OP_DECODE_STEP = 1,
+    HS2_OP_SPARSE_ATTN = 2,
+    HS2_OP_SELECT_TOPK = 3
+} hs2_op;
+
+/* HS2_ABI_VERSION of the built library. */
+int hs2_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* hs2_status_string(int status);
+
+/*
+ * Workspace bytes an op needs for the given shape (0 if none, SIZE_MAX if the
+ * arguments are invalid). For HS2_OP_SELECT_TOPK pass B = rows, n_ctx = row
+ * length and k_global = k; the other arguments are ignored. Pure host code.
+ */
+size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int d, int window,
+                          int k_global, int kv_dtype);
+
+/*
+ * Full-attention layer of a hybrid block, with token selection
+ * (HySparse2 page, "무엇과 다른가" and "어떻게 쓰나"; prefill or chunked
+ * prefill: n_q query tokens per sequence at positions q_pos0 .. q_pos0+n_q-1).
+ *   q        [B][n_q][H][d]        q_dtype
+ *   k, v     [B][n_ctx][d]         kv_dtype
+ *   k_scale, v_scale [B][n_ctx]    fp32, required iff kv_dtype == FP8, else NULL
+ *   out      [B][n_q][H][d]        q_dtype       attention output O
+ *   lse      [B][n_q][H]           fp32          LSE (natural log)
+ *   indices  [B][n_q][window+k_global] int32     index rows (layout above)
+ *   workspace >= hs2_workspace_size(HS2_OP_FULL_ATTN_SELECT, ...) bytes
+ * Scores are computed on the fly and never stored as an n_q x n_ctx matrix.
+ */
+int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* v,
+                         const float* k_scale, const float* v_scale, int kv_dtype, int B,
+                         int64_t n_q, int64_t q_pos0, int64_t n_ctx, int H, int d, int window,
+                         int k_global, float sm_scale, void* out, float* lse, int32_t* indices,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * n_layers sparse layers reusing one index set and the full layer's KV cache
+ * (KV Reuse, HySparse2 page, "어떻게 동작하나"). Layer l attends with its own
+ * queries q[l] to the positions of indices; the layers are launched one after
+ * the other on `stream`.
+ *   q        [n_layers][B][n_q][H][d]   q_dtype
+ *   k, v, k_scale, v_scale              as for hs2_full_attn_select
+ *   indices  [B][n_q][n_sel]  int32     entries in [-1, n_ctx); -1 = empty
+ *   out      [n_layers][B][n_q][H][d]   q_dtype
+ *   lse      [n_layers][B][n_q][H]      fp32, may be NULL (not written);
+ *                                       a row with no valid index gets O = 0
+ *                                       and LSE = -inf
+ *   workspace >= hs2_workspace_size(HS2_OP_SPARSE_ATTN, B, n_q, n_ctx, H, d,
+ *                n_sel, 0, kv_dtype) bytes (the window argument carries n_sel)
+ * 1 <= n_sel <= 4096. Index values are not range-checked on the host; an
+ * out-of-range entry is undefined behaviour.
+ */
+int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                    const float* k_scale, const float* v_scale, int kv_dtype, int B, int64_t n_q,
+                    int64_t n_ctx, int H, int d, const int32_t* indices, int n_sel,
+                    float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * One decode step of a hybrid block: for every sequence the newest token
+ * (position n_ctx-1, already in the cache) runs the full layer with
+ * selection, then n_sparse sparse layers reuse the indices.
+ *   q_full   [B][H][d]                 q_dtype
+ *   q_sparse [n_sparse][B][H][d]       q_dtype (NULL iff n_sparse == 0)
+ *   out_full [B][H][d], lse_full [B][H] fp32
+ *   out_sparse [n_sparse][B][H][d]     (NULL iff n_sparse == 0)
+ *   lse_sparse [n_sparse][B][H] fp32   may be NULL
+ *   indices  [B][window+k_global]      int32
+ *   scores   [B][n_ctx] fp32           may be NULL; else score_j for every j
+ *   workspace >= hs2_workspace_size(HS2_OP_DECODE_STEP, B, 1, n_ctx, H, d,
+ *                window, k_global, kv_dtype) bytes
+ */
+int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n_sparse,
+                    const void* k, const void* v, const float* k_scale, const float* v_scale,
+                    int kv_dtype, int B, int64_t n_ctx, int H, int d, int window, int k_global,
+                    float sm_scale, void* out_full, float* lse_full, void* out_sparse,
+                    float* lse_sparse, int32_t* indices, float* scores, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * Top-k of given scores (the selection rule of the IndexCache page, section 3,
+ * "표기법", T = Top-k(I), with this library's tie rule): for each row r, the
+ * first n_cand[r] entries of scores[r][0..row_len) are ranked by (score
+ * descending, position ascending) and the first min(k, n_cand[r]) positions
+ * are written ascending to out[r][0..k), padded with -1.
+ *   scores  [rows][row_len] fp32, finite and >= 0 (+0 and -0 rank equal)
+ *   n_cand  [rows] int32 in [0, row_len], or NULL (= row_len for every row)
+ *   out     [rows][k] int32
+ *   workspace >= hs2_workspace_size(HS2_OP_SELECT_TOPK, rows, 0, row_len, 0,
+ *                0, 0, k, 0) bytes
+ * 1 <= k <= 2048.
+ */
+int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const int32_t* n_cand,
+                    int k, int32_t* out, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H */

@@ -1,0 +1,121 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/hs2.h declares, sizes workspaces and rejects bad arguments
+before it touches any device memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_top_amd as hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned address that is never dereferenced
+MIS = 0x10004           # misaligned
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hs2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 7
+    L = hs2.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert hs2.abi_version() == 1
+    assert hs2.status_string(2) == "unsupported dtype or shape"
+
+
+def test_workspace_sizes():
+    ws = hs2.workspace_size
+    d3 = ws(hs2.OP_DECODE_STEP, 64, 1, 131072, 16, 128, 128, 1024, hs2.HS2_BF16)
+    assert d3 >= 64 * 131072 * 16 * 4            # fp32 logits of every key and head
+    assert ws(hs2.OP_SELECT_TOPK, 4, 0, 1000, 0, 0, 0, 16, 0) > 0
+    assert ws(hs2.OP_SPARSE_ATTN, 1, 4096, 5000, 16, 128, 1152, 0, hs2.HS2_BF16) == 0   # no split
+    assert ws(hs2.OP_SPARSE_ATTN, 64, 1, 5000, 16, 128, 1152, 0, hs2.HS2_BF16) > 0
+    with pytest.raises(ValueError):
+        ws(7, 1, 1, 1, 16, 128, 128, 1024, 1)
+
+
+def _full(**kw):
+    a = dict(q=FAKE, qdt=1, k=FAKE, v=FAKE, ks=None, vs=None, kvdt=1, B=1, n_q=10, q_pos0=0, n_ctx=10, H=16,
+             d=128, W=128, K=1024, scale=0.1, out=FAKE, lse=FAKE, idx=FAKE, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return hs2.lib().hs2_full_attn_select(*a.values())
+
+
+def test_full_attn_select_validation():
+    E = hs2
+    assert _full(q=None) == E.HS2_ERR_INVALID_ARG
+    assert _full(q=MIS) == E.HS2_ERR_INVALID_ARG
+    assert _full(n_q=11) == E.HS2_ERR_INVALID_ARG           # q_pos0 + n_q > n_ctx
+    assert _full(q_pos0=-1) == E.HS2_ERR_INVALID_ARG
+    assert _full(W=0) == E.HS2_ERR_INVALID_ARG
+    assert _full(K=-1) == E.HS2_ERR_INVALID_ARG
+    assert _full(scale=0.0) == E.HS2_ERR_INVALID_ARG
+    assert _full(scale=float("nan")) == E.HS2_ERR_INVALID_ARG
+    assert _full(kvdt=2) == E.HS2_ERR_INVALID_ARG           # fp8 without scales
+    assert _full(ks=FAKE, vs=FAKE) == E.HS2_ERR_INVALID_ARG  # scales with a bf16 cache
+    assert _full(kvdt=7) == E.HS2_ERR_INVALID_ARG
+    assert _full(n_ctx=2 ** 31, n_q=1, q_pos0=0) == E.HS2_ERR_INVALID_ARG
+    assert _full(H=12) == E.HS2_ERR_UNSUPPORTED
+    assert _full(d=96) == E.HS2_ERR_UNSUPPORTED
+    assert _full(qdt=0) == E.HS2_ERR_UNSUPPORTED            # f32 queries with a bf16 cache
+    assert _full(K=4096) == E.HS2_ERR_UNSUPPORTED
+    assert _full() == E.HS2_ERR_WORKSPACE                   # valid, but no workspace
+    need = hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, 1, 10, 10, 16, 128, 128, 1024, 1)
+    assert _full(ws=FAKE, wsb=need - 1) == E.HS2_ERR_WORKSPACE
+    assert _full(ws=MIS, wsb=need) == E.HS2_ERR_WORKSPACE
+
+
+def _decode(**kw):
+    a = dict(qf=FAKE, qs=FAKE, qdt=1, L=2, k=FAKE, v=FAKE, ks=None, vs=None, kvdt=1, B=2, n_ctx=1000, H=16,
+             d=128, W=128, K=1024, scale=0.1, of=FAKE, lf=FAKE, os_=FAKE, ls=None, idx=FAKE, sc=None, ws=None,
+             wsb=0, st=None)
+    a.update(kw)
+    return hs2.lib().hs2_decode_step(*a.values())
+
+
+def test_decode_step_validation():
+    E = hs2
+    assert _decode(qs=None) == E.HS2_ERR_INVALID_ARG         # n_sparse > 0 needs sparse queries
+    assert _decode(L=0) == E.HS2_ERR_INVALID_ARG             # ... and none when n_sparse == 0
+    assert _decode(L=0, qs=None, os_=None) == E.HS2_ERR_WORKSPACE
+    assert _decode(idx=None) == E.HS2_ERR_INVALID_ARG
+    assert _decode(sc=MIS) == E.HS2_ERR_INVALID_ARG
+    assert _decode(B=0) == E.HS2_ERR_INVALID_ARG
+    assert _decode(kvdt=2, ks=FAKE, vs=FAKE) == E.HS2_ERR_WORKSPACE
+    assert _decode(kvdt=2, ks=FAKE, vs=FAKE, qdt=0) == E.HS2_ERR_UNSUPPORTED
+    assert _decode() == E.HS2_ERR_WORKSPACE
+
+
+def test_sparse_and_select_validation():
+    L = hs2.lib()
+    # q, qdt, n_layers, k, v, ks, vs, kvdt, B, n_q, n_ctx, H, d, idx, n_sel, scale, out, lse, ws, wsb, stream
+    args = [FAKE, 1, 2, FAKE, FAKE, None, None, 1, 64, 1, 5000, 16, 128, FAKE, 1152, 0.1, FAKE, None, None, 0,
+            None]
+    assert L.hs2_sparse_attn(*args) == hs2.HS2_ERR_WORKSPACE
+    bad = list(args)
+    bad[14] = 0
+    assert L.hs2_sparse_attn(*bad) == hs2.HS2_ERR_INVALID_ARG
+    bad = list(args)
+    bad[14] = 5000
+    assert L.hs2_sparse_attn(*bad) == hs2.HS2_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[13] = None
+    assert L.hs2_sparse_attn(*bad) == hs2.HS2_ERR_INVALID_ARG
+    # scores, rows, row_len, n_cand, k, out, ws, wsb, stream
+    assert L.hs2_select_topk(FAKE, 4, 100, None, 8, FAKE, None, 0, None) == hs2.HS2_ERR_WORKSPACE
+    assert L.hs2_select_topk(FAKE, 4, 100, None, 0, FAKE, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+    assert L.hs2_select_topk(FAKE, 4, 100, None, 4096, FAKE, None, 0, None) == hs2.HS2_ERR_UNSUPPORTED
+    assert L.hs2_select_topk(None, 4, 100, None, 8, FAKE, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        hs2.select_topk(torch.zeros(2, 10), 3)

@@ -1,0 +1,457 @@
+// Host layer of the C ABI declared in include/hs2.h: argument validation,
+// workspace layout and the sequence of kernel launches for each entry point.
+// Validation touches no HIP API, so every error path runs without a GPU.
+#include "hs2.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "hs2_internal.h"
+
+namespace {
+
+using namespace hs2;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over a caller-provided workspace (or a null base to size it).
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t bytes) {
+        T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+        used += align_up(bytes);
+        return p;
+    }
+};
+
+bool dtype_pair_ok(int q_dtype, int kv_dtype) {
+    return (q_dtype == HS2_F32 && kv_dtype == HS2_F32) || (q_dtype == HS2_BF16 && kv_dtype == HS2_BF16) ||
+           (q_dtype == HS2_BF16 && kv_dtype == HS2_FP8_E4M3);
+}
+bool dtype_known(int dt) { return dt == HS2_F32 || dt == HS2_BF16 || dt == HS2_FP8_E4M3; }
+bool shape_supported(int H, int d) { return (H == 4 || H == 8 || H == 16) && (d == 64 || d == 128); }
+size_t esize(int dt) { return dt == HS2_F32 ? 4 : dt == HS2_BF16 ? 2 : 1; }
+
+// Common checks of the (q, kv) arrays and shapes. Returns HS2_OK or an error.
+int check_common(int q_dtype, int kv_dtype, const void* k, const void* v, const float* ks, const float* vs, int B,
+                 int64_t n_ctx, int H, int d, float sm_scale) {
+    if (!dtype_known(q_dtype) || !dtype_known(kv_dtype)) return HS2_ERR_INVALID_ARG;
+    if (B <= 0 || n_ctx <= 0 || H <= 0 || d <= 0) return HS2_ERR_INVALID_ARG;
+    if (n_ctx >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return HS2_ERR_INVALID_ARG;
+    if (!k || !v) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(ks) || !aligned16(vs)) return HS2_ERR_INVALID_ARG;
+    if (kv_dtype == HS2_FP8_E4M3) {
+        if (!ks || !vs) return HS2_ERR_INVALID_ARG;
+    } else if (ks || vs) {
+        return HS2_ERR_INVALID_ARG;
+    }
+    if (!dtype_pair_ok(q_dtype, kv_dtype) || !shape_supported(H, d)) return HS2_ERR_UNSUPPORTED;
+    return HS2_OK;
+}
+
+int check_select_shape(int window, int k_global) {
+    if (window < 1 || k_global < 0) return HS2_ERR_INVALID_ARG;
+    if (k_global > 2048 || window + k_global > 4096) return HS2_ERR_UNSUPPORTED;
+    return HS2_OK;
+}
+
+// ---- decode layout
+constexpr int kTile = 128;
+int decode_rows_per_split(int B, int64_t n_ctx) {
+    // aim for >= 2048 workgroups over the batch, 1024..8192 keys each
+    int64_t target = (B * n_ctx + 2047) / 2048;
+    int64_t rps = (target + kTile - 1) / kTile * kTile;
+    if (rps < 1024) rps = 1024;
+    if (rps > 8192) rps = 8192;
+    return (int)rps;
+}
+int decode_splits(int B, int64_t n_ctx) {
+    const int rps = decode_rows_per_split(B, n_ctx);
+    return (int)((n_ctx + rps - 1) / rps);
+}
+// sparse layers: split a token's index row over workgroups when there are few tokens
+int sparse_splits(int64_t n_tok, int n_sel) {
+    if (n_tok >= 1024) return 1;
+    return (n_sel + kTile - 1) / kTile;
+}
+
+struct DecodeWs {
+    float *logits, *part, *lse2, *scores, *spart;
+    uint32_t *hist, *cand_count;
+    uint64_t* cand;
+    size_t bytes;
+};
+DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, int k_global) {
+    Carver c(base);
+    DecodeWs w;
+    const int ns = decode_splits(B, n_ctx);
+    w.logits = c.take<float>(sizeof(float) * (size_t)B * n_ctx * H);
+    w.part = ns > 1 ? c.take<float>(sizeof(float) * (size_t)B * ns * H * (d + 2)) : nullptr;
+    w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
+    w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
+    w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * kHistBins);
+    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B);
+    w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
+    const int ss = sparse_splits(B, window + k_global);
+    w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)B * ss * H * (d + 2)) : nullptr;
+    w.bytes = c.used;
+    return w;
+}
+
+struct SparseWs {
+    float* part;
+    size_t bytes;
+};
+SparseWs sparse_ws(void* base, int64_t n_tok, int n_sel, int H, int d) {
+    Carver c(base);
+    SparseWs w;
+    const int ss = sparse_splits(n_tok, n_sel);
+    w.part = ss > 1 ? c.take<float>(sizeof(float) * (size_t)n_tok * ss * H * (d + 2)) : nullptr;
+    w.bytes = c.used;
+    return w;
+}
+
+struct SelectWs {
+    uint32_t *hist, *cand_count;
+    uint64_t* cand;
+    size_t bytes;
+};
+SelectWs select_ws(void* base, int64_t rows) {
+    Carver c(base);
+    SelectWs w;
+    w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * kHistBins);
+    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows);
+    w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)rows * kCandCap);
+    w.bytes = c.used;
+    return w;
+}
+
+constexpr int kPrefillCandCap = 4096;
+constexpr int kVtPad = 64;
+struct PrefillWs {
+    void* vt;
+    uint16_t* kc;
+    float* lse2;
+    uint64_t* cand;
+    uint32_t* cand_count;
+    int64_t n_ctx_pad;
+    size_t bytes;
+};
+PrefillWs prefill_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d, int kv_dtype) {
+    Carver c(base);
+    PrefillWs w;
+    w.n_ctx_pad = (n_ctx + kVtPad - 1) / kVtPad * kVtPad;
+    const size_t vt_el = kv_dtype == HS2_F32 ? 4 : 2;
+    w.vt = c.take<void>(vt_el * (size_t)B * d * w.n_ctx_pad);
+    w.kc = kv_dtype == HS2_FP8_E4M3 ? c.take<uint16_t>(2 * (size_t)B * n_ctx * d) : nullptr;
+    w.lse2 = c.take<float>(sizeof(float) * (size_t)B * n_q * H);
+    w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * n_q * kPrefillCandCap);
+    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * n_q);
+    w.bytes = c.used;
+    return w;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_ERR_HIP; }
+#define HS2_TRY(expr)                                   \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess) return HS2_ERR_HIP;       \
+    } while (0)
+
+constexpr float kLog2eF = 1.4426950408889634f;
+
+// Enqueue n_layers sparse layers (shared by hs2_sparse_attn and hs2_decode_step).
+int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* ks,
+               const float* vs, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+               const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, float* part,
+               hipStream_t st) {
+    const int64_t n_tok = (int64_t)B * n_q;
+    const int ns = sparse_splits(n_tok, n_sel);
+    const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
+    for (int l = 0; l < n_layers; ++l) {
+        RowsArgs a{};
+        a.q = static_cast<const char*>(q) + qstride * l;
+        a.k = k;
+        a.v = v;
+        a.ks = ks;
+        a.vs = vs;
+        a.idx = indices;
+        a.n_ctx = n_ctx;
+        a.n_rows = n_sel;
+        a.n_tok = (int)n_tok;
+        a.n_q = (int)n_q;
+        a.n_split = ns;
+        a.rows_per_split = ns > 1 ? kTile : ((n_sel + kTile - 1) / kTile) * kTile;
+        a.scale_log2 = sm_scale * kLog2eF;
+        void* o = static_cast<char*>(out) + qstride * l;
+        float* ls = lse ? lse + (size_t)n_tok * H * l : nullptr;
+        if (ns > 1) {
+            a.part = part;
+        } else {
+            a.out = o;
+            a.lse = ls;
+        }
+        HS2_TRY(launch_rows_attn(a, H, d, kv_dtype, true, false, st));
+        if (ns > 1) {
+            CombineArgs c{};
+            c.part = part;
+            c.n_tok = (int)n_tok;
+            c.n_split = ns;
+            c.out = o;
+            c.lse = ls;
+            HS2_TRY(launch_combine(c, H, d, q_dtype, st));
+        }
+    }
+    return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs2_abi_version(void) { return HS2_ABI_VERSION; }
+
+const char* hs2_status_string(int status) {
+    switch (status) {
+        case HS2_OK: return "ok";
+        case HS2_ERR_INVALID_ARG: return "invalid argument";
+        case HS2_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+        case HS2_ERR_WORKSPACE: return "workspace missing or too small";
+        case HS2_ERR_HIP: return "HIP launch or runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int d, int window, int k_global,
+                          int kv_dtype) {
+    if (B <= 0 || n_ctx <= 0) return SIZE_MAX;
+    switch (op) {
+        case HS2_OP_FULL_ATTN_SELECT:
+            if (n_q <= 0 || H <= 0 || d <= 0 || !dtype_known(kv_dtype)) return SIZE_MAX;
+            return prefill_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype).bytes;
+        case HS2_OP_DECODE_STEP:
+            if (H <= 0 || d <= 0 || window < 1 || k_global < 0) return SIZE_MAX;
+            return decode_ws(nullptr, B, n_ctx, H, d, window, k_global).bytes;
+        case HS2_OP_SPARSE_ATTN:
+            if (n_q <= 0 || H <= 0 || d <= 0 || window < 1) return SIZE_MAX;
+            return sparse_ws(nullptr, (int64_t)B * n_q, window, H, d).bytes;
+        case HS2_OP_SELECT_TOPK:
+            if (k_global < 1) return SIZE_MAX;
+            return select_ws(nullptr, B).bytes;
+        default: return SIZE_MAX;
+    }
+}
+
+int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* k_scale,
+                    const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+                    const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* workspace,
+                    size_t ws_bytes, void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    if (n_layers < 0 || n_q <= 0 || n_sel < 1 || n_sel > 4096) return n_sel > 4096 ? HS2_ERR_UNSUPPORTED
+                                                                                   : HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if (n_layers > 0 && (!q || !out || !indices)) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    const SparseWs need = sparse_ws(nullptr, (int64_t)B * n_q, n_sel, H, d);
+    if (need.bytes > 0 && (!workspace || ws_bytes < need.bytes || !aligned16(workspace))) return HS2_ERR_WORKSPACE;
+    if (n_layers == 0) return HS2_OK;
+    const SparseWs w = sparse_ws(workspace, (int64_t)B * n_q, n_sel, H, d);
+    return run_sparse(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, indices, n_sel,
+                      sm_scale, out, lse, w.part, static_cast<hipStream_t>(stream));
+}
+
+int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const int32_t* n_cand, int k, int32_t* out,
+                    void* workspace, size_t ws_bytes, void* stream) {
+    if (!scores || !out || rows < 1 || row_len < 1 || k < 1) return HS2_ERR_INVALID_ARG;
+    if (rows >= (int64_t(1) << 31) || row_len >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(scores) || !aligned16(out) || !aligned16(n_cand)) return HS2_ERR_INVALID_ARG;
+    if (k > 2048) return HS2_ERR_UNSUPPORTED;
+    const SelectWs need = select_ws(nullptr, rows);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const SelectWs w = select_ws(workspace, rows);
+    SelectArgs a{};
+    a.scores = scores;
+    a.rows = rows;
+    a.row_stride = row_len;
+    a.row_len = row_len;
+    a.n_cand = n_cand;
+    a.k = k;
+    a.hist = w.hist;
+    a.cand = w.cand;
+    a.cand_count = w.cand_count;
+    a.out = out;
+    a.out_stride = k;
+    a.out_offset = 0;
+    HS2_TRY(launch_fill_u32(w.hist, rows * kHistBins, 0u, s));
+    HS2_TRY(launch_fill_u32(w.cand_count, rows, 0u, s));
+    HS2_TRY(launch_select_hist(a, s));
+    HS2_TRY(launch_select_collect(a, s));
+    HS2_TRY(launch_select_final(a, s));
+    return HS2_OK;
+}
+
+int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n_sparse, const void* k,
+                    const void* v, const float* k_scale, const float* v_scale, int kv_dtype, int B, int64_t n_ctx,
+                    int H, int d, int window, int k_global, float sm_scale, void* out_full, float* lse_full,
+                    void* out_sparse, float* lse_sparse, int32_t* indices, float* scores, void* workspace,
+                    size_t ws_bytes, void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    int ss = check_select_shape(window, k_global);
+    if (ss == HS2_ERR_INVALID_ARG) return ss;
+    if (n_sparse < 0 || !q_full || !out_full || !lse_full || !indices) return HS2_ERR_INVALID_ARG;
+    if ((n_sparse > 0) != (q_sparse != nullptr) || (n_sparse > 0) != (out_sparse != nullptr))
+        return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q_full) || !aligned16(q_sparse) || !aligned16(out_full) || !aligned16(lse_full) ||
+        !aligned16(out_sparse) || !aligned16(lse_sparse) || !aligned16(indices) || !aligned16(scores))
+        return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    if (ss != HS2_OK) return ss;
+    const DecodeWs need = decode_ws(nullptr, B, n_ctx, H, d, window, k_global);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const DecodeWs w = decode_ws(workspace, B, n_ctx, H, d, window, k_global);
+    const int n_sel = window + k_global;
+
+    // 1. full layer, split over the cache: logits + partial (m, l, O)
+    const int ns = decode_splits(B, n_ctx);
+    RowsArgs a{};
+    a.q = q_full;
+    a.k = k;
+    a.v = v;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.n_ctx = n_ctx;
+    a.n_rows = n_ctx;
+    a.n_tok = B;
+    a.n_q = 1;
+    a.n_split = ns;
+    a.rows_per_split = decode_rows_per_split(B, n_ctx);
+    a.scale_log2 = sm_scale * kLog2eF;
+    a.logits = w.logits;
+    if (ns > 1) {
+        a.part = w.part;
+    } else {
+        a.out = out_full;
+        a.lse = lse_full;
+        a.lse2 = w.lse2;
+    }
+    HS2_TRY(launch_rows_attn(a, H, d, kv_dtype, false, true, s));
+    if (ns > 1) {
+        CombineArgs c{};
+        c.part = w.part;
+        c.n_tok = B;
+        c.n_split = ns;
+        c.out = out_full;
+        c.lse = lse_full;
+        c.lse2 = w.lse2;
+        HS2_TRY(launch_combine(c, H, d, q_dtype, s));
+    }
+    // 2. token scores + histogram of the candidates j <= n_ctx-1-window
+    const int64_t n_cand = n_ctx - window > 0 ? n_ctx - window : 0;
+    float* sc = scores ? scores : w.scores;
+    HS2_TRY(launch_fill_u32(w.hist, (int64_t)B * kHistBins, 0u, s));
+    HS2_TRY(launch_fill_u32(w.cand_count, B, 0u, s));
+    ScoreArgs sa{};
+    sa.logits = w.logits;
+    sa.lse2 = w.lse2;
+    sa.scores = sc;
+    sa.hist = w.hist;
+    sa.n_ctx = n_ctx;
+    sa.n_cand = n_cand;
+    sa.H = H;
+    HS2_TRY(launch_decode_score(sa, B, s));
+    // 3. window + top-k_global
+    if (k_global > 0) {
+        SelectArgs se{};
+        se.scores = sc;
+        se.rows = B;
+        se.row_stride = n_ctx;
+        se.row_len = n_cand;
+        se.k = k_global;
+        se.hist = w.hist;
+        se.cand = w.cand;
+        se.cand_count = w.cand_count;
+        se.out = indices;
+        se.out_stride = n_sel;
+        se.out_offset = window;
+        if (n_cand > 0) HS2_TRY(launch_select_collect(se, s));
+        HS2_TRY(launch_select_final_w(se, window, n_ctx - 1, s));
+    } else {
+        SelectArgs se{};
+        se.rows = B;
+        se.row_len = 0;
+        se.k = 0;
+        se.cand_count = w.cand_count;
+        se.out = indices;
+        se.out_stride = n_sel;
+        se.out_offset = window;
+        HS2_TRY(launch_select_final_w(se, window, n_ctx - 1, s));
+    }
+    // 4. sparse layers reuse the indices and the cache
+    if (n_sparse > 0)
+        return run_sparse(q_sparse, q_dtype, n_sparse, k, v, k_scale, v_scale, kv_dtype, B, 1, n_ctx, H, d, indices,
+                          n_sel, sm_scale, out_sparse, lse_sparse, w.spart, s);
+    return HS2_OK;
+}
+
+int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* v, const float* k_scale,
+                         const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t q_pos0, int64_t n_ctx,
+                         int H, int d, int window, int k_global, float sm_scale, void* out, float* lse,
+                         int32_t* indices, void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    int ss = check_select_shape(window, k_global);
+    if (ss == HS2_ERR_INVALID_ARG) return ss;
+    if (n_q <= 0 || q_pos0 < 0 || q_pos0 + n_q > n_ctx) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if (!q || !out || !lse || !indices) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    if (ss != HS2_OK) return ss;
+    const PrefillWs need = prefill_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const PrefillWs w = prefill_ws(workspace, B, n_q, n_ctx, H, d, kv_dtype);
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.kc = w.kc;
+    a.vt = w.vt;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.n_q = n_q;
+    a.q_pos0 = q_pos0;
+    a.n_ctx = n_ctx;
+    a.n_ctx_pad = w.n_ctx_pad;
+    a.B = B;
+    a.scale_log2 = sm_scale * kLog2eF;
+    a.out = out;
+    a.lse = lse;
+    a.lse2 = w.lse2;
+    a.window = window;
+    a.k_global = k_global;
+    a.cand = w.cand;
+    a.cand_count = w.cand_count;
+    a.cand_cap = kPrefillCandCap;
+    a.indices = indices;
+    HS2_TRY(launch_prep_kv(k, v, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s));
+    HS2_TRY(launch_attn_fwd(a, H, d, kv_dtype, s));
+    HS2_TRY(launch_fill_u32(w.cand_count, (int64_t)B * n_q, 0u, s));
+    HS2_TRY(launch_score_stream(a, H, d, kv_dtype, s));
+    HS2_TRY(launch_prefill_final(a, s));
+    return HS2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device helpers shared by the HIP kernels of the HySparse2 hot path (gfx950).
+//
+// MFMA lane layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16  A[32][16], B[16][32]: lane l holds row/col l%32,
+//                             k = 8*(l/32) .. +7; C lane l holds column l%32,
+//                             rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
+//   v_mfma_f32_32x32x2f32     same, with one k value per lane (k = l/32).
+//   v_mfma_f32_16x16x32_bf16  A[16][32], B[32][16]: lane l holds row/col l%16,
+//                             k = 8*(l/16) .. +7; C lane l holds column l%16,
+//                             rows 4*(l/16) + i, i = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Four OCP E4M3FN codes (one dword) -> four floats, exact (hardware convert).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    o[0] = lo[0];
+    o[1] = lo[1];
+    o[2] = hi[0];
+    o[3] = hi[1];
+}
+
+// Four E4M3 codes -> two dwords of packed bf16. Exact: an E4M3 value has at
+// most 4 significant bits and its exponent fits bf16, so the low 16 bits of
+// the float are zero and truncation loses nothing.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    u32x2 r;
+    r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+    r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// value of the lane l^32 (other half of the wave), via one permlane32 swap
+__device__ __forceinline__ float xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+// lanes l < 32 receive a_lo + a_hi(of lane l+32)... precisely: with a held in
+// every lane and b held in every lane, returns a[l] + a[l+32] in the low half
+// and b[l-32] + b[l] in the high half.
+__device__ __forceinline__ float halves_sum(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+// 64-bit ranking key of a (score, position) pair: larger key = better.
+// Scores are >= 0, so their IEEE bits order like the values (-0 maps to +0);
+// the low word is the complemented position, so among equal scores the lower
+// position has the larger key.
+__device__ __forceinline__ uint64_t rank_key(float s, uint32_t pos) {
+    uint32_t b = __float_as_uint(s) & 0x7FFFFFFFu;
+    return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+}
+__device__ __forceinline__ uint32_t key_pos(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+}  // namespace hs2

@@ -1,0 +1,112 @@
+// Launch interface between the host layer (hs2_api.cpp) and the kernel files.
+// Plain structs of device pointers and sizes; every launcher enqueues on the
+// given stream and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+// rows_attn_kernel: one query token attends to a list of K/V rows.
+struct RowsArgs {
+    const void* q;          // [n_tok][H][D] query (f32 when kv is f32, else bf16)
+    const void* k;          // [B][n_ctx][D]
+    const void* v;
+    const float* ks;        // [B][n_ctx] FP8 scales (else unused)
+    const float* vs;
+    const int32_t* idx;     // gather: [n_tok][n_rows] positions, -1 = empty
+    int64_t n_ctx;
+    int64_t n_rows;         // rows per token (gather: n_sel; contiguous: n_ctx)
+    int n_tok;              // query tokens (grid.y)
+    int n_q;                // tokens per sequence (token t reads sequence t / n_q)
+    int rows_per_split;     // rows per workgroup (multiple of the 128-row tile)
+    int n_split;            // workgroups per token (grid.x)
+    float scale_log2;       // sm_scale * log2(e)
+    float* logits;          // contiguous + store: [B][n_ctx][H] base-2 logits
+    float* part;            // n_split > 1: [n_tok][n_split][H*(D+2)] = m[H], l[H], O[H][D]
+    void* out;              // n_split == 1: [n_tok][H][D] in the query type
+    float* lse;             // n_split == 1: [n_tok][H] natural log, nullable
+    float* lse2;            // n_split == 1: [n_tok][H] base 2, nullable
+};
+
+struct CombineArgs {
+    const float* part;      // [n_tok][n_split][H*(D+2)]
+    int n_tok, n_split;
+    void* out;              // [n_tok][H][D]
+    float* lse;             // nullable, natural log
+    float* lse2;            // nullable, base 2
+};
+
+hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather, bool store_logits,
+                            hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_t st);
+
+// ---- selection ------------------------------------------------------------
+constexpr int kHistBins = 4096;      // top 12 bits of a non-negative fp32 (bits 30..19)
+constexpr int kCandCap = 8192;       // candidates one workgroup sorts in LDS
+
+// decode: score_j = sum_h exp2(logit2[j][h] - lse2[h]) for j < n_ctx; writes
+// scores [B][n_ctx] and the histogram of candidates j < n_cand.
+struct ScoreArgs {
+    const float* logits;    // [B][n_ctx][H] base 2
+    const float* lse2;      // [B][H]
+    float* scores;          // [B][n_ctx]
+    uint32_t* hist;         // [B][kHistBins], zeroed by the caller
+    int64_t n_ctx;
+    int64_t n_cand;         // candidates per row (n_ctx - window, >= 0)
+    int H;
+};
+hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st);
+
+// Top-k of rows of non-negative fp32 scores.
+struct SelectArgs {
+    const float* scores;    // [rows][row_stride]
+    int64_t rows;
+    int64_t row_stride;
+    int64_t row_len;        // candidates per row unless n_cand != nullptr
+    const int32_t* n_cand;  // [rows] or nullptr
+    int k;
+    uint32_t* hist;         // [rows][kHistBins]
+    uint64_t* cand;         // [rows][kCandCap]
+    uint32_t* cand_count;   // [rows]
+    int32_t* out;           // [rows][out_stride]
+    int64_t out_stride;
+    int out_offset;         // first column written in each out row
+};
+// hist must be zeroed; fills it from the scores
+hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);
+// cand_count must be zeroed; hist must be complete
+hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st);
+hipError_t launch_select_final(const SelectArgs& a, hipStream_t st);
+
+// also writes the forced window of every row (all rows at position p_last) when window > 0
+hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+
+// ---- prefill ----------------------------------------------------------------
+struct PrefillArgs {
+    const void* q;          // [B][n_q][H][D]
+    const void* k;          // [B][n_ctx][D] (bf16 or f32; fp8 is pre-converted into kc)
+    const uint16_t* kc;     // FP8 only: [B][n_ctx][D] bf16 values of the codes
+    const void* vt;         // [B][D][n_ctx_pad] transposed V (bf16 or f32)
+    const float* ks;        // [B][n_ctx]
+    const float* vs;
+    int64_t n_q, q_pos0, n_ctx, n_ctx_pad;
+    int B;
+    float scale_log2;
+    void* out;              // [B][n_q][H][D]
+    float* lse;             // [B][n_q][H] natural log
+    float* lse2;            // [B][n_q][H] base 2 (workspace)
+    int window, k_global;
+    uint64_t* cand;         // [B*n_q][cand_cap] candidate keys
+    uint32_t* cand_count;   // [B*n_q]
+    int cand_cap;
+    int32_t* indices;       // [B][n_q][window + k_global]
+};
+hipError_t launch_prep_kv(const void* k, const void* v, int kv, int B, int64_t n_ctx, int64_t n_ctx_pad, int D,
+                          uint16_t* kc, void* vt, hipStream_t st);
+hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+hipError_t launch_prefill_final(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace hs2

@@ -1,0 +1,374 @@
+// Attention of single query tokens over a list of KV rows, on MFMA.
+//
+// One kernel serves two steps of the HySparse2 path:
+//  * decode full layer (HySparse2 page, "무엇과 다른가": the full layer's exact
+//    attention is computed for the newest token over the whole cache): the rows
+//    are a contiguous key range of one sequence, split over many workgroups
+//    (split-K); each split also stores its base-2 logits so the token scores
+//    can be formed once the global LSE is known;
+//  * sparse layers (KV Reuse, "어떻게 동작하나"): the rows are the positions of
+//    a token's index row, gathered from the shared cache.
+// MQA has one K/V head, so a K/V row staged in LDS serves all H query heads:
+// S^T = K Q^T runs on v_mfma 16x16 with the 16 key rows on M and the heads on N,
+// and O^T = V^T P^T reuses the same V rows for every head.
+//
+// A workgroup is 4 waves; a tile is 128 rows (32 per wave). Each wave keeps its
+// own running max / sum / output per head; the 4 waves are merged at the end,
+// into a partial record (m, l, O) per split or straight into the output.
+#include "hs2_device.h"
+#include "hs2_internal.h"
+
+namespace hs2 {
+
+constexpr int kRowsTile = 128;
+constexpr int kRowsThreads = 256;
+
+template <int KV>
+struct RowsTypes;
+template <>
+struct RowsTypes<DT_F32> {
+    using L = float;  // LDS element
+    static constexpr int VPL = 1, KD = 4, ESZ = 4, PAD = 4;
+};
+template <>
+struct RowsTypes<DT_BF16> {
+    using L = uint16_t;
+    static constexpr int VPL = 8, KD = 32, ESZ = 2, PAD = 8;
+};
+template <>
+struct RowsTypes<DT_FP8> {
+    using L = uint16_t;
+    static constexpr int VPL = 8, KD = 32, ESZ = 1, PAD = 8;
+};
+
+// 16x16 MFMA step of S^T = K Q^T: a = key row fragment, b = query fragment
+__device__ __forceinline__ f32x4 mfma16(const float* a, const float* b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(*a, *b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const uint16_t* a, const uint16_t* b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(a)),
+                                                   as_bf16x8(*reinterpret_cast<const u32x4*>(b)), c, 0, 0, 0);
+}
+
+// Key row (16 B aligned chunks) of one tile row into LDS; converts FP8 to bf16.
+template <int KV, int D>
+__device__ __forceinline__ void stage_chunk(typename RowsTypes<KV>::L* dst, const void* src_row, int cc, bool ok) {
+    if constexpr (KV == DT_FP8) {
+        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src_row) + cc * 16)
+                     : u32x4{0, 0, 0, 0};
+        u32x2 a = fp8x4_to_bf16x4(w[0]), b = fp8x4_to_bf16x4(w[1]);
+        u32x2 c = fp8x4_to_bf16x4(w[2]), e = fp8x4_to_bf16x4(w[3]);
+        u32x4* o = reinterpret_cast<u32x4*>(dst + cc * 16);
+        o[0] = u32x4{a[0], a[1], b[0], b[1]};
+        o[1] = u32x4{c[0], c[1], e[0], e[1]};
+    } else {
+        constexpr int EPC = 16 / RowsTypes<KV>::ESZ;  // elements per 16-byte chunk
+        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src_row) + cc * 16)
+                     : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(dst + cc * EPC) = w;
+    }
+}
+
+template <int H, int D, int KV, bool GATHER, bool STORE_LOGITS>
+__global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
+    using T = RowsTypes<KV>;
+    using LT = typename T::L;
+    constexpr int VPL = T::VPL, KD = T::KD, PAD = T::PAD;
+    constexpr int LD = D + PAD;               // LDS row stride (elements)
+    constexpr int RB = D * T::ESZ;            // global bytes per row
+    constexpr int CPR = RB / 16;              // 16-byte chunks per row
+    constexpr int CPT = kRowsTile * CPR / kRowsThreads;
+    constexpr int NS = D / KD;                // MFMA k-steps over d
+    constexpr int NDT = D / 16;               // d tiles of the output
+    static_assert(H <= 16, "heads map to the 16 MFMA columns");
+    static_assert((kRowsTile * CPR) % kRowsThreads == 0, "tile chunks");
+
+    __shared__ __attribute__((aligned(16))) LT k_lds[kRowsTile * LD];
+    __shared__ __attribute__((aligned(16))) LT v_lds[kRowsTile * LD];
+    __shared__ int pos_lds[kRowsTile];
+    __shared__ float ksc_lds[kRowsTile];
+    __shared__ float vsc_lds[kRowsTile];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hl = lane & 15, g = lane >> 4;
+    const int tok = blockIdx.y, split = blockIdx.x;
+    const int seq = tok / a.n_q;
+    const int64_t r_begin = (int64_t)split * a.rows_per_split;
+    const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
+    const size_t kv_base = (size_t)seq * (size_t)a.n_ctx;
+    const int32_t* idx_row = GATHER ? a.idx + (size_t)tok * (size_t)a.n_rows : nullptr;
+
+    // query fragment (B operand of S^T = K Q^T): head hl, d = KD*s + VPL*g + [0, VPL)
+    LT qf[NS][VPL];
+    {
+        const bool hv = hl < H;
+        const size_t qb = ((size_t)tok * H + (hv ? hl : 0)) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int d0 = KD * s + VPL * g;
+            if constexpr (KV == DT_F32) {
+                qf[s][0] = hv ? reinterpret_cast<const float*>(a.q)[qb + d0] : 0.f;
+            } else {
+                u32x4 w4 = hv ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qb + d0)
+                              : u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(&qf[s][0]) = w4;
+            }
+        }
+    }
+
+    float m_run = kNegBig, l_run = 0.f;
+    f32x4 o_acc[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
+
+    for (int64_t t0 = r_begin; t0 < r_end; t0 += kRowsTile) {
+        // ---- stage the tile: row metadata, then K and V rows (coalesced 16-B chunks)
+        if (tid < kRowsTile) {
+            const int64_t r = t0 + tid;
+            int p = -1;
+            if (r < r_end) p = GATHER ? idx_row[r] : (int)r;
+            pos_lds[tid] = p;
+            if constexpr (KV == DT_FP8) {
+                ksc_lds[tid] = p >= 0 ? a.ks[kv_base + p] : 0.f;
+                vsc_lds[tid] = p >= 0 ? a.vs[kv_base + p] : 0.f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int ch = tid + kRowsThreads * c;
+            const int row = ch / CPR, cc = ch % CPR;
+            const int p = pos_lds[row];
+            const bool ok = p >= 0;
+            const size_t off = (kv_base + (size_t)(ok ? p : 0)) * (size_t)RB;
+            stage_chunk<KV, D>(k_lds + row * LD, reinterpret_cast<const uint8_t*>(a.k) + off, cc, ok);
+            stage_chunk<KV, D>(v_lds + row * LD, reinterpret_cast<const uint8_t*>(a.v) + off, cc, ok);
+        }
+        __syncthreads();
+
+        // ---- S^T for the wave's 32 rows: two 16-row groups
+        f32x4 sacc[2];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            sacc[grp] = f32x4{0, 0, 0, 0};
+            const LT* krow = k_lds + (32 * w + 16 * grp + hl) * LD;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sacc[grp] = mfma16(krow + KD * s + VPL * g, &qf[s][0], sacc[grp]);
+        }
+        // logits in base 2; lane holds head hl, wave rows 16*grp + 4*g + i
+        float x[2][4];
+        float mx = kNegBig;
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 32 * w + 16 * grp + 4 * g + i;
+                const int p = pos_lds[row];
+                float v = sacc[grp][i] * a.scale_log2;
+                if constexpr (KV == DT_FP8) v *= ksc_lds[row];
+                v = p >= 0 ? v : -INFINITY;
+                x[grp][i] = v;
+                mx = fmaxf(mx, v);
+                if constexpr (STORE_LOGITS) {
+                    if (p >= 0 && hl < H) a.logits[(kv_base + (size_t)p) * H + hl] = v;
+                }
+            }
+        // per-head maximum over the wave's 32 rows (lanes hl, hl+16, hl+32, hl+48)
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        float pr[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[grp][i] = exp2f(x[grp][i] - m_new);
+                psum += pr[grp][i];
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
+        if constexpr (KV == DT_FP8) {
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pr[grp][i] *= vsc_lds[32 * w + 16 * grp + 4 * g + i];
+        }
+
+        // ---- O^T += V^T P^T
+        if constexpr (KV == DT_F32) {
+            // k = 4 rows per MFMA: step (grp, i) takes wave row 16*grp + 4*g + i from lane group g
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float* vrow = v_lds + (32 * w + 16 * grp + 4 * g + i) * LD;
+#pragma unroll
+                    for (int t = 0; t < NDT; ++t)
+                        o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * t + hl], pr[grp][i], o_acc[t], 0,
+                                                                        0, 0);
+                }
+        } else {
+            // k = 32 rows per MFMA; slot (g, i<4) = row 4g+i, slot (g, i>=4) = row 16+4g+i-4
+            u32x4 pb;
+            pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+            pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+            pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+            pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+            const bf16x8 pbf = as_bf16x8(pb);
+            const uint16_t* vb = v_lds + (32 * w + 4 * g) * LD;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const int dcol = 16 * t + hl;
+                u32x4 va;
+                va[0] = (uint32_t)vb[0 * LD + dcol] | ((uint32_t)vb[1 * LD + dcol] << 16);
+                va[1] = (uint32_t)vb[2 * LD + dcol] | ((uint32_t)vb[3 * LD + dcol] << 16);
+                va[2] = (uint32_t)vb[16 * LD + dcol] | ((uint32_t)vb[17 * LD + dcol] << 16);
+                va[3] = (uint32_t)vb[18 * LD + dcol] | ((uint32_t)vb[19 * LD + dcol] << 16);
+                o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pbf, o_acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- merge the 4 waves: per head m, l (summed over lane groups), O
+    l_run += __shfl_xor(l_run, 16);
+    l_run += xor32(l_run);
+    float* red = reinterpret_cast<float*>(k_lds);  // reuse: [4 waves][16 heads][D] O, then m, l
+    float* red_m = red + 4 * 16 * D;
+    float* red_l = red_m + 4 * 16;
+    static_assert(sizeof(k_lds) >= sizeof(float) * (4 * 16 * D + 128), "reduction scratch");
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(w * 16 + hl) * D + 16 * t + 4 * g + i] = o_acc[t][i];
+    if (g == 0) {
+        red_m[w * 16 + hl] = m_run;
+        red_l[w * 16 + hl] = l_run;
+    }
+    __syncthreads();
+    const bool final_out = a.n_split == 1;
+    for (int e = tid; e < H * D; e += kRowsThreads) {
+        const int h = e / D, dd = e % D;
+        float mm = kNegBig;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww * 16 + h]);
+        float ll = 0.f, oo = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float f = exp2f(red_m[ww * 16 + h] - mm);
+            ll += red_l[ww * 16 + h] * f;
+            oo += red[(ww * 16 + h) * D + dd] * f;
+        }
+        if (final_out) {
+            const float o = ll > 0.f ? oo / ll : 0.f;
+            const size_t oi = ((size_t)tok * H + h) * D + dd;
+            if constexpr (KV == DT_F32)
+                reinterpret_cast<float*>(a.out)[oi] = o;
+            else
+                reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
+            if (dd == 0) {
+                const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+                if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
+                if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
+            }
+        } else {
+            float* rec = a.part + ((size_t)tok * a.n_split + split) * (size_t)(H * (D + 2));
+            rec[2 * H + e] = oo;
+            if (dd == 0) {
+                rec[h] = mm;
+                rec[H + h] = ll;
+            }
+        }
+    }
+}
+
+// Merge split partials (m, l, O per head, base-2) into O, LSE.
+template <int H, int D, int QT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    const int tok = blockIdx.x;
+    const float* base = a.part + (size_t)tok * a.n_split * (size_t)(H * (D + 2));
+    for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+        const int h = e / D, dd = e % D;
+        float mm = kNegBig;
+        for (int s = 0; s < a.n_split; ++s) mm = fmaxf(mm, base[(size_t)s * H * (D + 2) + h]);
+        float ll = 0.f, oo = 0.f;
+        for (int s = 0; s < a.n_split; ++s) {
+            const float* rec = base + (size_t)s * H * (D + 2);
+            const float f = exp2f(rec[h] - mm);
+            ll += rec[H + h] * f;
+            oo += rec[2 * H + e] * f;
+        }
+        const float o = ll > 0.f ? oo / ll : 0.f;
+        const size_t oi = ((size_t)tok * H + h) * D + dd;
+        if constexpr (QT == DT_F32)
+            reinterpret_cast<float*>(a.out)[oi] = o;
+        else
+            reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
+        if (dd == 0) {
+            const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+            if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
+            if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
+        }
+    }
+}
+
+template <int H, int D, int KV, bool GATHER, bool STORE>
+static hipError_t launch_rows_t(const RowsArgs& a, hipStream_t st) {
+    dim3 grid(a.n_split, a.n_tok);
+    hipLaunchKernelGGL((rows_attn_kernel<H, D, KV, GATHER, STORE>), grid, dim3(kRowsThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int H, int D, int KV>
+static hipError_t launch_rows_hdk(const RowsArgs& a, bool gather, bool store, hipStream_t st) {
+    if (gather) return launch_rows_t<H, D, KV, true, false>(a, st);
+    if (store) return launch_rows_t<H, D, KV, false, true>(a, st);
+    return launch_rows_t<H, D, KV, false, false>(a, st);
+}
+
+template <int H, int D>
+static hipError_t launch_rows_hd(const RowsArgs& a, int kv, bool gather, bool store, hipStream_t st) {
+    switch (kv) {
+        case DT_F32: return launch_rows_hdk<H, D, DT_F32>(a, gather, store, st);
+        case DT_BF16: return launch_rows_hdk<H, D, DT_BF16>(a, gather, store, st);
+        default: return launch_rows_hdk<H, D, DT_FP8>(a, gather, store, st);
+    }
+}
+
+hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather, bool store_logits,
+                            hipStream_t st) {
+    if (D == 64) {
+        if (H == 4) return launch_rows_hd<4, 64>(a, kv, gather, store_logits, st);
+        if (H == 8) return launch_rows_hd<8, 64>(a, kv, gather, store_logits, st);
+        return launch_rows_hd<16, 64>(a, kv, gather, store_logits, st);
+    }
+    if (H == 4) return launch_rows_hd<4, 128>(a, kv, gather, store_logits, st);
+    if (H == 8) return launch_rows_hd<8, 128>(a, kv, gather, store_logits, st);
+    return launch_rows_hd<16, 128>(a, kv, gather, store_logits, st);
+}
+
+template <int H, int D>
+static hipError_t launch_combine_hd(const CombineArgs& a, int qt, hipStream_t st) {
+    if (qt == DT_F32)
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), dim3(a.n_tok), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), dim3(a.n_tok), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_t st) {
+    if (D == 64) {
+        if (H == 4) return launch_combine_hd<4, 64>(a, qt, st);
+        if (H == 8) return launch_combine_hd<8, 64>(a, qt, st);
+        return launch_combine_hd<16, 64>(a, qt, st);
+    }
+    if (H == 4) return launch_combine_hd<4, 128>(a, qt, st);
+    if (H == 8) return launch_combine_hd<8, 128>(a, qt, st);
+    return launch_combine_hd<16, 128>(a, qt, st);
+}
+
+}  // namespace hs2
