@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the HySparse2 attention hot path on one MI355X.
+
+One step = the whole path for one batch of synthetic inputs:
+  decode workloads  -- hs2_decode_step: full layer over the cache (split-K
+                       attention + token scores + window/top-k selection) and
+                       the reusing sparse layers;
+  prefill workloads -- hs2_full_attn_select (pass 1, pass 2 with streaming
+                       top-k, final selection) then hs2_sparse_attn over all
+                       reusing layers.
+Inputs are generated on the host (hs2_inputs), copied to HBM before timing,
+and every output buffer and workspace is allocated before the timed region.
+
+Prints one JSON line. `value` is query tokens per second for the whole step.
+`roofline` prices the dominant kernel (decode: split-K attention, HBM-bound;
+prefill: pass-1 attention, MFMA-bound) from its algorithmic bytes or flops per
+launch and its average duration, measured with hipEvents recorded on the
+launch stream by the library's timing hook during the timed steps.
+`cpu_baseline` times the double-precision CPU oracle on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query tok/s, full attn+top-1024 select+sparse reuse @128k; % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+# kernel classes of the library's timing hook (include/hs2.h)
+KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
+      "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
+      "prefill_final": 10, "fill": 11}
+# kernel source file each priced kernel lives in (for the traffic record's freshness check)
+KSRC = {"decode_split_attn": "k_rows.hip", "attn_fwd": "k_prefill.hip"}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kv_bytes(kv: str) -> int:
+    return {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+
+
+def causal_pairs(wl) -> int:
+    # sum over queries of (p + 1), p = q_pos0 + i
+    n, p0 = wl.n_q, wl.q_pos0
+    return wl.B * (n * p0 + n * (n + 1) // 2)
+
+
+def path_roofline_seconds(wl) -> float:
+    """Lower bound on one step from the method's algorithmic work (HBM or MFMA)."""
+    b = kv_bytes(wl.kv_dtype)
+    sb = 4 if wl.kv_dtype == "fp8" else 0
+    S = wl.window + wl.k_global
+    if wl.decode:
+        full = wl.B * wl.n_ctx * (2 * (wl.d * b + sb) + 2 * wl.H * 4 + 8) / (HBM_PEAK_GBS * 1e9)
+        sparse = wl.n_sparse * wl.B * S * 2 * (wl.d * b + sb) / (HBM_PEAK_GBS * 1e9)
+        return full + sparse
+    peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"] * 1e12
+    full = 6 * wl.d * wl.H * causal_pairs(wl) / peak
+    # every query attends to min(p+1, S) selected rows in each sparse layer
+    sel = sum(min(wl.q_pos0 + i + 1, S) for i in range(wl.n_q)) * wl.B
+    sparse = wl.n_sparse * 4 * wl.d * wl.H * sel / peak
+    return full + sparse
+
+
+def dominant(wl):
+    """(timing class, bound, algorithmic units per launch, unit label)."""
+    if wl.decode:
+        b = kv_bytes(wl.kv_dtype)
+        sb = 4 if wl.kv_dtype == "fp8" else 0
+        per_key = 2 * (wl.d * b + sb) + 4 * wl.H          # K + V rows read, fp32 logits written
+        return "decode_split_attn", "hbm", wl.B * wl.n_ctx * per_key, "GB/s"
+    return "attn_fwd", "mfma", 4 * wl.d * wl.H * causal_pairs(wl), "TFLOP/s"
+
+
+def traffic_record(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+        src = os.path.join(ROOT, "token_level_top_amd", "csrc", KSRC[name])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if not rec or rec.get("src_sha") != sha:
+            return None
+        return rec
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, x, seconds: float):
+    import numpy as np
+    import oracle
+    oracle.lib()
+    cores = oracle.num_threads()
+    rng = np.random.default_rng(12345)
+    rows_all = np.arange(wl.B * wl.n_q)
+    order = rng.permutation(rows_all)
+    done = 0
+    t0 = time.perf_counter()
+    for r in order:
+        r = int(r)
+        ref = oracle.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global,
+                                 x.sm_scale, [r])
+        for l in range(wl.n_sparse):
+            oracle.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["idx"], x.sm_scale, [r])
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    what = "sequences" if wl.decode else "query rows (uniform over positions)"
+    return {"value": done / el, "unit": "query tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {wl.B * wl.n_q} {what}: full attention + score + select + "
+                      f"{wl.n_sparse} sparse layers, fp64, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: decode @128k)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (extra steps)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import token_level_top_amd as hs2
+    from hs2_inputs import make_inputs, workload
+
+    wl = workload(args.config)
+    log(f"workload {wl.name}: generating inputs on the host")
+    t0 = time.perf_counter()
+    x = make_inputs(wl)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; copying to the GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = lambda t: None if t is None else t.to(dev, non_blocking=False).contiguous()
+    k, v, ks, vs = g(x.k), g(x.v), g(x.k_scale), g(x.v_scale)
+    kvdt = {"f32": hs2.HS2_F32, "bf16": hs2.HS2_BF16, "fp8": hs2.HS2_FP8_E4M3}[wl.kv_dtype]
+    S = wl.window + wl.k_global
+
+    if wl.decode:
+        qf = g(x.q[:, 0])
+        qs = g(x.q_sparse[:, :, 0])
+        ws = torch.empty(hs2.workspace_size(hs2.OP_DECODE_STEP, wl.B, 1, wl.n_ctx, wl.H, wl.d, wl.window,
+                                            wl.k_global, kvdt), dtype=torch.uint8, device=dev)
+        bufs = dict(out_full=torch.empty_like(qf), lse_full=torch.empty((wl.B, wl.H), device=dev),
+                    out_sparse=torch.empty_like(qs), lse_sparse=torch.empty((wl.n_sparse, wl.B, wl.H), device=dev),
+                    indices=torch.empty((wl.B, S), dtype=torch.int32, device=dev))
+
+        def step():
+            hs2.decode_step(qf, qs, k, v, ks, vs, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale,
+                            workspace=ws, **bufs)
+    else:
+        q = g(x.q)
+        qs = g(x.q_sparse)
+        ws_full = torch.empty(hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d,
+                                                 wl.window, wl.k_global, kvdt), dtype=torch.uint8, device=dev)
+        nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
+        ws_sp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((wl.B, wl.n_q, wl.H), device=dev)
+        idx = torch.empty((wl.B, wl.n_q, S), dtype=torch.int32, device=dev)
+        out_s = torch.empty_like(qs)
+        lse_s = torch.empty((wl.n_sparse, wl.B, wl.n_q, wl.H), device=dev)
+
+        def step():
+            hs2.full_attn_select(q, k, v, ks, vs, q_pos0=wl.q_pos0, window=wl.window, k_global=wl.k_global,
+                                 sm_scale=x.sm_scale, out=out, lse=lse, indices=idx, workspace=ws_full)
+            hs2.sparse_attn(qs, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
+                            workspace=ws_sp)
+
+    L = hs2.lib()
+    import ctypes
+    L.hs2_timing_enable.argtypes = [ctypes.c_uint32]
+    L.hs2_timing_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def read_timing():
+        ms = (ctypes.c_double * 16)()
+        n = (ctypes.c_int64 * 16)()
+        rc = L.hs2_timing_read(ctypes.addressof(ms), ctypes.addressof(n))
+        if rc != 0:
+            raise RuntimeError("hs2_timing_read failed")
+        return list(ms), list(n)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    read_timing()
+
+    dom, bound, units, unit = dominant(wl)
+    L.hs2_timing_enable(1 << KC[dom])
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    L.hs2_timing_enable(0)
+    ms_total = e0.elapsed_time(e1)
+    ms, n = read_timing()
+    ms_step = ms_total / args.steps
+    tokens = wl.B * wl.n_q
+    value = tokens * args.steps / (ms_total / 1e3)
+    kavg_s = ms[KC[dom]] / max(n[KC[dom]], 1) / 1e3
+    if bound == "hbm":
+        achieved, peak = units / kavg_s / 1e9, HBM_PEAK_GBS
+    else:
+        achieved = units / kavg_s / 1e12
+        peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"]
+    tr = traffic_record(dom)
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
+            "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),
+            "algorithmic_per_launch": units}
+    t_roof = path_roofline_seconds(wl)
+    res = {"metric": METRIC, "value": round(value, 2), "unit": "query tok/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
+           "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
+           "config": {"workload": wl.name, "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
+                      "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
+                      "k_global": wl.k_global, "n_sparse": wl.n_sparse},
+           "roofline": roof,
+           "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)}}
+    if args.breakdown:
+        L.hs2_timing_enable(0xFFF)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        L.hs2_timing_enable(0)
+        ms, n = read_timing()
+        names = {v_: k_ for k_, v_ in KC.items()}
+        res["breakdown_ms_per_step"] = {names[c]: round(ms[c] / 3, 4) for c in range(12) if n[c]}
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -172,6 +172,24 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
 int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const int32_t* n_cand,
                     int k, int32_t* out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement hook (not part of the computation). Kernel classes, one bit each:
+ *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
+ *   bit 2 decode token scores          bit 3 selection histogram
+ *   bit 4 selection candidates         bit 5 selection final
+ *   bit 6 sparse-layer attention       bit 7 prefill K/V preparation
+ *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
+ *   bit 10 prefill final selection     bit 11 buffer fills
+ * hs2_timing_enable(mask): from now on every launch of a class in `mask` is
+ * bracketed by two hipEvents recorded on its launch stream (0 disables).
+ * hs2_timing_read(ms, launches): waits for the recorded events and adds, per
+ * class c < 16, the elapsed milliseconds to ms[c] and the launch count to
+ * launches[c] (both arrays of 16, host memory), then forgets the events.
+ * Returns HS2_OK or HS2_ERR_HIP. Process-wide state guarded by a mutex.
+ */
+int hs2_timing_enable(uint32_t mask);
+int hs2_timing_read(double* ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,9 +3,12 @@
 // Validation touches no HIP API, so every error path runs without a GPU.
 #include "hs2.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "hs2_internal.h"
 
@@ -159,6 +162,60 @@ PrefillWs prefill_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d
     return w;
 }
 
+// ---- measurement hook: hipEvents around launches of selected kernel classes
+enum KClass {
+    KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
+    KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_PF_FINAL = 10, KC_FILL = 11
+};
+struct TimedPair {
+    int cls;
+    hipEvent_t a, b;
+};
+struct TimingState {
+    std::mutex mu;
+    std::vector<TimedPair> pending;
+    std::vector<hipEvent_t> pool;
+};
+TimingState& timing_state() {
+    static TimingState t;
+    return t;
+}
+std::atomic<uint32_t> g_timing_mask{0};
+
+hipEvent_t pooled_event(TimingState& T) {
+    if (!T.pool.empty()) {
+        hipEvent_t e = T.pool.back();
+        T.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <typename F>
+hipError_t timed(int cls, hipStream_t st, F&& launch) {
+    if (!(g_timing_mask.load(std::memory_order_relaxed) & (1u << cls))) return launch();
+    TimingState& T = timing_state();
+    hipEvent_t a, b;
+    {
+        std::lock_guard<std::mutex> g(T.mu);
+        a = pooled_event(T);
+        b = pooled_event(T);
+    }
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    hipError_t e2 = hipEventRecord(b, st);
+    {
+        std::lock_guard<std::mutex> g(T.mu);
+        T.pending.push_back({cls, a, b});
+    }
+    return e != hipSuccess ? e : e2;
+}
+#define TIMED(cls, st, expr) timed((cls), (st), [&]() { return (expr); })
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_ERR_HIP; }
 #define HS2_TRY(expr)                                   \
     do {                                                \
@@ -199,7 +256,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
             a.out = o;
             a.lse = ls;
         }
-        HS2_TRY(launch_rows_attn(a, H, d, kv_dtype, true, false, st));
+        HS2_TRY(TIMED(KC_SPARSE, st, launch_rows_attn(a, H, d, kv_dtype, true, false, st)));
         if (ns > 1) {
             CombineArgs c{};
             c.part = part;
@@ -207,7 +264,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
             c.n_split = ns;
             c.out = o;
             c.lse = ls;
-            HS2_TRY(launch_combine(c, H, d, q_dtype, st));
+            HS2_TRY(TIMED(KC_COMBINE, st, launch_combine(c, H, d, q_dtype, st)));
         }
     }
     return HS2_OK;
@@ -218,6 +275,30 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
 extern "C" {
 
 int hs2_abi_version(void) { return HS2_ABI_VERSION; }
+
+int hs2_timing_enable(uint32_t mask) {
+    g_timing_mask.store(mask);
+    return HS2_OK;
+}
+
+int hs2_timing_read(double* ms, int64_t* launches) {
+    TimingState& T = timing_state();
+    std::lock_guard<std::mutex> g(T.mu);
+    int rc = HS2_OK;
+    for (const TimedPair& p : T.pending) {
+        float el = 0.f;
+        if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&el, p.a, p.b) != hipSuccess) {
+            rc = HS2_ERR_HIP;
+        } else if (p.cls >= 0 && p.cls < 16) {
+            if (ms) ms[p.cls] += el;
+            if (launches) launches[p.cls] += 1;
+        }
+        T.pool.push_back(p.a);
+        T.pool.push_back(p.b);
+    }
+    T.pending.clear();
+    return rc;
+}
 
 const char* hs2_status_string(int status) {
     switch (status) {
@@ -293,11 +374,11 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     a.out = out;
     a.out_stride = k;
     a.out_offset = 0;
-    HS2_TRY(launch_fill_u32(w.hist, rows * kHistBins, 0u, s));
-    HS2_TRY(launch_fill_u32(w.cand_count, rows, 0u, s));
-    HS2_TRY(launch_select_hist(a, s));
-    HS2_TRY(launch_select_collect(a, s));
-    HS2_TRY(launch_select_final(a, s));
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, rows * kHistBins, 0u, s)));
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, rows, 0u, s)));
+    HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_hist(a, s)));
+    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(a, s)));
+    HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final(a, s)));
     return HS2_OK;
 }
 
@@ -347,7 +428,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         a.lse = lse_full;
         a.lse2 = w.lse2;
     }
-    HS2_TRY(launch_rows_attn(a, H, d, kv_dtype, false, true, s));
+    HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_rows_attn(a, H, d, kv_dtype, false, true, s)));
     if (ns > 1) {
         CombineArgs c{};
         c.part = w.part;
@@ -356,13 +437,13 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         c.out = out_full;
         c.lse = lse_full;
         c.lse2 = w.lse2;
-        HS2_TRY(launch_combine(c, H, d, q_dtype, s));
+        HS2_TRY(TIMED(KC_COMBINE, s, launch_combine(c, H, d, q_dtype, s)));
     }
     // 2. token scores + histogram of the candidates j <= n_ctx-1-window
     const int64_t n_cand = n_ctx - window > 0 ? n_ctx - window : 0;
     float* sc = scores ? scores : w.scores;
-    HS2_TRY(launch_fill_u32(w.hist, (int64_t)B * kHistBins, 0u, s));
-    HS2_TRY(launch_fill_u32(w.cand_count, B, 0u, s));
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, (int64_t)B * kHistBins, 0u, s)));
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, B, 0u, s)));
     ScoreArgs sa{};
     sa.logits = w.logits;
     sa.lse2 = w.lse2;
@@ -371,7 +452,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     sa.n_ctx = n_ctx;
     sa.n_cand = n_cand;
     sa.H = H;
-    HS2_TRY(launch_decode_score(sa, B, s));
+    HS2_TRY(TIMED(KC_SCORE, s, launch_decode_score(sa, B, s)));
     // 3. window + top-k_global
     if (k_global > 0) {
         SelectArgs se{};
@@ -386,8 +467,8 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         se.out = indices;
         se.out_stride = n_sel;
         se.out_offset = window;
-        if (n_cand > 0) HS2_TRY(launch_select_collect(se, s));
-        HS2_TRY(launch_select_final_w(se, window, n_ctx - 1, s));
+        if (n_cand > 0) HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
+        HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     } else {
         SelectArgs se{};
         se.rows = B;
@@ -397,7 +478,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         se.out = indices;
         se.out_stride = n_sel;
         se.out_offset = window;
-        HS2_TRY(launch_select_final_w(se, window, n_ctx - 1, s));
+        HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     }
     // 4. sparse layers reuse the indices and the cache
     if (n_sparse > 0)
@@ -446,11 +527,11 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     a.cand_count = w.cand_count;
     a.cand_cap = kPrefillCandCap;
     a.indices = indices;
-    HS2_TRY(launch_prep_kv(k, v, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s));
-    HS2_TRY(launch_attn_fwd(a, H, d, kv_dtype, s));
-    HS2_TRY(launch_fill_u32(w.cand_count, (int64_t)B * n_q, 0u, s));
-    HS2_TRY(launch_score_stream(a, H, d, kv_dtype, s));
-    HS2_TRY(launch_prefill_final(a, s));
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
+    HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, (int64_t)B * n_q, 0u, s)));
+    HS2_TRY(TIMED(KC_STREAM, s, launch_score_stream(a, H, d, kv_dtype, s)));
+    HS2_TRY(TIMED(KC_PF_FINAL, s, launch_prefill_final(a, s)));
     return HS2_OK;
 }
 
