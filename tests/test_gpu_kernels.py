@@ -149,6 +149,9 @@ def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
     (2, 1000, 0, 1000, 300),         # bf16, H=16, d=128
     (4, 77, 3000, 3077, 1024),       # fp8 KV, chunk at an offset, ragged block
     (2, 130, 0, 130, 1024),          # shorter than window + k
+    (2, 48, 9952, 10000, 1024),      # > 4096 candidates per token: compaction while streaming
+    (4, 40, 12000, 12040, 1024),     # fp8 with clustered (tied) needles, streaming compaction
+    (1, 96, 5000, 5096, 256),        # f32, H=4: 8 tokens per wave, streaming compaction
 ])
 def test_full_attn_select_matches_oracle(hs2, orc, cfg, n_q, q_pos0, n_ctx, kg):
     wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, k_global=kg, n_needles=4)
@@ -177,3 +180,21 @@ def test_prefill_and_decode_are_deterministic(hs2):
                              sm_scale=x.sm_scale)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_prefill_all_tied_scores(hs2, orc):
+    """Zero queries give every key the same score: the lowest positions win."""
+    wl = workload(2).with_(n_q=64, q_pos0=6000, n_ctx=6064, n_needles=0, needles="none")
+    x = make_inputs(wl)
+    x.q[0, ::3] = 0
+    say("prefill all tied")
+    out, lse, idx = hs2.full_attn_select(dev(x.q), dev(x.k), dev(x.v), q_pos0=wl.q_pos0, window=128,
+                                         k_global=1024, sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    g = to_np(idx[0])
+    for i in range(0, 64, 3):
+        assert g[i, 128:].tolist() == list(range(1024))
+    rows = list(range(64))
+    ref = orc.full_select(x.q, x.k, x.v, None, None, wl.q_pos0, 128, 1024, x.sm_scale, rows, want_scores=True)
+    check_index_rows(idx[0], ref["idx"], ref["scores"], ref["kth"], 128)
+    rows_close(out[0], ref["out"], 1e-2)

@@ -137,14 +137,13 @@ SelectWs select_ws(void* base, int64_t rows) {
     return w;
 }
 
-constexpr int kPrefillCandCap = 4096;
+constexpr int kPrefillCandCap = 2048;  // = 64 lanes x 32 keys held in registers by the compaction
 constexpr int kVtPad = 64;
 struct PrefillWs {
     void* vt;
     uint16_t* kc;
     float* lse2;
     uint64_t* cand;
-    uint32_t* cand_count;
     int64_t n_ctx_pad;
     size_t bytes;
 };
@@ -157,7 +156,6 @@ PrefillWs prefill_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d
     w.kc = kv_dtype == HS2_FP8_E4M3 ? c.take<uint16_t>(2 * (size_t)B * n_ctx * d) : nullptr;
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * n_q * H);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * n_q * kPrefillCandCap);
-    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * n_q);
     w.bytes = c.used;
     return w;
 }
@@ -524,14 +522,11 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     a.window = window;
     a.k_global = k_global;
     a.cand = w.cand;
-    a.cand_count = w.cand_count;
     a.cand_cap = kPrefillCandCap;
     a.indices = indices;
     HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
     HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
-    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, (int64_t)B * n_q, 0u, s)));
     HS2_TRY(TIMED(KC_STREAM, s, launch_score_stream(a, H, d, kv_dtype, s)));
-    HS2_TRY(TIMED(KC_PF_FINAL, s, launch_prefill_final(a, s)));
     return HS2_OK;
 }
 

@@ -33,9 +33,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// 2^x with the hardware instruction alone. Results below 2^-126 flush to zero;
+// callers keep their arguments in a range where that cannot change a result
+// (softmax terms relative to a running maximum, scores shifted by 2^64).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scores are formed as 2^(s - LSE + kScoreShift), i.e. scaled by 2^64, which
+// keeps every term above the flush limit unless it is below 2^-190; the
+// ranking is unchanged and stored scores are scaled back exactly.
+constexpr float kScoreShift = 64.0f;
+constexpr float kScoreUnshift = 5.421010862427522e-20f;  // 2^-64
 
 // Four OCP E4M3FN codes (one dword) -> four floats, exact (hardware convert).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {

@@ -99,14 +99,13 @@ struct PrefillArgs {
     float* lse2;            // [B][n_q][H] base 2 (workspace)
     int window, k_global;
     uint64_t* cand;         // [B*n_q][cand_cap] candidate keys
-    uint32_t* cand_count;   // [B*n_q]
     int cand_cap;
     int32_t* indices;       // [B][n_q][window + k_global]
 };
 hipError_t launch_prep_kv(const void* k, const void* v, int kv, int B, int64_t n_ctx, int64_t n_ctx_pad, int D,
                           uint16_t* kc, void* vt, hipStream_t st);
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+// pass 2 also writes the index rows (window + global part)
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
-hipError_t launch_prefill_final(const PrefillArgs& a, hipStream_t st);
 
 }  // namespace hs2

@@ -24,8 +24,11 @@
 //                 buffer is compacted to its exact top k by a wave-level radix
 //                 select, which raises the threshold. No token x key score
 //                 matrix is ever stored.
-//  prefill_final  per token: exact top-k of the buffer (bitonic sort in LDS),
-//                 positions sorted ascending, forced window written first.
+//                 When the stream ends, each buffer is compacted to exactly k
+//                 entries; appends follow the key order and compaction is
+//                 stable, so the buffer already lists the selected positions in
+//                 ascending order and is written out as the index row (after the
+//                 forced window).
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -35,6 +38,7 @@ constexpr int kPfTile = 64;      // keys per LDS tile
 constexpr int kPfWaves = 8;      // waves per workgroup, 32 (token, head) rows each
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 32 * kPfWaves;
+constexpr float kLazy = 8.0f;    // log2 headroom before the running maximum is raised
 
 template <bool F32>
 struct PfTypes;
@@ -126,28 +130,34 @@ struct TileStage {
     static constexpr int KCH = kPfTile * D * T::ESZ / 16;   // 16-B pieces per K tile
     static constexpr int VCH = D * kPfTile * T::ESZ / 16;
     static constexpr int KPT = (KCH + kPfThreads - 1) / kPfThreads;
-    static constexpr int VPT = WITH_V ? (VCH + kPfThreads - 1) / kPfThreads : 0;
+    static constexpr int VPT = WITH_V ? VCH / kPfThreads : 0;
+    static_assert(!WITH_V || VCH % kPfThreads == 0, "every thread stages whole V pieces");
     static constexpr int EPC = 16 / T::ESZ;                  // elements per piece
+    static_assert(KCH % kPfThreads == 0, "every thread stages whole K pieces");
     u32x4 kr[KPT];
     u32x4 vr[VPT > 0 ? VPT : 1];
+    uint32_t kvalid;  // bit i: K piece i lies inside the cache (else stored as zero)
 
+    // Loads are unconditional (row index clamped into the cache) so that no
+    // register write has to wait behind an in-flight load.
     __device__ void load(const LT* kg, const LT* vtg, int64_t j0, int64_t n_ctx, int64_t n_ctx_pad) {
         const int tid = threadIdx.x;
+        kvalid = 0;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int ch = tid + kPfThreads * i;
             const int row = ch / (D / EPC), cc = ch % (D / EPC);
             const int64_t j = j0 + row;
-            kr[i] = (ch < KCH && j < n_ctx) ? *reinterpret_cast<const u32x4*>(kg + (size_t)j * D + cc * EPC)
-                                            : u32x4{0, 0, 0, 0};
+            kvalid |= (j < n_ctx ? 1u : 0u) << i;
+            const int64_t jc = j < n_ctx ? j : n_ctx - 1;
+            kr[i] = *reinterpret_cast<const u32x4*>(kg + (size_t)jc * D + cc * EPC);
         }
         if constexpr (WITH_V) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int ch = tid + kPfThreads * i;
                 const int d = ch / (kPfTile / EPC), cc = ch % (kPfTile / EPC);
-                vr[i] = ch < VCH ? *reinterpret_cast<const u32x4*>(vtg + (size_t)d * n_ctx_pad + j0 + cc * EPC)
-                                 : u32x4{0, 0, 0, 0};
+                vr[i] = *reinterpret_cast<const u32x4*>(vtg + (size_t)d * n_ctx_pad + j0 + cc * EPC);
             }
         }
     }
@@ -156,36 +166,33 @@ struct TileStage {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int ch = tid + kPfThreads * i;
-            if (ch < KCH) {
-                const int row = ch / (D / EPC), cc = ch % (D / EPC);
-                LT* dst = k_lds + row * KLD + cc * EPC;
-                if constexpr (F32) {
-                    dst[0] = __uint_as_float(kr[i][0]);
-                    dst[1] = __uint_as_float(kr[i][1]);
-                    dst[2] = __uint_as_float(kr[i][2]);
-                    dst[3] = __uint_as_float(kr[i][3]);
-                } else {
-                    *reinterpret_cast<u32x4*>(dst) = kr[i];
-                }
+            const int row = ch / (D / EPC), cc = ch % (D / EPC);
+            LT* dst = k_lds + row * KLD + cc * EPC;
+            const u32x4 w = (kvalid >> i) & 1u ? kr[i] : u32x4{0, 0, 0, 0};
+            if constexpr (F32) {
+                dst[0] = __uint_as_float(w[0]);
+                dst[1] = __uint_as_float(w[1]);
+                dst[2] = __uint_as_float(w[2]);
+                dst[3] = __uint_as_float(w[3]);
+            } else {
+                *reinterpret_cast<u32x4*>(dst) = w;
             }
         }
         if constexpr (WITH_V) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int ch = tid + kPfThreads * i;
-                if (ch < VCH) {
-                    const int d = ch / (kPfTile / EPC), cc = ch % (kPfTile / EPC);
-                    LT* dst = v_lds + d * VLD + cc * EPC;
-                    if constexpr (F32) {
-                        dst[0] = __uint_as_float(vr[i][0]);
-                        dst[1] = __uint_as_float(vr[i][1]);
-                        dst[2] = __uint_as_float(vr[i][2]);
-                        dst[3] = __uint_as_float(vr[i][3]);
-                    } else {
-                        u32x2* d2 = reinterpret_cast<u32x2*>(dst);
-                        d2[0] = u32x2{vr[i][0], vr[i][1]};
-                        d2[1] = u32x2{vr[i][2], vr[i][3]};
-                    }
+                const int d = ch / (kPfTile / EPC), cc = ch % (kPfTile / EPC);
+                LT* dst = v_lds + d * VLD + cc * EPC;
+                if constexpr (F32) {
+                    dst[0] = __uint_as_float(vr[i][0]);
+                    dst[1] = __uint_as_float(vr[i][1]);
+                    dst[2] = __uint_as_float(vr[i][2]);
+                    dst[3] = __uint_as_float(vr[i][3]);
+                } else {
+                    u32x2* d2 = reinterpret_cast<u32x2*>(dst);
+                    d2[0] = u32x2{vr[i][0], vr[i][1]};
+                    d2[1] = u32x2{vr[i][2], vr[i][3]};
                 }
             }
         }
@@ -264,10 +271,20 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
+    float ks_pf = 0.f, vs_pf = 0.f;  // FP8 scales of the next tile (thread < 64)
     for (int it = 0; it < n_tiles; ++it) {
         const int cur = it & 1;
         const int64_t j0 = (int64_t)it * kPfTile;
-        if (it + 1 < n_tiles) stg.load(kg, vtg, j0 + kPfTile, a.n_ctx, a.n_ctx_pad);
+        if (it + 1 < n_tiles) {
+            stg.load(kg, vtg, j0 + kPfTile, a.n_ctx, a.n_ctx_pad);
+            if constexpr (SCALED) {
+                if (tid < kPfTile) {
+                    const int64_t j = min<int64_t>(j0 + kPfTile + tid, a.n_ctx - 1);
+                    ks_pf = ksg[j];
+                    vs_pf = vsg[j];
+                }
+            }
+        }
         const bool need_mask = j0 + kPfTile - 1 > p_min;
         const LT* kl = k_lds[cur];
         const LT* vl = v_lds[cur];
@@ -280,30 +297,39 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
             const LT* krow = kl + (32 * sub + n) * KLD + VPL * hh;
 #pragma unroll
             for (int s = 0; s < NS; ++s) sacc = mfma32(krow + KD * s, &qf[s][0], sacc);
+            // x = logits in base-2 units (FP8: per-key scale folded in); the running
+            // maximum m_run is only raised when a block exceeds it by more than
+            // kLazy (2^8), so the O rescale is rare; p <= 2^kLazy stays exact
+            // enough in bf16/fp32 and the final LSE uses the same m_run.
             float x[16];
-            float mx = kNegBig;
+            float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kk = 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
-                float v = sacc[i] * a.scale_log2;
-                if constexpr (SCALED) v *= ks_lds[cur][kk];
+                float v = sacc[i];
+                if constexpr (SCALED) v *= a.scale_log2 * ks_lds[cur][kk];
                 if (need_mask && j0 + kk > my_p) v = -INFINITY;
                 x[i] = v;
                 mx = fmaxf(mx, v);
             }
             mx = fmaxf(mx, xor32(mx));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = exp2f(m_run - m_new);
-            m_run = m_new;
+            if constexpr (!SCALED) mx *= a.scale_log2;
+            const bool grow = mx > m_run + kLazy;
+            if (__ballot(grow)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
+            }
             float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                x[i] = exp2f(x[i] - m_new);
+                x[i] = SCALED ? fast_exp2(x[i] - m_run) : fast_exp2(__builtin_fmaf(x[i], a.scale_log2, -m_run));
                 psum += x[i];
             }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
+            l_run += psum;
             if constexpr (SCALED) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[i] *= vs_lds[cur][32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3)];
@@ -343,9 +369,9 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
             stg.store(k_lds[cur ^ 1], v_lds[cur ^ 1]);
             if constexpr (SCALED) {
                 if (tid < kPfTile) {
-                    const int64_t j = j0 + kPfTile + tid;
-                    ks_lds[cur ^ 1][tid] = j < a.n_ctx ? ksg[j] : 0.f;
-                    vs_lds[cur ^ 1][tid] = j < a.n_ctx ? vsg[j] : 0.f;
+                    const bool ok = j0 + kPfTile + tid < a.n_ctx;
+                    ks_lds[cur ^ 1][tid] = ok ? ks_pf : 0.f;
+                    vs_lds[cur ^ 1][tid] = ok ? vs_pf : 0.f;
                 }
             }
         }
@@ -382,72 +408,151 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------- score_stream
-// Wave-level exact compaction of one token's candidate buffer to its top kk
-// keys. Returns the kk-th largest key (the new threshold). All 64 lanes call it.
-__device__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist /*256 per wave*/) {
+__device__ __forceinline__ uint64_t u64_shfl_xor(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = u64_shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = u64_shfl_xor(v, m);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+constexpr int kCompactScratch = 16 * 64;  // uint32 per wave: 16 digit bins x 64 lanes
+constexpr int kKeysPerLane = 32;          // a token buffer of up to 2048 keys, in registers
+
+// Wave-level exact top-kk of one token's candidate buffer (1 <= kk <= cnt <=
+// 64 * kKeysPerLane). The whole buffer is read once into registers (slot
+// i = lane + 64 j), so every pass below is ALU/LDS work with no memory waits.
+// The kk-th largest key T is found digit by digit (4 bits), starting below the
+// prefix every key shares; each lane counts into its own LDS column (no two
+// lanes touch one counter) and the search stops as soon as the chosen bin
+// holds exactly the keys still needed. The keys >= T are then written in
+// buffer order (which is ascending position order): back to `buf` as keys, or,
+// if `pos_out` is given, as positions. Returns T. All 64 lanes call it.
+__device__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist, int32_t* pos_out) {
     const uint32_t lane = lane_id();
-    uint64_t prefix = 0, pmask = 0;
+    // the wave's own earlier appends must be complete before they are read back
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    uint64_t key[kKeysPerLane];
+#pragma unroll
+    for (int j = 0; j < kKeysPerLane; ++j) {
+        const uint32_t i = lane + 64u * j;
+        key[j] = buf[i < cnt ? i : 0u];
+    }
+#pragma unroll
+    for (int j = 0; j < kKeysPerLane; ++j)
+        if (lane + 64u * j >= cnt) key[j] = 0;  // 0 ranks below every real key
+    if (kk >= cnt) {
+        // keep everything: T = smallest key
+        uint64_t m = ~0ull;
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j)
+            if (lane + 64u * j < cnt && key[j] < m) m = key[j];
+        const uint64_t T = wave_min_u64(m);
+        uint32_t wr = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j) {
+            const bool keep = lane + 64u * j < cnt;
+            const uint64_t mm = __ballot(keep);
+            if (keep) {
+                const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
+                if (pos_out) pos_out[at] = (int32_t)key_pos(key[j]);
+                else buf[at] = key[j];
+            }
+            wr += __popcll(mm);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        return T;
+    }
+    uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+    for (int j = 0; j < kKeysPerLane; ++j) {
+        if (key[j] > kmax) kmax = key[j];
+        if (lane + 64u * j < cnt && key[j] < kmin) kmin = key[j];
+    }
+    kmax = wave_max_u64(kmax);
+    kmin = wave_min_u64(kmin);
+    int hi = 64 - __clzll((long long)(kmax ^ kmin));          // bits [hi, 64) are shared by every key
+    uint64_t pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
+    uint64_t prefix = kmax & pmask;
     uint32_t need = kk;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int i = lane; i < 256; i += 64) hist[i] = 0;
+    uint64_t T = 0;
+    bool found = false;
+    while (hi > 0 && !found) {
+        const int lo = hi > 4 ? hi - 4 : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) hist[b * 64 + lane] = 0;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        for (uint32_t i = lane; i < cnt; i += 64) {
-            const uint64_t key = buf[i];
-            if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 0xFFu], 1u);
-        }
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j)
+            if (lane + 64u * j < cnt && (key[j] & pmask) == prefix)
+                atomicAdd(&hist[(((uint32_t)(key[j] >> lo)) & dmask) * 64 + lane], 1u);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        // lane j owns digits 255-4j .. 252-4j; scan from the top
-        uint32_t c4[4], s4 = 0;
+        // bin totals: lane 4b+q sums lanes 16q..16q+15 of bin b, then 4 lanes combine
+        uint32_t part = 0;
+        {
+            const int b = lane >> 2, q = lane & 3;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            c4[q] = hist[255 - 4 * lane - q];
-            s4 += c4[q];
+            for (int jj = 0; jj < 16; ++jj) part += hist[b * 64 + 16 * q + jj];
+            part += __shfl_xor(part, 1);
+            part += __shfl_xor(part, 2);
         }
-        uint32_t incl = s4;
+        uint32_t above = 0, dd = 0, in_bin = 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if ((int)lane >= o) incl += y;
-        }
-        const uint32_t excl = incl - s4;
-        uint32_t digit = 0, above = 0;
-        bool mine = excl < need && incl >= need;
-        if (mine) {
-            uint32_t acc = excl;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (acc + c4[q] >= need) {
-                    digit = 255 - 4 * lane - q;
-                    above = acc;
-                    break;
-                }
-                acc += c4[q];
+        for (int b = 15; b >= 0; --b) {
+            const uint32_t c = __builtin_amdgcn_readlane(part, 4 * b);
+            if (!in_bin && b <= (int)dmask && above + c >= need) {
+                dd = (uint32_t)b;
+                in_bin = c;
+            } else if (!in_bin) {
+                above += c;
             }
         }
-        const uint64_t bal = __ballot(mine);
-        const int src = __ffsll((unsigned long long)bal) - 1;
-        digit = __shfl(digit, src);
-        above = __shfl(above, src);
         need -= above;
-        prefix |= (uint64_t)digit << shift;
-        pmask |= (uint64_t)0xFF << shift;
+        prefix |= (uint64_t)dd << lo;
+        pmask |= (uint64_t)dmask << lo;
         __builtin_amdgcn_wave_barrier();
+        if (in_bin == need) {
+            // every key under this prefix is selected: T is the smallest of them
+            uint64_t m = ~0ull;
+#pragma unroll
+            for (int j = 0; j < kKeysPerLane; ++j)
+                if (lane + 64u * j < cnt && (key[j] & pmask) == prefix && key[j] < m) m = key[j];
+            T = wave_min_u64(m);
+            found = true;
+        }
+        hi = lo;
     }
-    const uint64_t kth = prefix;  // exact: keys are distinct
-    // in-place ordered compaction (write index never passes read index)
+    if (!found) T = prefix;  // all 64 bits fixed
     uint32_t wr = 0;
-    for (uint32_t base = 0; base < cnt; base += 64) {
-        const uint32_t i = base + lane;
-        const uint64_t key = i < cnt ? buf[i] : 0ull;
-        const bool keep = i < cnt && key >= kth;
-        const uint64_t m = __ballot(keep);
-        __builtin_amdgcn_wave_barrier();
-        if (keep) buf[wr + __popcll(m & ((1ull << lane) - 1ull))] = key;
-        wr += __popcll(m);
+#pragma unroll
+    for (int j = 0; j < kKeysPerLane; ++j) {
+        const bool keep = lane + 64u * j < cnt && key[j] >= T;
+        const uint64_t mm = __ballot(keep);
+        if (keep) {
+            const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
+            if (pos_out) pos_out[at] = (int32_t)key_pos(key[j]);
+            else buf[at] = key[j];
+        }
+        wr += __popcll(mm);
     }
-    return kth;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    return T;
 }
 
 template <int H, int D, int KV>
@@ -465,7 +570,7 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
 
     __shared__ __attribute__((aligned(16))) LT k_lds[2][kPfTile * KLD];
     __shared__ float ks_lds[2][kPfTile];
-    __shared__ uint32_t whist[kPfWaves][256];
+    __shared__ uint32_t whist[kPfWaves][kCompactScratch];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
@@ -478,8 +583,25 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     const uint32_t kglob = (uint32_t)a.k_global;
     const int64_t p_max = a.q_pos0 + min<int64_t>(tok0 + TB, a.n_q) - 1;
     const int64_t c_max = p_max - W;  // last candidate position of the block
-    if (c_max < 0 || kglob == 0) return;
+    const bool any_cand = c_max >= 0 && kglob > 0;
 
+    // per score slot u: the token it belongs to (relative to the wave), its last
+    // candidate position, the token's threshold and candidate count
+    int tslot[NSC];
+    int64_t climit[NSC];
+    uint64_t thr[NSC];
+    uint32_t cnt[NSC];
+#pragma unroll
+    for (int u = 0; u < NSC; ++u) {
+        tslot[u] = H == 16 ? hh : (H == 8 ? 2 * hh + u : 2 * u + hh);
+        const int64_t tk = wtok0 + tslot[u];
+        climit[u] = tk < a.n_q ? a.q_pos0 + tk - W : -1;
+        thr[u] = 0;
+        cnt[u] = 0;
+    }
+    const size_t row0 = (size_t)b * a.n_q;  // flat token index base
+    const int cap = a.cand_cap;
+    if (any_cand) {
     // Q fragment (A operand of S = Q K^T): row R = 32w + n, k = KD*s + VPL*hh + [0, VPL)
     LT qf[NS][VPL];
     {
@@ -502,32 +624,42 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     // base-2 LSE of the 16 rows this lane's accumulator holds: m = 8(i/4) + 4hh + i%4
     float lse_r[16];
 #pragma unroll
+    for (int i = 0; i < 16; ++i) {  // loads first (clamped addresses), selects after
+        const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int64_t tk = min<int64_t>(tok0 + R / H, a.n_q - 1);
+        lse_r[i] = a.lse2[((size_t)b * a.n_q + (size_t)tk) * H + (R % H)];
+    }
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const int64_t tk = tok0 + R / H;
-        lse_r[i] = tk < a.n_q ? a.lse2[((size_t)b * a.n_q + (size_t)tk) * H + (R % H)] : INFINITY;
-    }
-    // per score slot u: the token it belongs to (relative to the wave), its last
-    // candidate position, the token's threshold and candidate count
-    int tslot[NSC];
-    int64_t climit[NSC];
-    uint64_t thr[NSC];
-    uint32_t cnt[NSC];
-#pragma unroll
-    for (int u = 0; u < NSC; ++u) {
-        tslot[u] = H == 16 ? hh : (H == 8 ? 2 * hh + u : 2 * u + hh);
-        const int64_t tk = wtok0 + tslot[u];
-        climit[u] = tk < a.n_q ? a.q_pos0 + tk - W : -1;
-        thr[u] = 0;
-        cnt[u] = 0;
+        lse_r[i] = tok0 + R / H < a.n_q ? lse_r[i] - kScoreShift : INFINITY;
     }
     const LT* kg = SCALED ? reinterpret_cast<const LT*>(a.kc) + (size_t)b * a.n_ctx * D
                           : reinterpret_cast<const LT*>(a.k) + (size_t)b * a.n_ctx * D;
     const float* ksg = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
-    const size_t row0 = (size_t)b * a.n_q;  // flat token index base
-    const int cap = a.cand_cap;
 
     const int n_tiles = (int)((c_max + kPfTile) / kPfTile);
+    // Appends of one tile are held in registers and issued at the top of the
+    // next tile, next to the prefetch loads: loads and stores share vmcnt, so a
+    // store issued mid-tile would be waited for at the tile's end.
+    uint64_t pend_key[2][NSC];
+    uint64_t* pend_ptr[2][NSC];
+    bool pend_take[2][NSC];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int u = 0; u < NSC; ++u) pend_take[sb][u] = false;
+    auto flush = [&]() {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int u = 0; u < NSC; ++u)
+                if (pend_take[sb][u]) {
+                    *pend_ptr[sb][u] = pend_key[sb][u];
+                    pend_take[sb][u] = false;
+                }
+    };
+    float ks_pf = 0.f;  // FP8 key scale of the next tile (thread < 64)
     Stage stg;
     stg.load(kg, nullptr, 0, a.n_ctx, a.n_ctx_pad);
     stg.store(k_lds[0], nullptr);
@@ -539,7 +671,13 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     for (int it = 0; it < n_tiles; ++it) {
         const int cur = it & 1;
         const int64_t j0 = (int64_t)it * kPfTile;
-        if (it + 1 < n_tiles) stg.load(kg, nullptr, j0 + kPfTile, a.n_ctx, a.n_ctx_pad);
+        flush();
+        if (it + 1 < n_tiles) {
+            stg.load(kg, nullptr, j0 + kPfTile, a.n_ctx, a.n_ctx_pad);
+            if constexpr (SCALED) {
+                if (tid < kPfTile) ks_pf = ksg[min<int64_t>(j0 + kPfTile + tid, a.n_ctx - 1)];
+            }
+        }
         const LT* kl = k_lds[cur];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -556,7 +694,7 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
             float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float e = exp2f(sacc[i] * c - lse_r[i]);
+                const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
                 if constexpr (H == 16) part[i >> 3] += e;     // token i/8 (both halves)
                 else part[i >> 2] += e;                      // H=8: token i/4; H=4: token 2(i/4)+hh
             }
@@ -580,7 +718,9 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
                 const uint64_t half = hh ? (m >> 32) : (m & 0xFFFFFFFFull);
                 const uint32_t rank = __popcll(half & ((1ull << n) - 1ull));
                 const int64_t tk = wtok0 + tslot[u];
-                if (take) a.cand[(row0 + (size_t)tk) * (size_t)cap + cnt[u] + rank] = key;
+                pend_take[sub][u] = take;
+                pend_key[sub][u] = key;
+                pend_ptr[sub][u] = a.cand + (row0 + (size_t)tk) * (size_t)cap + cnt[u] + rank;
                 cnt[u] += __popcll(half);
             }
             // compact any token whose buffer cannot take another block
@@ -588,12 +728,13 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
             for (int u = 0; u < NSC; ++u) {
 #pragma unroll
                 for (int side = 0; side < 2; ++side) {
-                    const uint32_t cs = __shfl(cnt[u], side ? 32 : 0);
+                    const uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
                     if (cs + 32 > (uint32_t)cap) {
+                        flush();
                         const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
                         const int64_t tk = wtok0 + ts;
                         uint64_t* buf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
-                        const uint64_t kth = compact_topk(buf, cs, kglob, whist[w]);
+                        const uint64_t kth = compact_topk(buf, cs, kglob, whist[w], nullptr);
                         if (hh == side) {
                             thr[u] = kth;
                             cnt[u] = kglob;
@@ -605,19 +746,39 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
         if (it + 1 < n_tiles) {
             stg.store(k_lds[cur ^ 1], nullptr);
             if constexpr (SCALED) {
-                if (tid < kPfTile) {
-                    const int64_t j = j0 + kPfTile + tid;
-                    ks_lds[cur ^ 1][tid] = j < a.n_ctx ? ksg[j] : 0.f;
-                }
+                if (tid < kPfTile) ks_lds[cur ^ 1][tid] = j0 + kPfTile + tid < a.n_ctx ? ks_pf : 0.f;
             }
         }
         __syncthreads();
     }
-    // publish the candidate counts (one lane per token)
+    flush();
+    }
+    // Epilogue: every token of the wave gets its index row. A buffer holds the
+    // token's candidates in ascending position order (appends follow the key
+    // order, compaction is stable), so after compacting it to exactly min(k,
+    // candidates) entries it is the global part as is.
 #pragma unroll
     for (int u = 0; u < NSC; ++u) {
-        const int64_t tk = wtok0 + tslot[u];
-        if (n == 0 && tk < a.n_q) a.cand_count[row0 + (size_t)tk] = cnt[u];
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
+            const int64_t tk = wtok0 + ts;
+            if (tk >= a.n_q) continue;
+            const int64_t p = a.q_pos0 + tk;
+            const size_t row = row0 + (size_t)tk;
+            int32_t* out = a.indices + row * (size_t)(W + a.k_global);
+            const int64_t nw = min<int64_t>(W, p + 1);
+            for (int t = lane; t < W; t += 64) out[t] = t < nw ? (int32_t)(p - nw + 1 + t) : -1;
+            out += W;
+            const int64_t n_cand = p - W + 1 > 0 ? p - W + 1 : 0;
+            const uint32_t kk = (uint32_t)min<int64_t>(a.k_global, n_cand);
+            uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
+            uint64_t* buf = a.cand + row * (size_t)cap;
+            if (kk == 0) cs = 0;
+            if (cs > 0) compact_topk(buf, cs, kk, whist[w], out);   // writes min(kk, cs) positions
+            const uint32_t wrote = cs < kk ? cs : kk;
+            for (uint32_t t = wrote + lane; t < (uint32_t)a.k_global; t += 64) out[t] = -1;
+        }
     }
 }
 
@@ -657,62 +818,6 @@ hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream
 }
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
     return launch_pf_any(a, H, D, kv, false, st);
-}
-
-// ------------------------------------------------------------- prefill_final
-template <typename K, bool DESC>
-__device__ void bitonic_block(K* x, int n) {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool dir = ((lo & size) == 0) == DESC;
-                const K u = x[lo], v = x[hi];
-                if (dir ? (u < v) : (u > v)) {
-                    x[lo] = v;
-                    x[hi] = u;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-constexpr int kFinPfThreads = 256;
-__global__ __launch_bounds__(kFinPfThreads) void prefill_final_kernel(PrefillArgs a) {
-    __shared__ uint64_t keys[4096];
-    __shared__ uint32_t pos[2048];
-    const int64_t row = blockIdx.x;  // flat token b*n_q + i
-    const int64_t i = row % a.n_q;
-    const int64_t p = a.q_pos0 + i;
-    const int W = a.window, K = a.k_global;
-    int32_t* out = a.indices + (size_t)row * (size_t)(W + K);
-    const int64_t nw = min<int64_t>(W, p + 1);
-    for (int t = threadIdx.x; t < W; t += blockDim.x) out[t] = t < nw ? (int32_t)(p - nw + 1 + t) : -1;
-    out += W;
-    const int64_t n_cand = p - W + 1 > 0 ? p - W + 1 : 0;
-    const uint32_t kk = (uint32_t)min<int64_t>(K, n_cand);
-    for (int t = threadIdx.x + kk; t < K; t += blockDim.x) out[t] = -1;
-    if (kk == 0) return;
-    const uint32_t nc = a.cand_count[row];
-    int np = 2;
-    while (np < (int)nc) np <<= 1;
-    const uint64_t* cand = a.cand + (size_t)row * (size_t)a.cand_cap;
-    for (int t = threadIdx.x; t < np; t += blockDim.x) keys[t] = t < (int)nc ? cand[t] : 0ull;
-    __syncthreads();
-    bitonic_block<uint64_t, true>(keys, np);
-    int nk = 2;
-    while (nk < (int)kk) nk <<= 1;
-    for (int t = threadIdx.x; t < nk; t += blockDim.x) pos[t] = t < (int)kk ? key_pos(keys[t]) : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_block<uint32_t, false>(pos, nk);
-    for (int t = threadIdx.x; t < (int)kk; t += blockDim.x) out[t] = (int32_t)pos[t];
-}
-
-hipError_t launch_prefill_final(const PrefillArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(prefill_final_kernel, dim3((unsigned)(a.B * a.n_q)), dim3(kFinPfThreads), 0, st, a);
-    return hipGetLastError();
 }
 
 }  // namespace hs2

@@ -50,22 +50,24 @@ __device__ __forceinline__ f32x4 mfma16(const uint16_t* a, const uint16_t* b, f3
                                                    as_bf16x8(*reinterpret_cast<const u32x4*>(b)), c, 0, 0, 0);
 }
 
-// Key row (16 B aligned chunks) of one tile row into LDS; converts FP8 to bf16.
-template <int KV, int D>
-__device__ __forceinline__ void stage_chunk(typename RowsTypes<KV>::L* dst, const void* src_row, int cc, bool ok) {
+// One 16-byte piece of a K or V row: loaded into registers (always from a valid
+// row, so no register write waits behind an in-flight load), later written to
+// LDS as zero if the row was empty (FP8 codes widened to bf16 on the way).
+__device__ __forceinline__ u32x4 load_piece(const void* row, int cc) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(row) + cc * 16);
+}
+
+template <int KV>
+__device__ __forceinline__ void store_piece(typename RowsTypes<KV>::L* dst_row, int cc, u32x4 w) {
     if constexpr (KV == DT_FP8) {
-        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src_row) + cc * 16)
-                     : u32x4{0, 0, 0, 0};
         u32x2 a = fp8x4_to_bf16x4(w[0]), b = fp8x4_to_bf16x4(w[1]);
         u32x2 c = fp8x4_to_bf16x4(w[2]), e = fp8x4_to_bf16x4(w[3]);
-        u32x4* o = reinterpret_cast<u32x4*>(dst + cc * 16);
+        u32x4* o = reinterpret_cast<u32x4*>(dst_row + cc * 16);
         o[0] = u32x4{a[0], a[1], b[0], b[1]};
         o[1] = u32x4{c[0], c[1], e[0], e[1]};
     } else {
-        constexpr int EPC = 16 / RowsTypes<KV>::ESZ;  // elements per 16-byte chunk
-        u32x4 w = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(src_row) + cc * 16)
-                     : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(dst + cc * EPC) = w;
+        constexpr int EPC = 16 / RowsTypes<KV>::ESZ;  // elements per 16-byte piece
+        *reinterpret_cast<u32x4*>(dst_row + cc * EPC) = w;
     }
 }
 
@@ -121,30 +123,81 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 #pragma unroll
     for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
 
-    for (int64_t t0 = r_begin; t0 < r_end; t0 += kRowsTile) {
-        // ---- stage the tile: row metadata, then K and V rows (coalesced 16-B chunks)
-        if (tid < kRowsTile) {
-            const int64_t r = t0 + tid;
-            int p = -1;
-            if (r < r_end) p = GATHER ? idx_row[r] : (int)r;
-            pos_lds[tid] = p;
-            if constexpr (KV == DT_FP8) {
-                ksc_lds[tid] = p >= 0 ? a.ks[kv_base + p] : 0.f;
-                vsc_lds[tid] = p >= 0 ? a.vs[kv_base + p] : 0.f;
-            }
-        }
-        __syncthreads();
+    // Row position of tile row `row` (tile starting at t0), -1 if empty.
+    auto row_pos = [&](int64_t t0, int row) -> int {
+        const int64_t r = t0 + row;
+        if (r >= r_end) return -1;
+        return GATHER ? idx_row[r] : (int)r;
+    };
+    // Registers holding the next tile while the current one is computed.
+    u32x4 kreg[CPT], vreg[CPT];
+    uint32_t kvalid = 0;
+    int meta_p = -1;
+    float meta_ks = 0.f, meta_vs = 0.f;
+    auto prefetch = [&](int64_t t0) {
+        kvalid = 0;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int ch = tid + kRowsThreads * c;
             const int row = ch / CPR, cc = ch % CPR;
-            const int p = pos_lds[row];
-            const bool ok = p >= 0;
-            const size_t off = (kv_base + (size_t)(ok ? p : 0)) * (size_t)RB;
-            stage_chunk<KV, D>(k_lds + row * LD, reinterpret_cast<const uint8_t*>(a.k) + off, cc, ok);
-            stage_chunk<KV, D>(v_lds + row * LD, reinterpret_cast<const uint8_t*>(a.v) + off, cc, ok);
+            const int p = row_pos(t0, row);
+            kvalid |= (p >= 0 ? 1u : 0u) << c;
+            const size_t off = (kv_base + (size_t)(p >= 0 ? p : 0)) * (size_t)RB;
+            kreg[c] = load_piece(reinterpret_cast<const uint8_t*>(a.k) + off, cc);
+            vreg[c] = load_piece(reinterpret_cast<const uint8_t*>(a.v) + off, cc);
+        }
+        if (tid < kRowsTile) {
+            meta_p = row_pos(t0, tid);
+            if constexpr (KV == DT_FP8) {
+                const size_t mi = kv_base + (size_t)(meta_p >= 0 ? meta_p : 0);
+                meta_ks = a.ks[mi];
+                meta_vs = a.vs[mi];
+            }
+        }
+    };
+    // base-2 logits of the previous tile, stored at the top of the next one
+    // (loads and stores share vmcnt; a store issued mid-tile would be waited for
+    // before the next tile's rows can be published)
+    float pend_x[2][4];
+    int pend_p[2][4];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pend_p[grp][i] = -1;
+    auto flush_logits = [&]() {
+        if constexpr (STORE_LOGITS) {
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (pend_p[grp][i] >= 0 && hl < H) {
+                        a.logits[(kv_base + (size_t)pend_p[grp][i]) * H + hl] = pend_x[grp][i];
+                        pend_p[grp][i] = -1;
+                    }
+        }
+    };
+    if (r_begin < r_end) prefetch(r_begin);
+
+    for (int64_t t0 = r_begin; t0 < r_end; t0 += kRowsTile) {
+        // ---- publish the prefetched tile to LDS, then start loading the next one
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int ch = tid + kRowsThreads * c;
+            const int row = ch / CPR, cc = ch % CPR;
+            const bool ok = (kvalid >> c) & 1u;
+            store_piece<KV>(k_lds + row * LD, cc, ok ? kreg[c] : u32x4{0, 0, 0, 0});
+            store_piece<KV>(v_lds + row * LD, cc, ok ? vreg[c] : u32x4{0, 0, 0, 0});
+        }
+        if (tid < kRowsTile) {
+            pos_lds[tid] = meta_p;
+            if constexpr (KV == DT_FP8) {
+                ksc_lds[tid] = meta_ks;
+                vsc_lds[tid] = meta_vs;
+            }
         }
         __syncthreads();
+        flush_logits();
+        if (t0 + kRowsTile < r_end) prefetch(t0 + kRowsTile);
 
         // ---- S^T for the wave's 32 rows: two 16-row groups
         f32x4 sacc[2];
@@ -170,14 +223,15 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
                 x[grp][i] = v;
                 mx = fmaxf(mx, v);
                 if constexpr (STORE_LOGITS) {
-                    if (p >= 0 && hl < H) a.logits[(kv_base + (size_t)p) * H + hl] = v;
+                    pend_x[grp][i] = v;
+                    pend_p[grp][i] = p;
                 }
             }
         // per-head maximum over the wave's 32 rows (lanes hl, hl+16, hl+32, hl+48)
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, xor32(mx));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         float pr[2][4];
         float psum = 0.f;
@@ -185,7 +239,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pr[grp][i] = exp2f(x[grp][i] - m_new);
+                pr[grp][i] = fast_exp2(x[grp][i] - m_new);
                 psum += pr[grp][i];
             }
         l_run = l_run * alpha + psum;
@@ -234,6 +288,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         __syncthreads();
     }
 
+    flush_logits();
+
     // ---- merge the 4 waves: per head m, l (summed over lane groups), O
     l_run += __shfl_xor(l_run, 16);
     l_run += xor32(l_run);
@@ -259,7 +315,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         float ll = 0.f, oo = 0.f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-            const float f = exp2f(red_m[ww * 16 + h] - mm);
+            const float f = fast_exp2(red_m[ww * 16 + h] - mm);
             ll += red_l[ww * 16 + h] * f;
             oo += red[(ww * 16 + h) * D + dd] * f;
         }
@@ -287,32 +343,40 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 }
 
 // Merge split partials (m, l, O per head, base-2) into O, LSE.
+// One block of D threads per (token, head): the weights 2^(m_s - M) are formed
+// once per split and thread d accumulates O[d] over the splits.
 template <int H, int D, int QT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-    const int tok = blockIdx.x;
-    const float* base = a.part + (size_t)tok * a.n_split * (size_t)(H * (D + 2));
-    for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
-        const int h = e / D, dd = e % D;
-        float mm = kNegBig;
-        for (int s = 0; s < a.n_split; ++s) mm = fmaxf(mm, base[(size_t)s * H * (D + 2) + h]);
-        float ll = 0.f, oo = 0.f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const float* rec = base + (size_t)s * H * (D + 2);
-            const float f = exp2f(rec[h] - mm);
-            ll += rec[H + h] * f;
-            oo += rec[2 * H + e] * f;
-        }
-        const float o = ll > 0.f ? oo / ll : 0.f;
-        const size_t oi = ((size_t)tok * H + h) * D + dd;
-        if constexpr (QT == DT_F32)
-            reinterpret_cast<float*>(a.out)[oi] = o;
-        else
-            reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
-        if (dd == 0) {
-            const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
-            if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
-            if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
-        }
+__global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
+    __shared__ float red[D / 64 + 1];
+    const int tok = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const size_t rec = (size_t)H * (D + 2);
+    const float* base = a.part + (size_t)tok * a.n_split * rec;
+    // M = max_s m_s
+    float mm = kNegBig;
+    for (int s = d; s < a.n_split; s += D) mm = fmaxf(mm, base[(size_t)s * rec + h]);
+    mm = wave_max(mm);
+    if ((d & 63) == 0) red[d >> 6] = mm;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) mm = fmaxf(mm, red[w]);
+    __syncthreads();
+    float ll = 0.f, oo = 0.f;
+    for (int s = 0; s < a.n_split; ++s) {
+        const float* r = base + (size_t)s * rec;
+        const float f = fast_exp2(r[h] - mm);
+        ll += r[H + h] * f;
+        oo += r[2 * H + h * D + d] * f;
+    }
+    const float o = ll > 0.f ? oo / ll : 0.f;
+    const size_t oi = ((size_t)tok * H + h) * D + d;
+    if constexpr (QT == DT_F32)
+        reinterpret_cast<float*>(a.out)[oi] = o;
+    else
+        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
+    if (d == 0) {
+        const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+        if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
+        if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
     }
 }
 
@@ -353,10 +417,11 @@ hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather
 
 template <int H, int D>
 static hipError_t launch_combine_hd(const CombineArgs& a, int qt, hipStream_t st) {
+    const dim3 grid((unsigned)a.n_tok, (unsigned)H);
     if (qt == DT_F32)
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), dim3(a.n_tok), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), grid, dim3(D), 0, st, a);
     else
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), dim3(a.n_tok), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), grid, dim3(D), 0, st, a);
     return hipGetLastError();
 }
 

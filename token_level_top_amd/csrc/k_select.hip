@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
     __shared__ float l2[H];
     const int b = blockIdx.y;
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0;
-    if (threadIdx.x < H) l2[threadIdx.x] = a.lse2[(size_t)b * H + threadIdx.x];
+    if (threadIdx.x < H) l2[threadIdx.x] = a.lse2[(size_t)b * H + threadIdx.x] - kScoreShift;
     __syncthreads();
     const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
     const int64_t j1 = min<int64_t>(j0 + kSelChunk, a.n_ctx);
@@ -73,8 +73,9 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
         for (int c = 0; c < H / 4; ++c) {
             const f32x4 x = row[c];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s += exp2f(x[i] - l2[4 * c + i]);
+            for (int i = 0; i < 4; ++i) s += fast_exp2(x[i] - l2[4 * c + i]);
         }
+        s *= kScoreUnshift;  // exact power-of-two rescale to the true score
         a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
         if (j < a.n_cand) atomicAdd(&hist[score_bin(s)], 1u);
     }
@@ -178,25 +179,29 @@ __global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs 
     const int64_t j1 = min<int64_t>(j0 + kSelChunk, n);
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    uint32_t* cnt = a.cand_count + r;
-    for (int64_t jb = j0; jb < j1; jb += kSelThreads) {
-        const int64_t j = jb + threadIdx.x;
-        float v = 0.f;
-        bool take = false;
-        if (j < j1) {
-            v = s[j];
-            take = score_bin(v) >= tbin;
+    // pass A: count this workgroup's candidates; one global atomic reserves the range
+    uint32_t mine = 0;
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) mine += score_bin(s[j]) >= tbin ? 1u : 0u;
+    if (threadIdx.x == 0) scan[0] = 0;
+    __syncthreads();
+    if (mine) atomicAdd(&scan[0], mine);
+    __syncthreads();
+    const uint32_t total = scan[0];
+    if (total == 0) return;
+    __shared__ uint32_t base_sh, fill_sh;
+    if (threadIdx.x == 0) {
+        base_sh = atomicAdd(a.cand_count + r, total);
+        fill_sh = 0;
+    }
+    __syncthreads();
+    const uint32_t base = base_sh;
+    // pass B: write the keys (order within the range is irrelevant: keys are distinct)
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) {
+        const float v = s[j];
+        if (score_bin(v) >= tbin) {
+            const uint32_t slot = base + atomicAdd(&fill_sh, 1u);
+            if (slot < (uint32_t)kCandCap) cand[slot] = rank_key(v, (uint32_t)j);
         }
-        const uint64_t mask = __ballot(take);
-        if (mask == 0) continue;
-        const uint32_t lane = lane_id();
-        const uint32_t nb = __popcll(mask);
-        const uint32_t rank = __popcll(mask & ((1ull << lane) - 1ull));
-        const uint32_t first = __ffsll((unsigned long long)mask) - 1;
-        uint32_t base = 0;
-        if (lane == first) base = atomicAdd(cnt, nb);
-        base = __shfl(base, (int)first);
-        if (take && base + rank < (uint32_t)kCandCap) cand[base + rank] = rank_key(v, (uint32_t)j);
     }
 }
 
