@@ -1,0 +1,131 @@
+"""GPU parity at the five workloads' full sizes, through the same C-ABI calls
+and shapes the benchmark times. The oracle checks sampled rows: every
+sequence of the decode workloads, all rows of the tiny prefill, 512 seeded
+rows (all needle rows + uniform rows) of the 32k prefill and 64 rows of the
+256k chunked prefill."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hs2_inputs import checked_rows, make_inputs, workload
+from tests.hs2_check import check_index_rows, lse_close, rows_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+
+
+def say(*a):
+    print("[gpu-full]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def hs2():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import token_level_top_amd as t
+    t.lib()
+    return t
+
+
+def g(t):
+    return None if t is None else t.cuda().contiguous()
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_decode_full_size(hs2, orc, cfg):
+    wl = workload(cfg)
+    say("generate", wl.name)
+    x = make_inputs(wl)
+    say("decode step on the GPU")
+    r = hs2.decode_step(g(x.q[:, 0]), g(x.q_sparse[:, :, 0]), g(x.k), g(x.v), g(x.k_scale), g(x.v_scale),
+                        window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale, want_scores=True)
+    torch.cuda.synchronize()
+    rows = list(range(wl.B))
+    say("oracle on", len(rows), "sequences")
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
+                          rows, want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    rows_close(r["out_full"], ref["out"], tol, "decode out")
+    lse_close(r["lse_full"], ref["lse"], tol)
+    sc = to_np(r["scores"]).astype(np.float64)
+    rel = np.abs(sc - ref["scores"]) / ref["scores"].max(axis=1, keepdims=True)
+    assert rel.max() < 2e-3, rel.max()
+    ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  overlap mean {ov:.5f} min {mn:.5f} swaps {sw}")
+    gidx = to_np(r["indices"]).astype(np.int32)
+    for l in range(wl.n_sparse):
+        s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
+        rows_close(r["out_sparse"][l], s["out"], tol, "decode sparse out")
+        lse_close(r["lse_sparse"][l], s["lse"], tol)
+
+
+@pytest.mark.parametrize("cfg,n_uniform,n_target", [(1, 2048, None), (2, 256, None), (4, 32, 32)])
+def test_prefill_full_size(hs2, orc, cfg, n_uniform, n_target):
+    wl = workload(cfg)
+    say("generate", wl.name)
+    x = make_inputs(wl)
+    needles = x.needles if n_target is None else x.needles[:n_target]
+    rows = checked_rows(wl, needles, n_uniform)
+    say("prefill on the GPU;", len(rows), "rows checked")
+    kw = dict(q_pos0=wl.q_pos0, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale)
+    out, lse, idx = hs2.full_attn_select(g(x.q), g(x.k), g(x.v), g(x.k_scale), g(x.v_scale), **kw)
+    so, sl = hs2.sparse_attn(g(x.q_sparse), g(x.k), g(x.v), g(x.k_scale), g(x.v_scale), indices=idx,
+                             sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
+                          rows, want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    ri = torch.tensor(rows)
+    rows_close(out[0, ri], ref["out"], tol, "prefill out")
+    lse_close(lse[0, ri], ref["lse"], tol)
+    ov, mn, sw = check_index_rows(idx[0, ri], ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  overlap mean {ov:.5f} min {mn:.5f} swaps {sw}")
+    gidx = to_np(idx[0, ri]).astype(np.int32)
+    for l in range(wl.n_sparse):
+        s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
+        rows_close(so[l, 0, ri], s["out"], tol, "prefill sparse out")
+        lse_close(sl[l, 0, ri], s["lse"], tol)
+    # every index row of the whole launch is well formed (window, order, causality)
+    full = to_np(idx[0]).astype(np.int64)
+    p = wl.q_pos0 + np.arange(wl.n_q)
+    win = full[:, :wl.window]
+    nw = np.minimum(wl.window, p + 1)
+    expect_win = np.where(np.arange(wl.window)[None, :] < nw[:, None],
+                          p[:, None] - nw[:, None] + 1 + np.arange(wl.window)[None, :], -1)
+    assert np.array_equal(win, expect_win)
+    glb = full[:, wl.window:]
+    valid = glb >= 0
+    n_cand = np.maximum(0, p - wl.window + 1)
+    assert np.array_equal(valid.sum(axis=1), np.minimum(wl.k_global, n_cand))
+    has = valid.any(axis=1)
+    assert (np.where(valid, glb, -1).max(axis=1)[has] <= (p - wl.window)[has]).all()
+    d = np.diff(np.where(valid, glb, np.iinfo(np.int64).max), axis=1)
+    assert (d[valid[:, 1:]] > 0).all()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_needle_recovery(hs2, orc, cfg):
+    """Planted needles are recovered by the GPU's selection: the literal
+    3*q/|q| needles at the tiny workload's shape, and needles three times a
+    typical key norm at the 32k prefill and the 128k decode shapes."""
+    wl = workload(cfg)
+    if cfg == 2:
+        wl = wl.with_(n_q=512, q_pos0=32768 - 512)
+    norm = "R18a" if cfg == 1 else "R18b"
+    x = make_inputs(wl, needle_norm=norm)
+    say("needles", wl.name, norm, len(x.needles))
+    if wl.decode:
+        r = hs2.decode_step(g(x.q[:, 0]), g(x.q_sparse[:, :, 0]), g(x.k), g(x.v), window=wl.window,
+                            k_global=wl.k_global, sm_scale=x.sm_scale)
+        idx = to_np(r["indices"])[:, None, :]
+    else:
+        _, _, ii = hs2.full_attn_select(g(x.q), g(x.k), g(x.v), q_pos0=wl.q_pos0, window=wl.window,
+                                        k_global=wl.k_global, sm_scale=x.sm_scale)
+        idx = to_np(ii)
+    torch.cuda.synchronize()
+    hit = sum(all((n.j + t) in idx[n.b, n.i, wl.window:] for t in range(n.length)) for n in x.needles)
+    assert hit == len(x.needles), f"{hit} of {len(x.needles)} needles recovered"
