@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (extra steps)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB twice (reference for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -190,6 +192,15 @@ def main():
                                  sm_scale=x.sm_scale, out=out, lse=lse, indices=idx, workspace=ws_full)
             hs2.sparse_attn(qs, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
                             workspace=ws_sp)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     L = hs2.lib()
     import ctypes
