@@ -88,7 +88,8 @@ int sparse_splits(int64_t n_tok, int n_sel) {
 
 struct DecodeWs {
     float *logits, *part, *lse2, *scores, *spart;
-    uint32_t *hist, *cand_count;
+    uint32_t *hist, *thr, *counts;
+    int n_sub;
     uint64_t* cand;
     size_t bytes;
 };
@@ -100,8 +101,11 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     w.part = ns > 1 ? c.take<float>(sizeof(float) * (size_t)B * ns * H * (d + 2)) : nullptr;
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
     w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
+    // hist and tickets are contiguous so one fill clears both
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * kHistBins);
-    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B);
+    w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * 2);
+    w.n_sub = (int)((n_ctx + kSelSub - 1) / kSelSub);
+    w.counts = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * w.n_sub);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
     const int ss = sparse_splits(B, window + k_global);
     w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)B * ss * H * (d + 2)) : nullptr;
@@ -123,15 +127,18 @@ SparseWs sparse_ws(void* base, int64_t n_tok, int n_sel, int H, int d) {
 }
 
 struct SelectWs {
-    uint32_t *hist, *cand_count;
+    uint32_t *hist, *thr, *counts;
+    int n_sub;
     uint64_t* cand;
     size_t bytes;
 };
-SelectWs select_ws(void* base, int64_t rows) {
+SelectWs select_ws(void* base, int64_t rows, int64_t row_len) {
     Carver c(base);
     SelectWs w;
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * kHistBins);
-    w.cand_count = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows);
+    w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * 2);
+    w.n_sub = (int)((row_len + kSelSub - 1) / kSelSub);
+    w.counts = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * w.n_sub);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)rows * kCandCap);
     w.bytes = c.used;
     return w;
@@ -324,7 +331,7 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
             return sparse_ws(nullptr, (int64_t)B * n_q, window, H, d).bytes;
         case HS2_OP_SELECT_TOPK:
             if (k_global < 1) return SIZE_MAX;
-            return select_ws(nullptr, B).bytes;
+            return select_ws(nullptr, B, n_ctx).bytes;
         default: return SIZE_MAX;
     }
 }
@@ -355,10 +362,10 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     if (rows >= (int64_t(1) << 31) || row_len >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
     if (!aligned16(scores) || !aligned16(out) || !aligned16(n_cand)) return HS2_ERR_INVALID_ARG;
     if (k > 2048) return HS2_ERR_UNSUPPORTED;
-    const SelectWs need = select_ws(nullptr, rows);
+    const SelectWs need = select_ws(nullptr, rows, row_len);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const SelectWs w = select_ws(workspace, rows);
+    const SelectWs w = select_ws(workspace, rows, row_len);
     SelectArgs a{};
     a.scores = scores;
     a.rows = rows;
@@ -367,15 +374,18 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     a.n_cand = n_cand;
     a.k = k;
     a.hist = w.hist;
+    a.thr = w.thr;
+    a.counts = w.counts;
+    a.n_sub = w.n_sub;
     a.cand = w.cand;
-    a.cand_count = w.cand_count;
     a.out = out;
     a.out_stride = k;
     a.out_offset = 0;
     HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, rows * kHistBins, 0u, s)));
-    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, rows, 0u, s)));
     HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_hist(a, s)));
-    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(a, s)));
+    HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(a, s)));
+    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_count(a, s)));
+    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_emit(a, s)));
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final(a, s)));
     return HS2_OK;
 }
@@ -426,7 +436,10 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         a.lse = lse_full;
         a.lse2 = w.lse2;
     }
-    HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_rows_attn(a, H, d, kv_dtype, false, true, s)));
+    if (kv_dtype == HS2_F32)
+        HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_rows_attn(a, H, d, kv_dtype, false, true, s)));
+    else
+        HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_decode_split(a, H, d, kv_dtype, s)));
     if (ns > 1) {
         CombineArgs c{};
         c.part = w.part;
@@ -437,11 +450,10 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         c.lse2 = w.lse2;
         HS2_TRY(TIMED(KC_COMBINE, s, launch_combine(c, H, d, q_dtype, s)));
     }
-    // 2. token scores + histogram of the candidates j <= n_ctx-1-window
+    // 2. token scores + histogram of the candidates j <= n_ctx-1-window (+ threshold bin)
     const int64_t n_cand = n_ctx - window > 0 ? n_ctx - window : 0;
     float* sc = scores ? scores : w.scores;
     HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, (int64_t)B * kHistBins, 0u, s)));
-    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.cand_count, B, 0u, s)));
     ScoreArgs sa{};
     sa.logits = w.logits;
     sa.lse2 = w.lse2;
@@ -451,33 +463,27 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     sa.n_cand = n_cand;
     sa.H = H;
     HS2_TRY(TIMED(KC_SCORE, s, launch_decode_score(sa, B, s)));
-    // 3. window + top-k_global
-    if (k_global > 0) {
-        SelectArgs se{};
-        se.scores = sc;
-        se.rows = B;
-        se.row_stride = n_ctx;
-        se.row_len = n_cand;
-        se.k = k_global;
-        se.hist = w.hist;
-        se.cand = w.cand;
-        se.cand_count = w.cand_count;
-        se.out = indices;
-        se.out_stride = n_sel;
-        se.out_offset = window;
-        if (n_cand > 0) HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
-        HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
-    } else {
-        SelectArgs se{};
-        se.rows = B;
-        se.row_len = 0;
-        se.k = 0;
-        se.cand_count = w.cand_count;
-        se.out = indices;
-        se.out_stride = n_sel;
-        se.out_offset = window;
-        HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
+    // 3. window + top-k_global, in position order
+    SelectArgs se{};
+    se.scores = sc;
+    se.rows = B;
+    se.row_stride = n_ctx;
+    se.row_len = n_cand;
+    se.k = k_global;
+    se.hist = w.hist;
+    se.thr = w.thr;
+    se.counts = w.counts;
+    se.n_sub = (int)((n_cand + kSelSub - 1) / kSelSub);
+    se.cand = w.cand;
+    se.out = indices;
+    se.out_stride = n_sel;
+    se.out_offset = window;
+    if (k_global > 0 && n_cand > 0) {
+        HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(se, s)));
+        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_count(se, s)));
+        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_emit(se, s)));
     }
+    HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     // 4. sparse layers reuse the indices and the cache
     if (n_sparse > 0)
         return run_sparse(q_sparse, q_dtype, n_sparse, k, v, k_scale, v_scale, kv_dtype, B, 1, n_ctx, H, d, indices,

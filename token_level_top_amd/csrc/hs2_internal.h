@@ -40,10 +40,13 @@ struct CombineArgs {
 hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather, bool store_logits,
                             hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_t st);
+// decode full layer over a contiguous cache range, bf16 or FP8 cache (logits always stored)
+hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStream_t st);
 
 // ---- selection ------------------------------------------------------------
 constexpr int kHistBins = 4096;      // top 12 bits of a non-negative fp32 (bits 30..19)
-constexpr int kCandCap = 8192;       // candidates one workgroup sorts in LDS
+constexpr int kCandCap = 4096;       // candidates the final wave holds in registers
+constexpr int kSelSub = 2048;        // scores per wave in the count / emit steps
 
 // decode: score_j = sum_h exp2(logit2[j][h] - lse2[h]) for j < n_ctx; writes
 // scores [B][n_ctx] and the histogram of candidates j < n_cand.
@@ -67,18 +70,21 @@ struct SelectArgs {
     const int32_t* n_cand;  // [rows] or nullptr
     int k;
     uint32_t* hist;         // [rows][kHistBins]
-    uint64_t* cand;         // [rows][kCandCap]
-    uint32_t* cand_count;   // [rows]
+    uint32_t* thr;          // [rows][2] threshold bin, count above it
+    uint32_t* counts;       // [rows][n_sub] candidates per 2048-score slice
+    int n_sub;              // ceil(row_len / kSelSub)
+    uint64_t* cand;         // [rows][kCandCap], position order
     int32_t* out;           // [rows][out_stride]
     int64_t out_stride;
     int out_offset;         // first column written in each out row
 };
-// hist must be zeroed; fills it from the scores
+// hist zeroed; fills hist
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);
-// cand_count must be zeroed; hist must be complete
-hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st);
+// thr from the complete hist
+hipError_t launch_select_threshold(const SelectArgs& a, hipStream_t st);
+hipError_t launch_select_count(const SelectArgs& a, hipStream_t st);
+hipError_t launch_select_emit(const SelectArgs& a, hipStream_t st);
 hipError_t launch_select_final(const SelectArgs& a, hipStream_t st);
-
 // also writes the forced window of every row (all rows at position p_last) when window > 0
 hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);

@@ -1,0 +1,327 @@
+// Decode full layer, split-K over the KV cache (bf16 or FP8 cache).
+//
+// HySparse2 page, "무엇과 다른가": the full layer's exact attention is computed
+// for the newest token over the whole cache and its scores select the tokens
+// the sparse layers reuse; "어떻게 쓰나": MQA (one K/V head) and NoPE.
+//
+// For one query token per sequence the work is a stream over the cache:
+// read each key and value row once, form the H logits of the key, keep an online
+// softmax per head, accumulate P V, and store the base-2 logits (the token score
+// needs the final LSE, which is only known once every split is done).
+//
+// Layout of the work: a workgroup owns `rows_per_split` keys of one sequence;
+// its 4 waves take interleaved blocks of 32 keys (so the workgroup streams one
+// contiguous region) with no workgroup barrier until the final merge.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: 16 keys on M, the heads on N. The
+//    A operand (K rows) comes straight from HBM into registers: for k-step c the
+//    lane group g reads d = 32c + 8g .. +7 of its key row, so one load
+//    instruction covers a contiguous 32-element segment of 16 rows. K of block
+//    n+1 is loaded while block n is computed.
+//  * O^T = V^T P^T: V rows go through a wave-private LDS buffer (the MFMA needs
+//    8 keys of one column per lane), FP8 codes widened to bf16 exactly on the way.
+//  * Logits are staged in LDS and written one block later as 16-byte stores, so
+//    the stores never sit in the same wait as the loads the next block needs.
+#include <type_traits>
+
+#include "hs2_device.h"
+#include "hs2_internal.h"
+
+namespace hs2 {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecBlock = 32;  // keys per wave per step
+
+template <int H, int D, int KV>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a) {
+    static_assert(KV == DT_BF16 || KV == DT_FP8, "bf16 or FP8 cache");
+    static_assert(H <= 16 && (H == 4 || H == 8 || H == 16), "heads on the 16 MFMA columns");
+    constexpr int ESZ = KV == DT_FP8 ? 1 : 2;
+    constexpr int RB = D * ESZ;           // bytes per cache row
+    constexpr int NC = D / 32;            // MFMA k-steps over d
+    constexpr int NDT = D / 16;           // output d tiles
+    constexpr int VLD = D + 8;            // LDS row stride of the V buffer (bf16 elements)
+    constexpr int VP = kDecBlock * RB / 16 / 64;  // 16-byte V pieces per lane per block
+    static_assert(VP >= 1, "pieces");
+    // K operand registers per lane per 16-key group and k-step: 8 elements
+    using KPiece = typename std::conditional<KV == DT_FP8, u32x2, u32x4>::type;
+
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][kDecBlock * VLD];
+    __shared__ __attribute__((aligned(16))) float lg_lds[4][kDecBlock * H];
+    __shared__ float vs_lds[4][kDecBlock];
+    __shared__ float ks_lds[4][kDecBlock];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hl = lane & 15, g = lane >> 4;
+    const int seq = blockIdx.y, split = blockIdx.x;
+    const int64_t r_begin = (int64_t)split * a.rows_per_split;
+    const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
+    // wave w takes blocks w, w+4, w+8, ...: the workgroup reads (and writes logits
+    // for) one contiguous region that advances 128 keys at a time
+    constexpr int64_t kStride = 4 * kDecBlock;
+    const int64_t w_begin = r_begin + w * kDecBlock;
+    const int nb = w_begin < r_end ? (int)((r_end - w_begin + kStride - 1) / kStride) : 0;
+    const size_t kv_base = (size_t)seq * (size_t)a.n_ctx;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + kv_base * RB;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + kv_base * RB;
+    uint16_t* vl = v_lds[w];
+    float* lgl = lg_lds[w];
+
+    // query fragment (B operand): head hl, k-step c, slots d = 32c + 8g .. +7
+    u32x4 qf[NC];
+    {
+        const bool hv = hl < H;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)seq * H + (hv ? hl : 0)) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 v4 = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * g);
+            qf[c] = hv ? v4 : u32x4{0, 0, 0, 0};
+        }
+    }
+
+    float m_run = kNegBig, l_run = 0.f;
+    f32x4 o_acc[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
+
+    // ---- loads of one block (registers) -------------------------------------
+    // K: lane (row hl of group grp, g) reads elements 32c + 8g .. +7 of key row
+    // j + 16*grp + hl for every k-step c. V: lane reads pieces lane + 64*i of the
+    // block's rows. Rows past the range are clamped to the last row (masked later).
+    KPiece kr[2][2][NC];
+    u32x4 vr[VP];
+    float ksr = 0.f, vsr = 0.f;
+    const int64_t last = r_end - 1;
+    auto load_block = [&](int buf, int64_t j) {
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            const int64_t row = min<int64_t>(j + 16 * grp + hl, last);
+            const uint8_t* p = kbase + (size_t)row * RB + (8 * g) * ESZ;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kr[buf][grp][c] = *reinterpret_cast<const KPiece*>(p + (32 * c) * ESZ);
+        }
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            const int piece = lane + 64 * i;
+            const int row = piece / (RB / 16), cc = piece % (RB / 16);
+            const int64_t rr = min<int64_t>(j + row, last);
+            vr[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)rr * RB + 16 * cc);
+        }
+        if constexpr (KV == DT_FP8) {
+            const int64_t rr = min<int64_t>(j + (lane & 31), last);
+            ksr = a.ks[kv_base + rr];
+            vsr = a.vs[kv_base + rr];
+        }
+    };
+    // V (and FP8 scales) of a block into the wave's LDS buffer
+    auto stage_v = [&]() {
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            const int piece = lane + 64 * i;
+            const int row = piece / (RB / 16), cc = piece % (RB / 16);
+            if constexpr (KV == DT_FP8) {
+                const u32x2 p0 = fp8x4_to_bf16x4(vr[i][0]), p1 = fp8x4_to_bf16x4(vr[i][1]);
+                const u32x2 p2 = fp8x4_to_bf16x4(vr[i][2]), p3 = fp8x4_to_bf16x4(vr[i][3]);
+                u32x4* o = reinterpret_cast<u32x4*>(vl + row * VLD + 16 * cc);
+                o[0] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+                o[1] = u32x4{p2[0], p2[1], p3[0], p3[1]};
+            } else {
+                *reinterpret_cast<u32x4*>(vl + row * VLD + 8 * cc) = vr[i];
+            }
+        }
+        if constexpr (KV == DT_FP8) {
+            if (lane < 32) {
+                ks_lds[w][lane] = ksr;
+                vs_lds[w][lane] = vsr;
+            }
+        }
+    };
+    // logits of the previous block: staged [32][H] in LDS, written as 16-B pieces
+    int64_t pend_j = -1;
+    auto flush_logits = [&]() {
+        if (pend_j < 0) return;
+        float* dst = a.logits + (kv_base + (size_t)pend_j) * H;
+        for (int p = lane; p < kDecBlock * H / 4; p += 64) {
+            const int key = (4 * p) / H;
+            if (pend_j + key < r_end)  // streaming (non-temporal) store: read once, later, by the score pass
+                __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(lgl + 4 * p),
+                                            reinterpret_cast<f32x4*>(dst + 4 * p));
+        }
+        pend_j = -1;
+    };
+
+    auto compute = [&](int buf, int64_t j) {
+        // S^T for two 16-key groups
+        f32x4 sacc[2];
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp) {
+            sacc[grp] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                u32x4 kk;
+                if constexpr (KV == DT_FP8) {
+                    const u32x2 lo = fp8x4_to_bf16x4(kr[buf][grp][c][0]);
+                    const u32x2 hi = fp8x4_to_bf16x4(kr[buf][grp][c][1]);
+                    kk = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    kk = kr[buf][grp][c];
+                }
+                sacc[grp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk), as_bf16x8(qf[c]), sacc[grp], 0,
+                                                                    0, 0);
+            }
+        }
+        // base-2 logits; lane holds head hl of block keys 16*grp + 4g + i
+        float x[2][4];
+        float mx = -INFINITY;
+        const bool tail = j + kDecBlock > r_end;
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * grp + 4 * g + i;
+                float v = sacc[grp][i] * a.scale_log2;
+                if constexpr (KV == DT_FP8) v *= ks_lds[w][key];
+                if (tail && j + key >= r_end) v = -INFINITY;
+                x[grp][i] = v;
+                mx = fmaxf(mx, v);
+                if (hl < H) lgl[key * H + hl] = v;
+            }
+        pend_j = j;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        float pr[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[grp][i] = fast_exp2(x[grp][i] - m_new);
+                psum += pr[grp][i];
+            }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
+        if constexpr (KV == DT_FP8) {
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pr[grp][i] *= vs_lds[w][16 * grp + 4 * g + i];
+        }
+        // O^T += V^T P^T: slot (g, i<4) = key 4g+i, slot (g, i>=4) = key 16+4g+i-4
+        u32x4 pb;
+        pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+        pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+        pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+        pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+        const bf16x8 pbf = as_bf16x8(pb);
+        const uint16_t* vb = vl + (4 * g) * VLD;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+            const int dcol = 16 * t + hl;
+            u32x4 va;
+            va[0] = (uint32_t)vb[0 * VLD + dcol] | ((uint32_t)vb[1 * VLD + dcol] << 16);
+            va[1] = (uint32_t)vb[2 * VLD + dcol] | ((uint32_t)vb[3 * VLD + dcol] << 16);
+            va[2] = (uint32_t)vb[16 * VLD + dcol] | ((uint32_t)vb[17 * VLD + dcol] << 16);
+            va[3] = (uint32_t)vb[18 * VLD + dcol] | ((uint32_t)vb[19 * VLD + dcol] << 16);
+            o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pbf, o_acc[t], 0, 0, 0);
+        }
+    };
+
+    if (nb > 0) {
+        load_block(0, w_begin);
+        stage_v();
+    }
+    // two blocks per trip so the K register buffer index is static
+    for (int n = 0; n < nb; n += 2) {
+        {
+            const int64_t j = w_begin + (int64_t)n * kStride;
+            flush_logits();
+            const bool more = n + 1 < nb;
+            if (more) load_block(1, j + kStride);
+            compute(0, j);
+            if (more) stage_v();
+        }
+        if (n + 1 < nb) {
+            const int64_t j = w_begin + (int64_t)(n + 1) * kStride;
+            flush_logits();
+            const bool more = n + 2 < nb;
+            if (more) load_block(0, j + kStride);
+            compute(1, j);
+            if (more) stage_v();
+        }
+    }
+    flush_logits();
+
+    // ---- merge the 4 waves into one partial record (m, l, O per head)
+    l_run += __shfl_xor(l_run, 16);
+    l_run += xor32(l_run);
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&v_lds[0][0]);  // [4 waves][16][D], then m, l
+    float* red_m = red + 4 * 16 * D;
+    float* red_l = red_m + 4 * 16;
+    static_assert(sizeof(v_lds) >= sizeof(float) * (4 * 16 * D + 128), "merge scratch");
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(w * 16 + hl) * D + 16 * t + 4 * g + i] = o_acc[t][i];
+    if (g == 0) {
+        red_m[w * 16 + hl] = m_run;
+        red_l[w * 16 + hl] = l_run;
+    }
+    __syncthreads();
+    const bool final_out = a.n_split == 1;
+    for (int e = tid; e < H * D; e += kDecThreads) {
+        const int h = e / D, dd = e % D;
+        float mm = kNegBig;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww * 16 + h]);
+        float ll = 0.f, oo = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float f = fast_exp2(red_m[ww * 16 + h] - mm);
+            ll += red_l[ww * 16 + h] * f;
+            oo += red[(ww * 16 + h) * D + dd] * f;
+        }
+        if (final_out) {
+            const float o = ll > 0.f ? oo / ll : 0.f;
+            reinterpret_cast<uint16_t*>(a.out)[((size_t)seq * H + h) * D + dd] = f32_to_bf16_bits(o);
+            if (dd == 0) {
+                const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+                if (a.lse) a.lse[(size_t)seq * H + h] = lse2 * kLn2;
+                if (a.lse2) a.lse2[(size_t)seq * H + h] = lse2;
+            }
+        } else {
+            float* rec = a.part + ((size_t)seq * a.n_split + split) * (size_t)(H * (D + 2));
+            rec[2 * H + e] = oo;
+            if (dd == 0) {
+                rec[h] = mm;
+                rec[H + h] = ll;
+            }
+        }
+    }
+}
+
+template <int H, int D>
+static hipError_t launch_dec_hd(const RowsArgs& a, int kv, hipStream_t st) {
+    const dim3 grid((unsigned)a.n_split, (unsigned)a.n_tok);
+    if (kv == DT_FP8)
+        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_FP8>), grid, dim3(kDecThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_BF16>), grid, dim3(kDecThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStream_t st) {
+    if (D == 64) {
+        if (H == 4) return launch_dec_hd<4, 64>(a, kv, st);
+        if (H == 8) return launch_dec_hd<8, 64>(a, kv, st);
+        return launch_dec_hd<16, 64>(a, kv, st);
+    }
+    if (H == 4) return launch_dec_hd<4, 128>(a, kv, st);
+    if (H == 8) return launch_dec_hd<8, 128>(a, kv, st);
+    return launch_dec_hd<16, 128>(a, kv, st);
+}
+
+}  // namespace hs2

@@ -31,6 +31,7 @@
 //                 forced window).
 #include "hs2_device.h"
 #include "hs2_internal.h"
+#include "hs2_wave_select.h"
 
 namespace hs2 {
 
@@ -408,151 +409,10 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------- score_stream
-__device__ __forceinline__ uint64_t u64_shfl_xor(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = u64_shfl_xor(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = u64_shfl_xor(v, m);
-        v = o < v ? o : v;
-    }
-    return v;
-}
+constexpr int kKeysPerLane = 32;  // a token buffer of up to 2048 keys, in registers
 
-constexpr int kCompactScratch = 16 * 64;  // uint32 per wave: 16 digit bins x 64 lanes
-constexpr int kKeysPerLane = 32;          // a token buffer of up to 2048 keys, in registers
-
-// Wave-level exact top-kk of one token's candidate buffer (1 <= kk <= cnt <=
-// 64 * kKeysPerLane). The whole buffer is read once into registers (slot
-// i = lane + 64 j), so every pass below is ALU/LDS work with no memory waits.
-// The kk-th largest key T is found digit by digit (4 bits), starting below the
-// prefix every key shares; each lane counts into its own LDS column (no two
-// lanes touch one counter) and the search stops as soon as the chosen bin
-// holds exactly the keys still needed. The keys >= T are then written in
-// buffer order (which is ascending position order): back to `buf` as keys, or,
-// if `pos_out` is given, as positions. Returns T. All 64 lanes call it.
 __device__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist, int32_t* pos_out) {
-    const uint32_t lane = lane_id();
-    // the wave's own earlier appends must be complete before they are read back
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    uint64_t key[kKeysPerLane];
-#pragma unroll
-    for (int j = 0; j < kKeysPerLane; ++j) {
-        const uint32_t i = lane + 64u * j;
-        key[j] = buf[i < cnt ? i : 0u];
-    }
-#pragma unroll
-    for (int j = 0; j < kKeysPerLane; ++j)
-        if (lane + 64u * j >= cnt) key[j] = 0;  // 0 ranks below every real key
-    if (kk >= cnt) {
-        // keep everything: T = smallest key
-        uint64_t m = ~0ull;
-#pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j)
-            if (lane + 64u * j < cnt && key[j] < m) m = key[j];
-        const uint64_t T = wave_min_u64(m);
-        uint32_t wr = 0;
-#pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j) {
-            const bool keep = lane + 64u * j < cnt;
-            const uint64_t mm = __ballot(keep);
-            if (keep) {
-                const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
-                if (pos_out) pos_out[at] = (int32_t)key_pos(key[j]);
-                else buf[at] = key[j];
-            }
-            wr += __popcll(mm);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        return T;
-    }
-    uint64_t kmax = 0, kmin = ~0ull;
-#pragma unroll
-    for (int j = 0; j < kKeysPerLane; ++j) {
-        if (key[j] > kmax) kmax = key[j];
-        if (lane + 64u * j < cnt && key[j] < kmin) kmin = key[j];
-    }
-    kmax = wave_max_u64(kmax);
-    kmin = wave_min_u64(kmin);
-    int hi = 64 - __clzll((long long)(kmax ^ kmin));          // bits [hi, 64) are shared by every key
-    uint64_t pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
-    uint64_t prefix = kmax & pmask;
-    uint32_t need = kk;
-    uint64_t T = 0;
-    bool found = false;
-    while (hi > 0 && !found) {
-        const int lo = hi > 4 ? hi - 4 : 0;
-        const uint32_t dmask = (1u << (hi - lo)) - 1u;
-#pragma unroll
-        for (int b = 0; b < 16; ++b) hist[b * 64 + lane] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j)
-            if (lane + 64u * j < cnt && (key[j] & pmask) == prefix)
-                atomicAdd(&hist[(((uint32_t)(key[j] >> lo)) & dmask) * 64 + lane], 1u);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        // bin totals: lane 4b+q sums lanes 16q..16q+15 of bin b, then 4 lanes combine
-        uint32_t part = 0;
-        {
-            const int b = lane >> 2, q = lane & 3;
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) part += hist[b * 64 + 16 * q + jj];
-            part += __shfl_xor(part, 1);
-            part += __shfl_xor(part, 2);
-        }
-        uint32_t above = 0, dd = 0, in_bin = 0;
-#pragma unroll
-        for (int b = 15; b >= 0; --b) {
-            const uint32_t c = __builtin_amdgcn_readlane(part, 4 * b);
-            if (!in_bin && b <= (int)dmask && above + c >= need) {
-                dd = (uint32_t)b;
-                in_bin = c;
-            } else if (!in_bin) {
-                above += c;
-            }
-        }
-        need -= above;
-        prefix |= (uint64_t)dd << lo;
-        pmask |= (uint64_t)dmask << lo;
-        __builtin_amdgcn_wave_barrier();
-        if (in_bin == need) {
-            // every key under this prefix is selected: T is the smallest of them
-            uint64_t m = ~0ull;
-#pragma unroll
-            for (int j = 0; j < kKeysPerLane; ++j)
-                if (lane + 64u * j < cnt && (key[j] & pmask) == prefix && key[j] < m) m = key[j];
-            T = wave_min_u64(m);
-            found = true;
-        }
-        hi = lo;
-    }
-    if (!found) T = prefix;  // all 64 bits fixed
-    uint32_t wr = 0;
-#pragma unroll
-    for (int j = 0; j < kKeysPerLane; ++j) {
-        const bool keep = lane + 64u * j < cnt && key[j] >= T;
-        const uint64_t mm = __ballot(keep);
-        if (keep) {
-            const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
-            if (pos_out) pos_out[at] = (int32_t)key_pos(key[j]);
-            else buf[at] = key[j];
-        }
-        wr += __popcll(mm);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    return T;
+    return wave_topk_ordered<kKeysPerLane>(buf, cnt, kk, hist, pos_out, buf);
 }
 
 template <int H, int D, int KV>

@@ -343,40 +343,52 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 }
 
 // Merge split partials (m, l, O per head, base-2) into O, LSE.
-// One block of D threads per (token, head): the weights 2^(m_s - M) are formed
-// once per split and thread d accumulates O[d] over the splits.
+// Grid (token, head, d/32); a block is 32 output columns x 8 groups of splits,
+// so even hundreds of splits are read with 8-way parallelism per column.
+constexpr int kCombThreads = 256;
 template <int H, int D, int QT>
-__global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
-    __shared__ float red[D / 64 + 1];
-    const int tok = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
+    __shared__ float red_m[kCombThreads / 64];
+    __shared__ float red_o[8][32], red_l[8][32];
+    const int tok = blockIdx.x, h = blockIdx.y, d0 = 32 * blockIdx.z;
+    const int tid = threadIdx.x, dl = tid & 31, gs = tid >> 5;
     const size_t rec = (size_t)H * (D + 2);
     const float* base = a.part + (size_t)tok * a.n_split * rec;
-    // M = max_s m_s
     float mm = kNegBig;
-    for (int s = d; s < a.n_split; s += D) mm = fmaxf(mm, base[(size_t)s * rec + h]);
+    for (int s = tid; s < a.n_split; s += kCombThreads) mm = fmaxf(mm, base[(size_t)s * rec + h]);
     mm = wave_max(mm);
-    if ((d & 63) == 0) red[d >> 6] = mm;
+    if ((tid & 63) == 0) red_m[tid >> 6] = mm;
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) mm = fmaxf(mm, red[w]);
-    __syncthreads();
+    for (int w = 0; w < kCombThreads / 64; ++w) mm = fmaxf(mm, red_m[w]);
     float ll = 0.f, oo = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
+#pragma unroll 4
+    for (int s = gs; s < a.n_split; s += 8) {
         const float* r = base + (size_t)s * rec;
         const float f = fast_exp2(r[h] - mm);
         ll += r[H + h] * f;
-        oo += r[2 * H + h * D + d] * f;
+        oo += r[2 * H + h * D + d0 + dl] * f;
     }
-    const float o = ll > 0.f ? oo / ll : 0.f;
-    const size_t oi = ((size_t)tok * H + h) * D + d;
-    if constexpr (QT == DT_F32)
-        reinterpret_cast<float*>(a.out)[oi] = o;
-    else
-        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
-    if (d == 0) {
-        const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
-        if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
-        if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
+    red_o[gs][dl] = oo;
+    red_l[gs][dl] = ll;
+    __syncthreads();
+    if (gs == 0) {
+#pragma unroll
+        for (int q = 1; q < 8; ++q) {
+            oo += red_o[q][dl];
+            ll += red_l[q][dl];
+        }
+        const float o = ll > 0.f ? oo / ll : 0.f;
+        const size_t oi = ((size_t)tok * H + h) * D + d0 + dl;
+        if constexpr (QT == DT_F32)
+            reinterpret_cast<float*>(a.out)[oi] = o;
+        else
+            reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
+        if (d0 == 0 && dl == 0) {
+            const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
+            if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
+            if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
+        }
     }
 }
 
@@ -417,11 +429,11 @@ hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather
 
 template <int H, int D>
 static hipError_t launch_combine_hd(const CombineArgs& a, int qt, hipStream_t st) {
-    const dim3 grid((unsigned)a.n_tok, (unsigned)H);
+    const dim3 grid((unsigned)a.n_tok, (unsigned)H, (unsigned)(D / 32));
     if (qt == DT_F32)
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), grid, dim3(D), 0, st, a);
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), grid, dim3(kCombThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), grid, dim3(D), 0, st, a);
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), grid, dim3(kCombThreads), 0, st, a);
     return hipGetLastError();
 }
 

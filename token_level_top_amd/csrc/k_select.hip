@@ -9,26 +9,31 @@
 // largest scores, ties to the lower position, written in ascending position
 // order.
 //
-// Selection runs in three steps over a row of non-negative fp32 scores:
-//  1. histogram of the top 12 bits (8 exponent + 4 mantissa bits) -- many
-//     workgroups per row, LDS histograms merged with global atomics;
-//  2. every workgroup finds the bin holding the k-th largest score from the
-//     complete histogram and appends the rank keys of all scores in that bin
-//     or above to a per-row candidate list (wave-aggregated atomics);
-//  3. one workgroup per row sorts the candidates (bitonic, in LDS), keeps the
-//     first k and sorts their positions. If the threshold bin held more
-//     candidates than fit, the row falls back to an exact multi-pass radix
-//     select over the whole row.
+// Selection over a row of non-negative fp32 scores, in position order throughout:
+//  1. histogram of the top 12 bits (8 exponent + 4 mantissa bits): many
+//     workgroups per row, LDS histograms merged with global atomics; then one
+//     workgroup per row finds the bin holding the k-th largest score;
+//  2. count: every wave counts the scores in that bin or above in its 2048-score
+//     slice;
+//  3. emit: every wave writes the rank keys of those scores, in position order,
+//     at the offset given by the counts of all earlier slices -- so the row's
+//     candidate list is ordered by position;
+//  4. final: one wave loads the candidates into registers, finds the exact k-th
+//     largest key and writes the positions of the keys at or above it, which come
+//     out ascending. Rows whose threshold bin holds more candidates than fit
+//     fall back to an exact multi-pass radix select over the whole row.
 // The 64-bit rank key (score bits, complemented position) makes every key
-// distinct, so the result is unique and independent of the candidate order.
+// distinct, so the result is unique.
 #include "hs2_device.h"
 #include "hs2_internal.h"
+#include "hs2_wave_select.h"
 
 namespace hs2 {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelChunk = 8192;      // scores per workgroup in steps 1 and 2
-constexpr int kFinThreads = 1024;
+constexpr int kFinThreads = 256;
+constexpr int kSubLen = 2048;     // scores per wave in the count / emit steps
 
 __device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s) & 0x7FFFFFFFu; }
 __device__ __forceinline__ uint32_t score_bin(float s) { return score_bits(s) >> 19; }
@@ -52,6 +57,82 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h_lds, uint32_t* h_gl
         const uint32_t c = h_lds[b];
         if (c) atomicAdd(h_glob + b, c);
     }
+}
+
+// Threshold bin: the largest b with (count of bins >= b) >= kk. Returns b and the
+// count of bins strictly above it. Called by all threads of a 256-thread block.
+__device__ void threshold_bin(const uint32_t* hist_glob, uint32_t kk, uint32_t* sh_scan, int* out_bin,
+                              uint32_t* out_above) {
+    constexpr int PER = kHistBins / kSelThreads;  // 16 bins per thread, thread t owns the t-th block from the top
+    const int t = threadIdx.x;
+    const int hi = kHistBins - 1 - PER * t;       // bins hi, hi-1, ..., hi-PER+1
+    uint32_t loc[PER];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        loc[i] = hist_glob[hi - i];
+        sum += loc[i];
+    }
+    sh_scan[t] = sum;
+    __syncthreads();
+    // inclusive prefix over threads (from the top bin down), Hillis-Steele
+    for (int off = 1; off < kSelThreads; off <<= 1) {
+        const uint32_t v = t >= off ? sh_scan[t - off] : 0u;
+        __syncthreads();
+        sh_scan[t] += v;
+        __syncthreads();
+    }
+    const uint32_t before = t ? sh_scan[t - 1] : 0u;
+    if (before < kk && before + sum >= kk) {
+        uint32_t acc = before;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (acc + loc[i] >= kk) {
+                *out_bin = hi - i;
+                *out_above = acc;
+                break;
+            }
+            acc += loc[i];
+        }
+    }
+    __syncthreads();
+}
+
+
+// One workgroup per row: the threshold bin of the complete histogram.
+// thr[0] = bin (kHistBins if nothing is to be selected), thr[1] = count above it.
+__global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(const uint32_t* hist, uint32_t* thr,
+                                                                        const int32_t* n_cand, int64_t row_len,
+                                                                        int k) {
+    __shared__ uint32_t scan[kSelThreads];
+    __shared__ int bin_sh;
+    __shared__ uint32_t above_sh;
+    const int64_t r = blockIdx.x;
+    const int64_t n = n_cand ? (int64_t)n_cand[r] : row_len;
+    const uint32_t kk = (uint32_t)min<int64_t>(k, n);
+    if (kk == 0) {
+        if (threadIdx.x == 0) {
+            thr[2 * r] = kHistBins;
+            thr[2 * r + 1] = 0;
+        }
+        return;
+    }
+    if (threadIdx.x == 0) {
+        bin_sh = 0;
+        above_sh = 0;
+    }
+    __syncthreads();
+    threshold_bin(hist + (size_t)r * kHistBins, kk, scan, &bin_sh, &above_sh);
+    if (threadIdx.x == 0) {
+        thr[2 * r] = (uint32_t)bin_sh;
+        thr[2 * r + 1] = above_sh;
+    }
+}
+
+hipError_t launch_select_threshold(const SelectArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(select_threshold_kernel, dim3((unsigned)a.rows), dim3(kSelThreads), 0, st, a.hist, a.thr,
+                       a.n_cand, a.row_len, a.k);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- decode score
@@ -119,118 +200,61 @@ hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Threshold bin: the largest b with (count of bins >= b) >= kk. Returns b and the
-// count of bins strictly above it. Called by all threads of a 256-thread block.
-__device__ void threshold_bin(const uint32_t* hist_glob, uint32_t kk, uint32_t* sh_scan, int* out_bin,
-                              uint32_t* out_above) {
-    constexpr int PER = kHistBins / kSelThreads;  // 16 bins per thread, thread t owns the t-th block from the top
-    const int t = threadIdx.x;
-    const int hi = kHistBins - 1 - PER * t;       // bins hi, hi-1, ..., hi-PER+1
-    uint32_t loc[PER];
-    uint32_t sum = 0;
+// ------------------------------------------------- steps 2, 3: count and emit
+// A wave owns the 2048-score slice `sub` = 4 * blockIdx.x + wave of its row.
+__global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a) {
+    const int64_t r = blockIdx.y;
+    const int lane = threadIdx.x & 63, sub = 4 * blockIdx.x + (threadIdx.x >> 6);
+    if (sub >= a.n_sub) return;
+    const int64_t n = row_cands(a, r);
+    const uint32_t tbin = a.thr[2 * r];
+    const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
+    const int64_t j0 = (int64_t)sub * kSubLen, j1 = min<int64_t>(j0 + kSubLen, n);
+    uint32_t c = 0;
+    for (int64_t j = j0 + lane; j < j1; j += 64) c += score_bin(s[j]) >= tbin ? 1u : 0u;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        loc[i] = hist_glob[hi - i];
-        sum += loc[i];
-    }
-    sh_scan[t] = sum;
-    __syncthreads();
-    // inclusive prefix over threads (from the top bin down), Hillis-Steele
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-        const uint32_t v = t >= off ? sh_scan[t - off] : 0u;
-        __syncthreads();
-        sh_scan[t] += v;
-        __syncthreads();
-    }
-    const uint32_t before = t ? sh_scan[t - 1] : 0u;
-    if (before < kk && before + sum >= kk) {
-        uint32_t acc = before;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (acc + loc[i] >= kk) {
-                *out_bin = hi - i;
-                *out_above = acc;
-                break;
-            }
-            acc += loc[i];
-        }
-    }
-    __syncthreads();
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) a.counts[(size_t)r * a.n_sub + sub] = c;
 }
 
-// -------------------------------------------------------- step 2: collect keys
-__global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs a) {
-    __shared__ uint32_t scan[kSelThreads];
-    __shared__ int bin_sh;
-    __shared__ uint32_t above_sh;
+__global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
     const int64_t r = blockIdx.y;
+    const int lane = threadIdx.x & 63, sub = 4 * blockIdx.x + (threadIdx.x >> 6);
+    if (sub >= a.n_sub) return;
     const int64_t n = row_cands(a, r);
-    const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
-    if (kk == 0) return;
-    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
-    if (j0 >= n) return;
-    if (threadIdx.x == 0) {
-        bin_sh = 0;
-        above_sh = 0;
-    }
-    __syncthreads();
-    threshold_bin(a.hist + (size_t)r * kHistBins, kk, scan, &bin_sh, &above_sh);
-    const uint32_t tbin = (uint32_t)bin_sh;
-    const int64_t j1 = min<int64_t>(j0 + kSelChunk, n);
+    const int64_t j0 = (int64_t)sub * kSubLen, j1 = min<int64_t>(j0 + kSubLen, n);
+    if (j0 >= j1) return;
+    const uint32_t tbin = a.thr[2 * r];
+    const uint32_t* cnt = a.counts + (size_t)r * a.n_sub;
+    uint32_t before = 0;  // candidates in earlier slices of the row
+    for (int q = lane; q < sub; q += 64) before += cnt[q];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o);
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    // pass A: count this workgroup's candidates; one global atomic reserves the range
-    uint32_t mine = 0;
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) mine += score_bin(s[j]) >= tbin ? 1u : 0u;
-    if (threadIdx.x == 0) scan[0] = 0;
-    __syncthreads();
-    if (mine) atomicAdd(&scan[0], mine);
-    __syncthreads();
-    const uint32_t total = scan[0];
-    if (total == 0) return;
-    __shared__ uint32_t base_sh, fill_sh;
-    if (threadIdx.x == 0) {
-        base_sh = atomicAdd(a.cand_count + r, total);
-        fill_sh = 0;
-    }
-    __syncthreads();
-    const uint32_t base = base_sh;
-    // pass B: write the keys (order within the range is irrelevant: keys are distinct)
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) {
-        const float v = s[j];
-        if (score_bin(v) >= tbin) {
-            const uint32_t slot = base + atomicAdd(&fill_sh, 1u);
-            if (slot < (uint32_t)kCandCap) cand[slot] = rank_key(v, (uint32_t)j);
-        }
+    for (int64_t jb = j0; jb < j1; jb += 64) {
+        const int64_t j = jb + lane;
+        const float v = j < j1 ? s[j] : 0.f;
+        const bool take = j < j1 && score_bin(v) >= tbin;
+        const uint64_t m = __ballot(take);
+        const uint32_t at = before + __popcll(m & ((1ull << lane) - 1ull));
+        if (take && at < (uint32_t)kCandCap) cand[at] = rank_key(v, (uint32_t)j);
+        before += __popcll(m);
     }
 }
 
-hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.row_len + kSelChunk - 1) / kSelChunk), (unsigned)a.rows);
-    hipLaunchKernelGGL(select_collect_kernel, grid, dim3(kSelThreads), 0, st, a);
+hipError_t launch_select_count(const SelectArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.n_sub + 3) / 4), (unsigned)a.rows);
+    hipLaunchKernelGGL(select_count_kernel, grid, dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_select_emit(const SelectArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.n_sub + 3) / 4), (unsigned)a.rows);
+    hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------- step 3: final
-template <typename K, bool DESC>
-__device__ void bitonic_lds(K* x, int n) {  // n is a power of two, all threads of the block
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool dir = ((lo & size) == 0) == DESC;  // true: larger first
-                const K a = x[lo], b = x[hi];
-                if (dir ? (a < b) : (a > b)) {
-                    x[lo] = b;
-                    x[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 // Block-wide exclusive prefix sum of one value per thread (1024 threads).
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -331,9 +355,9 @@ __device__ void select_row_exact(const float* s, int64_t n, uint32_t kk, int32_t
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a, int window, int64_t p_last) {
+    __shared__ uint32_t scratch[kCompactScratch];
     __shared__ uint64_t keys[kCandCap];
-    __shared__ uint32_t pos[2048];
-    __shared__ uint32_t sh[256];
+    __shared__ uint32_t nc_sh;
     const int64_t r = blockIdx.x;
     int32_t* out = a.out + (size_t)r * (size_t)a.out_stride;
     // forced window (decode rows all sit at p_last)
@@ -347,23 +371,24 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
     for (int t = threadIdx.x + kk; t < a.k; t += blockDim.x) out[t] = -1;
     if (kk == 0) return;
-    const uint32_t nc = a.cand_count[r];
+    if (threadIdx.x < 64) {
+        uint32_t c = 0;
+        for (int q = threadIdx.x; q < a.n_sub; q += 64) c += a.counts[(size_t)r * a.n_sub + q];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+        if (threadIdx.x == 0) nc_sh = c;
+    }
+    __syncthreads();
+    const uint32_t nc = nc_sh;
     if (nc > (uint32_t)kCandCap) {
-        select_row_exact(a.scores + (size_t)r * (size_t)a.row_stride, n, kk, out, sh, reinterpret_cast<uint32_t*>(keys));
+        uint32_t* tmp = reinterpret_cast<uint32_t*>(scratch);
+        select_row_exact(a.scores + (size_t)r * (size_t)a.row_stride, n, kk, out, tmp + 512, tmp);
         return;
     }
-    int np = 2;
-    while (np < (int)nc) np <<= 1;
     const uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    for (int i = threadIdx.x; i < np; i += blockDim.x) keys[i] = i < (int)nc ? cand[i] : 0ull;
+    for (uint32_t i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = cand[i];
     __syncthreads();
-    bitonic_lds<uint64_t, true>(keys, np);
-    int nk = 2;
-    while (nk < (int)kk) nk <<= 1;
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) pos[i] = i < (int)kk ? key_pos(keys[i]) : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_lds<uint32_t, false>(pos, nk);
-    for (int i = threadIdx.x; i < (int)kk; i += blockDim.x) out[i] = (int32_t)pos[i];
+    if (threadIdx.x < 64) wave_topk_ordered_lds(keys, nc, kk, scratch, out);
 }
 
 hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st) {
