@@ -41,7 +41,7 @@ KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
       "prefill_final": 10, "fill": 11}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
-KSRC = {"decode_split_attn": "k_rows.hip", "attn_fwd": "k_prefill.hip"}
+KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip"}
 
 
 def log(*a):

@@ -105,6 +105,9 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
  *   indices  [B][n_q][window+k_global] int32     index rows (layout above)
  *   workspace >= hs2_workspace_size(HS2_OP_FULL_ATTN_SELECT, ...) bytes
  * Scores are computed on the fly and never stored as an n_q x n_ctx matrix.
+ * Limit: d * n_ctx (rounded up to a multiple of 64) < 2^31, else
+ * HS2_ERR_INVALID_ARG. With an FP8 cache the PV product uses the bf16
+ * rounding of code x v_scale; logits use the exact K values and k_scale.
  */
 int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* v,
                          const float* k_scale, const float* v_scale, int kv_dtype, int B,

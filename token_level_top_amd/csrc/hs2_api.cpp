@@ -501,6 +501,7 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     if (ss == HS2_ERR_INVALID_ARG) return ss;
     if (n_q <= 0 || q_pos0 < 0 || q_pos0 + n_q > n_ctx) return HS2_ERR_INVALID_ARG;
     if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if ((n_ctx + kVtPad - 1) / kVtPad * kVtPad * (int64_t)d >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
     if (!q || !out || !lse || !indices) return HS2_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
     if (st != HS2_OK) return st;
@@ -530,7 +531,7 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     a.cand = w.cand;
     a.cand_cap = kPrefillCandCap;
     a.indices = indices;
-    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
     HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
     HS2_TRY(TIMED(KC_STREAM, s, launch_score_stream(a, H, d, kv_dtype, s)));
     return HS2_OK;

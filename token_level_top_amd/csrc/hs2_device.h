@@ -76,6 +76,9 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// By value on purpose: clang's __builtin_bit_cast applied directly to an
+// ext_vector element (v[e]) reads element 0 whatever e is.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
 // value of the lane l^32 (other half of the wave), via one permlane32 swap
 __device__ __forceinline__ float xor32(float x) {

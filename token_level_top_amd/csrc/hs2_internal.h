@@ -94,7 +94,7 @@ struct PrefillArgs {
     const void* q;          // [B][n_q][H][D]
     const void* k;          // [B][n_ctx][D] (bf16 or f32; fp8 is pre-converted into kc)
     const uint16_t* kc;     // FP8 only: [B][n_ctx][D] bf16 values of the codes
-    const void* vt;         // [B][D][n_ctx_pad] transposed V (bf16 or f32)
+    const void* vt;         // [B][D][n_ctx_pad] transposed V (f32, or bf16; FP8: bf16 of code x scale)
     const float* ks;        // [B][n_ctx]
     const float* vs;
     int64_t n_q, q_pos0, n_ctx, n_ctx_pad;
@@ -108,8 +108,8 @@ struct PrefillArgs {
     int cand_cap;
     int32_t* indices;       // [B][n_q][window + k_global]
 };
-hipError_t launch_prep_kv(const void* k, const void* v, int kv, int B, int64_t n_ctx, int64_t n_ctx_pad, int D,
-                          uint16_t* kc, void* vt, hipStream_t st);
+hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
+                          int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st);
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
 // pass 2 also writes the index rows (window + global part)
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);

@@ -8,17 +8,23 @@
 // head average; the sum ranks identically).
 //
 // Kernels, all on one stream:
-//  prep_kv        V -> V^T (bf16 or f32, padded to 64 keys) and FP8 K -> bf16 K
-//                 (exact), so both MFMA operands read contiguous LDS rows.
-//  attn_fwd       pass 1: flash attention on v_mfma_f32_32x32x16_bf16 (or
-//                 32x32x2f32). A workgroup owns 256 (token, head) rows: 256/H
-//                 consecutive tokens with all their heads, because MQA lets every
-//                 head share one K/V tile. S^T = K Q^T puts the keys of a 32x32
-//                 block in-lane, so the row maximum is an in-lane max plus one
-//                 lane swap. Writes O and the per-head LSE.
+//  prep_kv        V -> V^T (bf16 or f32, padded to 64 keys; FP8 V as the bf16
+//                 rounding of code x scale) and FP8 K -> bf16 K (exact), so
+//                 both MFMA operands read contiguous LDS rows.
+//  attn_fwd_pipe  pass 1 (bf16 and FP8 caches): flash attention on
+//                 v_mfma_f32_32x32x16_bf16. A workgroup owns 256 (token, head)
+//                 rows: 256/H consecutive tokens with all their heads, because
+//                 MQA lets every head share one K/V tile. S^T = K Q^T puts the
+//                 keys of a 32x32 block in-lane, so the row maximum is an in-lane
+//                 max plus one lane swap. The QK^T MFMAs of the next 32-key block
+//                 are issued next to the softmax of the current one; tiles are
+//                 triple-buffered in LDS (one barrier per tile). Writes O and
+//                 the per-head LSE.
+//  attn_fwd       pass 1 for fp32 caches (v_mfma_f32_32x32x2f32), not pipelined.
 //  score_stream   pass 2: recomputes S = Q K^T (rows on M, keys on N, so one lane
 //                 holds several heads of one key), forms score = sum_h
-//                 exp(s - LSE_h) with at most one lane swap, and streams each
+//                 exp(s - LSE_h) with at most one lane swap (the next block's
+//                 MFMAs issued next to it, as in pass 1), and streams each
 //                 token's candidates: scores above the token's current k-th best
 //                 key are appended (wave ballot) to a per-token buffer; a full
 //                 buffer is compacted to its exact top k by a wave-level radix
@@ -66,8 +72,8 @@ __device__ __forceinline__ f32x16 mfma32(const float* a, const float* b, f32x16 
 // grid (n_ctx_pad / 64, B), 256 threads. V^T[b][d][j] for j < n_ctx_pad (0 past
 // n_ctx); FP8: kc[b][j][d] = bf16(code value), exact.
 template <int D, int KV>
-__global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void* v, int64_t n_ctx, int64_t n_ctx_pad,
-                                                      uint16_t* kc, void* vt) {
+__global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void* v, const float* vs, int64_t n_ctx,
+                                                      int64_t n_ctx_pad, uint16_t* kc, void* vt) {
     constexpr bool F32 = KV == DT_F32;
     using LT = typename PfTypes<F32>::L;
     __shared__ LT tile[kPfTile][D + 1];
@@ -86,7 +92,9 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void*
                 val = reinterpret_cast<const uint16_t*>(v)[gi];
             } else {
                 const uint32_t code = reinterpret_cast<const uint8_t*>(v)[gi];
-                val = (uint16_t)(fp8x4_to_bf16x4(code)[0] & 0xFFFFu);
+                float f[4];
+                fp8x4_to_f32(code, f);
+                val = f32_to_bf16_bits(f[0] * vs[base + (size_t)j]);
                 const uint32_t kcode = reinterpret_cast<const uint8_t*>(k)[gi];
                 kc[gi] = (uint16_t)(fp8x4_to_bf16x4(kcode)[0] & 0xFFFFu);
             }
@@ -94,17 +102,23 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void*
         tile[r][c] = val;
     }
     __syncthreads();
+    // bf16 V^T: within every 16 keys the middle two quads are swapped (keys
+    // 0-3 8-11 4-7 12-15), so that the 8 keys one lane of the PV MFMA takes
+    // are one contiguous 16-byte piece
     LT* out = reinterpret_cast<LT*>(vt) + (size_t)b * D * (size_t)n_ctx_pad;
     for (int e = threadIdx.x; e < kPfTile * D; e += 256) {
         const int c = e / kPfTile, r = e % kPfTile;
-        out[(size_t)c * n_ctx_pad + j0 + r] = tile[r][c];
+        const int q = (r >> 2) & 3;
+        const int slot = F32 ? r : (r & ~15) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2) | (r & 3);
+        out[(size_t)c * n_ctx_pad + j0 + slot] = tile[r][c];
     }
 }
 
-hipError_t launch_prep_kv(const void* k, const void* v, int kv, int B, int64_t n_ctx, int64_t n_ctx_pad, int D,
-                          uint16_t* kc, void* vt, hipStream_t st) {
+hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
+                          int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st) {
     dim3 grid((unsigned)(n_ctx_pad / kPfTile), (unsigned)B);
-#define HS2_PREP(DD, KK) hipLaunchKernelGGL((prep_kv_kernel<DD, KK>), grid, dim3(256), 0, st, k, v, n_ctx, n_ctx_pad, kc, vt)
+#define HS2_PREP(DD, KK) \
+    hipLaunchKernelGGL((prep_kv_kernel<DD, KK>), grid, dim3(256), 0, st, k, v, vs, n_ctx, n_ctx_pad, kc, vt)
     if (D == 64) {
         if (kv == DT_F32) HS2_PREP(64, DT_F32);
         else if (kv == DT_BF16) HS2_PREP(64, DT_BF16);
@@ -273,7 +287,11 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
     __syncthreads();
 
     float ks_pf = 0.f, vs_pf = 0.f;  // FP8 scales of the next tile (thread < 64)
-    for (int it = 0; it < n_tiles; ++it) {
+    // One 64-key tile. Tiles that end at or before the block's first query
+    // position need no causal mask; only the last one or two tiles of a block
+    // do, and they compare 32-bit positions relative to the tile.
+    auto tile = [&](int it, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int cur = it & 1;
         const int64_t j0 = (int64_t)it * kPfTile;
         if (it + 1 < n_tiles) {
@@ -286,7 +304,8 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
                 }
             }
         }
-        const bool need_mask = j0 + kPfTile - 1 > p_min;
+        // keys kk of this tile with kk > rel lie after this lane's query
+        const int rel = MASK ? (int)min<int64_t>(my_p - j0, kPfTile) - 4 * hh : 0;
         const LT* kl = k_lds[cur];
         const LT* vl = v_lds[cur];
 #pragma unroll
@@ -298,21 +317,23 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
             const LT* krow = kl + (32 * sub + n) * KLD + VPL * hh;
 #pragma unroll
             for (int s = 0; s < NS; ++s) sacc = mfma32(krow + KD * s, &qf[s][0], sacc);
-            // x = logits in base-2 units (FP8: per-key scale folded in); the running
+            // x = logits (FP8: per-key scale folded in, base-2 units); the running
             // maximum m_run is only raised when a block exceeds it by more than
             // kLazy (2^8), so the O rescale is rare; p <= 2^kLazy stays exact
             // enough in bf16/fp32 and the final LSE uses the same m_run.
             float x[16];
-            float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int kk = 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
                 float v = sacc[i];
-                if constexpr (SCALED) v *= a.scale_log2 * ks_lds[cur][kk];
-                if (need_mask && j0 + kk > my_p) v = -INFINITY;
+                if constexpr (SCALED) v *= a.scale_log2 * ks_lds[cur][32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3)];
+                if constexpr (MASK) {
+                    if (32 * sub + 8 * (i >> 2) + (i & 3) > rel) v = -INFINITY;
+                }
                 x[i] = v;
-                mx = fmaxf(mx, v);
             }
+            float mx = x[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
             mx = fmaxf(mx, xor32(mx));
             if constexpr (!SCALED) mx *= a.scale_log2;
             const bool grow = mx > m_run + kLazy;
@@ -377,7 +398,11 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
             }
         }
         __syncthreads();
-    }
+    };
+    const int n_full = min<int>(n_tiles, (int)((p_min + 1) / kPfTile));
+    int it = 0;
+    for (; it < n_full; ++it) tile(it, std::integral_constant<bool, false>{});
+    for (; it < n_tiles; ++it) tile(it, std::integral_constant<bool, true>{});
 
     // finish: both wave halves hold disjoint key subsets of the same row
     const float l_tot = l_run + xor32(l_run);
@@ -408,6 +433,264 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
     }
 }
 
+// --------------------------------------------------------- attn_fwd (bf16)
+// Pass 1 for bf16 operands (bf16 K and V, or FP8 K widened to bf16 with its
+// per-key scale applied to the logits, and FP8 V with its scale folded into
+// the bf16 V^T copy). The 32-key blocks of a row are software-pipelined: the
+// QK^T MFMAs of block g+1 are issued next to the softmax of block g, so matrix
+// and vector work of one wave overlap. The running maximum is lazy: exponents
+// are taken against the current m_run and only when a lane's 16 terms sum past
+// 16 * 2^kLazy (or overflow) is the block's maximum formed, O and l rescaled
+// and the block redone; for a row that rarely happens after its first block.
+// Tiles are triple-buffered in LDS, so one barrier per 64-key tile suffices.
+constexpr int kPfBufs = 3;
+constexpr float kPsumMax = 16.0f * 256.0f;  // 16 terms of at most 2^kLazy each
+
+template <int D, bool SCALED>
+struct PipeStage {
+    static constexpr int KLD = D + 8;                          // K tile row stride (elements)
+    static constexpr int VLD = kPfTile + 8;                    // V^T tile row stride
+    static constexpr int KPT = kPfTile * D / 8 / kPfThreads;   // 16-B K pieces per thread
+    static constexpr int VPT = D * kPfTile / 8 / kPfThreads;   // 16-B V^T pieces per thread
+    static_assert(KPT >= 1 && VPT >= 1, "whole pieces per thread");
+    u32x4 kr[KPT], vr[VPT];
+    f32x4 cr;
+
+    // Tile t: K rows 64t.. (clamped into the cache; rows past the end are
+    // masked by causality), V^T columns 64t.. of the zero-padded copy, and
+    // for FP8 the 64 key scales.
+    __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vtb, const float* ksb, int t, int n_ctx,
+                                         int n_ctx_pad) {
+        const int tid = threadIdx.x, j0 = kPfTile * t;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int ch = tid + kPfThreads * i, row = ch / (D / 8), cc = ch % (D / 8);
+            const int j = min(j0 + row, n_ctx - 1);
+            kr[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)(j * D + cc * 8));
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int ch = tid + kPfThreads * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
+            vr[i] = *reinterpret_cast<const u32x4*>(vtb + (uint32_t)(d * n_ctx_pad + j0 + cc * 8));
+        }
+        if constexpr (SCALED) {
+            if (tid < kPfTile / 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cr[e] = ksb[min(j0 + 4 * tid + e, n_ctx - 1)];
+            }
+        }
+    }
+    // (the bf16 V^T copy already holds its keys quad-permuted within each 16)
+    __device__ __forceinline__ void store(uint16_t* kl, uint16_t* vl, float* cl, float scale_log2) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int ch = tid + kPfThreads * i, row = ch / (D / 8), cc = ch % (D / 8);
+            *reinterpret_cast<u32x4*>(kl + row * KLD + cc * 8) = kr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int ch = tid + kPfThreads * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
+            *reinterpret_cast<u32x4*>(vl + d * VLD + cc * 8) = vr[i];
+        }
+        if constexpr (SCALED) {
+            if (tid < kPfTile / 4) *reinterpret_cast<f32x4*>(cl + 4 * tid) = cr * scale_log2;
+        }
+    }
+};
+
+template <int H, int D, int KV>
+__global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a) {
+    constexpr bool SCALED = KV == DT_FP8;
+    using Stage = PipeStage<D, SCALED>;
+    constexpr int KLD = Stage::KLD, VLD = Stage::VLD, NS = D / 16, NDT = D / 32;
+    constexpr int TB = kPfRows / H;  // tokens per workgroup
+
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPfBufs][kPfTile * KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPfBufs][D * VLD];
+    __shared__ __attribute__((aligned(16))) float c_lds[kPfBufs][kPfTile];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int n_blk = (int)((a.n_q + TB - 1) / TB);
+    const int blk = n_blk - 1 - (int)blockIdx.x;  // longest rows first
+    const int b = blockIdx.y;
+    const int64_t tok0 = (int64_t)blk * TB;
+    const int R = 32 * w + n;  // this lane's (token, head) row in the block
+    const int64_t my_tok = tok0 + R / H;
+    const int my_head = R % H;
+    const bool row_ok = my_tok < a.n_q;
+    const int64_t my_p = a.q_pos0 + my_tok;
+    const int64_t p_min = a.q_pos0 + tok0;
+    const int64_t p_max = a.q_pos0 + min<int64_t>(tok0 + TB, a.n_q) - 1;
+
+    // Q^T fragment (B operand of S^T = K Q^T): column = row R, k = 16s + 8hh + [0, 8)
+    u32x4 qf[NS];
+    {
+        const size_t qb = (((size_t)b * a.n_q + (size_t)(row_ok ? my_tok : 0)) * H + my_head) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qb + 16 * s + 8 * hh);
+            qf[s] = row_ok ? w4 : u32x4{0, 0, 0, 0};
+        }
+    }
+    const uint16_t* kb = (SCALED ? a.kc : reinterpret_cast<const uint16_t*>(a.k)) + (size_t)b * a.n_ctx * D;
+    const uint16_t* vtb = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)b * D * a.n_ctx_pad;
+    const float* ksb = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
+    const int n_ctx = (int)a.n_ctx, n_ctx_pad = (int)a.n_ctx_pad;
+    const float scale_log2 = a.scale_log2;
+
+    float m_run = kNegBig, l_run = 0.f;
+    f32x16 o_acc[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o_acc[t][i] = 0.f;
+
+    const int n_tiles = (int)((p_max + kPfTile) / kPfTile);
+    const int n_full = min<int>(n_tiles, (int)((p_min + 1) / kPfTile));  // tiles needing no causal mask
+
+    // S^T block of keys 32*sub.. of an LDS tile (M) x this wave's 32 rows (N)
+    auto qk = [&](int buf, int sub) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const uint16_t* kr = k_lds[buf] + (32 * sub + n) * KLD + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * s)),
+                                                          as_bf16x8(qf[s]), acc, 0, 0, 0);
+        return acc;
+    };
+    // P = 2^(S * c - m_run) as the packed bf16 B operand of the PV MFMA; returns
+    // this lane's sum of the (rounded) terms. Accumulator i holds key
+    // 32*sub + 8(i/4) + 4hh + i%4; keys with 8(i/4) + i%4 > rel are masked.
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    auto softmax = [&](const f32x16& s, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float c[16];
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(&c_lds[buf][32 * sub + 8 * q4 + 4 * hh]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c[4 * q4 + e] = c4[e];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = scale_log2;
+        }
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            p[i] = fast_exp2(__builtin_fmaf(s[i], c[i], -m_run));
+            if constexpr (MASK) {
+                if (32 * sub + 8 * (i >> 2) + (i & 3) > rel) p[i] = 0.f;
+            }
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pb[h][e] = pack_bf16x2(p[8 * h + 2 * e], p[8 * h + 2 * e + 1]);
+                ps = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pb[h][e]), ones, ps, false);
+            }
+        }
+        return ps;
+    };
+    // rare: some term of the block exceeded 2^kLazy (or this is the row's first
+    // block); raise m_run to the block's row maximum, rescale, redo the block
+    auto settle = [&](float& ps, const f32x16& s, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        if (__ballot(!(ps <= kPsumMax))) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
+                const float ci = SCALED ? c_lds[buf][kk] : scale_log2;
+                float v = s[i] * ci;
+                if (MASK && 32 * sub + 8 * (i >> 2) + (i & 3) > rel) v = -INFINITY;
+                mx = fmaxf(mx, v);
+            }
+            mx = fmaxf(mx, xor32(mx));
+            const float m_new = mx > m_run + kLazy ? mx : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
+            ps = softmax(s, buf, sub, rel, pb, mask_tag);
+        }
+        l_run += ps;
+    };
+    // O^T += V^T P^T over keys 32*sub.. of an LDS tile
+    auto pv = [&](int buf, int sub, const u32x4* pb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const uint16_t* vr = v_lds[buf] + (32 * t + n) * VLD + 32 * sub + 16 * c + 8 * hh;
+                o_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(vr)),
+                                                                   as_bf16x8(pb[c]), o_acc[t], 0, 0, 0);
+            }
+    };
+
+    Stage stg;
+    stg.load(kb, vtb, ksb, 0, n_ctx, n_ctx_pad);
+    stg.store(k_lds[0], v_lds[0], c_lds[0], scale_log2);
+    __syncthreads();
+    if (n_tiles > 1) stg.load(kb, vtb, ksb, 1, n_ctx, n_ctx_pad);
+    f32x16 s_cur = qk(0, 0);
+    int buf = 0, nbuf = 1;  // LDS buffers of tiles T and T+1
+    // Tile T: [S(2T+1) | softmax 2T] [PV 2T] store T+1, barrier, load T+2,
+    //         [S(2T+2) | softmax 2T+1] [PV 2T+1]
+    auto tile = [&](int T, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int rel = MASK ? (int)min<int64_t>(my_p - (int64_t)kPfTile * T, kPfTile) - 4 * hh : 0;
+        u32x4 pb[2];
+        f32x16 s_nxt = qk(buf, 1);
+        float ps = softmax(s_cur, buf, 0, rel, pb, mask_tag);
+        settle(ps, s_cur, buf, 0, rel, pb, mask_tag);
+        pv(buf, 0, pb);
+        if (T + 1 < n_tiles) stg.store(k_lds[nbuf], v_lds[nbuf], c_lds[nbuf], scale_log2);
+        __syncthreads();
+        if (T + 2 < n_tiles) stg.load(kb, vtb, ksb, T + 2, n_ctx, n_ctx_pad);
+        s_cur = qk(nbuf, 0);  // after the last tile this reads a stale buffer; unused
+        ps = softmax(s_nxt, buf, 1, rel, pb, mask_tag);
+        settle(ps, s_nxt, buf, 1, rel, pb, mask_tag);
+        pv(buf, 1, pb);
+        buf = nbuf;
+        nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
+    };
+    int T = 0;
+    for (; T < n_full; ++T) tile(T, std::integral_constant<bool, false>{});
+    for (; T < n_tiles; ++T) tile(T, std::integral_constant<bool, true>{});
+
+    // finish: both wave halves hold disjoint key subsets of the same row
+    const float l_tot = l_run + xor32(l_run);
+    if (row_ok) {
+        const float inv = 1.f / l_tot;
+        const size_t ob = (((size_t)b * a.n_q + (size_t)my_tok) * H + my_head) * D;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const int d0 = 32 * t + 8 * (i >> 2) + 4 * hh;
+                u32x2 o2;
+                o2[0] = pack_bf16x2(o_acc[t][i] * inv, o_acc[t][i + 1] * inv);
+                o2[1] = pack_bf16x2(o_acc[t][i + 2] * inv, o_acc[t][i + 3] * inv);
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + ob + d0) = o2;
+            }
+        if (hh == 0) {
+            const float lse2 = m_run + log2f(l_tot);
+            const size_t li = ((size_t)b * a.n_q + (size_t)my_tok) * H + my_head;
+            a.lse[li] = lse2 * kLn2;
+            a.lse2[li] = lse2;
+        }
+    }
+}
+
 // ------------------------------------------------------------- score_stream
 constexpr int kKeysPerLane = 32;  // a token buffer of up to 2048 keys, in registers
 
@@ -428,8 +711,8 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     constexpr int TW = 32 / H;        // tokens per wave
     constexpr int NSC = 16 / H;       // scores per lane per 32-key block
 
-    __shared__ __attribute__((aligned(16))) LT k_lds[2][kPfTile * KLD];
-    __shared__ float ks_lds[2][kPfTile];
+    __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
+    __shared__ float ks_lds[kPfBufs][kPfTile];
     __shared__ uint32_t whist[kPfWaves][kCompactScratch];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -499,9 +782,9 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     const float* ksg = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
 
     const int n_tiles = (int)((c_max + kPfTile) / kPfTile);
-    // Appends of one tile are held in registers and issued at the top of the
-    // next tile, next to the prefetch loads: loads and stores share vmcnt, so a
-    // store issued mid-tile would be waited for at the tile's end.
+    // Appends are held in registers and issued after the next LDS tile store
+    // (whose wait covers the staged tile loads): loads and stores share vmcnt,
+    // so a store issued ahead of a tile load would be waited for with it.
     uint64_t pend_key[2][NSC];
     uint64_t* pend_ptr[2][NSC];
     bool pend_take[2][NSC];
@@ -519,97 +802,123 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
                     pend_take[sb][u] = false;
                 }
     };
-    float ks_pf = 0.f;  // FP8 key scale of the next tile (thread < 64)
-    Stage stg;
-    stg.load(kg, nullptr, 0, a.n_ctx, a.n_ctx_pad);
-    stg.store(k_lds[0], nullptr);
-    if constexpr (SCALED) {
-        if (tid < kPfTile) ks_lds[0][tid] = tid < a.n_ctx ? ksg[tid] : 0.f;
-    }
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int cur = it & 1;
-        const int64_t j0 = (int64_t)it * kPfTile;
-        flush();
-        if (it + 1 < n_tiles) {
-            stg.load(kg, nullptr, j0 + kPfTile, a.n_ctx, a.n_ctx_pad);
-            if constexpr (SCALED) {
-                if (tid < kPfTile) ks_pf = ksg[min<int64_t>(j0 + kPfTile + tid, a.n_ctx - 1)];
-            }
+    // S block: this wave's 32 rows (M) x keys 32*sub.. of an LDS tile (N)
+    auto qk = [&](int buf, int sub) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const LT* krow = k_lds[buf] + (32 * sub + n) * KLD + VPL * hh;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = mfma32(&qf[s][0], krow + KD * s, acc);
+        return acc;
+    };
+    // token scores of one S block, and the appends of keys above each token's
+    // current threshold (held in pend_*[sub])
+    auto score = [&](const f32x16& sacc, int buf, int sub, int64_t j0) {
+        const int64_t jpos = j0 + 32 * sub + n;  // this lane's key
+        float c = a.scale_log2;
+        if constexpr (SCALED) c *= ks_lds[buf][32 * sub + n];
+        // head sums: accumulator i holds row 8(i/4) + 4hh + i%4 of the wave
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
+            if constexpr (H == 16) part[i >> 3] += e;     // token i/8 (both halves)
+            else part[i >> 2] += e;                      // H=8: token i/4; H=4: token 2(i/4)+hh
         }
-        const LT* kl = k_lds[cur];
+        float sc[NSC];
+        if constexpr (H == 16) {
+            sc[0] = halves_sum(part[0], part[1]);
+        } else if constexpr (H == 8) {
+            sc[0] = halves_sum(part[0], part[2]);
+            sc[1] = halves_sum(part[1], part[3]);
+        } else {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int64_t jpos = j0 + 32 * sub + n;   // this lane's key
-            f32x16 sacc;
+            for (int u = 0; u < 4; ++u) sc[u] = part[u];
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-            const LT* krow = kl + (32 * sub + n) * KLD + VPL * hh;
+        for (int u = 0; u < NSC; ++u) {
+            const uint64_t key = rank_key(sc[u], (uint32_t)jpos);
+            const bool take = jpos <= climit[u] && key > thr[u];
+            const uint64_t m = __ballot(take);
+            const uint64_t half = hh ? (m >> 32) : (m & 0xFFFFFFFFull);
+            const uint32_t rank = __popcll(half & ((1ull << n) - 1ull));
+            const int64_t tk = wtok0 + tslot[u];
+            pend_take[sub][u] = take;
+            pend_key[sub][u] = key;
+            pend_ptr[sub][u] = a.cand + (row0 + (size_t)tk) * (size_t)cap + cnt[u] + rank;
+            cnt[u] += __popcll(half);
+        }
+    };
+    // a tile appends at most 64 keys per token: compact any buffer that could
+    // overflow before the tile's scores are appended
+    auto make_room = [&]() {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) sacc = mfma32(&qf[s][0], krow + KD * s, sacc);
-            float c = a.scale_log2;
-            if constexpr (SCALED) c *= ks_lds[cur][32 * sub + n];
-            // head sums: accumulator i holds row 8(i/4) + 4hh + i%4 of the wave
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < NSC; ++u) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
-                if constexpr (H == 16) part[i >> 3] += e;     // token i/8 (both halves)
-                else part[i >> 2] += e;                      // H=8: token i/4; H=4: token 2(i/4)+hh
-            }
-            float sc[NSC];
-            if constexpr (H == 16) {
-                sc[0] = halves_sum(part[0], part[1]);
-            } else if constexpr (H == 8) {
-                sc[0] = halves_sum(part[0], part[2]);
-                sc[1] = halves_sum(part[1], part[3]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) sc[u] = part[u];
-            }
-            // stream: append keys above the token's threshold
-#pragma unroll
-            for (int u = 0; u < NSC; ++u) {
-                const uint64_t key = rank_key(sc[u], (uint32_t)jpos);
-                const bool take = jpos <= climit[u] && key > thr[u];
-                const uint64_t m = __ballot(take);
-                if (m == 0) continue;
-                const uint64_t half = hh ? (m >> 32) : (m & 0xFFFFFFFFull);
-                const uint32_t rank = __popcll(half & ((1ull << n) - 1ull));
-                const int64_t tk = wtok0 + tslot[u];
-                pend_take[sub][u] = take;
-                pend_key[sub][u] = key;
-                pend_ptr[sub][u] = a.cand + (row0 + (size_t)tk) * (size_t)cap + cnt[u] + rank;
-                cnt[u] += __popcll(half);
-            }
-            // compact any token whose buffer cannot take another block
-#pragma unroll
-            for (int u = 0; u < NSC; ++u) {
-#pragma unroll
-                for (int side = 0; side < 2; ++side) {
-                    const uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
-                    if (cs + 32 > (uint32_t)cap) {
-                        flush();
-                        const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
-                        const int64_t tk = wtok0 + ts;
-                        uint64_t* buf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
-                        const uint64_t kth = compact_topk(buf, cs, kglob, whist[w], nullptr);
-                        if (hh == side) {
-                            thr[u] = kth;
-                            cnt[u] = kglob;
-                        }
+            for (int side = 0; side < 2; ++side) {
+                const uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
+                if (cs + 2 * 32 > (uint32_t)cap) {
+                    flush();
+                    const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
+                    const int64_t tk = wtok0 + ts;
+                    uint64_t* buf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
+                    const uint64_t kth = compact_topk(buf, cs, kglob, whist[w], nullptr);
+                    if (hh == side) {
+                        thr[u] = kth;
+                        cnt[u] = kglob;
                     }
                 }
             }
         }
-        if (it + 1 < n_tiles) {
-            stg.store(k_lds[cur ^ 1], nullptr);
-            if constexpr (SCALED) {
-                if (tid < kPfTile) ks_lds[cur ^ 1][tid] = j0 + kPfTile + tid < a.n_ctx ? ks_pf : 0.f;
-            }
+    };
+    auto store_ks = [&](int buf, int t, float ks_v) {
+        if constexpr (SCALED) {
+            if (tid < kPfTile) ks_lds[buf][tid] = (int64_t)kPfTile * t + tid < a.n_ctx ? ks_v : 0.f;
         }
+    };
+    auto load_ks = [&](int t) {
+        float v = 0.f;
+        if constexpr (SCALED) {
+            if (tid < kPfTile) v = ksg[min<int64_t>((int64_t)kPfTile * t + tid, a.n_ctx - 1)];
+        }
+        return v;
+    };
+    // Tile T: [S of block 2T+1 | scores of block 2T], store tile T+1 (loaded
+    // one tile earlier) and flush appends, barrier, load tile T+2, [S of block
+    // 2T+2 | scores of block 2T+1]. Three LDS buffers: tile T+1 is stored while
+    // tile T is read and tile T-1's buffer is no longer.
+    Stage stg;
+    stg.load(kg, nullptr, 0, a.n_ctx, a.n_ctx_pad);
+    float ks_pf = load_ks(0);
+    stg.store(k_lds[0], nullptr);
+    store_ks(0, 0, ks_pf);
+    __syncthreads();
+    if (n_tiles > 1) {
+        stg.load(kg, nullptr, kPfTile, a.n_ctx, a.n_ctx_pad);
+        ks_pf = load_ks(1);
+    }
+    f32x16 s_cur = qk(0, 0);
+    int buf = 0, nbuf = 1;
+    for (int T = 0; T < n_tiles; ++T) {
+        const int64_t j0 = (int64_t)T * kPfTile;
+        make_room();
+        f32x16 s_nxt = qk(buf, 1);
+        score(s_cur, buf, 0, j0);
+        if (T + 1 < n_tiles) {
+            stg.store(k_lds[nbuf], nullptr);
+            store_ks(nbuf, T + 1, ks_pf);
+        }
+        flush();
         __syncthreads();
+        if (T + 2 < n_tiles) {
+            stg.load(kg, nullptr, j0 + 2 * kPfTile, a.n_ctx, a.n_ctx_pad);
+            ks_pf = load_ks(T + 2);
+        }
+        s_cur = qk(nbuf, 0);  // after the last tile this reads a stale buffer; unused
+        score(s_nxt, buf, 1, j0);
+        buf = nbuf;
+        nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
     }
     flush();
     }
@@ -646,8 +955,12 @@ template <int H, int D, int KV>
 static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
     constexpr int TB = kPfRows / H;
     dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
-    if (fwd)
-        hipLaunchKernelGGL((attn_fwd_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+    if (fwd) {
+        if constexpr (KV == DT_F32)
+            hipLaunchKernelGGL((attn_fwd_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+    }
     else
         hipLaunchKernelGGL((score_stream_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
     return hipGetLastError();
