@@ -144,7 +144,7 @@ SelectWs select_ws(void* base, int64_t rows, int64_t row_len) {
     return w;
 }
 
-constexpr int kPrefillCandCap = 2048;  // = 64 lanes x 32 keys held in registers by the compaction
+constexpr int kPrefillCandCap = 4096;  // candidate keys per token (compacted to k_global when full)
 constexpr int kVtPad = 64;
 struct PrefillWs {
     void* vt;

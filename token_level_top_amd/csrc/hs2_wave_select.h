@@ -242,4 +242,120 @@ __device__ __noinline__ void wave_topk_ordered_lds(const uint64_t* keys, uint32_
     }
 }
 
+constexpr int kCompactScratchMem = 16 * 16;  // uint32 per wave: 16 digit bins x 16 lanes
+
+// Same selection over keys that stay in memory (global or LDS) and are read
+// again on every pass, U keys per lane in flight, so that it needs few
+// registers and can be inlined into a register-heavy loop. Returns T and writes
+// the keys >= T in list order to pos_out (as positions) or, when pos_out is
+// null, back into buf (as keys; buf may be `keys` itself: a chunk is read
+// before any key of it is written, and writes never pass the chunk being read).
+// The wave's own earlier stores to `keys` are made visible first. The digit
+// histogram has 16 columns (kCompactScratchMem words), shared by 4 lanes each.
+// All 64 lanes of one wave call it.
+template <int U>
+__device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t cnt, uint32_t kk, uint32_t* hist,
+                                                  int32_t* pos_out, uint64_t* buf) {
+    const uint32_t lane = lane_id();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    // fn(key, valid) over every key, U per lane at a time (clamped loads)
+    auto each = [&](auto fn) {
+        for (uint32_t base = 0; base < cnt; base += 64u * U) {
+            uint64_t k[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = base + 64u * u + lane;
+                k[u] = keys[i < cnt ? i : 0u];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) fn(k[u], base + 64u * u + lane < cnt);
+        }
+    };
+    uint64_t T;
+    if (kk >= cnt) {
+        uint64_t m = ~0ull;
+        each([&](uint64_t k, bool ok) {
+            if (ok && k < m) m = k;
+        });
+        T = wave_min_u64(m);
+    } else {
+        uint64_t kmax = 0, kmin = ~0ull;
+        each([&](uint64_t k, bool ok) {
+            if (ok) {
+                kmax = k > kmax ? k : kmax;
+                kmin = k < kmin ? k : kmin;
+            }
+        });
+        kmax = wave_max_u64(kmax);
+        kmin = wave_min_u64(kmin);
+        int hi = 64 - __clzll((long long)(kmax ^ kmin));  // bits [hi, 64) are shared by every key
+        uint64_t pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
+        uint64_t prefix = kmax & pmask;
+        uint32_t need = kk;
+        bool found = false;
+        T = 0;
+        while (hi > 0 && !found) {
+            const int lo = hi > 4 ? hi - 4 : 0;
+            const uint32_t dmask = (1u << (hi - lo)) - 1u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hist[4 * lane + e] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            each([&](uint64_t k, bool ok) {
+                if (ok && (k & pmask) == prefix) atomicAdd(&hist[(((uint32_t)(k >> lo)) & dmask) * 16 + (lane & 15)], 1u);
+            });
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            // bin totals: lane 4b+q sums columns 4q..4q+3 of bin b, then 4 lanes combine
+            uint32_t part = 0;
+            {
+                const int b = lane >> 2, q = lane & 3;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) part += hist[b * 16 + 4 * q + jj];
+                part += __shfl_xor(part, 1);
+                part += __shfl_xor(part, 2);
+            }
+            uint32_t above = 0, dd = 0, in_bin = 0;
+#pragma unroll
+            for (int b = 15; b >= 0; --b) {
+                const uint32_t c = __builtin_amdgcn_readlane(part, 4 * b);
+                if (!in_bin && b <= (int)dmask && above + c >= need) {
+                    dd = (uint32_t)b;
+                    in_bin = c;
+                } else if (!in_bin) {
+                    above += c;
+                }
+            }
+            need -= above;
+            prefix |= (uint64_t)dd << lo;
+            pmask |= (uint64_t)dmask << lo;
+            __builtin_amdgcn_wave_barrier();
+            if (in_bin == need) {
+                // every key under this prefix is selected: T is the smallest of them
+                uint64_t m = ~0ull;
+                each([&](uint64_t k, bool ok) {
+                    if (ok && (k & pmask) == prefix && k < m) m = k;
+                });
+                T = wave_min_u64(m);
+                found = true;
+            }
+            hi = lo;
+        }
+        if (!found) T = prefix;  // all 64 bits fixed
+    }
+    uint32_t wr = 0;
+    each([&](uint64_t k, bool ok) {
+        const bool keep = ok && k >= T;
+        const uint64_t mm = __ballot(keep);
+        if (keep) {
+            const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
+            if (pos_out) pos_out[at] = (int32_t)key_pos(k);
+            else buf[at] = k;
+        }
+        wr += __popcll(mm);
+    });
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    return T;
+}
+
 }  // namespace hs2

@@ -446,12 +446,12 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
 constexpr int kPfBufs = 3;
 constexpr float kPsumMax = 16.0f * 256.0f;  // 16 terms of at most 2^kLazy each
 
-template <int D, bool SCALED>
+template <int D, bool SCALED, int NT>
 struct PipeStage {
     static constexpr int KLD = D + 8;                          // K tile row stride (elements)
     static constexpr int VLD = kPfTile + 8;                    // V^T tile row stride
-    static constexpr int KPT = kPfTile * D / 8 / kPfThreads;   // 16-B K pieces per thread
-    static constexpr int VPT = D * kPfTile / 8 / kPfThreads;   // 16-B V^T pieces per thread
+    static constexpr int KPT = kPfTile * D / 8 / NT;           // 16-B K pieces per thread
+    static constexpr int VPT = D * kPfTile / 8 / NT;           // 16-B V^T pieces per thread
     static_assert(KPT >= 1 && VPT >= 1, "whole pieces per thread");
     u32x4 kr[KPT], vr[VPT];
     f32x4 cr;
@@ -464,13 +464,13 @@ struct PipeStage {
         const int tid = threadIdx.x, j0 = kPfTile * t;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int ch = tid + kPfThreads * i, row = ch / (D / 8), cc = ch % (D / 8);
+            const int ch = tid + NT * i, row = ch / (D / 8), cc = ch % (D / 8);
             const int j = min(j0 + row, n_ctx - 1);
             kr[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)(j * D + cc * 8));
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int ch = tid + kPfThreads * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
+            const int ch = tid + NT * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
             vr[i] = *reinterpret_cast<const u32x4*>(vtb + (uint32_t)(d * n_ctx_pad + j0 + cc * 8));
         }
         if constexpr (SCALED) {
@@ -485,12 +485,12 @@ struct PipeStage {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int ch = tid + kPfThreads * i, row = ch / (D / 8), cc = ch % (D / 8);
+            const int ch = tid + NT * i, row = ch / (D / 8), cc = ch % (D / 8);
             *reinterpret_cast<u32x4*>(kl + row * KLD + cc * 8) = kr[i];
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int ch = tid + kPfThreads * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
+            const int ch = tid + NT * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
             *reinterpret_cast<u32x4*>(vl + d * VLD + cc * 8) = vr[i];
         }
         if constexpr (SCALED) {
@@ -499,10 +499,13 @@ struct PipeStage {
     }
 };
 
-template <int H, int D, int KV>
-__global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a) {
+template <int H, int D, int KV, int RB>
+__global__ __launch_bounds__(kPfThreads / RB) void attn_fwd_pipe_kernel(PrefillArgs a) {
+    // RB 32-row blocks per wave, 8 / RB waves: the workgroup keeps 256 rows and
+    // every K or V^T fragment read from LDS feeds RB MFMAs.
     constexpr bool SCALED = KV == DT_FP8;
-    using Stage = PipeStage<D, SCALED>;
+    constexpr int NT = kPfThreads / RB;
+    using Stage = PipeStage<D, SCALED, NT>;
     constexpr int KLD = Stage::KLD, VLD = Stage::VLD, NS = D / 16, NDT = D / 32;
     constexpr int TB = kPfRows / H;  // tokens per workgroup
 
@@ -516,22 +519,26 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
     const int blk = n_blk - 1 - (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y;
     const int64_t tok0 = (int64_t)blk * TB;
-    const int R = 32 * w + n;  // this lane's (token, head) row in the block
-    const int64_t my_tok = tok0 + R / H;
-    const int my_head = R % H;
-    const bool row_ok = my_tok < a.n_q;
-    const int64_t my_p = a.q_pos0 + my_tok;
     const int64_t p_min = a.q_pos0 + tok0;
     const int64_t p_max = a.q_pos0 + min<int64_t>(tok0 + TB, a.n_q) - 1;
 
-    // Q^T fragment (B operand of S^T = K Q^T): column = row R, k = 16s + 8hh + [0, 8)
-    u32x4 qf[NS];
-    {
-        const size_t qb = (((size_t)b * a.n_q + (size_t)(row_ok ? my_tok : 0)) * H + my_head) * D;
+    // row block r of this wave: (token, head) row R = 32 (RB w + r) + n
+    int64_t my_tok[RB], my_p[RB];
+    int my_head[RB];
+    bool row_ok[RB];
+    u32x4 qf[RB][NS];  // Q^T fragment: column = row R, k = 16s + 8hh + [0, 8)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int R = 32 * (RB * w + r) + n;
+        my_tok[r] = tok0 + R / H;
+        my_head[r] = R % H;
+        row_ok[r] = my_tok[r] < a.n_q;
+        my_p[r] = a.q_pos0 + my_tok[r];
+        const size_t qb = (((size_t)b * a.n_q + (size_t)(row_ok[r] ? my_tok[r] : 0)) * H + my_head[r]) * D;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const u32x4 w4 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qb + 16 * s + 8 * hh);
-            qf[s] = row_ok ? w4 : u32x4{0, 0, 0, 0};
+            qf[r][s] = row_ok[r] ? w4 : u32x4{0, 0, 0, 0};
         }
     }
     const uint16_t* kb = (SCALED ? a.kc : reinterpret_cast<const uint16_t*>(a.k)) + (size_t)b * a.n_ctx * D;
@@ -540,33 +547,42 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
     const int n_ctx = (int)a.n_ctx, n_ctx_pad = (int)a.n_ctx_pad;
     const float scale_log2 = a.scale_log2;
 
-    float m_run = kNegBig, l_run = 0.f;
-    f32x16 o_acc[NDT];
+    float m_run[RB], l_run[RB];
+    f32x16 o_acc[RB][NDT];
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+    for (int r = 0; r < RB; ++r) {
+        m_run[r] = kNegBig;
+        l_run[r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o_acc[t][i] = 0.f;
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o_acc[r][t][i] = 0.f;
+    }
 
     const int n_tiles = (int)((p_max + kPfTile) / kPfTile);
     const int n_full = min<int>(n_tiles, (int)((p_min + 1) / kPfTile));  // tiles needing no causal mask
 
-    // S^T block of keys 32*sub.. of an LDS tile (M) x this wave's 32 rows (N)
-    auto qk = [&](int buf, int sub) {
-        f32x16 acc;
+    // S^T blocks of keys 32*sub.. of an LDS tile (M) x each row block (N)
+    auto qk = [&](int buf, int sub, f32x16* acc) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
         const uint16_t* kr = k_lds[buf] + (32 * sub + n) * KLD + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * s)),
-                                                          as_bf16x8(qf[s]), acc, 0, 0, 0);
-        return acc;
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * s));
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, as_bf16x8(qf[r][s]), acc[r], 0, 0, 0);
+        }
     };
-    // P = 2^(S * c - m_run) as the packed bf16 B operand of the PV MFMA; returns
-    // this lane's sum of the (rounded) terms. Accumulator i holds key
-    // 32*sub + 8(i/4) + 4hh + i%4; keys with 8(i/4) + i%4 > rel are masked.
+    // P = 2^(S * c - m_run) of row block r as the packed bf16 B operand of the
+    // PV MFMA; returns this lane's sum of the (rounded) terms. Accumulator i
+    // holds key 32*sub + 8(i/4) + 4hh + i%4; keys with 8(i/4) + i%4 > rel are
+    // masked.
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-    auto softmax = [&](const f32x16& s, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+    auto softmax = [&](const f32x16& s, int r, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         float c[16];
         if constexpr (SCALED) {
@@ -583,7 +599,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
         float p[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            p[i] = fast_exp2(__builtin_fmaf(s[i], c[i], -m_run));
+            p[i] = fast_exp2(__builtin_fmaf(s[i], c[i], -m_run[r]));
             if constexpr (MASK) {
                 if (32 * sub + 8 * (i >> 2) + (i & 3) > rel) p[i] = 0.f;
             }
@@ -601,7 +617,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
     };
     // rare: some term of the block exceeded 2^kLazy (or this is the row's first
     // block); raise m_run to the block's row maximum, rescale, redo the block
-    auto settle = [&](float& ps, const f32x16& s, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+    auto settle = [&](float& ps, const f32x16& s, int r, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         if (__ballot(!(ps <= kPsumMax))) {
             float mx = -INFINITY;
@@ -614,26 +630,35 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
                 mx = fmaxf(mx, v);
             }
             mx = fmaxf(mx, xor32(mx));
-            const float m_new = mx > m_run + kLazy ? mx : m_run;
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+            const float m_new = mx > m_run[r] + kLazy ? mx : m_run[r];
+            const float alpha = fast_exp2(m_run[r] - m_new);
+            m_run[r] = m_new;
+            l_run[r] *= alpha;
 #pragma unroll
-            for (int t = 0; t < NDT; ++t) o_acc[t] *= alpha;
-            ps = softmax(s, buf, sub, rel, pb, mask_tag);
+            for (int t = 0; t < NDT; ++t) o_acc[r][t] *= alpha;
+            ps = softmax(s, r, buf, sub, rel, pb, mask_tag);
         }
-        l_run += ps;
+        l_run[r] += ps;
     };
-    // O^T += V^T P^T over keys 32*sub.. of an LDS tile
-    auto pv = [&](int buf, int sub, const u32x4* pb) {
+    // O^T += V^T P^T over keys 32*sub.. of an LDS tile, for every row block
+    auto pv = [&](int buf, int sub, u32x4 (*pb)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int t = 0; t < NDT; ++t) {
                 const uint16_t* vr = v_lds[buf] + (32 * t + n) * VLD + 32 * sub + 16 * c + 8 * hh;
-                o_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(vr)),
-                                                                   as_bf16x8(pb[c]), o_acc[t], 0, 0, 0);
+                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(vr));
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                    o_acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pb[r][c]), o_acc[r][t], 0, 0, 0);
             }
+    };
+    auto softmax_all = [&](f32x16* s, int buf, int sub, const int* rel, u32x4 (*pb)[2], auto mask_tag) {
+        float ps[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) ps[r] = softmax(s[r], r, buf, sub, rel[r], pb[r], mask_tag);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) settle(ps[r], s[r], r, buf, sub, rel[r], pb[r], mask_tag);
     };
 
     Stage stg;
@@ -641,24 +666,26 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
     stg.store(k_lds[0], v_lds[0], c_lds[0], scale_log2);
     __syncthreads();
     if (n_tiles > 1) stg.load(kb, vtb, ksb, 1, n_ctx, n_ctx_pad);
-    f32x16 s_cur = qk(0, 0);
+    f32x16 s_cur[RB], s_nxt[RB];
+    qk(0, 0, s_cur);
     int buf = 0, nbuf = 1;  // LDS buffers of tiles T and T+1
     // Tile T: [S(2T+1) | softmax 2T] [PV 2T] store T+1, barrier, load T+2,
     //         [S(2T+2) | softmax 2T+1] [PV 2T+1]
     auto tile = [&](int T, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int rel = MASK ? (int)min<int64_t>(my_p - (int64_t)kPfTile * T, kPfTile) - 4 * hh : 0;
-        u32x4 pb[2];
-        f32x16 s_nxt = qk(buf, 1);
-        float ps = softmax(s_cur, buf, 0, rel, pb, mask_tag);
-        settle(ps, s_cur, buf, 0, rel, pb, mask_tag);
+        int rel[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            rel[r] = MASK ? (int)min<int64_t>(my_p[r] - (int64_t)kPfTile * T, kPfTile) - 4 * hh : 0;
+        u32x4 pb[RB][2];
+        qk(buf, 1, s_nxt);
+        softmax_all(s_cur, buf, 0, rel, pb, mask_tag);
         pv(buf, 0, pb);
         if (T + 1 < n_tiles) stg.store(k_lds[nbuf], v_lds[nbuf], c_lds[nbuf], scale_log2);
         __syncthreads();
         if (T + 2 < n_tiles) stg.load(kb, vtb, ksb, T + 2, n_ctx, n_ctx_pad);
-        s_cur = qk(nbuf, 0);  // after the last tile this reads a stale buffer; unused
-        ps = softmax(s_nxt, buf, 1, rel, pb, mask_tag);
-        settle(ps, s_nxt, buf, 1, rel, pb, mask_tag);
+        qk(nbuf, 0, s_cur);  // after the last tile this reads a stale buffer; unused
+        softmax_all(s_nxt, buf, 1, rel, pb, mask_tag);
         pv(buf, 1, pb);
         buf = nbuf;
         nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
@@ -668,38 +695,47 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_pipe_kernel(PrefillArgs a
     for (; T < n_tiles; ++T) tile(T, std::integral_constant<bool, true>{});
 
     // finish: both wave halves hold disjoint key subsets of the same row
-    const float l_tot = l_run + xor32(l_run);
-    if (row_ok) {
-        const float inv = 1.f / l_tot;
-        const size_t ob = (((size_t)b * a.n_q + (size_t)my_tok) * H + my_head) * D;
 #pragma unroll
-        for (int t = 0; t < NDT; ++t)
+    for (int r = 0; r < RB; ++r) {
+        const float l_tot = l_run[r] + xor32(l_run[r]);
+        if (row_ok[r]) {
+            const float inv = 1.f / l_tot;
+            const size_t ob = (((size_t)b * a.n_q + (size_t)my_tok[r]) * H + my_head[r]) * D;
 #pragma unroll
-            for (int i = 0; i < 16; i += 4) {
-                const int d0 = 32 * t + 8 * (i >> 2) + 4 * hh;
-                u32x2 o2;
-                o2[0] = pack_bf16x2(o_acc[t][i] * inv, o_acc[t][i + 1] * inv);
-                o2[1] = pack_bf16x2(o_acc[t][i + 2] * inv, o_acc[t][i + 3] * inv);
-                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + ob + d0) = o2;
+            for (int t = 0; t < NDT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    const int d0 = 32 * t + 8 * (i >> 2) + 4 * hh;
+                    u32x2 o2;
+                    o2[0] = pack_bf16x2(o_acc[r][t][i] * inv, o_acc[r][t][i + 1] * inv);
+                    o2[1] = pack_bf16x2(o_acc[r][t][i + 2] * inv, o_acc[r][t][i + 3] * inv);
+                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + ob + d0) = o2;
+                }
+            if (hh == 0) {
+                const float lse2 = m_run[r] + log2f(l_tot);
+                const size_t li = ((size_t)b * a.n_q + (size_t)my_tok[r]) * H + my_head[r];
+                a.lse[li] = lse2 * kLn2;
+                a.lse2[li] = lse2;
             }
-        if (hh == 0) {
-            const float lse2 = m_run + log2f(l_tot);
-            const size_t li = ((size_t)b * a.n_q + (size_t)my_tok) * H + my_head;
-            a.lse[li] = lse2 * kLn2;
-            a.lse2[li] = lse2;
         }
     }
 }
 
+#ifndef HS2_SS_OCC
+#define HS2_SS_OCC 2
+#endif
 // ------------------------------------------------------------- score_stream
-constexpr int kKeysPerLane = 32;  // a token buffer of up to 2048 keys, in registers
+constexpr int kGroupTiles = 8;  // tiles between candidate-buffer room checks
 
-__device__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist, int32_t* pos_out) {
-    return wave_topk_ordered<kKeysPerLane>(buf, cnt, kk, hist, pos_out, buf);
+// exact top-kk of a token's candidate buffer (kept in global memory), inline
+__device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
+                                                 int32_t* pos_out) {
+    return wave_topk_mem<8>(buf, cnt, kk, hist, pos_out, buf);
 }
 
 template <int H, int D, int KV>
-__global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(HS2_SS_OCC)))
+void score_stream_kernel(PrefillArgs a) {
     constexpr bool F32 = KV == DT_F32;
     constexpr bool SCALED = KV == DT_FP8;
     using T = PfTypes<F32>;
@@ -713,7 +749,7 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
 
     __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
     __shared__ float ks_lds[kPfBufs][kPfTile];
-    __shared__ uint32_t whist[kPfWaves][kCompactScratch];
+    __shared__ uint32_t whist[kPfWaves][kCompactScratchMem];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
@@ -850,20 +886,22 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
             cnt[u] += __popcll(half);
         }
     };
-    // a tile appends at most 64 keys per token: compact any buffer that could
-    // overflow before the tile's scores are appended
-    auto make_room = [&]() {
+    // Room check, once per group of kGroupTiles tiles (outside the inner
+    // tile loop, so that loop makes no calls): a tile appends at most 64 keys
+    // per token, so any buffer that could overflow within the group is
+    // compacted first.
+    auto make_room = [&](int tiles) {
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
                 const uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
-                if (cs + 2 * 32 > (uint32_t)cap) {
+                if (cs + (uint32_t)(64 * tiles) > (uint32_t)cap) {
                     flush();
                     const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
                     const int64_t tk = wtok0 + ts;
-                    uint64_t* buf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
-                    const uint64_t kth = compact_topk(buf, cs, kglob, whist[w], nullptr);
+                    uint64_t* cbuf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
+                    const uint64_t kth = compact_topk(cbuf, cs, kglob, whist[w], nullptr);
                     if (hh == side) {
                         thr[u] = kth;
                         cnt[u] = kglob;
@@ -900,9 +938,11 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     }
     f32x16 s_cur = qk(0, 0);
     int buf = 0, nbuf = 1;
-    for (int T = 0; T < n_tiles; ++T) {
+    for (int T0 = 0; T0 < n_tiles; T0 += kGroupTiles) {
+    const int T1 = min(n_tiles, T0 + kGroupTiles);
+    make_room(T1 - T0);
+    for (int T = T0; T < T1; ++T) {
         const int64_t j0 = (int64_t)T * kPfTile;
-        make_room();
         f32x16 s_nxt = qk(buf, 1);
         score(s_cur, buf, 0, j0);
         if (T + 1 < n_tiles) {
@@ -919,6 +959,7 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
         score(s_nxt, buf, 1, j0);
         buf = nbuf;
         nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
+    }
     }
     flush();
     }
@@ -951,6 +992,9 @@ __global__ __launch_bounds__(kPfThreads) void score_stream_kernel(PrefillArgs a)
     }
 }
 
+#ifndef HS2_PF_RB
+#define HS2_PF_RB 1
+#endif
 template <int H, int D, int KV>
 static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
     constexpr int TB = kPfRows / H;
@@ -959,7 +1003,8 @@ static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
         if constexpr (KV == DT_F32)
             hipLaunchKernelGGL((attn_fwd_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+            hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, KV, HS2_PF_RB>), grid, dim3(kPfThreads / HS2_PF_RB), 0, st,
+                               a);
     }
     else
         hipLaunchKernelGGL((score_stream_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
