@@ -85,14 +85,15 @@ def dominant(wl):
     return "attn_fwd", "mfma", 4 * wl.d * wl.H * causal_pairs(wl), "TFLOP/s"
 
 
-def traffic_record(name: str):
+def traffic_record(name: str, workload_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken for this kernel on this workload with the current kernel source;
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(name)
+        rec = json.load(open(path)).get(f"{name}@{workload_name}")
         src = os.path.join(ROOT, "token_level_top_amd", "csrc", KSRC[name])
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         if not rec or rec.get("src_sha") != sha:
@@ -243,7 +244,7 @@ def main():
     else:
         achieved = units / kavg_s / 1e12
         peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"]
-    tr = traffic_record(dom)
+    tr = traffic_record(dom, wl.name)
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
             "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),

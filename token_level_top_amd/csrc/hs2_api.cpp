@@ -80,10 +80,23 @@ int decode_splits(int B, int64_t n_ctx) {
     const int rps = decode_rows_per_split(B, n_ctx);
     return (int)((n_ctx + rps - 1) / rps);
 }
-// sparse layers: split a token's index row over workgroups when there are few tokens
+// sparse layers: with few tokens a token's index row is split over
+// workgroups, as evenly as whole 128-row tiles allow, so that one round of
+// the sparse kernel (2 workgroups per CU) covers the grid and every split
+// streams several tiles
+constexpr int kSparseSlots = 512;
+int sparse_rows_per_split(int64_t n_tok, int n_sel) {
+    const int tiles = (n_sel + kTile - 1) / kTile;
+    if (n_tok >= 1024 || tiles <= 1) return tiles * kTile;
+    int64_t want = kSparseSlots / n_tok;  // splits per token
+    if (want < 1) want = 1;
+    if (want > tiles) want = tiles;
+    const int tps = (int)((tiles + want - 1) / want);
+    return tps * kTile;
+}
 int sparse_splits(int64_t n_tok, int n_sel) {
-    if (n_tok >= 1024) return 1;
-    return (n_sel + kTile - 1) / kTile;
+    const int rps = sparse_rows_per_split(n_tok, n_sel);
+    return (n_sel + rps - 1) / rps;
 }
 
 struct DecodeWs {
@@ -251,7 +264,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
         a.n_tok = (int)n_tok;
         a.n_q = (int)n_q;
         a.n_split = ns;
-        a.rows_per_split = ns > 1 ? kTile : ((n_sel + kTile - 1) / kTile) * kTile;
+        a.rows_per_split = sparse_rows_per_split(n_tok, n_sel);
         a.scale_log2 = sm_scale * kLog2eF;
         void* o = static_cast<char*>(out) + qstride * l;
         float* ls = lse ? lse + (size_t)n_tok * H * l : nullptr;
