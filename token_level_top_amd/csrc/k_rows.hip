@@ -22,6 +22,8 @@ namespace hs2 {
 
 constexpr int kRowsTile = 128;
 constexpr int kRowsThreads = 256;
+constexpr int kIdxChunk = 1024;  // index entries staged in LDS at a time (a multiple of kRowsTile)
+static_assert(kIdxChunk % kRowsTile == 0, "tiles never straddle an index chunk");
 
 template <int KV>
 struct RowsTypes;
@@ -90,6 +92,9 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     __shared__ int pos_lds[kRowsTile];
     __shared__ float ksc_lds[kRowsTile];
     __shared__ float vsc_lds[kRowsTile];
+    // gathered rows: the index row is staged here kIdxChunk entries at a time, so
+    // a tile's K/V loads never wait behind the load of their own indices
+    __shared__ int idx_lds[GATHER ? kIdxChunk : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hl = lane & 15, g = lane >> 4;
@@ -127,7 +132,17 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     auto row_pos = [&](int64_t t0, int row) -> int {
         const int64_t r = t0 + row;
         if (r >= r_end) return -1;
-        return GATHER ? idx_row[r] : (int)r;
+        return GATHER ? idx_lds[(r - r_begin) % kIdxChunk] : (int)r;
+    };
+    // stage index entries [c0, c0 + kIdxChunk) of the split (GATHER)
+    auto stage_idx = [&](int64_t c0) {
+        if constexpr (GATHER) {
+            for (int e = tid; e < kIdxChunk; e += kRowsThreads) {
+                const int64_t r = r_begin + c0 + e;
+                idx_lds[e] = r < r_end ? idx_row[r] : -1;
+            }
+            __syncthreads();
+        }
     };
     // Registers holding the next tile while the current one is computed.
     u32x4 kreg[CPT], vreg[CPT];
@@ -176,7 +191,10 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
                     }
         }
     };
-    if (r_begin < r_end) prefetch(r_begin);
+    if (r_begin < r_end) {
+        stage_idx(0);
+        prefetch(r_begin);
+    }
 
     for (int64_t t0 = r_begin; t0 < r_end; t0 += kRowsTile) {
         // ---- publish the prefetched tile to LDS, then start loading the next one
@@ -197,7 +215,12 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         }
         __syncthreads();
         flush_logits();
-        if (t0 + kRowsTile < r_end) prefetch(t0 + kRowsTile);
+        if (t0 + kRowsTile < r_end) {
+            // the next tile starts a new chunk of the index row: every thread has
+            // read its indices of the current chunk (they are in registers)
+            if (GATHER && (t0 + kRowsTile - r_begin) % kIdxChunk == 0) stage_idx(t0 + kRowsTile - r_begin);
+            prefetch(t0 + kRowsTile);
+        }
 
         // ---- S^T for the wave's 32 rows: two 16-row groups
         f32x4 sacc[2];
