@@ -450,9 +450,10 @@ template <int D, bool SCALED, int NT>
 struct PipeStage {
     static constexpr int KLD = D + 8;                          // K tile row stride (elements)
     static constexpr int VLD = kPfTile + 8;                    // V^T tile row stride
-    static constexpr int KPT = kPfTile * D / 8 / NT;           // 16-B K pieces per thread
-    static constexpr int VPT = D * kPfTile / 8 / NT;           // 16-B V^T pieces per thread
-    static_assert(KPT >= 1 && VPT >= 1, "whole pieces per thread");
+    static constexpr int KCH = kPfTile * D / 8;                // 16-B K pieces per tile
+    static constexpr int VCH = D * kPfTile / 8;                // 16-B V^T pieces per tile
+    static constexpr int KPT = (KCH + NT - 1) / NT;            // per thread (the last round may be partial)
+    static constexpr int VPT = (VCH + NT - 1) / NT;
     u32x4 kr[KPT], vr[VPT];
     f32x4 cr;
 
@@ -464,13 +465,13 @@ struct PipeStage {
         const int tid = threadIdx.x, j0 = kPfTile * t;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int ch = tid + NT * i, row = ch / (D / 8), cc = ch % (D / 8);
+            const int ch = min(tid + NT * i, KCH - 1), row = ch / (D / 8), cc = ch % (D / 8);
             const int j = min(j0 + row, n_ctx - 1);
             kr[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)(j * D + cc * 8));
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int ch = tid + NT * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
+            const int ch = min(tid + NT * i, VCH - 1), d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
             vr[i] = *reinterpret_cast<const u32x4*>(vtb + (uint32_t)(d * n_ctx_pad + j0 + cc * 8));
         }
         if constexpr (SCALED) {
@@ -486,12 +487,12 @@ struct PipeStage {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int ch = tid + NT * i, row = ch / (D / 8), cc = ch % (D / 8);
-            *reinterpret_cast<u32x4*>(kl + row * KLD + cc * 8) = kr[i];
+            if (KCH % NT == 0 || ch < KCH) *reinterpret_cast<u32x4*>(kl + row * KLD + cc * 8) = kr[i];
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int ch = tid + NT * i, d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
-            *reinterpret_cast<u32x4*>(vl + d * VLD + cc * 8) = vr[i];
+            if (VCH % NT == 0 || ch < VCH) *reinterpret_cast<u32x4*>(vl + d * VLD + cc * 8) = vr[i];
         }
         if constexpr (SCALED) {
             if (tid < kPfTile / 4) *reinterpret_cast<f32x4*>(cl + 4 * tid) = cr * scale_log2;
@@ -499,15 +500,18 @@ struct PipeStage {
     }
 };
 
-template <int H, int D, int KV, int RB>
-__global__ __launch_bounds__(kPfThreads / RB) void attn_fwd_pipe_kernel(PrefillArgs a) {
-    // RB 32-row blocks per wave, 8 / RB waves: the workgroup keeps 256 rows and
-    // every K or V^T fragment read from LDS feeds RB MFMAs.
+template <int H, int D, int KV, int RB, int NW, bool PIPE>
+__global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
+    // NW waves of RB 32-row blocks each: 32 NW RB (token, head) rows per
+    // workgroup; every K or V^T fragment read from LDS feeds RB MFMAs. PIPE
+    // issues the QK^T MFMAs of the next block beside the current softmax.
     constexpr bool SCALED = KV == DT_FP8;
-    constexpr int NT = kPfThreads / RB;
+    constexpr int NT = 64 * NW;
     using Stage = PipeStage<D, SCALED, NT>;
     constexpr int KLD = Stage::KLD, VLD = Stage::VLD, NS = D / 16, NDT = D / 32;
-    constexpr int TB = kPfRows / H;  // tokens per workgroup
+    constexpr int ROWS = 32 * NW * RB;
+    static_assert(ROWS % H == 0, "whole tokens per workgroup");
+    constexpr int TB = ROWS / H;  // tokens per workgroup
 
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPfBufs][kPfTile * KLD];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPfBufs][D * VLD];
@@ -667,7 +671,7 @@ __global__ __launch_bounds__(kPfThreads / RB) void attn_fwd_pipe_kernel(PrefillA
     __syncthreads();
     if (n_tiles > 1) stg.load(kb, vtb, ksb, 1, n_ctx, n_ctx_pad);
     f32x16 s_cur[RB], s_nxt[RB];
-    qk(0, 0, s_cur);
+    if constexpr (PIPE) qk(0, 0, s_cur);
     int buf = 0, nbuf = 1;  // LDS buffers of tiles T and T+1
     // Tile T: [S(2T+1) | softmax 2T] [PV 2T] store T+1, barrier, load T+2,
     //         [S(2T+2) | softmax 2T+1] [PV 2T+1]
@@ -678,6 +682,21 @@ __global__ __launch_bounds__(kPfThreads / RB) void attn_fwd_pipe_kernel(PrefillA
         for (int r = 0; r < RB; ++r)
             rel[r] = MASK ? (int)min<int64_t>(my_p[r] - (int64_t)kPfTile * T, kPfTile) - 4 * hh : 0;
         u32x4 pb[RB][2];
+        if constexpr (!PIPE) {
+            // one block at a time; more waves per SIMD hide the latencies
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                qk(buf, sub, s_cur);
+                softmax_all(s_cur, buf, sub, rel, pb, mask_tag);
+                pv(buf, sub, pb);
+            }
+            if (T + 1 < n_tiles) stg.store(k_lds[nbuf], v_lds[nbuf], c_lds[nbuf], scale_log2);
+            __syncthreads();
+            if (T + 2 < n_tiles) stg.load(kb, vtb, ksb, T + 2, n_ctx, n_ctx_pad);
+            buf = nbuf;
+            nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
+            return;
+        }
         qk(buf, 1, s_nxt);
         softmax_all(s_cur, buf, 0, rel, pb, mask_tag);
         pv(buf, 0, pb);
@@ -722,10 +741,14 @@ __global__ __launch_bounds__(kPfThreads / RB) void attn_fwd_pipe_kernel(PrefillA
 }
 
 #ifndef HS2_SS_OCC
-#define HS2_SS_OCC 2
+#define HS2_SS_OCC 4
+#endif
+#ifndef HS2_SS_PIPE
+#define HS2_SS_PIPE 0
 #endif
 // ------------------------------------------------------------- score_stream
 constexpr int kGroupTiles = 8;  // tiles between candidate-buffer room checks
+
 
 // exact top-kk of a token's candidate buffer (kept in global memory), inline
 __device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
@@ -734,7 +757,7 @@ __device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, ui
 }
 
 template <int H, int D, int KV>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(HS2_SS_OCC)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(KV == DT_F32 ? 2 : HS2_SS_OCC)))
 void score_stream_kernel(PrefillArgs a) {
     constexpr bool F32 = KV == DT_F32;
     constexpr bool SCALED = KV == DT_FP8;
@@ -936,6 +959,29 @@ void score_stream_kernel(PrefillArgs a) {
         stg.load(kg, nullptr, kPfTile, a.n_ctx, a.n_ctx_pad);
         ks_pf = load_ks(1);
     }
+    if constexpr (!HS2_SS_PIPE) {
+    // not pipelined: more waves per SIMD hide the MFMA latency instead
+    int buf = 0, nbuf = 1;
+    for (int T = 0; T < n_tiles; ++T) {
+        const int64_t j0 = (int64_t)T * kPfTile;
+        if (T % kGroupTiles == 0) make_room(min(kGroupTiles, n_tiles - T));
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) score(qk(buf, sub), buf, sub, j0);
+        if (T + 1 < n_tiles) {
+            stg.store(k_lds[nbuf], nullptr);
+            store_ks(nbuf, T + 1, ks_pf);
+        }
+        flush();
+        __syncthreads();
+        if (T + 2 < n_tiles) {
+            stg.load(kg, nullptr, j0 + 2 * kPfTile, a.n_ctx, a.n_ctx_pad);
+            ks_pf = load_ks(T + 2);
+        }
+        buf = nbuf;
+        nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
+    }
+    flush();
+    } else {
     f32x16 s_cur = qk(0, 0);
     int buf = 0, nbuf = 1;
     for (int T0 = 0; T0 < n_tiles; T0 += kGroupTiles) {
@@ -962,6 +1008,7 @@ void score_stream_kernel(PrefillArgs a) {
     }
     }
     flush();
+    }
     }
     // Epilogue: every token of the wave gets its index row. A buffer holds the
     // token's candidates in ascending position order (appends follow the key
@@ -995,16 +1042,24 @@ void score_stream_kernel(PrefillArgs a) {
 #ifndef HS2_PF_RB
 #define HS2_PF_RB 1
 #endif
+#ifndef HS2_PF_NW
+#define HS2_PF_NW 8
+#endif
+#ifndef HS2_PF_PIPE
+#define HS2_PF_PIPE true
+#endif
 template <int H, int D, int KV>
 static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
     constexpr int TB = kPfRows / H;
+    constexpr int kFwdTB = 32 * HS2_PF_NW * HS2_PF_RB / H;  // tokens per pass-1 workgroup (bf16 / FP8)
     dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
     if (fwd) {
         if constexpr (KV == DT_F32)
             hipLaunchKernelGGL((attn_fwd_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, KV, HS2_PF_RB>), grid, dim3(kPfThreads / HS2_PF_RB), 0, st,
-                               a);
+            hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, KV, HS2_PF_RB, HS2_PF_NW, HS2_PF_PIPE>),
+                               dim3((unsigned)((a.n_q + kFwdTB - 1) / kFwdTB), (unsigned)a.B), dim3(64 * HS2_PF_NW), 0,
+                               st, a);
     }
     else
         hipLaunchKernelGGL((score_stream_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
