@@ -101,8 +101,7 @@ int sparse_splits(int64_t n_tok, int n_sel) {
 
 struct DecodeWs {
     float *logits, *part, *lse2, *scores, *spart;
-    uint32_t *hist, *thr, *counts;
-    int n_sub;
+    uint32_t *hist, *thr;
     uint64_t* cand;
     size_t bytes;
 };
@@ -117,8 +116,6 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     // hist and tickets are contiguous so one fill clears both
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * kHistBins);
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * 2);
-    w.n_sub = (int)((n_ctx + kSelSub - 1) / kSelSub);
-    w.counts = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * w.n_sub);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
     const int ss = sparse_splits(B, window + k_global);
     w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)B * ss * H * (d + 2)) : nullptr;
@@ -140,8 +137,7 @@ SparseWs sparse_ws(void* base, int64_t n_tok, int n_sel, int H, int d) {
 }
 
 struct SelectWs {
-    uint32_t *hist, *thr, *counts;
-    int n_sub;
+    uint32_t *hist, *thr;
     uint64_t* cand;
     size_t bytes;
 };
@@ -150,8 +146,6 @@ SelectWs select_ws(void* base, int64_t rows, int64_t row_len) {
     SelectWs w;
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * kHistBins);
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * 2);
-    w.n_sub = (int)((row_len + kSelSub - 1) / kSelSub);
-    w.counts = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * w.n_sub);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)rows * kCandCap);
     w.bytes = c.used;
     return w;
@@ -388,8 +382,6 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     a.k = k;
     a.hist = w.hist;
     a.thr = w.thr;
-    a.counts = w.counts;
-    a.n_sub = w.n_sub;
     a.cand = w.cand;
     a.out = out;
     a.out_stride = k;
@@ -397,8 +389,7 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, rows * kHistBins, 0u, s)));
     HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_hist(a, s)));
     HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(a, s)));
-    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_count(a, s)));
-    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_emit(a, s)));
+    HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(a, s)));
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final(a, s)));
     return HS2_OK;
 }
@@ -485,16 +476,13 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     se.k = k_global;
     se.hist = w.hist;
     se.thr = w.thr;
-    se.counts = w.counts;
-    se.n_sub = (int)((n_cand + kSelSub - 1) / kSelSub);
     se.cand = w.cand;
     se.out = indices;
     se.out_stride = n_sel;
     se.out_offset = window;
     if (k_global > 0 && n_cand > 0) {
         HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(se, s)));
-        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_count(se, s)));
-        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_emit(se, s)));
+        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
     }
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     // 4. sparse layers reuse the indices and the cache

@@ -46,7 +46,6 @@ hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStrea
 // ---- selection ------------------------------------------------------------
 constexpr int kHistBins = 4096;      // top 12 bits of a non-negative fp32 (bits 30..19)
 constexpr int kCandCap = 4096;       // candidates the final wave holds in registers
-constexpr int kSelSub = 2048;        // scores per wave in the count / emit steps
 
 // decode: score_j = sum_h exp2(logit2[j][h] - lse2[h]) for j < n_ctx; writes
 // scores [B][n_ctx] and the histogram of candidates j < n_cand.
@@ -70,10 +69,8 @@ struct SelectArgs {
     const int32_t* n_cand;  // [rows] or nullptr
     int k;
     uint32_t* hist;         // [rows][kHistBins]
-    uint32_t* thr;          // [rows][2] threshold bin, count above it
-    uint32_t* counts;       // [rows][n_sub] candidates per 2048-score slice
-    int n_sub;              // ceil(row_len / kSelSub)
-    uint64_t* cand;         // [rows][kCandCap], position order
+    uint32_t* thr;          // [rows][2] threshold bin, candidate count
+    uint64_t* cand;         // [rows][kCandCap] candidate rank keys (unordered)
     int32_t* out;           // [rows][out_stride]
     int64_t out_stride;
     int out_offset;         // first column written in each out row
@@ -82,8 +79,8 @@ struct SelectArgs {
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);
 // thr from the complete hist
 hipError_t launch_select_threshold(const SelectArgs& a, hipStream_t st);
-hipError_t launch_select_count(const SelectArgs& a, hipStream_t st);
-hipError_t launch_select_emit(const SelectArgs& a, hipStream_t st);
+// candidates (scores in the threshold bin or above) appended to cand, counted in thr[2r+1]
+hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st);
 hipError_t launch_select_final(const SelectArgs& a, hipStream_t st);
 // also writes the forced window of every row (all rows at position p_last) when window > 0
 hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st);

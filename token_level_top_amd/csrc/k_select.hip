@@ -9,18 +9,17 @@
 // largest scores, ties to the lower position, written in ascending position
 // order.
 //
-// Selection over a row of non-negative fp32 scores, in position order throughout:
+// Selection over a row of non-negative fp32 scores:
 //  1. histogram of the top 12 bits (8 exponent + 4 mantissa bits): many
 //     workgroups per row, LDS histograms merged with global atomics; then one
 //     workgroup per row finds the bin holding the k-th largest score;
-//  2. count: every wave counts the scores in that bin or above in its 2048-score
-//     slice;
-//  3. emit: every wave writes the rank keys of those scores, in position order,
-//     at the offset given by the counts of all earlier slices -- so the row's
-//     candidate list is ordered by position;
-//  4. final: one wave loads the candidates into registers, finds the exact k-th
-//     largest key and writes the positions of the keys at or above it, which come
-//     out ascending. Rows whose threshold bin holds more candidates than fit
+//  2. collect: many workgroups per row append the rank keys of the scores in
+//     that bin or above to the row's candidate list (one atomic per wave and
+//     64 scores; the list is unordered);
+//  3. final: one 1024-thread workgroup per row loads the candidates into LDS,
+//     finds the exact k-th largest key by 4-bit digit passes (per-wave LDS
+//     histograms), gathers the positions of the keys at or above it and sorts
+//     them ascending (bitonic, in LDS). Rows whose candidates overflow the list
 //     fall back to an exact multi-pass radix select over the whole row.
 // The 64-bit rank key (score bits, complemented position) makes every key
 // distinct, so the result is unique.
@@ -32,8 +31,7 @@ namespace hs2 {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelChunk = 8192;      // scores per workgroup in steps 1 and 2
-constexpr int kFinThreads = 256;
-constexpr int kSubLen = 2048;     // scores per wave in the count / emit steps
+constexpr int kFinThreads = 1024;
 
 __device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s) & 0x7FFFFFFFu; }
 __device__ __forceinline__ uint32_t score_bin(float s) { return score_bits(s) >> 19; }
@@ -100,7 +98,8 @@ __device__ void threshold_bin(const uint32_t* hist_glob, uint32_t kk, uint32_t* 
 
 
 // One workgroup per row: the threshold bin of the complete histogram.
-// thr[0] = bin (kHistBins if nothing is to be selected), thr[1] = count above it.
+// thr[0] = bin (kHistBins if nothing is to be selected), thr[1] = 0 (the
+// collect step counts its candidates there).
 __global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(const uint32_t* hist, uint32_t* thr,
                                                                         const int32_t* n_cand, int64_t row_len,
                                                                         int k) {
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(const uin
     threshold_bin(hist + (size_t)r * kHistBins, kk, scan, &bin_sh, &above_sh);
     if (threadIdx.x == 0) {
         thr[2 * r] = (uint32_t)bin_sh;
-        thr[2 * r + 1] = above_sh;
+        thr[2 * r + 1] = 0;  // candidate counter of the collect step
     }
 }
 
@@ -200,57 +199,66 @@ hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// ------------------------------------------------- steps 2, 3: count and emit
-// A wave owns the 2048-score slice `sub` = 4 * blockIdx.x + wave of its row.
-__global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a) {
+// ------------------------------------------------------------ step 2: collect
+// grid (chunks of kSelChunk scores, rows). A workgroup counts its candidates
+// (LDS), reserves room with one global atomic, then writes them (its chunk is
+// read twice, the second time from cache). Candidates beyond kCandCap are
+// counted but not stored (the final step then selects over the whole row).
+__global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs a) {
+    __shared__ uint32_t wg_count, wg_base;
     const int64_t r = blockIdx.y;
-    const int lane = threadIdx.x & 63, sub = 4 * blockIdx.x + (threadIdx.x >> 6);
-    if (sub >= a.n_sub) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t n = row_cands(a, r);
     const uint32_t tbin = a.thr[2 * r];
-    const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
-    const int64_t j0 = (int64_t)sub * kSubLen, j1 = min<int64_t>(j0 + kSubLen, n);
-    uint32_t c = 0;
-    for (int64_t j = j0 + lane; j < j1; j += 64) c += score_bin(s[j]) >= tbin ? 1u : 0u;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-    if (lane == 0) a.counts[(size_t)r * a.n_sub + sub] = c;
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
-    const int64_t r = blockIdx.y;
-    const int lane = threadIdx.x & 63, sub = 4 * blockIdx.x + (threadIdx.x >> 6);
-    if (sub >= a.n_sub) return;
-    const int64_t n = row_cands(a, r);
-    const int64_t j0 = (int64_t)sub * kSubLen, j1 = min<int64_t>(j0 + kSubLen, n);
-    if (j0 >= j1) return;
-    const uint32_t tbin = a.thr[2 * r];
-    const uint32_t* cnt = a.counts + (size_t)r * a.n_sub;
-    uint32_t before = 0;  // candidates in earlier slices of the row
-    for (int q = lane; q < sub; q += 64) before += cnt[q];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o);
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    for (int64_t jb = j0; jb < j1; jb += 64) {
+    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk, j1 = min<int64_t>(j0 + kSelChunk, n);
+    if (threadIdx.x == 0) wg_count = 0;
+    __syncthreads();
+    uint32_t c = 0;
+    const bool vec = ((r * a.row_stride) & 3) == 0;  // rows 16-byte aligned: 4 scores per load
+    if (vec) {
+        for (int64_t j = j0 + 4 * threadIdx.x; j < j1; j += 4 * kSelThreads) {
+            if (j + 4 <= j1) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(s + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c += score_bin(v[e]) >= tbin ? 1u : 0u;
+            } else {
+                for (int64_t jj = j; jj < j1; ++jj) c += score_bin(s[jj]) >= tbin ? 1u : 0u;
+            }
+        }
+    } else {
+        for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) c += score_bin(s[j]) >= tbin ? 1u : 0u;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0 && c) atomicAdd(&wg_count, c);
+    __syncthreads();
+    if (wg_count == 0) return;
+    if (threadIdx.x == 0) {
+        wg_base = atomicAdd(&a.thr[2 * r + 1], wg_count);
+        wg_count = 0;  // reused as the running offset of the writes
+    }
+    __syncthreads();
+    const uint32_t base = wg_base;
+    for (int64_t jb = j0 + 64 * w; jb < j1; jb += kSelThreads) {
         const int64_t j = jb + lane;
         const float v = j < j1 ? s[j] : 0.f;
         const bool take = j < j1 && score_bin(v) >= tbin;
         const uint64_t m = __ballot(take);
-        const uint32_t at = before + __popcll(m & ((1ull << lane) - 1ull));
+        if (m == 0) continue;
+        uint32_t off = 0;
+        if (lane == 0) off = atomicAdd(&wg_count, (uint32_t)__popcll(m));
+        off = __shfl(off, 0);
+        const uint32_t at = base + off + __popcll(m & ((1ull << lane) - 1ull));
         if (take && at < (uint32_t)kCandCap) cand[at] = rank_key(v, (uint32_t)j);
-        before += __popcll(m);
     }
 }
 
-hipError_t launch_select_count(const SelectArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.n_sub + 3) / 4), (unsigned)a.rows);
-    hipLaunchKernelGGL(select_count_kernel, grid, dim3(kSelThreads), 0, st, a);
-    return hipGetLastError();
-}
-hipError_t launch_select_emit(const SelectArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.n_sub + 3) / 4), (unsigned)a.rows);
-    hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kSelThreads), 0, st, a);
+hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.row_len + kSelChunk - 1) / kSelChunk), (unsigned)a.rows);
+    if (a.row_len <= 0) return hipSuccess;
+    hipLaunchKernelGGL(select_collect_kernel, grid, dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -354,10 +362,140 @@ __device__ void select_row_exact(const float* s, int64_t n, uint32_t kk, int32_t
     (void)gt;
 }
 
+// Block-wide min / max of a 64-bit value (all threads call; red holds 2 words per wave).
+__device__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
+    v = wave_min_u64(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    uint64_t m = ~0ull;
+    for (int i = 0; i < nw; ++i) m = red[i] < m ? red[i] : m;
+    __syncthreads();
+    return m;
+}
+__device__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
+    v = wave_max_u64(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    uint64_t m = 0;
+    for (int i = 0; i < nw; ++i) m = red[i] > m ? red[i] : m;
+    __syncthreads();
+    return m;
+}
+
+// The kk-th largest of the distinct keys[0..nc) (1 <= kk < nc), by 8-bit digits
+// below the prefix all keys share; every wave counts into its own 256 bins
+// (hist holds 256 words per wave).
+__device__ uint64_t block_kth_key(const uint64_t* keys, uint32_t nc, uint32_t kk, uint32_t* hist, uint32_t* ctl,
+                                  uint64_t* red) {
+    const int tid = threadIdx.x, w = tid >> 6, nw = blockDim.x >> 6;
+    uint64_t kmax = 0, kmin = ~0ull;
+    for (uint32_t i = tid; i < nc; i += blockDim.x) {
+        const uint64_t k = keys[i];
+        kmax = k > kmax ? k : kmax;
+        kmin = k < kmin ? k : kmin;
+    }
+    kmax = block_max_u64(kmax, red);
+    kmin = block_min_u64(kmin, red);
+    int hi = 64 - __clzll((long long)(kmax ^ kmin));
+    uint64_t pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
+    uint64_t prefix = kmax & pmask;
+    uint32_t need = kk;
+    while (hi > 0) {
+        const int lo = hi > 8 ? hi - 8 : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        for (int i = tid; i < 256 * nw; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < nc; i += blockDim.x) {
+            const uint64_t k = keys[i];
+            if ((k & pmask) == prefix) atomicAdd(&hist[256 * w + (((uint32_t)(k >> lo)) & dmask)], 1u);
+        }
+        __syncthreads();
+        // bin totals over the waves (thread b sums bin b), then the bin of the
+        // need-th largest: a suffix scan over the 256 totals by wave 0
+        uint32_t tot = 0;
+        if (tid < 256) {
+            for (int q = 0; q < nw; ++q) tot += hist[256 * q + tid];
+        }
+        __syncthreads();
+        if (tid < 256) hist[tid] = tot;
+        __syncthreads();
+        if (tid < 64) {
+            // lane l owns bins 255-4l .. 252-4l (descending)
+            uint32_t c4[4], sum = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c4[e] = hist[255 - 4 * tid - e];
+                sum += c4[e];
+            }
+            uint32_t incl = sum;  // inclusive prefix over lanes (higher bins first)
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (tid >= o) incl += y;
+            }
+            uint32_t acc = incl - sum;
+            if (acc < need && incl >= need) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (acc + c4[e] >= need) {
+                        ctl[0] = (uint32_t)(255 - 4 * tid - e);
+                        ctl[1] = acc;
+                        ctl[2] = c4[e];
+                        break;
+                    }
+                    acc += c4[e];
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t dd = ctl[0], above = ctl[1], in_bin = ctl[2];
+        __syncthreads();
+        need -= above;
+        prefix |= (uint64_t)dd << lo;
+        pmask |= (uint64_t)dmask << lo;
+        if (in_bin == need) {
+            // every key under this prefix is selected: the k-th is the smallest of them
+            uint64_t m = ~0ull;
+            for (uint32_t i = tid; i < nc; i += blockDim.x) {
+                const uint64_t k = keys[i];
+                if ((k & pmask) == prefix && k < m) m = k;
+            }
+            return block_min_u64(m, red);
+        }
+        hi = lo;
+    }
+    return prefix;  // all 64 bits fixed
+}
+
+// Ascending bitonic sort of v[0..n) in LDS, n a power of two <= 2 * blockDim.x.
+__device__ void block_bitonic_sort(int32_t* v, int n) {
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < n; i += blockDim.x) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool up = (i & size) == 0;
+                    const int32_t x = v[i], y = v[j];
+                    if ((x > y) == up) {
+                        v[i] = y;
+                        v[j] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a, int window, int64_t p_last) {
-    __shared__ uint32_t scratch[kCompactScratch];
     __shared__ uint64_t keys[kCandCap];
-    __shared__ uint32_t nc_sh;
+    __shared__ int32_t pos[2048];
+    __shared__ uint32_t hist[256 * (kFinThreads / 64)];
+    __shared__ uint32_t ctl[20];
+    __shared__ uint64_t red[kFinThreads / 64];
+    __shared__ uint32_t scratch[1024];  // the whole-row fallback
     const int64_t r = blockIdx.x;
     int32_t* out = a.out + (size_t)r * (size_t)a.out_stride;
     // forced window (decode rows all sit at p_last)
@@ -371,24 +509,35 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
     for (int t = threadIdx.x + kk; t < a.k; t += blockDim.x) out[t] = -1;
     if (kk == 0) return;
-    if (threadIdx.x < 64) {
-        uint32_t c = 0;
-        for (int q = threadIdx.x; q < a.n_sub; q += 64) c += a.counts[(size_t)r * a.n_sub + q];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-        if (threadIdx.x == 0) nc_sh = c;
-    }
-    __syncthreads();
-    const uint32_t nc = nc_sh;
+    const uint32_t nc = a.thr[2 * r + 1];
     if (nc > (uint32_t)kCandCap) {
-        uint32_t* tmp = reinterpret_cast<uint32_t*>(scratch);
-        select_row_exact(a.scores + (size_t)r * (size_t)a.row_stride, n, kk, out, tmp + 512, tmp);
+        select_row_exact(a.scores + (size_t)r * (size_t)a.row_stride, n, kk, out, scratch + 512, scratch);
         return;
     }
     const uint64_t* cand = a.cand + (size_t)r * kCandCap;
     for (uint32_t i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = cand[i];
+    if (threadIdx.x == 0) ctl[3] = 0;
     __syncthreads();
-    if (threadIdx.x < 64) wave_topk_ordered_lds(keys, nc, kk, scratch, out);
+    const uint64_t T = kk < nc ? block_kth_key(keys, nc, kk, hist, ctl, red) : 0ull;
+    // positions of the keys >= T (exactly kk of them), then ascending order
+    for (uint32_t ib = 0; ib < nc; ib += blockDim.x) {
+        const uint32_t i = ib + threadIdx.x;
+        const uint64_t k = i < nc ? keys[i] : 0ull;
+        const bool keep = i < nc && k >= T;
+        const uint64_t m = __ballot(keep);
+        if (m == 0) continue;
+        uint32_t off = 0;
+        if ((threadIdx.x & 63) == 0) off = atomicAdd(&ctl[3], (uint32_t)__popcll(m));
+        off = __shfl(off, 0);
+        if (keep) pos[off + __popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull))] = (int32_t)key_pos(k);
+    }
+    int np = 1;
+    while (np < (int)kk) np <<= 1;
+    __syncthreads();
+    for (int i = (int)kk + threadIdx.x; i < np; i += blockDim.x) pos[i] = 0x7FFFFFFF;
+    __syncthreads();
+    block_bitonic_sort(pos, np);
+    for (uint32_t i = threadIdx.x; i < kk; i += blockDim.x) out[i] = pos[i];
 }
 
 hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st) {
