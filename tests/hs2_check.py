@@ -41,7 +41,8 @@ def lse_close(got, ref, rtol: float) -> float:
     g = to_np(got).astype(np.float64)
     r = np.asarray(ref, dtype=np.float64)
     both_inf = np.isneginf(g) & np.isneginf(r)
-    d = np.where(both_inf, 0.0, np.abs(g - r))
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(g - r))
     tol = rtol * np.maximum(1.0, np.abs(np.where(both_inf, 0.0, r)))
     bad = ~(d <= tol)
     if bad.any():

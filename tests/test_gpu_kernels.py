@@ -84,6 +84,7 @@ def _rand_index_rows(rng, n_tok, n_sel, n_ctx, fill):
     (2, 5, 4100, 1152, 1152),      # bf16, H=16, d=128, split path
     (4, 6, 5000, 1152, 0),         # fp8 KV, split path
     (2, 1100, 2000, 200, 0),       # bf16, one workgroup per token (no split)
+    (2, 1030, 6000, 2300, 0),      # bf16, no split, index rows longer than one LDS index chunk
 ])
 def test_sparse_matches_oracle(hs2, orc, cfg, n_q, n_ctx, n_sel, fill):
     wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=n_ctx - n_q, n_ctx=n_ctx, n_needles=0, needles="none",
@@ -112,6 +113,7 @@ def test_sparse_matches_oracle(hs2, orc, cfg, n_q, n_ctx, n_sel, fill):
     (1, 2, 4099, 1),        # f32, H=4, d=64, K=256
     (3, 2, 100, 1),         # shorter than the window: no candidates
     (3, 2, 700, 1),         # fewer candidates than k_global
+    (3, 2, 3000, 9),        # more sparse layers than one launch batch
 ])
 def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
     wl = workload(cfg).with_(B=B, n_q=1, q_pos0=n_ctx - 1, n_ctx=n_ctx, n_sparse=n_sparse, needles="decode",
@@ -152,9 +154,10 @@ def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
     (2, 48, 9952, 10000, 1024),      # > 4096 candidates per token: compaction while streaming
     (4, 40, 12000, 12040, 1024),     # fp8 with clustered (tied) needles, streaming compaction
     (1, 96, 5000, 5096, 256),        # f32, H=4: 8 tokens per wave, streaming compaction
+    (2, 300, 500, 800, 0),           # window only (k_global = 0)
 ])
 def test_full_attn_select_matches_oracle(hs2, orc, cfg, n_q, q_pos0, n_ctx, kg):
-    wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, k_global=kg, n_needles=4)
+    wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, k_global=kg, n_needles=4 if kg else 0)
     x = make_inputs(wl)
     say("prefill", wl.name, n_q, q_pos0, n_ctx)
     out, lse, idx = hs2.full_attn_select(dev(x.q), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale),
@@ -198,3 +201,32 @@ def test_prefill_all_tied_scores(hs2, orc):
     ref = orc.full_select(x.q, x.k, x.v, None, None, wl.q_pos0, 128, 1024, x.sm_scale, rows, want_scores=True)
     check_index_rows(idx[0], ref["idx"], ref["scores"], ref["kth"], 128)
     rows_close(out[0], ref["out"], 1e-2)
+
+
+@pytest.mark.parametrize("cfg,B,H,d,n_q,q_pos0,n_ctx", [
+    (2, 2, 16, 128, 200, 300, 500),     # two sequences in one launch
+    (2, 1, 8, 64, 500, 4000, 4500),     # bf16, H=8, d=64 instantiations
+    (4, 2, 4, 128, 160, 5000, 5160),    # fp8, H=4, two sequences
+])
+def test_prefill_batched_and_head_shapes(hs2, orc, cfg, B, H, d, n_q, q_pos0, n_ctx):
+    wl = workload(cfg).with_(B=B, H=H, d=d, n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, n_needles=4, n_sparse=1)
+    x = make_inputs(wl)
+    say("prefill shapes", wl.name, B, H, d, n_q, q_pos0, n_ctx)
+    kw = dict(q_pos0=q_pos0, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale)
+    out, lse, idx = hs2.full_attn_select(dev(x.q), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale), **kw)
+    so, sl = hs2.sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale), indices=idx,
+                             sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    rows = list(range(B * n_q))
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, q_pos0, wl.window, wl.k_global, x.sm_scale, rows,
+                          want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    rows_close(out.reshape(B * n_q, H, d), ref["out"], tol, "prefill out")
+    lse_close(lse.reshape(B * n_q, H), ref["lse"], tol)
+    g = idx.reshape(B * n_q, -1)
+    ov, mn, sw = check_index_rows(g, ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
+    s = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, to_np(g).astype(np.int32),
+                   x.sm_scale, rows)
+    rows_close(so[0].reshape(B * n_q, H, d), s["out"], tol, "prefill sparse out")
+    lse_close(sl[0].reshape(B * n_q, H), s["lse"], tol)
