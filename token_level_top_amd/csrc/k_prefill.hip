@@ -35,6 +35,8 @@
 //                 stable, so the buffer already lists the selected positions in
 //                 ascending order and is written out as the index row (after the
 //                 forced window).
+#include <type_traits>
+
 #include "hs2_device.h"
 #include "hs2_internal.h"
 #include "hs2_wave_select.h"
@@ -446,15 +448,15 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
 constexpr int kPfBufs = 3;
 constexpr float kPsumMax = 16.0f * 256.0f;  // 16 terms of at most 2^kLazy each
 
-template <int D, bool SCALED, int NT>
+template <int D, bool SCALED, int NT, bool WITH_V = true>
 struct PipeStage {
     static constexpr int KLD = D + 8;                          // K tile row stride (elements)
     static constexpr int VLD = kPfTile + 8;                    // V^T tile row stride
     static constexpr int KCH = kPfTile * D / 8;                // 16-B K pieces per tile
     static constexpr int VCH = D * kPfTile / 8;                // 16-B V^T pieces per tile
     static constexpr int KPT = (KCH + NT - 1) / NT;            // per thread (the last round may be partial)
-    static constexpr int VPT = (VCH + NT - 1) / NT;
-    u32x4 kr[KPT], vr[VPT];
+    static constexpr int VPT = WITH_V ? (VCH + NT - 1) / NT : 0;
+    u32x4 kr[KPT], vr[VPT > 0 ? VPT : 1];
     f32x4 cr;
 
     // Tile t: K rows 64t.. (clamped into the cache; rows past the end are
@@ -749,21 +751,30 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
 // ------------------------------------------------------------- score_stream
 constexpr int kGroupTiles = 8;  // tiles between candidate-buffer room checks
 
-
 // exact top-kk of a token's candidate buffer (kept in global memory), inline
 __device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
                                                  int32_t* pos_out) {
     return wave_topk_mem<8>(buf, cnt, kk, hist, pos_out, buf);
 }
 
+// Waves per SIMD for pass 2. The tile loop is VALU-issue bound, so four waves
+// pay where the kernel fits in 128 VGPRs (16 heads; 8 heads at d = 64). With
+// fewer heads a wave holds more tokens' state and would spill there.
 template <int H, int D, int KV>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(KV == DT_F32 ? 2 : HS2_SS_OCC)))
+constexpr int score_stream_occupancy() {
+    return KV == DT_F32 ? 2 : (H >= 16 || (H >= 8 && D <= 64)) ? HS2_SS_OCC : 2;
+}
+
+template <int H, int D, int KV>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(score_stream_occupancy<H, D, KV>())))
 void score_stream_kernel(PrefillArgs a) {
     constexpr bool F32 = KV == DT_F32;
     constexpr bool SCALED = KV == DT_FP8;
     using T = PfTypes<F32>;
     using LT = typename T::L;
-    using Stage = TileStage<D, F32, false>;
+    // K tiles only; fp32 keeps its own staging, bf16 / FP8 use the 32-bit
+    // clamped loads of pass 1 (rows past the cache are never candidates)
+    using Stage = typename std::conditional<F32, TileStage<D, true, false>, PipeStage<D, SCALED, kPfThreads, false>>::type;
     constexpr int VPL = T::VPL, KD = T::KD, NS = D / KD;
     constexpr int KLD = Stage::KLD;
     constexpr int TB = kPfRows / H;   // tokens per workgroup
@@ -771,7 +782,7 @@ void score_stream_kernel(PrefillArgs a) {
     constexpr int NSC = 16 / H;       // scores per lane per 32-key block
 
     __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
-    __shared__ float ks_lds[kPfBufs][kPfTile];
+    __shared__ __attribute__((aligned(16))) float ks_lds[kPfBufs][kPfTile];  // FP8: k_scale * log2(e) * sm_scale
     __shared__ uint32_t whist[kPfWaves][kCompactScratchMem];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -875,8 +886,7 @@ void score_stream_kernel(PrefillArgs a) {
     // current threshold (held in pend_*[sub])
     auto score = [&](const f32x16& sacc, int buf, int sub, int64_t j0) {
         const int64_t jpos = j0 + 32 * sub + n;  // this lane's key
-        float c = a.scale_log2;
-        if constexpr (SCALED) c *= ks_lds[buf][32 * sub + n];
+        const float c = SCALED ? ks_lds[buf][32 * sub + n] : a.scale_log2;
         // head sums: accumulator i holds row 8(i/4) + 4hh + i%4 of the wave
         float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -933,32 +943,23 @@ void score_stream_kernel(PrefillArgs a) {
             }
         }
     };
-    auto store_ks = [&](int buf, int t, float ks_v) {
-        if constexpr (SCALED) {
-            if (tid < kPfTile) ks_lds[buf][tid] = (int64_t)kPfTile * t + tid < a.n_ctx ? ks_v : 0.f;
-        }
-    };
-    auto load_ks = [&](int t) {
-        float v = 0.f;
-        if constexpr (SCALED) {
-            if (tid < kPfTile) v = ksg[min<int64_t>((int64_t)kPfTile * t + tid, a.n_ctx - 1)];
-        }
-        return v;
-    };
-    // Tile T: [S of block 2T+1 | scores of block 2T], store tile T+1 (loaded
-    // one tile earlier) and flush appends, barrier, load tile T+2, [S of block
-    // 2T+2 | scores of block 2T+1]. Three LDS buffers: tile T+1 is stored while
-    // tile T is read and tile T-1's buffer is no longer.
     Stage stg;
-    stg.load(kg, nullptr, 0, a.n_ctx, a.n_ctx_pad);
-    float ks_pf = load_ks(0);
-    stg.store(k_lds[0], nullptr);
-    store_ks(0, 0, ks_pf);
+    auto stage_load = [&](int t) {
+        if constexpr (F32)
+            stg.load(kg, nullptr, (int64_t)t * kPfTile, a.n_ctx, a.n_ctx_pad);
+        else
+            stg.load(kg, nullptr, ksg, t, (int)a.n_ctx, (int)a.n_ctx_pad);
+    };
+    auto stage_store = [&](int buf) {
+        if constexpr (F32)
+            stg.store(k_lds[buf], nullptr);
+        else
+            stg.store(k_lds[buf], nullptr, ks_lds[buf], a.scale_log2);
+    };
+    stage_load(0);
+    stage_store(0);
     __syncthreads();
-    if (n_tiles > 1) {
-        stg.load(kg, nullptr, kPfTile, a.n_ctx, a.n_ctx_pad);
-        ks_pf = load_ks(1);
-    }
+    if (n_tiles > 1) stage_load(1);
     if constexpr (!HS2_SS_PIPE) {
     // not pipelined: more waves per SIMD hide the MFMA latency instead
     int buf = 0, nbuf = 1;
@@ -967,16 +968,10 @@ void score_stream_kernel(PrefillArgs a) {
         if (T % kGroupTiles == 0) make_room(min(kGroupTiles, n_tiles - T));
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) score(qk(buf, sub), buf, sub, j0);
-        if (T + 1 < n_tiles) {
-            stg.store(k_lds[nbuf], nullptr);
-            store_ks(nbuf, T + 1, ks_pf);
-        }
+        if (T + 1 < n_tiles) stage_store(nbuf);
         flush();
         __syncthreads();
-        if (T + 2 < n_tiles) {
-            stg.load(kg, nullptr, j0 + 2 * kPfTile, a.n_ctx, a.n_ctx_pad);
-            ks_pf = load_ks(T + 2);
-        }
+        if (T + 2 < n_tiles) stage_load(T + 2);
         buf = nbuf;
         nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
     }
@@ -991,16 +986,10 @@ void score_stream_kernel(PrefillArgs a) {
         const int64_t j0 = (int64_t)T * kPfTile;
         f32x16 s_nxt = qk(buf, 1);
         score(s_cur, buf, 0, j0);
-        if (T + 1 < n_tiles) {
-            stg.store(k_lds[nbuf], nullptr);
-            store_ks(nbuf, T + 1, ks_pf);
-        }
+        if (T + 1 < n_tiles) stage_store(nbuf);
         flush();
         __syncthreads();
-        if (T + 2 < n_tiles) {
-            stg.load(kg, nullptr, j0 + 2 * kPfTile, a.n_ctx, a.n_ctx_pad);
-            ks_pf = load_ks(T + 2);
-        }
+        if (T + 2 < n_tiles) stage_load(T + 2);
         s_cur = qk(nbuf, 0);  // after the last tile this reads a stale buffer; unused
         score(s_nxt, buf, 1, j0);
         buf = nbuf;
