@@ -89,6 +89,13 @@ __device__ __forceinline__ float xor32(float x) {
 // lanes l < 32 receive a_lo + a_hi(of lane l+32)... precisely: with a held in
 // every lane and b held in every lane, returns a[l] + a[l+32] in the low half
 // and b[l-32] + b[l] in the high half.
+// Raw (stride 0) buffer descriptor over `bytes` bytes from `base`: a load at
+// an offset at or past the end returns zero and a store there is dropped.
+// Word 3 is the untyped-access setting of the gfx9 family (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float halves_sum(float a, float b) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -745,12 +745,10 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
 #ifndef HS2_SS_OCC
 #define HS2_SS_OCC 4
 #endif
-#ifndef HS2_SS_PIPE
-#define HS2_SS_PIPE 0
+#ifndef HS2_SS_GSTORE
+#define HS2_SS_GSTORE 0
 #endif
 // ------------------------------------------------------------- score_stream
-constexpr int kGroupTiles = 8;  // tiles between candidate-buffer room checks
-
 // exact top-kk of a token's candidate buffer (kept in global memory), inline
 __device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
                                                  int32_t* pos_out) {
@@ -765,6 +763,49 @@ constexpr int score_stream_occupancy() {
     return KV == DT_F32 ? 2 : (H >= 16 || (H >= 8 && D <= 64)) ? HS2_SS_OCC : 2;
 }
 
+// K tile staging of the bf16 / FP8 score pass. Each thread moves the same 16-B
+// pieces of every tile, so its buffer offsets are fixed for the whole scan; the
+// tile start goes into the descriptor, whose range ends at the cache end, and
+// rows past it read as zero (they are never candidates). FP8: the tile's 64
+// key scales (one per thread of the first wave), stored multiplied by the
+// base-2 softmax scale.
+template <int D, bool SCALED>
+struct ScoreStage {
+    static constexpr int KLD = D + 8;                 // K tile row stride (elements)
+    static constexpr int KCH = kPfTile * D / 8;       // 16-B K pieces per tile
+    static constexpr int KPT = KCH / kPfThreads;
+    static_assert(KCH % kPfThreads == 0, "every thread stages whole K pieces");
+    u32x4 kr[KPT];
+    float cr;  // FP8: one key scale per thread of the first wave
+
+    __device__ __forceinline__ void load(const uint16_t* kb, const float* ksb, int t, int n_ctx) {
+        const int tid = threadIdx.x, j0 = kPfTile * t;
+        const auto rk = raw_buffer(kb + (size_t)j0 * D, (uint32_t)(n_ctx - j0) * (uint32_t)(2 * D));
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * (tid + kPfThreads * i), 0, 0);
+        if constexpr (SCALED) {
+            if (tid < kPfTile) {
+                const auto rc = raw_buffer(ksb + j0, (uint32_t)(n_ctx - j0) * 4u);
+                cr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, 4 * tid, 0, 0));
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* kl, float* cl, float scale_log2) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int ch = tid + kPfThreads * i, row = ch / (D / 8), cc = ch % (D / 8);
+            *reinterpret_cast<u32x4*>(kl + row * KLD + cc * 8) = kr[i];
+        }
+        if constexpr (SCALED) {
+            if (tid < kPfTile) cl[tid] = cr * scale_log2;
+        }
+    }
+};
+
+template <int B>
+using ic = std::integral_constant<int, B>;
+
 template <int H, int D, int KV>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(score_stream_occupancy<H, D, KV>())))
 void score_stream_kernel(PrefillArgs a) {
@@ -772,20 +813,20 @@ void score_stream_kernel(PrefillArgs a) {
     constexpr bool SCALED = KV == DT_FP8;
     using T = PfTypes<F32>;
     using LT = typename T::L;
-    // K tiles only; fp32 keeps its own staging, bf16 / FP8 use the 32-bit
-    // clamped loads of pass 1 (rows past the cache are never candidates)
-    using Stage = typename std::conditional<F32, TileStage<D, true, false>, PipeStage<D, SCALED, kPfThreads, false>>::type;
+    using Stage = typename std::conditional<F32, TileStage<D, true, false>, ScoreStage<D, SCALED>>::type;
     constexpr int VPL = T::VPL, KD = T::KD, NS = D / KD;
     constexpr int KLD = Stage::KLD;
     constexpr int TB = kPfRows / H;   // tokens per workgroup
     constexpr int TW = 32 / H;        // tokens per wave
     constexpr int NSC = 16 / H;       // scores per lane per 32-key block
+    static_assert(kPfBufs == 3, "the tile loop is unrolled over the three LDS buffers");
 
     __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
     __shared__ __attribute__((aligned(16))) float ks_lds[kPfBufs][kPfTile];  // FP8: k_scale * log2(e) * sm_scale
     __shared__ uint32_t whist[kPfWaves][kCompactScratchMem];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave addresses scalar
     const int n = lane & 31, hh = lane >> 5;
     const int n_blk = (int)((a.n_q + TB - 1) / TB);
     const int blk = n_blk - 1 - (int)blockIdx.x;
@@ -798,19 +839,21 @@ void score_stream_kernel(PrefillArgs a) {
     const int64_t c_max = p_max - W;  // last candidate position of the block
     const bool any_cand = c_max >= 0 && kglob > 0;
 
-    // per score slot u: the token it belongs to (relative to the wave), its last
-    // candidate position, the token's threshold and candidate count
-    int tslot[NSC];
-    int64_t climit[NSC];
-    uint64_t thr[NSC];
-    uint32_t cnt[NSC];
+    // Score slot u of the lanes in half `side` belongs to token wtok0 + slot_token(u, side).
+    auto slot_token = [](int u, int side) { return H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side); };
+    // Per slot: the lane's last candidate position minus n (so key j0 + n is a
+    // candidate iff j0 <= cl_n), the score bits of its token's threshold key
+    // (-1: none yet), and the candidate count of each half's token, which is
+    // the same on all lanes.
+    int cl_n[NSC];
+    int thr_hi[NSC];
+    uint32_t cnt[NSC][2];
 #pragma unroll
     for (int u = 0; u < NSC; ++u) {
-        tslot[u] = H == 16 ? hh : (H == 8 ? 2 * hh + u : 2 * u + hh);
-        const int64_t tk = wtok0 + tslot[u];
-        climit[u] = tk < a.n_q ? a.q_pos0 + tk - W : -1;
-        thr[u] = 0;
-        cnt[u] = 0;
+        const int64_t tk = wtok0 + slot_token(u, hh);
+        cl_n[u] = (tk < a.n_q ? (int)(a.q_pos0 + tk - W) : -1) - n;
+        thr_hi[u] = -1;
+        cnt[u][0] = cnt[u][1] = 0;
     }
     const size_t row0 = (size_t)b * a.n_q;  // flat token index base
     const int cap = a.cand_cap;
@@ -852,24 +895,35 @@ void score_stream_kernel(PrefillArgs a) {
     const float* ksg = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
 
     const int n_tiles = (int)((c_max + kPfTile) / kPfTile);
+    // this wave's candidate rows: TW tokens x cap keys
+    uint64_t* const cwave = a.cand + (row0 + (size_t)wtok0) * (size_t)cap;
+    const auto crs = raw_buffer(cwave, (uint32_t)(TW * cap * 8));
+    const uint32_t hhm = hh ? ~0u : 0u;  // lanes of the upper half
     // Appends are held in registers and issued after the next LDS tile store
     // (whose wait covers the staged tile loads): loads and stores share vmcnt,
     // so a store issued ahead of a tile load would be waited for with it.
-    uint64_t pend_key[2][NSC];
-    uint64_t* pend_ptr[2][NSC];
-    bool pend_take[2][NSC];
+    uint64_t pend_m[2][NSC];
+    uint32_t pend_lo[2][NSC], pend_hi[2][NSC], pend_off[2][NSC];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int u = 0; u < NSC; ++u) pend_take[sb][u] = false;
+        for (int u = 0; u < NSC; ++u) pend_m[sb][u] = 0;
     auto flush = [&]() {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int u = 0; u < NSC; ++u)
-                if (pend_take[sb][u]) {
-                    *pend_ptr[sb][u] = pend_key[sb][u];
-                    pend_take[sb][u] = false;
+                if (pend_m[sb][u]) {
+                    if (__builtin_amdgcn_inverse_ballot_w64(pend_m[sb][u])) {
+#if HS2_SS_GSTORE
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(cwave) + pend_off[sb][u]) =
+                            u32x2{pend_lo[sb][u], pend_hi[sb][u]};
+#else
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend_lo[sb][u], pend_hi[sb][u]}, crs,
+                                                              pend_off[sb][u], 0, 0);
+#endif
+                    }
+                    pend_m[sb][u] = 0;
                 }
     };
     // S block: this wave's 32 rows (M) x keys 32*sub.. of an LDS tile (N)
@@ -882,18 +936,18 @@ void score_stream_kernel(PrefillArgs a) {
         for (int s = 0; s < NS; ++s) acc = mfma32(&qf[s][0], krow + KD * s, acc);
         return acc;
     };
-    // token scores of one S block, and the appends of keys above each token's
-    // current threshold (held in pend_*[sub])
-    auto score = [&](const f32x16& sacc, int buf, int sub, int64_t j0) {
-        const int64_t jpos = j0 + 32 * sub + n;  // this lane's key
+    // token scores of one S block, and the appends of keys that beat each
+    // token's threshold key (held in pend_*[sub]). Keys arrive in ascending
+    // position, so a key whose score bits equal the threshold's loses the tie.
+    auto score = [&](const f32x16& sacc, int buf, int sub, int j0) {
         const float c = SCALED ? ks_lds[buf][32 * sub + n] : a.scale_log2;
         // head sums: accumulator i holds row 8(i/4) + 4hh + i%4 of the wave
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
-            if constexpr (H == 16) part[i >> 3] += e;     // token i/8 (both halves)
-            else part[i >> 2] += e;                      // H=8: token i/4; H=4: token 2(i/4)+hh
+            const int pi = H == 16 ? (i >> 3) : (i >> 2);  // H=16: token i/8; H=8: token i/4; H=4: token 2(i/4)+hh
+            part[pi] = (H == 16 ? (i & 7) : (i & 3)) == 0 ? e : part[pi] + e;
         }
         float sc[NSC];
         if constexpr (H == 16) {
@@ -905,40 +959,44 @@ void score_stream_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) sc[u] = part[u];
         }
+        const int js = j0 + 32 * sub;  // lane n holds key js + n
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
-            const uint64_t key = rank_key(sc[u], (uint32_t)jpos);
-            const bool take = jpos <= climit[u] && key > thr[u];
+            const uint32_t sb = __float_as_uint(sc[u]);  // a sum of exponentials: never negative
+            const bool take = (js <= cl_n[u]) & ((int)sb > thr_hi[u]);
             const uint64_t m = __ballot(take);
-            const uint64_t half = hh ? (m >> 32) : (m & 0xFFFFFFFFull);
-            const uint32_t rank = __popcll(half & ((1ull << n) - 1ull));
-            const int64_t tk = wtok0 + tslot[u];
-            pend_take[sub][u] = take;
-            pend_key[sub][u] = key;
-            pend_ptr[sub][u] = a.cand + (row0 + (size_t)tk) * (size_t)cap + cnt[u] + rank;
-            cnt[u] += __popcll(half);
+            pend_m[sub][u] = m;
+            if (m) {
+                const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32), plo = __popc(mlo);
+                // rank among the wave's taken lanes; an upper lane's also counts the lower half's
+                const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0));
+                const uint32_t s0 = (uint32_t)(slot_token(u, 0) * cap) + cnt[u][0];
+                const uint32_t s1 = (uint32_t)(slot_token(u, 1) * cap) + cnt[u][1] - plo;
+                pend_off[sub][u] = (rank + s0 + (hhm & (s1 - s0))) * 8u;
+                pend_lo[sub][u] = ~(uint32_t)(js + n);  // the key's low word: 2^32 - 1 - position
+                pend_hi[sub][u] = sb;
+                cnt[u][0] += plo;
+                cnt[u][1] += __popc(mhi);
+            }
         }
     };
-    // Room check, once per group of kGroupTiles tiles (outside the inner
-    // tile loop, so that loop makes no calls): a tile appends at most 64 keys
-    // per token, so any buffer that could overflow within the group is
-    // compacted first.
+    // Room check, once per turn of the LDS ring (outside the tile steps, so
+    // they make no calls): a tile appends at most 64 keys per token, so any
+    // buffer that could overflow within the next `tiles` tiles is compacted
+    // first.
     auto make_room = [&](int tiles) {
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
-                const uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
+                const uint32_t cs = cnt[u][side];
                 if (cs + (uint32_t)(64 * tiles) > (uint32_t)cap) {
                     flush();
-                    const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
-                    const int64_t tk = wtok0 + ts;
+                    const int64_t tk = wtok0 + slot_token(u, side);
                     uint64_t* cbuf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
                     const uint64_t kth = compact_topk(cbuf, cs, kglob, whist[w], nullptr);
-                    if (hh == side) {
-                        thr[u] = kth;
-                        cnt[u] = kglob;
-                    }
+                    if (hh == side) thr_hi[u] = (int)(uint32_t)(kth >> 32);
+                    cnt[u][side] = kglob;
                 }
             }
         }
@@ -948,56 +1006,38 @@ void score_stream_kernel(PrefillArgs a) {
         if constexpr (F32)
             stg.load(kg, nullptr, (int64_t)t * kPfTile, a.n_ctx, a.n_ctx_pad);
         else
-            stg.load(kg, nullptr, ksg, t, (int)a.n_ctx, (int)a.n_ctx_pad);
+            stg.load(kg, ksg, t, (int)a.n_ctx);
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](auto bufc) {
+        constexpr int bb = decltype(bufc)::value;
         if constexpr (F32)
-            stg.store(k_lds[buf], nullptr);
+            stg.store(k_lds[bb], nullptr);
         else
-            stg.store(k_lds[buf], nullptr, ks_lds[buf], a.scale_log2);
+            stg.store(k_lds[bb], ks_lds[bb], a.scale_log2);
+    };
+    // tile t sits in LDS buffer t % 3; fixed buffer indices give fixed LDS offsets
+    auto step = [&](auto bufc, int t) {
+        constexpr int bb = decltype(bufc)::value;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) score(qk(bb, sub), bb, sub, t * kPfTile);
+        if (t + 1 < n_tiles) stage_store(ic<(bb + 1) % kPfBufs>{});
+        flush();
+        __syncthreads();
+        if (t + 2 < n_tiles) stage_load(t + 2);
     };
     stage_load(0);
-    stage_store(0);
+    stage_store(ic<0>{});
     __syncthreads();
     if (n_tiles > 1) stage_load(1);
-    if constexpr (!HS2_SS_PIPE) {
-    // not pipelined: more waves per SIMD hide the MFMA latency instead
-    int buf = 0, nbuf = 1;
-    for (int T = 0; T < n_tiles; ++T) {
-        const int64_t j0 = (int64_t)T * kPfTile;
-        if (T % kGroupTiles == 0) make_room(min(kGroupTiles, n_tiles - T));
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) score(qk(buf, sub), buf, sub, j0);
-        if (T + 1 < n_tiles) stage_store(nbuf);
-        flush();
-        __syncthreads();
-        if (T + 2 < n_tiles) stage_load(T + 2);
-        buf = nbuf;
-        nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
+    for (int t = 0; t < n_tiles; t += kPfBufs) {
+        make_room(min(kPfBufs, n_tiles - t));
+        step(ic<0>{}, t);
+        if (t + 1 >= n_tiles) break;
+        step(ic<1>{}, t + 1);
+        if (t + 2 >= n_tiles) break;
+        step(ic<2>{}, t + 2);
     }
     flush();
-    } else {
-    f32x16 s_cur = qk(0, 0);
-    int buf = 0, nbuf = 1;
-    for (int T0 = 0; T0 < n_tiles; T0 += kGroupTiles) {
-    const int T1 = min(n_tiles, T0 + kGroupTiles);
-    make_room(T1 - T0);
-    for (int T = T0; T < T1; ++T) {
-        const int64_t j0 = (int64_t)T * kPfTile;
-        f32x16 s_nxt = qk(buf, 1);
-        score(s_cur, buf, 0, j0);
-        if (T + 1 < n_tiles) stage_store(nbuf);
-        flush();
-        __syncthreads();
-        if (T + 2 < n_tiles) stage_load(T + 2);
-        s_cur = qk(nbuf, 0);  // after the last tile this reads a stale buffer; unused
-        score(s_nxt, buf, 1, j0);
-        buf = nbuf;
-        nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
-    }
-    }
-    flush();
-    }
     }
     // Epilogue: every token of the wave gets its index row. A buffer holds the
     // token's candidates in ascending position order (appends follow the key
@@ -1007,8 +1047,7 @@ void score_stream_kernel(PrefillArgs a) {
     for (int u = 0; u < NSC; ++u) {
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            const int ts = H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side);
-            const int64_t tk = wtok0 + ts;
+            const int64_t tk = wtok0 + slot_token(u, side);
             if (tk >= a.n_q) continue;
             const int64_t p = a.q_pos0 + tk;
             const size_t row = row0 + (size_t)tk;
@@ -1018,7 +1057,7 @@ void score_stream_kernel(PrefillArgs a) {
             out += W;
             const int64_t n_cand = p - W + 1 > 0 ? p - W + 1 : 0;
             const uint32_t kk = (uint32_t)min<int64_t>(a.k_global, n_cand);
-            uint32_t cs = __builtin_amdgcn_readlane(cnt[u], side ? 32 : 0);
+            uint32_t cs = cnt[u][side];
             uint64_t* buf = a.cand + row * (size_t)cap;
             if (kk == 0) cs = 0;
             if (cs > 0) compact_topk(buf, cs, kk, whist[w], out);   // writes min(kk, cs) positions
