@@ -745,9 +745,6 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
 #ifndef HS2_SS_OCC
 #define HS2_SS_OCC 4
 #endif
-#ifndef HS2_SS_GSTORE
-#define HS2_SS_GSTORE 0
-#endif
 // ------------------------------------------------------------- score_stream
 // exact top-kk of a token's candidate buffer (kept in global memory), inline
 __device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
@@ -896,8 +893,7 @@ void score_stream_kernel(PrefillArgs a) {
 
     const int n_tiles = (int)((c_max + kPfTile) / kPfTile);
     // this wave's candidate rows: TW tokens x cap keys
-    uint64_t* const cwave = a.cand + (row0 + (size_t)wtok0) * (size_t)cap;
-    const auto crs = raw_buffer(cwave, (uint32_t)(TW * cap * 8));
+    const auto crs = raw_buffer(a.cand + (row0 + (size_t)wtok0) * (size_t)cap, (uint32_t)(TW * cap * 8));
     const uint32_t hhm = hh ? ~0u : 0u;  // lanes of the upper half
     // Appends are held in registers and issued after the next LDS tile store
     // (whose wait covers the staged tile loads): loads and stores share vmcnt,
@@ -914,15 +910,9 @@ void score_stream_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < NSC; ++u)
                 if (pend_m[sb][u]) {
-                    if (__builtin_amdgcn_inverse_ballot_w64(pend_m[sb][u])) {
-#if HS2_SS_GSTORE
-                        *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(cwave) + pend_off[sb][u]) =
-                            u32x2{pend_lo[sb][u], pend_hi[sb][u]};
-#else
+                    if (__builtin_amdgcn_inverse_ballot_w64(pend_m[sb][u]))
                         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pend_lo[sb][u], pend_hi[sb][u]}, crs,
                                                               pend_off[sb][u], 0, 0);
-#endif
-                    }
                     pend_m[sb][u] = 0;
                 }
     };
