@@ -113,7 +113,7 @@ def test_sparse_matches_oracle(hs2, orc, cfg, n_q, n_ctx, n_sel, fill):
     (1, 2, 4099, 1),        # f32, H=4, d=64, K=256
     (3, 2, 100, 1),         # shorter than the window: no candidates
     (3, 2, 700, 1),         # fewer candidates than k_global
-    (3, 2, 3000, 9),        # more sparse layers than one launch batch
+    (3, 2, 3000, 9),        # nine sparse layers, one launch and combine each
 ])
 def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
     wl = workload(cfg).with_(B=B, n_q=1, q_pos0=n_ctx - 1, n_ctx=n_ctx, n_sparse=n_sparse, needles="decode",

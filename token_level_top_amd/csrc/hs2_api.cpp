@@ -98,10 +98,6 @@ int sparse_splits(int64_t n_tok, int n_sel) {
     const int rps = sparse_rows_per_split(n_tok, n_sel);
     return (n_sel + rps - 1) / rps;
 }
-// sparse layers sharing one index set run as one launch, up to this many at a
-// time (the split partials are sized for it)
-constexpr int kLayerBatch = 8;
-
 struct DecodeWs {
     float *logits, *part, *lse2, *scores, *spart;
     uint32_t *hist, *thr;
@@ -116,12 +112,11 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     w.part = ns > 1 ? c.take<float>(sizeof(float) * (size_t)B * ns * H * (d + 2)) : nullptr;
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
     w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
-    // hist and tickets are contiguous so one fill clears both
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * kHistBins);
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * 2);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
     const int ss = sparse_splits(B, window + k_global);
-    w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)kLayerBatch * B * ss * H * (d + 2)) : nullptr;
+    w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)B * ss * H * (d + 2)) : nullptr;
     w.bytes = c.used;
     return w;
 }
@@ -134,7 +129,7 @@ SparseWs sparse_ws(void* base, int64_t n_tok, int n_sel, int H, int d) {
     Carver c(base);
     SparseWs w;
     const int ss = sparse_splits(n_tok, n_sel);
-    w.part = ss > 1 ? c.take<float>(sizeof(float) * (size_t)kLayerBatch * n_tok * ss * H * (d + 2)) : nullptr;
+    w.part = ss > 1 ? c.take<float>(sizeof(float) * (size_t)n_tok * ss * H * (d + 2)) : nullptr;
     w.bytes = c.used;
     return w;
 }
@@ -240,7 +235,9 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_ERR_
 
 constexpr float kLog2eF = 1.4426950408889634f;
 
-// Enqueue n_layers sparse layers (shared by hs2_sparse_attn and hs2_decode_step).
+// Enqueue n_layers sparse layers (shared by hs2_sparse_attn and hs2_decode_step),
+// one launch (and combine) per layer in layer order: in a model each sparse
+// layer's query depends on the layer before it, so no two layers share a launch.
 int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* ks,
                const float* vs, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
                const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, float* part,
@@ -248,10 +245,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
     const int64_t n_tok = (int64_t)B * n_q;
     const int ns = sparse_splits(n_tok, n_sel);
     const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
-    // the layers of one call share the index rows and the cache: each batch of
-    // layers is one launch whose workgroups for the same token run together
-    for (int l0 = 0; l0 < n_layers; l0 += kLayerBatch) {
-        const int nl = n_layers - l0 < kLayerBatch ? n_layers - l0 : kLayerBatch;
+    for (int l0 = 0; l0 < n_layers; ++l0) {
         RowsArgs a{};
         a.q = static_cast<const char*>(q) + qstride * l0;
         a.k = k;
@@ -262,7 +256,6 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
         a.n_ctx = n_ctx;
         a.n_rows = n_sel;
         a.n_tok = (int)n_tok;
-        a.n_layers = nl;
         a.n_q = (int)n_q;
         a.n_split = ns;
         a.rows_per_split = sparse_rows_per_split(n_tok, n_sel);
@@ -279,7 +272,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
         if (ns > 1) {
             CombineArgs c{};
             c.part = part;
-            c.n_tok = (int)(n_tok * nl);
+            c.n_tok = (int)n_tok;
             c.n_split = ns;
             c.out = o;
             c.lse = ls;

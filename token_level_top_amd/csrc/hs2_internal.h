@@ -17,9 +17,7 @@ struct RowsArgs {
     const int32_t* idx;     // gather: [n_tok][n_rows] positions, -1 = empty
     int64_t n_ctx;
     int64_t n_rows;         // rows per token (gather: n_sel; contiguous: n_ctx)
-    int n_tok;              // query tokens per layer
-    int n_layers;           // layers sharing idx and cache (q, out, lse, part: [n_layers][n_tok]...);
-                            // grid.y = n_tok * n_layers, the layers of one token adjacent
+    int n_tok;              // query tokens (grid.y)
     int n_q;                // tokens per sequence (token t reads sequence t / n_q)
     int rows_per_split;     // rows per workgroup (multiple of the 128-row tile)
     int n_split;            // workgroups per token (grid.x)

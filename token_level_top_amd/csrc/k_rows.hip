@@ -98,17 +98,12 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hl = lane & 15, g = lane >> 4;
-    // grid.y enumerates (token, layer) with the layers of a token adjacent, so
-    // workgroups gathering the same rows for different layers run together;
-    // `tok` is the row of q / out / lse / part, `t` the token of idx and cache
-    const int L = a.n_layers > 0 ? a.n_layers : 1;
-    const int t = (int)blockIdx.y / L, layer = (int)blockIdx.y - t * L;
-    const int tok = layer * a.n_tok + t, split = blockIdx.x;
-    const int seq = t / a.n_q;
+    const int tok = blockIdx.y, split = blockIdx.x;
+    const int seq = tok / a.n_q;
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
     const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
     const size_t kv_base = (size_t)seq * (size_t)a.n_ctx;
-    const int32_t* idx_row = GATHER ? a.idx + (size_t)t * (size_t)a.n_rows : nullptr;
+    const int32_t* idx_row = GATHER ? a.idx + (size_t)tok * (size_t)a.n_rows : nullptr;
 
     // query fragment (B operand of S^T = K Q^T): head hl, d = KD*s + VPL*g + [0, VPL)
     LT qf[NS][VPL];
@@ -422,7 +417,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
 
 template <int H, int D, int KV, bool GATHER, bool STORE>
 static hipError_t launch_rows_t(const RowsArgs& a, hipStream_t st) {
-    dim3 grid(a.n_split, a.n_tok * (a.n_layers > 0 ? a.n_layers : 1));
+    dim3 grid(a.n_split, a.n_tok);
     hipLaunchKernelGGL((rows_attn_kernel<H, D, KV, GATHER, STORE>), grid, dim3(kRowsThreads), 0, st, a);
     return hipGetLastError();
 }
