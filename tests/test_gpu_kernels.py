@@ -185,6 +185,43 @@ def test_prefill_and_decode_are_deterministic(hs2):
         assert torch.equal(u, v)
 
 
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_results_do_not_depend_on_workspace_contents(hs2, cfg):
+    """Workspace bytes left by earlier calls never reach the results: a prefill
+    and a decode step give bit-identical outputs with the workspace zeroed and
+    with every byte 0xFF (an unwritten candidate slot would then read as the
+    largest key), three calls each."""
+    wl = workload(cfg).with_(B=1, n_q=64, q_pos0=6000, n_ctx=6064, n_needles=2, n_sparse=2)
+    x = make_inputs(wl)
+    kv = (dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale))
+    B, n_q, H, d = x.q.shape
+    kvdt = hs2._KVDT[x.k.dtype]
+    say("workspace contents", wl.name)
+    n = hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, B, n_q, wl.n_ctx, H, d, 128, 1024, kvdt)
+    runs = []
+    for fill in (0, 255, 255, 0, 255):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        r = hs2.full_attn_select(dev(x.q), *kv, q_pos0=wl.q_pos0, window=128, k_global=1024, sm_scale=x.sm_scale,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in r])
+    for r in runs[1:]:
+        for u, v in zip(runs[0], r):
+            assert torch.equal(u, v)
+    qf, qs = dev(x.q[:, -1]).contiguous(), dev(x.q_sparse[:, :, -1]).contiguous()
+    n = hs2.workspace_size(hs2.OP_DECODE_STEP, B, 1, wl.n_ctx, H, d, 128, 1024, kvdt)
+    runs = []
+    for fill in (0, 255, 255):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        r = hs2.decode_step(qf, qs, *kv, window=128, k_global=1024, sm_scale=x.sm_scale, want_scores=True,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        runs.append({k: v.clone() for k, v in r.items() if v is not None})
+    for r in runs[1:]:
+        for k in runs[0]:
+            assert torch.equal(runs[0][k], r[k]), k
+
+
 def test_prefill_all_tied_scores(hs2, orc):
     """Zero queries give every key the same score: the lowest positions win."""
     wl = workload(2).with_(n_q=64, q_pos0=6000, n_ctx=6064, n_needles=0, needles="none")
