@@ -15,8 +15,8 @@
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: 16 keys on M, the heads on N. The
 //    A operand (K rows) comes straight from HBM into registers: for k-step c the
 //    lane group g reads d = 32c + 8g .. +7 of its key row, so one load
-//    instruction covers a contiguous 32-element segment of 16 rows. K of block
-//    n+1 is loaded while block n is computed.
+//    instruction covers a contiguous 32-element segment of 16 rows. K and V of
+//    blocks n+1 and n+2 are in flight while block n is computed.
 //  * O^T = V^T P^T: V rows go through a wave-private LDS buffer (the MFMA needs
 //    8 keys of one column per lane), FP8 codes widened to bf16 exactly on the way.
 //  * Logits are staged in LDS and written one block later as 16-byte stores, so
@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     __shared__ float vs_lds[4][kDecBlock];
     __shared__ float ks_lds[4][kDecBlock];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps block addresses scalar
     const int hl = lane & 15, g = lane >> 4;
     const int seq = blockIdx.y, split = blockIdx.x;
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
@@ -84,74 +85,84 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
 
     // ---- loads of one block (registers) -------------------------------------
+    // Two blocks are in flight per wave: while block n is computed, the loads
+    // of blocks n+1 and n+2 are outstanding (block n+2's as soon as block n's
+    // QK^T MFMAs have read its K registers). Loads go through a descriptor
+    // whose range ends at the split's last row, so rows past it read as zero
+    // (their logits are masked) and no row index needs clamping.
     // K: lane (row hl of group grp, g) reads elements 32c + 8g .. +7 of key row
     // j + 16*grp + hl for every k-step c. V: lane reads pieces lane + 64*i of the
-    // block's rows. Rows past the range are clamped to the last row (masked later).
+    // block's rows (contiguous in the cache).
     KPiece kr[2][2][NC];
-    u32x4 vr[VP];
-    float ksr = 0.f, vsr = 0.f;
-    const int64_t last = r_end - 1;
+    u32x4 vr[2][VP];
+    float ksr[2] = {0.f, 0.f}, vsr[2] = {0.f, 0.f};
+    const int n_split_rows = (int)(r_end - r_begin);
+    // rows of the split at and after row j (0 past its end: every access then misses the range)
+    auto rows_left = [&](int64_t j) -> uint32_t { return (uint32_t)max(0, n_split_rows - (int)(j - r_begin)); };
     auto load_block = [&](int buf, int64_t j) {
+        const uint32_t left = rows_left(j);
+        const auto rk = raw_buffer(kbase + (size_t)j * RB, left * (uint32_t)RB);
+        const auto rv = raw_buffer(vbase + (size_t)j * RB, left * (uint32_t)RB);
 #pragma unroll
         for (int grp = 0; grp < 2; ++grp) {
-            const int64_t row = min<int64_t>(j + 16 * grp + hl, last);
-            const uint8_t* p = kbase + (size_t)row * RB + (8 * g) * ESZ;
+            const int off = (16 * grp + hl) * RB + 8 * g * ESZ;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) kr[buf][grp][c] = *reinterpret_cast<const KPiece*>(p + (32 * c) * ESZ);
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (KV == DT_FP8)
+                    kr[buf][grp][c] = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 32 * c * ESZ, 0, 0);
+                else
+                    kr[buf][grp][c] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 32 * c * ESZ, 0, 0);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < VP; ++i) {
-            const int piece = lane + 64 * i;
-            const int row = piece / (RB / 16), cc = piece % (RB / 16);
-            const int64_t rr = min<int64_t>(j + row, last);
-            vr[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)rr * RB + 16 * cc);
-        }
+        for (int i = 0; i < VP; ++i) vr[buf][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * (lane + 64 * i), 0, 0);
         if constexpr (KV == DT_FP8) {
-            const int64_t rr = min<int64_t>(j + (lane & 31), last);
-            ksr = a.ks[kv_base + rr];
-            vsr = a.vs[kv_base + rr];
+            const auto rs = raw_buffer(a.ks + kv_base + j, left * 4u);
+            const auto rt = raw_buffer(a.vs + kv_base + j, left * 4u);
+            ksr[buf] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (lane & 31), 0, 0));
+            vsr[buf] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rt, 4 * (lane & 31), 0, 0));
         }
     };
     // V (and FP8 scales) of a block into the wave's LDS buffer
-    auto stage_v = [&]() {
+    auto stage_v = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < VP; ++i) {
             const int piece = lane + 64 * i;
             const int row = piece / (RB / 16), cc = piece % (RB / 16);
             if constexpr (KV == DT_FP8) {
-                const u32x2 p0 = fp8x4_to_bf16x4(vr[i][0]), p1 = fp8x4_to_bf16x4(vr[i][1]);
-                const u32x2 p2 = fp8x4_to_bf16x4(vr[i][2]), p3 = fp8x4_to_bf16x4(vr[i][3]);
+                const u32x2 p0 = fp8x4_to_bf16x4(vr[buf][i][0]), p1 = fp8x4_to_bf16x4(vr[buf][i][1]);
+                const u32x2 p2 = fp8x4_to_bf16x4(vr[buf][i][2]), p3 = fp8x4_to_bf16x4(vr[buf][i][3]);
                 u32x4* o = reinterpret_cast<u32x4*>(vl + row * VLD + 16 * cc);
                 o[0] = u32x4{p0[0], p0[1], p1[0], p1[1]};
                 o[1] = u32x4{p2[0], p2[1], p3[0], p3[1]};
             } else {
-                *reinterpret_cast<u32x4*>(vl + row * VLD + 8 * cc) = vr[i];
+                *reinterpret_cast<u32x4*>(vl + row * VLD + 8 * cc) = vr[buf][i];
             }
         }
         if constexpr (KV == DT_FP8) {
             if (lane < 32) {
-                ks_lds[w][lane] = ksr;
-                vs_lds[w][lane] = vsr;
+                ks_lds[w][lane] = ksr[buf];
+                vs_lds[w][lane] = vsr[buf];
             }
         }
     };
-    // logits of the previous block: staged [32][H] in LDS, written as 16-B pieces
-    int64_t pend_j = -1;
+    // logits of the previous block: staged [32][H] in LDS, written as 16-B
+    // streaming stores through a descriptor ending at the split's last row
+    // (before the first block its range is empty). Every load and store of the
+    // loop is issued unconditionally, so the compiler's waits on the loads of
+    // the next block count exactly the operations issued after them.
+    int64_t pend_j = r_end;
     auto flush_logits = [&]() {
-        if (pend_j < 0) return;
-        float* dst = a.logits + (kv_base + (size_t)pend_j) * H;
-        for (int p = lane; p < kDecBlock * H / 4; p += 64) {
-            const int key = (4 * p) / H;
-            if (pend_j + key < r_end)  // streaming (non-temporal) store: read once, later, by the score pass
-                __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(lgl + 4 * p),
-                                            reinterpret_cast<f32x4*>(dst + 4 * p));
-        }
-        pend_j = -1;
+        const auto rl = raw_buffer(a.logits + (kv_base + (size_t)pend_j) * H,
+                                   (uint32_t)max<int64_t>(0, r_end - pend_j) * (uint32_t)(H * 4));
+#pragma unroll
+        for (int p = lane; p < kDecBlock * H / 4; p += 64)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(lgl + 4 * p)),
+                                                   rl, 16 * p, 0, 2);
     };
 
-    auto compute = [&](int buf, int64_t j) {
-        // S^T for two 16-key groups
-        f32x4 sacc[2];
+    // S^T for the two 16-key groups of a block
+    auto scores = [&](int buf, f32x4* sacc) {
 #pragma unroll
         for (int grp = 0; grp < 2; ++grp) {
             sacc[grp] = f32x4{0, 0, 0, 0};
@@ -169,6 +180,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
                                                                     0, 0);
             }
         }
+    };
+    // logits, online softmax and O^T += V^T P^T for the block at j (V in LDS)
+    auto finish = [&](const f32x4* sacc, int64_t j) {
         // base-2 logits; lane holds head hl of block keys 16*grp + 4g + i
         float x[2][4];
         float mx = -INFINITY;
@@ -228,29 +242,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
             o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pbf, o_acc[t], 0, 0, 0);
         }
     };
-
-    if (nb > 0) {
-        load_block(0, w_begin);
-        stage_v();
-    }
-    // two blocks per trip so the K register buffer index is static
+    // block n of the wave uses register set n % 2; two blocks per trip keep the
+    // set index static. With an odd block count the last trip's second block
+    // lies past the split: its loads read zeros, its logits are all masked
+    // (no change to m, l, O) and its stores are dropped.
+    auto step = [&](int buf, int n) {
+        const int64_t j = w_begin + (int64_t)n * kStride;
+        flush_logits();
+        f32x4 sacc[2];
+        scores(buf, sacc);
+        load_block(buf, j + 2 * kStride);
+        finish(sacc, j);
+        stage_v(buf ^ 1);
+    };
+    load_block(0, w_begin);
+    load_block(1, w_begin + kStride);
+    stage_v(0);
     for (int n = 0; n < nb; n += 2) {
-        {
-            const int64_t j = w_begin + (int64_t)n * kStride;
-            flush_logits();
-            const bool more = n + 1 < nb;
-            if (more) load_block(1, j + kStride);
-            compute(0, j);
-            if (more) stage_v();
-        }
-        if (n + 1 < nb) {
-            const int64_t j = w_begin + (int64_t)(n + 1) * kStride;
-            flush_logits();
-            const bool more = n + 2 < nb;
-            if (more) load_block(0, j + kStride);
-            compute(1, j);
-            if (more) stage_v();
-        }
+        step(0, n);
+        step(1, n + 1);
     }
     flush_logits();
 
