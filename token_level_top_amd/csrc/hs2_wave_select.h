@@ -253,9 +253,14 @@ constexpr int kCompactScratchMem = 16 * 16;  // uint32 per wave: 16 digit bins x
 // The wave's own earlier stores to `keys` are made visible first. The digit
 // histogram has 16 columns (kCompactScratchMem words), shared by 4 lanes each.
 // All 64 lanes of one wave call it.
+// With max_keep >= kk the threshold may stop short of the kk-th key: as soon as
+// the keys above the current digit bin plus the bin itself number at most
+// max_keep, T is the bin's lower edge and all of them are kept (a superset of
+// the top kk, still in list order). *kept (if given) receives the number kept.
 template <int U>
 __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t cnt, uint32_t kk, uint32_t* hist,
-                                                  int32_t* pos_out, uint64_t* buf) {
+                                                  int32_t* pos_out, uint64_t* buf, uint32_t max_keep = 0,
+                                                  uint32_t* kept = nullptr) {
     const uint32_t lane = lane_id();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     // fn(key, valid) over every key, U per lane at a time (clamped loads)
@@ -330,7 +335,11 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
             prefix |= (uint64_t)dd << lo;
             pmask |= (uint64_t)dmask << lo;
             __builtin_amdgcn_wave_barrier();
-            if (in_bin == need) {
+            if (max_keep >= kk && (kk - need) + in_bin <= max_keep) {
+                // keys above the bin and the whole bin: at most max_keep of them
+                T = prefix;
+                found = true;
+            } else if (in_bin == need) {
                 // every key under this prefix is selected: T is the smallest of them
                 uint64_t m = ~0ull;
                 each([&](uint64_t k, bool ok) {
@@ -355,6 +364,7 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
         wr += __popcll(mm);
     });
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (kept) *kept = wr;
     return T;
 }
 

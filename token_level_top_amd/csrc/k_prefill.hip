@@ -745,11 +745,26 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
 #ifndef HS2_SS_OCC
 #define HS2_SS_OCC 4
 #endif
+#ifndef HS2_FINAL_U
+#define HS2_FINAL_U 16
+#endif
+#ifndef HS2_TRIM_EIGHTHS
+#define HS2_TRIM_EIGHTHS 3
+#endif
 // ------------------------------------------------------------- score_stream
-// exact top-kk of a token's candidate buffer (kept in global memory), inline
-__device__ __forceinline__ uint64_t compact_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
-                                                 int32_t* pos_out) {
-    return wave_topk_mem<8>(buf, cnt, kk, hist, pos_out, buf);
+// A token's candidate buffer (kept in global memory) cut down during the scan:
+// to at most max_keep keys that include its top kk (fewer digit passes than
+// the exact cut), in place; returns the cut key, *kept the number kept. Inline,
+// few registers: it runs inside the tile loop.
+__device__ __forceinline__ uint64_t trim_candidates(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t max_keep,
+                                                    uint32_t* hist, uint32_t* kept) {
+    return wave_topk_mem<8>(buf, cnt, kk, hist, nullptr, buf, max_keep, kept);
+}
+// exact top-kk of a token's candidate buffer, written as positions (after the
+// scan: registers are free, so more keys per lane are in flight)
+__device__ __forceinline__ void final_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
+                                           int32_t* pos_out) {
+    wave_topk_mem<HS2_FINAL_U>(buf, cnt, kk, hist, pos_out, buf);
 }
 
 // Waves per SIMD for pass 2. The tile loop is VALU-issue bound, so four waves
@@ -854,6 +869,9 @@ void score_stream_kernel(PrefillArgs a) {
     }
     const size_t row0 = (size_t)b * a.n_q;  // flat token index base
     const int cap = a.cand_cap;
+    // a trim during the scan keeps at most this many candidates (>= k_global;
+    // cap - trim_keep >= 64 keys per tile of the next room check)
+    const uint32_t trim_keep = max(kglob, (uint32_t)cap * HS2_TRIM_EIGHTHS / 8u);
     if (any_cand) {
     // Q fragment (A operand of S = Q K^T): row R = 32w + n, k = KD*s + VPL*hh + [0, VPL)
     LT qf[NS][VPL];
@@ -972,8 +990,8 @@ void score_stream_kernel(PrefillArgs a) {
     };
     // Room check, once per turn of the LDS ring (outside the tile steps, so
     // they make no calls): a tile appends at most 64 keys per token, so any
-    // buffer that could overflow within the next `tiles` tiles is compacted
-    // first.
+    // buffer that could overflow within the next `tiles` tiles is trimmed
+    // first, to a superset of its top k_global.
     auto make_room = [&](int tiles) {
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
@@ -984,9 +1002,11 @@ void score_stream_kernel(PrefillArgs a) {
                     flush();
                     const int64_t tk = wtok0 + slot_token(u, side);
                     uint64_t* cbuf = a.cand + (row0 + (size_t)tk) * (size_t)cap;
-                    const uint64_t kth = compact_topk(cbuf, cs, kglob, whist[w], nullptr);
-                    if (hh == side) thr_hi[u] = (int)(uint32_t)(kth >> 32);
-                    cnt[u][side] = kglob;
+                    uint32_t kept;
+                    const uint64_t cut = trim_candidates(cbuf, cs, kglob, trim_keep, whist[w], &kept);
+                    // a later key may still be needed if its score bits reach the cut's
+                    if (hh == side) thr_hi[u] = (int)(uint32_t)(cut >> 32) - 1;
+                    cnt[u][side] = __builtin_amdgcn_readfirstlane(kept);
                 }
             }
         }
@@ -1050,7 +1070,7 @@ void score_stream_kernel(PrefillArgs a) {
             uint32_t cs = cnt[u][side];
             uint64_t* buf = a.cand + row * (size_t)cap;
             if (kk == 0) cs = 0;
-            if (cs > 0) compact_topk(buf, cs, kk, whist[w], out);   // writes min(kk, cs) positions
+            if (cs > 0) final_topk(buf, cs, kk, whist[w], out);   // writes min(kk, cs) positions
             const uint32_t wrote = cs < kk ? cs : kk;
             for (uint32_t t = wrote + lane; t < (uint32_t)a.k_global; t += 64) out[t] = -1;
         }
