@@ -352,17 +352,22 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
         }
         if (!found) T = prefix;  // all 64 bits fixed
     }
+    // Distinct keys give exactly kk (or at most max_keep) keys >= T; the writes
+    // are capped there anyway, so equal keys in the list can never make the
+    // output (a row of kk positions, or the caller's buffer) overflow.
+    const uint32_t limit = max_keep > kk ? max_keep : kk;
     uint32_t wr = 0;
     each([&](uint64_t k, bool ok) {
         const bool keep = ok && k >= T;
         const uint64_t mm = __ballot(keep);
-        if (keep) {
-            const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
+        const uint32_t at = wr + __popcll(mm & ((1ull << lane) - 1ull));
+        if (keep && at < limit) {
             if (pos_out) pos_out[at] = (int32_t)key_pos(k);
             else buf[at] = k;
         }
         wr += __popcll(mm);
     });
+    if (wr > limit) wr = limit;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     if (kept) *kept = wr;
     return T;
