@@ -242,7 +242,7 @@ __device__ __noinline__ void wave_topk_ordered_lds(const uint64_t* keys, uint32_
     }
 }
 
-constexpr int kCompactScratchMem = 16 * 16;  // uint32 per wave: 16 digit bins x 16 lanes
+constexpr int kCompactScratchMem = 256;  // uint32 per wave: one bin per value of an 8-bit digit
 
 // Same selection over keys that stay in memory (global or LDS) and are read
 // again on every pass, U keys per lane in flight, so that it needs few
@@ -250,8 +250,8 @@ constexpr int kCompactScratchMem = 16 * 16;  // uint32 per wave: 16 digit bins x
 // the keys >= T in list order to pos_out (as positions) or, when pos_out is
 // null, back into buf (as keys; buf may be `keys` itself: a chunk is read
 // before any key of it is written, and writes never pass the chunk being read).
-// The wave's own earlier stores to `keys` are made visible first. The digit
-// histogram has 16 columns (kCompactScratchMem words), shared by 4 lanes each.
+// The wave's own earlier stores to `keys` are made visible first. Digits are
+// 8 bits wide, one histogram bin per value (kCompactScratchMem words).
 // All 64 lanes of one wave call it.
 // With max_keep >= kk the threshold may stop short of the kk-th key: as soon as
 // the keys above the current digit bin plus the bin itself number at most
@@ -300,37 +300,50 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
         bool found = false;
         T = 0;
         while (hi > 0 && !found) {
-            const int lo = hi > 4 ? hi - 4 : 0;
+            // next digit: up to 8 bits below the fixed prefix, 256 bins (lane l owns 4l .. 4l+3)
+            const int lo = hi > 8 ? hi - 8 : 0;
             const uint32_t dmask = (1u << (hi - lo)) - 1u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) hist[4 * lane + e] = 0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             each([&](uint64_t k, bool ok) {
-                if (ok && (k & pmask) == prefix) atomicAdd(&hist[(((uint32_t)(k >> lo)) & dmask) * 16 + (lane & 15)], 1u);
+                if (ok && (k & pmask) == prefix) atomicAdd(&hist[((uint32_t)(k >> lo)) & dmask], 1u);
             });
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            // bin totals: lane 4b+q sums columns 4q..4q+3 of bin b, then 4 lanes combine
-            uint32_t part = 0;
-            {
-                const int b = lane >> 2, q = lane & 3;
+            uint32_t c[4];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) part += hist[b * 16 + 4 * q + jj];
-                part += __shfl_xor(part, 1);
-                part += __shfl_xor(part, 2);
+            for (int e = 0; e < 4; ++e) c[e] = hist[4 * lane + e];
+            const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+            // keys in the bins above this lane's four: suffix sum over the higher lanes
+            uint32_t incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t v = __shfl_down(incl, o);
+                if (lane + o < 64) incl += v;
             }
-            uint32_t above = 0, dd = 0, in_bin = 0;
+            const uint32_t excl = incl - tot;
+            // the one lane whose bins reach the need-th key from the top picks the bin
+            const bool mine = excl < need && incl >= need;
+            uint32_t my_dd = 0, my_above = excl, my_in = 0;
+            if (mine) {
+                uint32_t acc = excl;
 #pragma unroll
-            for (int b = 15; b >= 0; --b) {
-                const uint32_t c = __builtin_amdgcn_readlane(part, 4 * b);
-                if (!in_bin && b <= (int)dmask && above + c >= need) {
-                    dd = (uint32_t)b;
-                    in_bin = c;
-                } else if (!in_bin) {
-                    above += c;
+                for (int e = 3; e >= 0; --e) {
+                    if (my_in == 0 && acc + c[e] >= need) {
+                        my_dd = 4 * lane + e;
+                        my_above = acc;
+                        my_in = c[e];
+                    } else if (my_in == 0) {
+                        acc += c[e];
+                    }
                 }
             }
+            const int src = __ffsll((long long)__ballot(mine)) - 1;
+            const uint32_t dd = __builtin_amdgcn_readlane(my_dd, src);
+            const uint32_t above = __builtin_amdgcn_readlane(my_above, src);
+            const uint32_t in_bin = __builtin_amdgcn_readlane(my_in, src);
             need -= above;
             prefix |= (uint64_t)dd << lo;
             pmask |= (uint64_t)dmask << lo;
