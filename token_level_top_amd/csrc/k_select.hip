@@ -470,23 +470,58 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, uint32_t nc, uint32_t kk
 }
 
 // Ascending bitonic sort of v[0..n) in LDS, n a power of two <= 2 * blockDim.x.
-__device__ void block_bitonic_sort(int32_t* v, int n) {
+// Ascending sort of v[0, n) (n a power of two, at most 2 * kFinThreads) by a
+// bitonic network with the whole workgroup: thread t holds elements t and
+// t + kFinThreads in registers. Partners less than 64 apart sit in the same
+// wave and are exchanged with shuffles, the pair at distance kFinThreads sits
+// in one thread, and only the stages with distance 64 .. kFinThreads/2 go
+// through LDS (alternating between v and tmp, one barrier each). The caller
+// has written v and synchronised; v holds the result on return.
+__device__ void block_sort_positions(int32_t* v, int32_t* tmp, int n) {
+    constexpr int NT = kFinThreads;
+    const int tid = threadIdx.x;
+    int32_t x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int i = tid + NT * e;
+        x[e] = i < n ? v[i] : 0x7FFFFFFF;
+    }
+    int32_t* bufs[2] = {tmp, v};
+    int nb = 0;
+    __syncthreads();  // every thread has read v before it is reused as a buffer
     for (int size = 2; size <= n; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n; i += blockDim.x) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const bool up = (i & size) == 0;
-                    const int32_t x = v[i], y = v[j];
-                    if ((x > y) == up) {
-                        v[i] = y;
-                        v[j] = x;
-                    }
-                }
+            int32_t y[2];
+            if (stride < 64) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) y[e] = __shfl_xor(x[e], stride);
+            } else if (stride == NT) {
+                y[0] = x[1];
+                y[1] = x[0];
+            } else {
+                int32_t* b = bufs[nb];
+                nb ^= 1;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) b[tid + NT * e] = x[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 2; ++e) y[e] = b[(tid + NT * e) ^ stride];
             }
-            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = tid + NT * e;
+                const bool up = (i & size) == 0, low = (i & stride) == 0;
+                x[e] = (low == up) ? min(x[e], y[e]) : max(x[e], y[e]);
+            }
         }
     }
+    __syncthreads();  // the last LDS stage's reads are done before v is rewritten
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int i = tid + NT * e;
+        if (i < n) v[i] = x[e];
+    }
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a, int window, int64_t p_last) {
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     __syncthreads();
     for (int i = (int)kk + threadIdx.x; i < np; i += blockDim.x) pos[i] = 0x7FFFFFFF;
     __syncthreads();
-    block_bitonic_sort(pos, np);
+    block_sort_positions(pos, reinterpret_cast<int32_t*>(keys), np);
     for (uint32_t i = threadIdx.x; i < kk; i += blockDim.x) out[i] = pos[i];
 }
 
