@@ -47,6 +47,10 @@ def lib():
         L.orc_select_scores_f32.restype = _i
         L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_value.restype = _d
+        L.orc_e4m3_encode.argtypes = [_d]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_kv_project.argtypes = [_p, _i64, _i, _p, _i, _i, _p, _i64, _p, _p, _p]
+        L.orc_kv_project.restype = _i
         L.orc_num_threads.restype = _i
         L.orc_set_threads.argtypes = [_i]
         _lib = L
@@ -136,3 +140,28 @@ def select_scores_f32(scores: np.ndarray, n_cand: Sequence[int], k: int) -> np.n
     if rc != 0:
         raise ValueError("oracle select: invalid arguments")
     return out
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest OCP E4M3FN code, ties to even, saturating at +-448."""
+    return int(lib().orc_e4m3_encode(float(x)))
+
+
+def kv_project(h, w, rows: Sequence[int], quantize: bool = False):
+    """KV Bridging projections of the hidden rows `rows`.
+    h [T][hidden] bf16, w [J][2][d][hidden] bf16 (CPU). Returns x [J][2][n][d]
+    float64 and, with quantize, codes uint8 [J][2][n][d] and scales [J][2][n]."""
+    T, hidden = h.shape
+    J, two, d, hid2 = w.shape
+    if two != 2 or hid2 != hidden:
+        raise ValueError("w must be [J][2][d][hidden]")
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = len(r)
+    x = np.zeros((J, 2, n, d), np.float64)
+    codes = np.zeros((J, 2, n, d), np.uint8) if quantize else None
+    scales = np.zeros((J, 2, n), np.float64) if quantize else None
+    rc = lib().orc_kv_project(_ptr(h.contiguous()), T, hidden, _ptr(w.contiguous()), J, d, _ptr(r), n, _ptr(x),
+                              _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle kv_project: invalid arguments")
+    return {"x": x, "codes": codes, "scales": scales}

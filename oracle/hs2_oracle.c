@@ -310,6 +310,75 @@ int orc_select_scores_f32(const float* scores, int64_t n_rows, int64_t stride,
     return 0;
 }
 
+/*
+ * Nearest E4M3FN value to x, ties to the even code (even last mantissa bit),
+ * saturating at +-448 (reading R10: the quantiser rounds to nearest even and
+ * never produces NaN). The finite non-negative codes 0x00..0x7E have strictly
+ * increasing values, so the largest code not above |x| is found by bisection.
+ */
+uint8_t orc_e4m3_encode(double x) {
+    uint8_t sgn = 0;
+    if (x < 0) {
+        sgn = 0x80;
+        x = -x;
+    }
+    if (x >= 448.0) return (uint8_t)(sgn | 0x7E);
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (orc_e4m3_value((uint8_t)mid) <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    const double a = orc_e4m3_value((uint8_t)lo), b = orc_e4m3_value((uint8_t)(lo + 1));
+    int c;
+    if (x - a < b - x) c = lo;
+    else if (x - a > b - x) c = lo + 1;
+    else c = (lo & 1) ? lo + 1 : lo;
+    return (uint8_t)(sgn | c);
+}
+
+/*
+ * KV Bridging (HySparse2 page, "어떻게 동작하나"): cross-decoder full layer j
+ * computes its keys and values with its own projections of the self-decoder
+ * full layer's input hidden state, K_j = Proj_j^K(H), V_j = Proj_j^V(H).
+ * Reading R22: each projection is a plain linear map without bias, its
+ * weight stored [out = d][in = hidden] (K then V for every layer).
+ *   h  [T][hidden] bf16, w [J][2][d][hidden] bf16
+ *   x_out  [J][2][n_rows][d] double: the projected rows `rows`
+ *   codes  [J][2][n_rows][d] (nullable): reading R10 on each projected row,
+ *          scale = max|x| / 448 (1 for an all-zero row), code = RNE(x / scale)
+ *   scales [J][2][n_rows] (nullable, with codes)
+ * Returns 0, or 1 on invalid arguments.
+ */
+int orc_kv_project(const uint16_t* h, int64_t T, int hidden, const uint16_t* w, int J, int d,
+                   const int64_t* rows, int64_t n_rows, double* x_out, uint8_t* codes, double* scales) {
+    if (T < 1 || hidden < 1 || J < 1 || d < 1 || n_rows < 0) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= T) return 1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t jk = 0; jk < 2 * (int64_t)J; ++jk)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            const uint16_t* hr = h + (size_t)rows[r] * (size_t)hidden;
+            const uint16_t* wm = w + (size_t)jk * (size_t)d * (size_t)hidden;
+            double* x = x_out + ((size_t)jk * (size_t)n_rows + (size_t)r) * (size_t)d;
+            double amax = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int k = 0; k < hidden; ++k)
+                    acc += orc_bf16(wm[(size_t)c * (size_t)hidden + (size_t)k]) * orc_bf16(hr[k]);
+                x[c] = acc;
+                if (fabs(acc) > amax) amax = fabs(acc);
+            }
+            if (codes) {
+                const double sc = amax > 0.0 ? amax / 448.0 : 1.0;
+                uint8_t* cr = codes + ((size_t)jk * (size_t)n_rows + (size_t)r) * (size_t)d;
+                for (int c = 0; c < d; ++c) cr[c] = orc_e4m3_encode(x[c] / sc);
+                if (scales) scales[(size_t)jk * (size_t)n_rows + (size_t)r] = sc;
+            }
+        }
+    return 0;
+}
+
 int orc_num_threads(void) { return omp_get_max_threads(); }
 void orc_set_threads(int n) {
     if (n > 0) omp_set_num_threads(n);

@@ -431,3 +431,89 @@ def test_clustered_needles_fp8_recovered_with_ties(orc):
     rows = sorted({n.b * wl.n_q + n.i for n in x.needles})
     hit, tot = _recovered(orc, x, rows)
     assert hit == tot == 4
+
+
+# ------------------------------------------------------------ KV Bridging
+
+def test_e4m3_encoder_matches_torch_cast(orc):
+    """The oracle's FP8 encoder (nearest, ties to even) against torch's
+    float8_e4m3fn cast of the same float32 values, inside the finite range."""
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([rng.standard_normal(4000) * 30.0, rng.uniform(-448, 448, 4000),
+                           rng.standard_normal(2000) * 1e-2, [0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10]])
+    vals = vals.astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(v)) for v in vals], np.uint8)
+    assert (got == ref).all(), (vals[got != ref][:5], got[got != ref][:5], ref[got != ref][:5])
+
+
+def test_e4m3_encoder_round_trip_and_ties(orc):
+    for c in list(range(0x00, 0x7F)) + list(range(0x81, 0xFF)):
+        assert orc.e4m3_encode(orc.e4m3_value(c)) == c
+    for c in range(0x00, 0x7E):  # the midpoint of two neighbours goes to the even code
+        mid = 0.5 * (orc.e4m3_value(c) + orc.e4m3_value(c + 1))
+        assert orc.e4m3_encode(mid) == (c if c % 2 == 0 else c + 1)
+    assert orc.e4m3_encode(1e6) == 0x7E and orc.e4m3_encode(-1e6) == 0xFE
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+
+
+def test_kv_project_one_hot_rows_give_weight_columns(orc):
+    """A hidden row e_k projects to column k of each [d][hidden] weight."""
+    J, d, hidden = 2, 8, 24
+    rng = np.random.default_rng(3)
+    w = _bf16(rng.standard_normal((J, 2, d, hidden)))
+    h = _bf16(np.eye(hidden))
+    r = orc.kv_project(h, w, list(range(hidden)))
+    wf = w.float().double().numpy()
+    for k in range(hidden):
+        assert np.array_equal(r["x"][:, :, k, :], wf[:, :, :, k])
+
+
+def test_kv_project_is_linear(orc):
+    """Additivity and scaling by 2 hold exactly (sums of bf16 products are exact
+    in float64 at this size), pinning every term of the contraction."""
+    J, d, hidden, T = 2, 16, 64, 5
+    rng = np.random.default_rng(4)
+    w = _bf16(rng.standard_normal((J, 2, d, hidden)))
+    a = _bf16(rng.standard_normal((T, hidden)))
+    b = _bf16(rng.standard_normal((T, hidden)))
+    s = _bf16(a.float() + b.float())
+    exact = (a.float() + b.float() == s.float()).all().item()
+    ra, rb = orc.kv_project(a, w, range(T))["x"], orc.kv_project(b, w, range(T))["x"]
+    r2 = orc.kv_project(_bf16(2 * a.float()), w, range(T))["x"]
+    assert np.array_equal(r2, 2 * ra)
+    if exact:
+        assert np.array_equal(orc.kv_project(s, w, range(T))["x"], ra + rb)
+    # additivity on rows whose sum is exactly representable
+    ok = (a.float() + b.float() == s.float()).all(dim=1).numpy()
+    rs = orc.kv_project(s, w, range(T))["x"]
+    assert np.allclose(rs[:, :, ok], (ra + rb)[:, :, ok], rtol=0, atol=1e-9)
+
+
+def test_kv_project_quantisation(orc):
+    """Per-token scale = max|x| / 448: the largest element of each row codes to
+    +-448, every code decodes within half a step of x / scale, and an all-zero
+    row has scale 1 and zero codes."""
+    J, d, hidden, T = 1, 32, 64, 6
+    rng = np.random.default_rng(5)
+    w = _bf16(rng.standard_normal((J, 2, d, hidden)))
+    h = rng.standard_normal((T, hidden)).astype(np.float32)
+    h[2] = 0.0
+    r = orc.kv_project(_bf16(h), w, range(T), quantize=True)
+    x, codes, sc = r["x"], r["codes"], r["scales"]
+    dec = np.vectorize(orc.e4m3_value)(codes)
+    grid = np.array([orc.e4m3_value(c) for c in range(0x7F)])  # the finite non-negative values
+    for kind in range(2):
+        for t in range(T):
+            if t == 2:
+                assert sc[0, kind, t] == 1.0 and (codes[0, kind, t] == 0).all()
+                continue
+            y = x[0, kind, t] / sc[0, kind, t]
+            assert np.isclose(np.abs(y).max(), 448.0)
+            assert np.abs(dec[0, kind, t]).max() == 448.0
+            # each code decodes to a representable value nearest to x / scale
+            best = np.abs(np.abs(y)[:, None] - grid[None, :]).min(axis=1)
+            assert np.allclose(np.abs(dec[0, kind, t] - y), best, rtol=0, atol=1e-12)
