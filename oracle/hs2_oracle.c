@@ -346,7 +346,10 @@ uint8_t orc_e4m3_encode(double x) {
  *   h  [T][hidden] bf16, w [J][2][d][hidden] bf16
  *   x_out  [J][2][n_rows][d] double: the projected rows `rows`
  *   codes  [J][2][n_rows][d] (nullable): reading R10 on each projected row,
- *          scale = max|x| / 448 (1 for an all-zero row), code = RNE(x / scale)
+ *          scale = max|x| / 448 (1 for an all-zero row), code = RNE(x / scale),
+ *          with the quantiser's two decisions taken in fp32, the precision
+ *          the projection's output has before it is stored: xf = fl32(x),
+ *          scale = fl32(max|xf| / 448), t = fl32(xf / scale), code = RNE(t)
  *   scales [J][2][n_rows] (nullable, with codes)
  * Returns 0, or 1 on invalid arguments.
  */
@@ -370,10 +373,14 @@ int orc_kv_project(const uint16_t* h, int64_t T, int hidden, const uint16_t* w, 
                 if (fabs(acc) > amax) amax = fabs(acc);
             }
             if (codes) {
-                const double sc = amax > 0.0 ? amax / 448.0 : 1.0;
+                const float af = (float)amax;  /* rounding is monotone: = max |fl32(x)| */
+                const float sc = af > 0.0f ? af / 448.0f : 1.0f;
                 uint8_t* cr = codes + ((size_t)jk * (size_t)n_rows + (size_t)r) * (size_t)d;
-                for (int c = 0; c < d; ++c) cr[c] = orc_e4m3_encode(x[c] / sc);
-                if (scales) scales[(size_t)jk * (size_t)n_rows + (size_t)r] = sc;
+                for (int c = 0; c < d; ++c) {
+                    const float t = (float)x[c] / sc;
+                    cr[c] = orc_e4m3_encode((double)t);
+                }
+                if (scales) scales[(size_t)jk * (size_t)n_rows + (size_t)r] = (double)sc;
             }
         }
     return 0;

@@ -511,9 +511,30 @@ def test_kv_project_quantisation(orc):
             if t == 2:
                 assert sc[0, kind, t] == 1.0 and (codes[0, kind, t] == 0).all()
                 continue
-            y = x[0, kind, t] / sc[0, kind, t]
+            # the quantiser works in fp32: t = fl32(fl32(x) / scale), scale an fp32 value
+            assert sc[0, kind, t] == np.float64(np.float32(sc[0, kind, t]))
+            y = (x[0, kind, t].astype(np.float32) / np.float32(sc[0, kind, t])).astype(np.float64)
             assert np.isclose(np.abs(y).max(), 448.0)
             assert np.abs(dec[0, kind, t]).max() == 448.0
             # each code decodes to a representable value nearest to x / scale
             best = np.abs(np.abs(y)[:, None] - grid[None, :]).min(axis=1)
             assert np.allclose(np.abs(dec[0, kind, t] - y), best, rtol=0, atol=1e-12)
+
+
+def test_kv_project_quantisation_matches_torch_fp32_cast(orc):
+    """The oracle's fp32 quantiser against torch's own float8_e4m3fn cast applied
+    to the same fp32 rows (scale = amax / 448 in fp32, divide, clamp, RNE cast):
+    codes and scales bit-identical on Gaussian rows and on rows with ties."""
+    J, d, hidden, T = 2, 64, 96, 40
+    rng = np.random.default_rng(11)
+    w = _bf16(rng.standard_normal((J, 2, d, hidden)) / np.sqrt(hidden))
+    h = rng.standard_normal((T, hidden)).astype(np.float32)
+    h[3] = 0.0
+    h[7] = np.round(h[7] * 4) / 4            # coarse values: more exact midpoints
+    r = orc.kv_project(_bf16(h), w, range(T), quantize=True)
+    x32 = torch.from_numpy(r["x"].astype(np.float32))
+    amax = x32.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    ref = (x32 / scale.unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(torch.from_numpy(r["codes"]), ref)
+    assert np.array_equal(r["scales"], scale.double().numpy())
