@@ -39,9 +39,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernel classes of the library's timing hook (include/hs2.h)
 KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
-      "prefill_final": 10, "fill": 11}
+      "prefill_final": 10, "fill": 11, "kv_project": 12}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
-KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip"}
+KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "kv_project": "k_project.hip"}
 
 
 def log(*a):
@@ -129,6 +129,92 @@ def cpu_baseline(wl, x, seconds: float):
                       f"{wl.n_sparse} sparse layers, fp64, {el:.1f} s"}
 
 
+def bench_kv_project(args, cache: str) -> int:
+    """KV Bridging projections alone (hs2_kv_project): the hidden state of a
+    32768-token prefill chunk, hidden 2048 (the pages' model width), projected
+    into K and V of 4 bridged full layers, d = 128, cache in bf16 or FP8.
+    One step = one call; value = hidden-state tokens per second."""
+    import ctypes
+    import numpy as np
+    import torch
+    import token_level_top_amd as hs2
+    from hs2_inputs import make_projection_inputs
+
+    T, hidden, J, d = 32768, 2048, 4, 128
+    name = f"kv_project_{T // 1024}k_hidden{hidden}_j{J}_{cache}"
+    log(f"workload {name}: generating inputs on the host")
+    h, w = make_projection_inputs(2024, T, hidden, J, d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hd, wd = h.to(dev), w.to(dev)
+    dt = hs2.HS2_FP8_E4M3 if cache == "fp8" else hs2.HS2_BF16
+    odt = torch.uint8 if cache == "fp8" else torch.bfloat16
+    bufs = dict(k_out=torch.empty((J, T, d), dtype=odt, device=dev), v_out=torch.empty((J, T, d), dtype=odt,
+                                                                                        device=dev))
+    if cache == "fp8":
+        bufs.update(k_scale=torch.empty((J, T), device=dev), v_scale=torch.empty((J, T), device=dev))
+
+    def step():
+        hs2.kv_project(hd, wd, dt, **bufs)
+
+    L = hs2.lib()
+    L.hs2_timing_enable.argtypes = [ctypes.c_uint32]
+    L.hs2_timing_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    ms_c, n_c = (ctypes.c_double * 16)(), (ctypes.c_int64 * 16)()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L.hs2_timing_read(ctypes.addressof(ms_c), ctypes.addressof(n_c))
+    ms_c, n_c = (ctypes.c_double * 16)(), (ctypes.c_int64 * 16)()
+    L.hs2_timing_enable(1 << KC["kv_project"])
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    L.hs2_timing_enable(0)
+    if L.hs2_timing_read(ctypes.addressof(ms_c), ctypes.addressof(n_c)) != 0:
+        raise RuntimeError("hs2_timing_read failed")
+    ms_total = e0.elapsed_time(e1)
+    kc = KC["kv_project"]
+    kavg_s = ms_c[kc] / max(n_c[kc], 1) / 1e3
+    flops = 2 * T * hidden * d * 2 * J
+    achieved = flops / kavg_s / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    out_b = 1 if cache == "fp8" else 2
+    bytes_alg = T * hidden * 2 + 2 * J * d * hidden * 2 + 2 * J * T * (d * out_b + (4 if cache == "fp8" else 0))
+    tr = traffic_record("kv_project", name)
+    res = {"metric": "KV Bridging projection hidden-state tok/s", "value": round(T * args.steps / (ms_total / 1e3), 2),
+           "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_total / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden states, N(0,1/hidden) weights)",
+           "config": {"workload": name, "T": T, "hidden": hidden, "n_layers": J, "d": d, "cache": cache},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
+                        "kernel": "kv_project", "kernel_ms": round(kavg_s * 1e3, 4),
+                        "algorithmic_per_launch": flops, "algorithmic_bytes_per_launch": bytes_alg}}
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        rng = np.random.default_rng(12345)
+        order = rng.permutation(T)
+        done, t0 = 0, time.perf_counter()
+        while done < T and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.kv_project(h, w, order[done:done + 16].tolist(), quantize=cache == "fp8")
+            done += 16
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"{done} of {T} hidden rows, all {2 * J} projections, fp64, {el:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,12 +226,16 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (extra steps)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB twice (reference for HBM counters)")
+    ap.add_argument("--kv-project", choices=["bf16", "fp8"], default=None,
+                    help="instead of the attention path, time the KV Bridging projections with this cache type")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         return 2
+    if args.kv_project:
+        return bench_kv_project(args, args.kv_project)
 
     import torch
     import token_level_top_amd as hs2
@@ -260,7 +350,7 @@ def main():
            "roofline": roof,
            "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)}}
     if args.breakdown:
-        L.hs2_timing_enable(0xFFF)
+        L.hs2_timing_enable(0xFFF)  # the attention path's classes (0..11)
         for _ in range(3):
             step()
         torch.cuda.synchronize()

@@ -197,3 +197,27 @@ def checked_rows(wl: Workload, needles: List[Needle], n_uniform: int) -> List[in
     n = min(n_uniform, len(rest))
     extra = rng.choice(rest, size=n, replace=False) if n else np.array([], dtype=np.int64)
     return sorted(set(rows) | {int(r) for r in extra})
+
+
+def make_projection_inputs(seed: int, T: int, hidden: int, J: int, d: int, exact: bool = False,
+                           zero_rows: Tuple[int, ...] = ()) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Hidden states h [T][hidden] and KV Bridging weights w [J][2][d][hidden],
+    both bf16 (CPU). Streams 70 (h) and 71 (w) of SeedSequence([seed, stream]).
+
+    Default: h ~ N(0,1) (a normalised hidden state), w ~ N(0, 1/hidden), so the
+    projected values are about N(0,1).
+    exact=True: h integers in [-3, 3] and w = k/16 with integer k in [-8, 8];
+    every product is a multiple of 1/16 and every partial sum stays below
+    2^24/16 for hidden < 5000, so an fp32 accumulation is exact in any order.
+    Rows listed in zero_rows are all-zero."""
+    g = [np.random.Generator(np.random.Philox(np.random.SeedSequence([seed, s]))) for s in (70, 71)]
+    if exact:
+        assert hidden < 5000
+        h = g[0].integers(-3, 4, size=(T, hidden)).astype(np.float32)
+        w = g[1].integers(-8, 9, size=(J, 2, d, hidden)).astype(np.float32) / 16.0
+    else:
+        h = g[0].standard_normal(size=(T, hidden), dtype=np.float32)
+        w = g[1].standard_normal(size=(J, 2, d, hidden), dtype=np.float32) / np.float32(math.sqrt(hidden))
+    for r in zero_rows:
+        h[r] = 0.0
+    return torch.from_numpy(h).to(torch.bfloat16), torch.from_numpy(w).to(torch.bfloat16)

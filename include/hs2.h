@@ -176,6 +176,32 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
                     int k, int32_t* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * KV Bridging projections (HySparse2 page, section "어떻게 동작하나": each
+ * cross-decoder full-attention layer j derives its own cache from the shared
+ * self-decoder hidden state, K_j = Proj_j^K(H), V_j = Proj_j^V(H)). Each
+ * projection is a linear map without bias onto the single KV head:
+ *   k_out[j][t][e] = sum_c w[j][0][e][c] * h[t][c]
+ *   v_out[j][t][e] = sum_c w[j][1][e][c] * h[t][c]
+ * accumulated in fp32 and written in the cache type kv_dtype:
+ *   HS2_BF16      rounded to nearest even; k_scale/v_scale unused (may be NULL)
+ *   HS2_FP8_E4M3  per row: scale = max_e |x| / 448 (1 for an all-zero row),
+ *                 code = x / scale rounded to nearest even (OCP E4M3FN), and
+ *                 k_scale[j][t] / v_scale[j][t] = scale, the same convention
+ *                 as the FP8 cache rows the attention entry points read.
+ *   h       [T][hidden] bf16
+ *   w       [n_layers][2][d][hidden] bf16 (index 0 = K, 1 = V)
+ *   k_out, v_out          [n_layers][T][d]  (bf16, or one byte per code)
+ *   k_scale, v_scale      [n_layers][T] fp32 (FP8 only)
+ * d in {64, 128} and hidden a multiple of 32 (else HS2_ERR_UNSUPPORTED);
+ * 512 * hidden < 2^31, n_layers <= 16384 and 2 * n_layers * ceil(T / 256)
+ * < 2^31 (else HS2_ERR_INVALID_ARG). T = 0 or n_layers = 0 enqueue nothing.
+ * Needs no workspace.
+ */
+int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_layers, int d,
+                   int kv_dtype, void* k_out, void* v_out, float* k_scale, float* v_scale,
+                   void* stream);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram
@@ -183,6 +209,7 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
  *   bit 6 sparse-layer attention       bit 7 prefill K/V preparation
  *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
  *   bit 10 prefill final selection     bit 11 buffer fills
+ *   bit 12 KV Bridging projections
  * hs2_timing_enable(mask): from now on every launch of a class in `mask` is
  * bracketed by two hipEvents recorded on its launch stream (0 disables).
  * hs2_timing_read(ms, launches): waits for the recorded events and adds, per

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -113,6 +113,32 @@ def test_sparse_and_select_validation():
     assert L.hs2_select_topk(FAKE, 4, 100, None, 0, FAKE, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
     assert L.hs2_select_topk(FAKE, 4, 100, None, 4096, FAKE, None, 0, None) == hs2.HS2_ERR_UNSUPPORTED
     assert L.hs2_select_topk(None, 4, 100, None, 8, FAKE, None, 0, None) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_kv_project_validation():
+    L = hs2.lib()
+    # h, T, hidden, w, n_layers, d, kv_dtype, k_out, v_out, k_scale, v_scale, stream
+    args = [FAKE, 1000, 2048, FAKE, 4, 128, hs2.HS2_BF16, FAKE, FAKE, None, None, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_kv_project(*a)
+
+    assert call(a5=96) == hs2.HS2_ERR_UNSUPPORTED              # d not in {64, 128}
+    assert call(a2=48) == hs2.HS2_ERR_UNSUPPORTED              # hidden % 32 != 0
+    assert call(a6=hs2.HS2_F32) == hs2.HS2_ERR_INVALID_ARG     # not a cache type
+    assert call(a6=hs2.HS2_FP8_E4M3) == hs2.HS2_ERR_INVALID_ARG  # FP8 without scales
+    assert call(a6=hs2.HS2_FP8_E4M3, a9=FAKE, a10=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a0=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a7=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a1=-1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a4=16385) == hs2.HS2_ERR_INVALID_ARG          # grid limit
+    assert call(a2=2 ** 22) == hs2.HS2_ERR_INVALID_ARG        # 256-row hidden block >= 2 GiB
+    # empty work enqueues nothing, even with null buffers
+    assert call(a1=0, a0=None, a7=None) == hs2.HS2_OK
+    assert call(a4=0, a3=None) == hs2.HS2_OK
 
 
 def test_binding_refuses_host_tensors():

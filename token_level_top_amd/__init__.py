@@ -33,6 +33,7 @@ _SIGS = {
     "hs2_decode_step": ([_p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _f, _p, _p,
                          _p, _p, _p, _p, _p, _sz, _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
+    "hs2_kv_project": ([_p, _i64, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
 }
 
 _lib = None
@@ -189,3 +190,23 @@ def select_topk(scores, k: int, n_cand=None, out=None, workspace=None, stream=No
                                _stream(stream))
     _check("hs2_select_topk", rc)
     return out
+
+
+def kv_project(h, w, kv_dtype: int = HS2_BF16, k_out=None, v_out=None, k_scale=None, v_scale=None, stream=None):
+    """hs2_kv_project. h [T][hidden] bf16, w [J][2][d][hidden] bf16 (K then V).
+    Returns k, v [J][T][d] (bf16, or uint8 E4M3 codes) and, for FP8, the scales [J][T] fp32."""
+    T, hidden = h.shape
+    J, two, d, hid2 = w.shape
+    if two != 2 or hid2 != hidden:
+        raise ValueError("w must be [J][2][d][hidden]")
+    dev = h.device
+    odt = torch.uint8 if kv_dtype == HS2_FP8_E4M3 else torch.bfloat16
+    k_out = torch.empty((J, T, d), dtype=odt, device=dev) if k_out is None else k_out
+    v_out = torch.empty((J, T, d), dtype=odt, device=dev) if v_out is None else v_out
+    if kv_dtype == HS2_FP8_E4M3:
+        k_scale = torch.empty((J, T), dtype=torch.float32, device=dev) if k_scale is None else k_scale
+        v_scale = torch.empty((J, T), dtype=torch.float32, device=dev) if v_scale is None else v_scale
+    rc = lib().hs2_kv_project(_ptr(h), T, hidden, _ptr(w), J, d, kv_dtype, _ptr(k_out), _ptr(v_out), _ptr(k_scale),
+                              _ptr(v_scale), _stream(stream))
+    _check("hs2_kv_project", rc)
+    return {"k": k_out, "v": v_out, "k_scale": k_scale, "v_scale": v_scale}

@@ -175,7 +175,8 @@ PrefillWs prefill_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d
 // ---- measurement hook: hipEvents around launches of selected kernel classes
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
-    KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_PF_FINAL = 10, KC_FILL = 11
+    KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_PF_FINAL = 10, KC_FILL = 11,
+    KC_PROJECT = 12
 };
 struct TimedPair {
     int cls;
@@ -361,6 +362,33 @@ int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, con
     const SparseWs w = sparse_ws(workspace, (int64_t)B * n_q, n_sel, H, d);
     return run_sparse(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, indices, n_sel,
                       sm_scale, out, lse, w.part, static_cast<hipStream_t>(stream));
+}
+
+int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_layers, int d, int kv_dtype,
+                   void* k_out, void* v_out, float* k_scale, float* v_scale, void* stream) {
+    if (T < 0 || hidden <= 0 || n_layers < 0) return HS2_ERR_INVALID_ARG;
+    if (kv_dtype != HS2_BF16 && kv_dtype != HS2_FP8_E4M3) return HS2_ERR_INVALID_ARG;
+    if ((d != 64 && d != 128) || hidden % 32 != 0) return HS2_ERR_UNSUPPORTED;
+    if ((int64_t)hidden * 256 * 2 >= (int64_t(1) << 31) || T >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (n_layers > 16384 || (T + 255) / 256 * 2 * n_layers >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (T == 0 || n_layers == 0) return HS2_OK;
+    const bool fp8 = kv_dtype == HS2_FP8_E4M3;
+    if (!h || !w || !k_out || !v_out || (fp8 && (!k_scale || !v_scale))) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(w) || !aligned16(k_out) || !aligned16(v_out)) return HS2_ERR_INVALID_ARG;
+    if (fp8 && (!aligned16(k_scale) || !aligned16(v_scale))) return HS2_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProjectArgs a{};
+    a.h = h;
+    a.w = w;
+    a.T = T;
+    a.hidden = hidden;
+    a.n_layers = n_layers;
+    a.k_out = k_out;
+    a.v_out = v_out;
+    a.k_scale = fp8 ? k_scale : nullptr;
+    a.v_scale = fp8 ? v_scale : nullptr;
+    HS2_TRY(TIMED(KC_PROJECT, s, launch_kv_project(a, d, fp8, s)));
+    return HS2_OK;
 }
 
 int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const int32_t* n_cand, int k, int32_t* out,

@@ -111,4 +111,18 @@ hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream
 // pass 2 also writes the index rows (window + global part)
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
 
+// KV Bridging projections: [J][2][d][hidden] bf16 weights applied to [T][hidden]
+// bf16 hidden states, out [J][T][d] (bf16 or e4m3 codes + [J][T] fp32 scales)
+struct ProjectArgs {
+    const void* h;
+    const void* w;
+    int64_t T;
+    int hidden, n_layers;
+    void* k_out;
+    void* v_out;
+    float* k_scale;
+    float* v_scale;
+};
+hipError_t launch_kv_project(const ProjectArgs& a, int D, bool fp8, hipStream_t st);
+
 }  // namespace hs2
