@@ -129,6 +129,20 @@ def cpu_baseline(wl, x, seconds: float):
                       f"{wl.n_sparse} sparse layers, fp64, {el:.1f} s"}
 
 
+def copy_calibration(mib: int, dev) -> None:
+    """A plain device copy of `mib` MiB, twice: the reference the HBM byte
+    counters of a profiled run are scaled by."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_kv_project(args, cache: str) -> int:
     """KV Bridging projections alone (hs2_kv_project): the hidden state of a
     32768-token prefill chunk, hidden 2048 (the pages' model width), projected
@@ -157,6 +171,7 @@ def bench_kv_project(args, cache: str) -> int:
     def step():
         hs2.kv_project(hd, wd, dt, **bufs)
 
+    copy_calibration(args.copy_calibration_mib, dev)
     L = hs2.lib()
     L.hs2_timing_enable.argtypes = [ctypes.c_uint32]
     L.hs2_timing_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -284,14 +299,7 @@ def main():
             hs2.sparse_attn(qs, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
                             workspace=ws_sp)
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * 1024 * 1024 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration_mib, dev)
 
     L = hs2.lib()
     import ctypes

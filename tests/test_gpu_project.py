@@ -117,7 +117,7 @@ def check_gauss(orc, hs2, h, w, rows, fp8, got=None):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("T,hidden,J", [(1000, 2048, 3), (257, 96, 1), (1, 32, 2), (512, 64, 2)])
+@pytest.mark.parametrize("T,hidden,J", [(1000, 2048, 3), (257, 96, 1), (1, 32, 2), (512, 64, 2), (200, 192, 1)])
 def test_kv_project_exact(hs2, orc, d, fp8, T, hidden, J):
     say("kv_project exact T", T, "hidden", hidden, "J", J, "d", d, "fp8", fp8)
     zero = (0, T - 1) if T > 2 else ()

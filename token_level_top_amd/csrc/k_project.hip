@@ -13,8 +13,9 @@
 // is an in-lane maximum plus one exchange between the wave halves. Wave w
 // works on head w/4 and tokens 64(w%4) .. 64(w%4)+63 (two 32-token tiles) for
 // all d, so every A fragment read from LDS feeds two MFMAs and every B
-// fragment D/32. Hidden is consumed 32 at a time through two LDS buffers,
-// staged in registers one chunk ahead.
+// fragment D/32. Hidden is consumed in chunks of KC = 64 elements (32 when
+// hidden is not a multiple of 64) through two LDS buffers, with the global
+// loads running two chunks ahead through two register sets.
 //
 // Every head of a token block reads the same 256 hidden rows, so the 1-D grid
 // is laid out for L2 reuse: workgroups are dealt to the 8 XCDs round-robin by
@@ -24,24 +25,36 @@
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
+#include <type_traits>
+
 namespace hs2 {
 
 constexpr int kProjThreads = 256;
 constexpr int kProjTokens = 256;  // tokens per workgroup
-constexpr int kProjKC = 32;       // hidden elements per chunk
-constexpr int kProjLD = kProjKC + 8;  // LDS row stride (bf16 elements): 80 B, conflict-free fragment reads
 
-template <int D, int NH, bool FP8OUT>
+// LDS rows are KC elements with no padding; the 16-byte unit u of row r is
+// stored at unit u ^ ((r / P) % U) (U = KC/8 units per row, P = 16/U rows per
+// 256 bytes). LDS serves a 16-byte access for 16 lanes at a time over 64
+// banks, so both the fragment reads (16 consecutive rows, one unit) and the
+// staging writes (P rows x U units) touch 16 distinct bank quads.
+template <int KC>
+__device__ __forceinline__ int proj_lds(int row, int unit) {
+    constexpr int U = KC / 8, P = 16 / U;
+    return row * KC + 8 * (unit ^ ((row / P) % U));
+}
+
+template <int D, int NH, int KC, bool FP8OUT>
 __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectArgs a) {
     constexpr int NT = kProjThreads * NH;                      // threads
     constexpr int NM = D / 32;                                 // 32-row tiles of d
-    constexpr int WPIECES = NH * D * kProjKC / 8;              // 16-B pieces of a weight chunk
-    constexpr int HPIECES = kProjTokens * kProjKC / 8;         // 16-B pieces of a hidden chunk
+    constexpr int U = KC / 8;                                  // 16-B units per row of a chunk
+    constexpr int WPIECES = NH * D * U;                        // 16-B pieces of a weight chunk
+    constexpr int HPIECES = kProjTokens * U;                   // 16-B pieces of a hidden chunk
     constexpr int WPT = WPIECES / NT, HPT = HPIECES / NT;
     static_assert(WPIECES % NT == 0 && HPIECES % NT == 0, "whole pieces per thread");
 
-    __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][NH * D * kProjLD];
-    __shared__ __attribute__((aligned(16))) uint16_t h_lds[2][kProjTokens * kProjLD];
+    __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][NH * D * KC];
+    __shared__ __attribute__((aligned(16))) uint16_t h_lds[2][kProjTokens * KC];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,30 +73,36 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.h) + (size_t)t0 * (size_t)hidden;
     // the workgroup's hidden rows: rows past T read as zero
     const auto rh = raw_buffer(hb, (uint32_t)rows * (uint32_t)hidden * 2u);
+    const int n_chunks = hidden / KC;
 
-    u32x4 wr[WPT], hr[HPT];
-    auto load = [&](int k0) {
+    // Two register sets: the loads of chunk c+2 are issued before the MFMAs of
+    // chunk c and written to LDS after those of chunk c+1. The chunk index is
+    // clamped so every load is issued unconditionally (the last chunk is read
+    // again at the end), which keeps the memory-counter waits exact.
+    u32x4 wr[2][WPT], hr[2][HPT];
+    auto load = [&](int set, int c) {
+        const int k0 = min(c, n_chunks - 1) * KC;
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
-            const int pc = tid + NT * i, row = pc / (kProjKC / 8), cc = pc % (kProjKC / 8);
-            wr[i] = *reinterpret_cast<const u32x4*>(wm + (size_t)row * hidden + k0 + 8 * cc);
+            const int pc = tid + NT * i, row = pc / U, cc = pc % U;
+            wr[set][i] = *reinterpret_cast<const u32x4*>(wm + (size_t)row * hidden + k0 + 8 * cc);
         }
 #pragma unroll
         for (int i = 0; i < HPT; ++i) {
-            const int pc = tid + NT * i, row = pc / (kProjKC / 8), cc = pc % (kProjKC / 8);
-            hr[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (row * hidden + k0 + 8 * cc) * 2, 0, 0);
+            const int pc = tid + NT * i, row = pc / U, cc = pc % U;
+            hr[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rh, (row * hidden + k0 + 8 * cc) * 2, 0, 0);
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int set, int buf) {
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
-            const int pc = tid + NT * i, row = pc / (kProjKC / 8), cc = pc % (kProjKC / 8);
-            *reinterpret_cast<u32x4*>(&w_lds[buf][row * kProjLD + 8 * cc]) = wr[i];
+            const int pc = tid + NT * i, row = pc / U, cc = pc % U;
+            *reinterpret_cast<u32x4*>(&w_lds[buf][proj_lds<KC>(row, cc)]) = wr[set][i];
         }
 #pragma unroll
         for (int i = 0; i < HPT; ++i) {
-            const int pc = tid + NT * i, row = pc / (kProjKC / 8), cc = pc % (kProjKC / 8);
-            *reinterpret_cast<u32x4*>(&h_lds[buf][row * kProjLD + 8 * cc]) = hr[i];
+            const int pc = tid + NT * i, row = pc / U, cc = pc % U;
+            *reinterpret_cast<u32x4*>(&h_lds[buf][proj_lds<KC>(row, cc)]) = hr[set][i];
         }
     };
 
@@ -95,23 +114,17 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[m][b][i] = 0.f;
 
-    const int n_chunks = hidden / kProjKC;
-    load(0);
-    store(0);
-    __syncthreads();
-    if (n_chunks > 1) load(kProjKC);
-    for (int c = 0; c < n_chunks; ++c) {
-        const int buf = c & 1;
+    auto mma = [&](int buf) {
 #pragma unroll
-        for (int ks = 0; ks < kProjKC / 16; ++ks) {
-            const int kof = 16 * ks + 8 * hh;
+        for (int ks = 0; ks < KC / 16; ++ks) {
+            const int unit = 2 * ks + hh;
             u32x4 bf[2], af[NM];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
-                bf[b] = *reinterpret_cast<const u32x4*>(&h_lds[buf][(64 * tg + 32 * b + n) * kProjLD + kof]);
+                bf[b] = *reinterpret_cast<const u32x4*>(&h_lds[buf][proj_lds<KC>(64 * tg + 32 * b + n, unit)]);
 #pragma unroll
             for (int m = 0; m < NM; ++m)
-                af[m] = *reinterpret_cast<const u32x4*>(&w_lds[buf][(head * D + 32 * m + n) * kProjLD + kof]);
+                af[m] = *reinterpret_cast<const u32x4*>(&w_lds[buf][proj_lds<KC>(head * D + 32 * m + n, unit)]);
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -119,10 +132,29 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
                     acc[m][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[m]), as_bf16x8(bf[b]),
                                                                          acc[m][b], 0, 0, 0);
         }
-        if (c + 1 < n_chunks) store(buf ^ 1);
+    };
+    // one chunk: set S is free (its chunk is in LDS), set 1-S holds chunk c+1
+    // (the scheduling barriers keep the compiler from sinking the early loads
+    // below the MFMAs)
+    auto chunk = [&](int c, auto S) {
+        load(S.value, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(c & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < n_chunks) store(1 - S.value, (c + 1) & 1);
         __syncthreads();
-        if (c + 2 < n_chunks) load((c + 2) * kProjKC);
+    };
+
+    load(0, 0);
+    load(1, 1);
+    store(0, 0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < n_chunks; c += 2) {
+        chunk(c, std::integral_constant<int, 0>{});
+        chunk(c + 1, std::integral_constant<int, 1>{});
     }
+    if (c < n_chunks) chunk(c, std::integral_constant<int, 0>{});
 
     // ---- epilogue: lane holds d = 32m + 8(i/4) + 4hh + i%4 of token 64tg + 32b + n
     const int64_t T = a.T;
@@ -166,14 +198,14 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
     }
 }
 
-template <int D, int NH>
+template <int D, int NH, int KC>
 static hipError_t launch_project_d(const ProjectArgs& a, bool fp8, hipStream_t st) {
     const int64_t n_tb = (a.T + kProjTokens - 1) / kProjTokens;
     const dim3 grid((unsigned)(n_tb * (2 * a.n_layers / NH)));
     if (fp8)
-        hipLaunchKernelGGL((kv_project_kernel<D, NH, true>), grid, dim3(kProjThreads * NH), 0, st, a);
+        hipLaunchKernelGGL((kv_project_kernel<D, NH, KC, true>), grid, dim3(kProjThreads * NH), 0, st, a);
     else
-        hipLaunchKernelGGL((kv_project_kernel<D, NH, false>), grid, dim3(kProjThreads * NH), 0, st, a);
+        hipLaunchKernelGGL((kv_project_kernel<D, NH, KC, false>), grid, dim3(kProjThreads * NH), 0, st, a);
     return hipGetLastError();
 }
 
@@ -181,8 +213,12 @@ static hipError_t launch_project_d(const ProjectArgs& a, bool fp8, hipStream_t s
 #define HS2_PROJ_NH 2
 #endif
 
+// hidden chunks of 64 where hidden allows, else 32
 hipError_t launch_kv_project(const ProjectArgs& a, int D, bool fp8, hipStream_t st) {
-    return D == 64 ? launch_project_d<64, HS2_PROJ_NH>(a, fp8, st) : launch_project_d<128, HS2_PROJ_NH>(a, fp8, st);
+    if (a.hidden % 64 == 0)
+        return D == 64 ? launch_project_d<64, HS2_PROJ_NH, 64>(a, fp8, st)
+                       : launch_project_d<128, HS2_PROJ_NH, 64>(a, fp8, st);
+    return D == 64 ? launch_project_d<64, HS2_PROJ_NH, 32>(a, fp8, st) : launch_project_d<128, HS2_PROJ_NH, 32>(a, fp8, st);
 }
 
 }  // namespace hs2
