@@ -51,6 +51,8 @@ def lib():
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_kv_project.argtypes = [_p, _i64, _i, _p, _i, _i, _p, _i64, _p, _p, _p]
         L.orc_kv_project.restype = _i
+        L.orc_block_select.argtypes = [_p, _i64, _i64, _p, _i, _i, _p, _p]
+        L.orc_block_select.restype = _i
         L.orc_num_threads.restype = _i
         L.orc_set_threads.argtypes = [_i]
         _lib = L
@@ -165,3 +167,70 @@ def kv_project(h, w, rows: Sequence[int], quantize: bool = False):
     if rc != 0:
         raise ValueError("oracle kv_project: invalid arguments")
     return {"x": x, "codes": codes, "scales": scales}
+
+
+def block_select_scores(scores: np.ndarray, pos: Sequence[int], block: int, k_blocks: int):
+    """Block scores (sum of each block's causal token scores) and the top
+    k_blocks blocks of each row (ascending, -1 padded). scores [n][stride] fp64."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    n, stride = s.shape
+    p = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    n_blk = (stride + block - 1) // block
+    bs = np.zeros((n, n_blk), np.float64)
+    bi = np.zeros((n, k_blocks), np.int32)
+    rc = lib().orc_block_select(_ptr(s), n, stride, _ptr(p), block, k_blocks, _ptr(bs), _ptr(bi))
+    if rc != 0:
+        raise ValueError("oracle block_select: invalid arguments")
+    return bs, bi
+
+
+def block_select(q, k, v, k_scale, v_scale, q_pos0: int, block: int, k_blocks: int, sm_scale: float,
+                 rows: Sequence[int]):
+    """HySparse (v1) full layer for flat query rows `rows`: exact attention (out,
+    lse), token scores, block scores and the selected blocks."""
+    r = full_select(q, k, v, k_scale, v_scale, q_pos0, 1, 0, sm_scale, rows, want_scores=True, select=False)
+    n_q = q.shape[1]
+    pos = q_pos0 + r["rows"] % n_q
+    bs, bi = block_select_scores(r["scores"], pos, block, k_blocks)
+    return {"out": r["out"], "lse": r["lse"], "scores": r["scores"], "block_scores": bs, "block_idx": bi,
+            "pos": pos, "rows": r["rows"]}
+
+
+def block_index_rows(pos: Sequence[int], block_idx: np.ndarray, block: int, window: int):
+    """Index rows of the two branches: the window max(0, p-window+1)..p (padded
+    with -1 to `window` entries) and the positions <= p of the selected blocks
+    (block by block, -1 for empty blocks and positions past p)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    n, kb = block_idx.shape
+    win = np.full((n, window), -1, np.int32)
+    blk = np.full((n, kb * block), -1, np.int32)
+    for r in range(n):
+        p = int(pos[r])
+        nw = min(p + 1, window)
+        win[r, :nw] = np.arange(p - nw + 1, p + 1)
+        for t in range(kb):
+            c = int(block_idx[r, t])
+            if c < 0:
+                continue
+            js = np.arange(c * block, (c + 1) * block)
+            blk[r, t * block:(t + 1) * block] = np.where(js <= p, js, -1)
+    return win, blk
+
+
+def block_sparse(q, k, v, k_scale, v_scale, block_idx, block: int, window: int, gates, q_pos0: int,
+                 sm_scale: float, rows: Sequence[int]):
+    """One HySparse (v1) sparse layer for flat query rows `rows` (reading R25):
+    attention over the selected blocks and, separately, over the sliding window,
+    each with its own softmax, fused as out = g[..., 0] o_blocks + g[..., 1] o_window.
+    block_idx [n][k_blocks] per entry of rows; gates [B*n_q][H][2]."""
+    rows_a = np.asarray(rows, dtype=np.int64)
+    n_q = q.shape[1]
+    pos = q_pos0 + rows_a % n_q
+    win, blk = block_index_rows(pos, np.asarray(block_idx), block, window)
+    ow = sparse(q, k, v, k_scale, v_scale, win, sm_scale, rows_a)
+    ob = sparse(q, k, v, k_scale, v_scale, blk, sm_scale, rows_a)
+    g = np.asarray(gates, dtype=np.float64)[rows_a]
+    out = g[..., 0:1] * ob["out"] + g[..., 1:2] * ow["out"]
+    return {"out": out, "out_blocks": ob["out"], "out_window": ow["out"], "lse_blocks": ob["lse"],
+            "lse_window": ow["lse"], "win_idx": win, "blk_idx": blk}
+

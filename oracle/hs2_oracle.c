@@ -386,6 +386,54 @@ int orc_kv_project(const uint16_t* h, int64_t T, int hidden, const uint16_t* w, 
     return 0;
 }
 
+/*
+ * HySparse (v1) block selection, the earlier method the HySparse2 page
+ * compares against (sections "무엇인가" and "어떻게 쓰나": 1,024 global tokens
+ * chosen in 64-token blocks, locality left to a separate gated 128-token SWA
+ * branch). Reading R24: block c covers positions [c*block, (c+1)*block); its
+ * score for a query at position p is the sum of the token scores score_j of
+ * its positions j <= p; every block with c*block <= p is a candidate; the
+ * min(k_blocks, candidates) blocks with the largest scores are taken, equal
+ * scores going to the lower block, and written ascending, padded with -1.
+ *   scores     [n_rows][stride] token scores; only j <= pos[r] is read
+ *   pos        [n_rows] query positions, 0 <= pos[r] < stride
+ *   blk_scores [n_rows][ceil(stride / block)] (nullable): block scores, in
+ *              ascending j within each block; 0 for blocks past pos[r]
+ *   blk_idx    [n_rows][k_blocks]
+ * Returns 0, or 1 on invalid arguments.
+ */
+int orc_block_select(const double* scores, int64_t n_rows, int64_t stride, const int64_t* pos,
+                     int block, int k_blocks, double* blk_scores, int32_t* blk_idx) {
+    if (n_rows < 0 || stride < 1 || block < 1 || k_blocks < 0) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (pos[r] < 0 || pos[r] >= stride) return 1;
+    const int64_t n_blk = (stride + block - 1) / block;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const double* sc = scores + (size_t)r * (size_t)stride;
+        const int64_t p = pos[r], n_cand = p / block + 1;
+        orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)n_cand);
+        for (int64_t b = 0; b < n_cand; ++b) {
+            double acc = 0.0;
+            for (int64_t j = b * block; j < (b + 1) * block && j <= p; ++j) acc += sc[j];
+            c[b].s = acc;
+            c[b].j = b;
+        }
+        if (blk_scores) {
+            double* dst = blk_scores + (size_t)r * (size_t)n_blk;
+            for (int64_t b = 0; b < n_blk; ++b) dst[b] = b < n_cand ? c[b].s : 0.0;
+        }
+        qsort(c, (size_t)n_cand, sizeof(orc_cand), orc_cand_cmp);
+        const int64_t take = n_cand < k_blocks ? n_cand : k_blocks;
+        int32_t* out = blk_idx + (size_t)r * (size_t)k_blocks;
+        for (int64_t t = 0; t < take; ++t) out[t] = (int32_t)c[t].j;
+        qsort(out, (size_t)take, sizeof(int32_t), orc_i32_cmp);
+        for (int64_t t = take; t < k_blocks; ++t) out[t] = -1;
+        free(c);
+    }
+    return 0;
+}
+
 int orc_num_threads(void) { return omp_get_max_threads(); }
 void orc_set_threads(int n) {
     if (n > 0) omp_set_num_threads(n);

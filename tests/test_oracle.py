@@ -538,3 +538,79 @@ def test_kv_project_quantisation_matches_torch_fp32_cast(orc):
     ref = (x32 / scale.unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     assert torch.equal(torch.from_numpy(r["codes"]), ref)
     assert np.array_equal(r["scales"], scale.double().numpy())
+
+
+# ------------------------------------------------- HySparse (v1) block variant
+
+def test_block_select_hand_example(orc):
+    """Block scores and choices worked by hand: sums of each block's causal
+    token scores, ties to the lower block, output ascending and -1 padded."""
+    s = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 9, 10]], float)
+    bs, bi = orc.block_select_scores(s, [9], 4, 2)
+    assert bs.tolist() == [[10, 26, 19]] and bi.tolist() == [[1, 2]]
+    bs, bi = orc.block_select_scores(s, [5], 4, 5)            # block 1 holds positions 4, 5 only
+    assert bs.tolist() == [[10, 11, 0]] and bi.tolist() == [[0, 1, -1, -1, -1]]
+    t = np.array([[1, 1, 1, 1, 2, 0, 0, 0, 1, 1, 1, 1]], float)
+    _, bi = orc.block_select_scores(t, [11], 4, 2)            # sums 4, 2, 4
+    assert bi.tolist() == [[0, 2]]
+    _, bi = orc.block_select_scores(t, [11], 4, 1)            # tie of blocks 0 and 2: the lower wins
+    assert bi.tolist() == [[0]]
+
+
+def test_block_scores_hold_the_whole_attention_mass(orc):
+    """Summed over a row's blocks, the block scores give sum_h sum_j p_hj = H."""
+    wl = workload(1)
+    x = make_inputs(wl)
+    rows = [0, 1, 63, 64, 65, 700, 2047]
+    r = orc.block_select(x.q, x.k, x.v, None, None, 0, 64, 16, x.sm_scale, rows)
+    assert np.allclose(r["block_scores"].sum(axis=1), wl.H, rtol=0, atol=1e-9)
+    # and block c's score is zero once c * 64 > p
+    for i, p in enumerate(r["pos"]):
+        assert (r["block_scores"][i, p // 64 + 1:] == 0).all()
+
+
+def test_block_select_of_one_token_blocks_is_token_topk(orc):
+    """With 1-token blocks the block choice is the top-k of the token scores
+    over all causal positions, checked against a plain sort."""
+    wl = workload(1)
+    x = make_inputs(wl)
+    rows = [5, 300, 1999]
+    r = orc.block_select(x.q, x.k, x.v, None, None, 0, 1, 40, x.sm_scale, rows)
+    for i, p in enumerate(r["pos"]):
+        s = r["scores"][i, :p + 1]
+        order = sorted(range(p + 1), key=lambda j: (-s[j], j))[:40]
+        want = sorted(order) + [-1] * (40 - len(order))
+        assert r["block_idx"][i].tolist() == want
+
+
+def test_block_select_recovers_planted_needles(orc):
+    """A strong needle key aimed at a query row puts its block among the row's
+    16 selected 64-token blocks."""
+    wl = workload(2).with_(n_q=64, q_pos0=4032, n_ctx=4096, n_needles=24)
+    x = make_inputs(wl, needle_norm="R18b")
+    rows = sorted({n.b * wl.n_q + n.i for n in x.needles})
+    r = orc.block_select(x.q, x.k, x.v, None, None, wl.q_pos0, 64, 16, x.sm_scale, rows)
+    where = {row: i for i, row in enumerate(rows)}
+    for n in x.needles:
+        assert n.j // 64 in r["block_idx"][where[n.b * wl.n_q + n.i]].tolist()
+
+
+def test_block_sparse_reduces_to_full_attention(orc):
+    """Gate (1, 0) with every causal block selected, and gate (0, 1) with a
+    window covering the whole prefix, both give the full layer's attention."""
+    wl = workload(1)
+    x = make_inputs(wl)
+    rows = [0, 7, 130, 1000, 2047]
+    full = orc.full_select(x.q, x.k, x.v, None, None, 0, 1, 0, x.sm_scale, rows, select=False)
+    n_blk = (wl.n_ctx + 63) // 64
+    sel = orc.block_select(x.q, x.k, x.v, None, None, 0, 64, n_blk, x.sm_scale, rows)
+    g = np.zeros((wl.B * wl.n_q, wl.H, 2))
+    g[..., 0] = 1.0
+    rb = orc.block_sparse(x.q, x.k, x.v, None, None, sel["block_idx"], 64, 128, g, 0, x.sm_scale, rows)
+    assert np.allclose(rb["out"], full["out"], rtol=0, atol=1e-12)
+    g = g[..., ::-1].copy()
+    rw = orc.block_sparse(x.q, x.k, x.v, None, None, sel["block_idx"], 64, wl.n_ctx, g, 0, x.sm_scale, rows)
+    assert np.allclose(rw["out"], full["out"], rtol=0, atol=1e-12)
+    # the window branch alone is attention over the last 128 positions
+    assert (rb["win_idx"][3] == np.arange(1000 - 127, 1001)).all()
+    assert (rb["win_idx"][1][:8] == np.arange(8)).all() and (rb["win_idx"][1][8:] == -1).all()
