@@ -221,3 +221,11 @@ def make_projection_inputs(seed: int, T: int, hidden: int, J: int, d: int, exact
     for r in zero_rows:
         h[r] = 0.0
     return torch.from_numpy(h).to(torch.bfloat16), torch.from_numpy(w).to(torch.bfloat16)
+
+
+def make_gates(seed: int, shape) -> torch.Tensor:
+    """Gate values in (0, 1) for the two-branch sparse layer, fp32 (CPU):
+    the logistic function of N(0,1) draws (stream 72 of SeedSequence([seed, 72]))."""
+    g = np.random.Generator(np.random.Philox(np.random.SeedSequence([seed, 72])))
+    z = g.standard_normal(size=shape)
+    return torch.from_numpy((1.0 / (1.0 + np.exp(-z))).astype(np.float32))

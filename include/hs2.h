@@ -76,7 +76,9 @@ typedef enum {
     HS2_OP_FULL_ATTN_SELECT = 0,
     HS2_OP_DECODE_STEP = 1,
     HS2_OP_SPARSE_ATTN = 2,
-    HS2_OP_SELECT_TOPK = 3
+    HS2_OP_SELECT_TOPK = 3,
+    HS2_OP_BLOCK_ATTN_SELECT = 4,
+    HS2_OP_BLOCK_SPARSE_ATTN = 5
 } hs2_op;
 
 /* HS2_ABI_VERSION of the built library. */
@@ -88,7 +90,9 @@ const char* hs2_status_string(int status);
 /*
  * Workspace bytes an op needs for the given shape (0 if none, SIZE_MAX if the
  * arguments are invalid). For HS2_OP_SELECT_TOPK pass B = rows, n_ctx = row
- * length and k_global = k; the other arguments are ignored. Pure host code.
+ * length and k_global = k; the other arguments are ignored. For
+ * HS2_OP_BLOCK_SPARSE_ATTN pass window, k_global = k_blocks and, in place of
+ * kv_dtype, the query type. Pure host code.
  */
 size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int d, int window,
                           int k_global, int kv_dtype);
@@ -202,6 +206,56 @@ int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_la
                    void* stream);
 
 /*
+ * HySparse (v1) block-level selection, the earlier method the HySparse2 page
+ * compares against (sections "무엇인가" and "어떻게 쓰나": the 1,024 global
+ * tokens are chosen as 64-token blocks and locality comes from a separate
+ * 128-token sliding-window branch merged by a gate). The full layer computes
+ * exact attention as hs2_full_attn_select does; its selection is per block:
+ *   block c = positions [64c, 64c+64); for a query at position p its score is
+ *   the sum of score_j (as defined above) over the block's positions j <= p;
+ *   every block with 64c <= p competes; the min(k_blocks, p/64 + 1) blocks
+ *   with the largest scores are taken, equal scores to the lower block.
+ *   q, k, v, k_scale, v_scale, out, lse   as for hs2_full_attn_select
+ *   block_idx    [B][n_q][k_blocks] int32  chosen blocks ascending, -1 padded
+ *   block_scores [B][n_q][ceil(n_ctx/64)] fp32, may be NULL; entries for
+ *                blocks past the query's position are unspecified
+ *   workspace >= hs2_workspace_size(HS2_OP_BLOCK_ATTN_SELECT, B, n_q, n_ctx,
+ *                H, d, 0, 0, kv_dtype) bytes
+ * block must be 64 and 1 <= k_blocks <= 64 (else HS2_ERR_UNSUPPORTED). The
+ * block scores are accumulated in fp32; the choice is exact on them.
+ */
+int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void* v,
+                          const float* k_scale, const float* v_scale, int kv_dtype, int B,
+                          int64_t n_q, int64_t q_pos0, int64_t n_ctx, int H, int d, int block,
+                          int k_blocks, float sm_scale, void* out, float* lse, int32_t* block_idx,
+                          float* block_scores, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * n_layers HySparse (v1) sparse layers over one block choice. Layer l, with
+ * its own queries q[l], attends (i) to every position <= p of the chosen
+ * blocks and (ii) to the window max(0, p-window+1) .. p, each with its own
+ * softmax, and returns per (token, head)
+ *   out = gates[l][t][h][0] * O_blocks + gates[l][t][h][1] * O_window.
+ * In a model the gates are a learned function of the layer input; here they
+ * are an input.
+ *   q        [n_layers][B][n_q][H][d]   q_dtype
+ *   k, v, k_scale, v_scale              as for hs2_full_attn_select
+ *   block_idx [B][n_q][k_blocks] int32  as written by hs2_block_attn_select
+ *   gates    [n_layers][B][n_q][H][2]   fp32
+ *   out      [n_layers][B][n_q][H][d]   q_dtype
+ *   workspace >= hs2_workspace_size(HS2_OP_BLOCK_SPARSE_ATTN, B, n_q, n_ctx,
+ *                H, d, window, k_blocks, q_dtype) bytes
+ * block must be 64, 1 <= k_blocks <= 64, 1 <= window <= 4096. With bf16
+ * queries each branch's output is rounded to bf16 before the fusion.
+ */
+int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                          const float* k_scale, const float* v_scale, int kv_dtype, int B,
+                          int64_t n_q, int64_t q_pos0, int64_t n_ctx, int H, int d,
+                          const int32_t* block_idx, int block, int k_blocks, int window,
+                          const float* gates, float sm_scale, void* out, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram
@@ -209,7 +263,8 @@ int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_la
  *   bit 6 sparse-layer attention       bit 7 prefill K/V preparation
  *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
  *   bit 10 prefill final selection     bit 11 buffer fills
- *   bit 12 KV Bridging projections
+ *   bit 12 KV Bridging projections     bit 13 block scores (block mode)
+ *   bit 14 block choice / expansion    bit 15 two-branch gate fusion
  * hs2_timing_enable(mask): from now on every launch of a class in `mask` is
  * bracketed by two hipEvents recorded on its launch stream (0 disables).
  * hs2_timing_read(ms, launches): waits for the recorded events and adds, per

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -139,6 +139,48 @@ def test_kv_project_validation():
     # empty work enqueues nothing, even with null buffers
     assert call(a1=0, a0=None, a7=None) == hs2.HS2_OK
     assert call(a4=0, a3=None) == hs2.HS2_OK
+
+
+def test_block_variant_validation():
+    L = hs2.lib()
+    E = hs2
+    # q, qdt, k, v, ks, vs, kvdt, B, n_q, q_pos0, n_ctx, H, d, block, k_blocks, scale, out, lse, idx, scores, ws,
+    # wsb, stream
+    sel = [FAKE, 1, FAKE, FAKE, None, None, 1, 1, 100, 0, 100, 16, 128, 64, 16, 0.1, FAKE, FAKE, FAKE, None,
+           None, 0, None]
+
+    def call_sel(**kw):
+        a = list(sel)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_block_attn_select(*a)
+
+    assert call_sel() == E.HS2_ERR_WORKSPACE
+    assert call_sel(a13=32) == E.HS2_ERR_UNSUPPORTED          # block must be 64
+    assert call_sel(a14=65) == E.HS2_ERR_UNSUPPORTED          # at most 64 blocks (4096 tokens)
+    assert call_sel(a14=0) == E.HS2_ERR_INVALID_ARG
+    assert call_sel(a18=None) == E.HS2_ERR_INVALID_ARG
+    assert call_sel(a19=MIS) == E.HS2_ERR_INVALID_ARG
+    assert call_sel(a8=101) == E.HS2_ERR_INVALID_ARG          # q_pos0 + n_q > n_ctx
+    assert hs2.workspace_size(E.OP_BLOCK_ATTN_SELECT, 1, 32768, 32768, 16, 128, 0, 0, 1) >= 32768 * 512 * 8
+    # q, qdt, L, k, v, ks, vs, kvdt, B, n_q, q_pos0, n_ctx, H, d, idx, block, k_blocks, window, gates, scale,
+    # out, ws, wsb, stream
+    sp = [FAKE, 1, 2, FAKE, FAKE, None, None, 1, 1, 100, 0, 100, 16, 128, FAKE, 64, 16, 128, FAKE, 0.1, FAKE,
+          None, 0, None]
+
+    def call_sp(**kw):
+        a = list(sp)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_block_sparse_attn(*a)
+
+    assert call_sp() == E.HS2_ERR_WORKSPACE
+    assert call_sp(a18=None) == E.HS2_ERR_INVALID_ARG         # gates
+    assert call_sp(a17=0) == E.HS2_ERR_INVALID_ARG            # window
+    assert call_sp(a17=5000) == E.HS2_ERR_UNSUPPORTED
+    assert call_sp(a15=16) == E.HS2_ERR_UNSUPPORTED
+    assert call_sp(a2=-1) == E.HS2_ERR_INVALID_ARG
+    assert hs2.workspace_size(E.OP_BLOCK_SPARSE_ATTN, 1, 100, 100, 16, 128, 128, 16, 1) > 0
 
 
 def test_binding_refuses_host_tensors():

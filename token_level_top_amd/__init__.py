@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhs2.so")
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = range(5)
 HS2_F32, HS2_BF16, HS2_FP8_E4M3 = 0, 1, 2
 OP_FULL_ATTN_SELECT, OP_DECODE_STEP, OP_SPARSE_ATTN, OP_SELECT_TOPK = 0, 1, 2, 3
+OP_BLOCK_ATTN_SELECT, OP_BLOCK_SPARSE_ATTN = 4, 5
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
@@ -34,6 +35,10 @@ _SIGS = {
                          _p, _p, _p, _p, _p, _sz, _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
     "hs2_kv_project": ([_p, _i64, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
+    "hs2_block_attn_select": ([_p, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _i, _i, _f, _p, _p,
+                               _p, _p, _p, _sz, _p], _i),
+    "hs2_block_sparse_attn": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _p, _i, _i, _i,
+                               _p, _f, _p, _p, _sz, _p], _i),
 }
 
 _lib = None
@@ -210,3 +215,51 @@ def kv_project(h, w, kv_dtype: int = HS2_BF16, k_out=None, v_out=None, k_scale=N
                               _ptr(v_scale), _stream(stream))
     _check("hs2_kv_project", rc)
     return {"k": k_out, "v": v_out, "k_scale": k_scale, "v_scale": v_scale}
+
+
+BLOCK = 64  # tokens per block of the block-level (HySparse v1) selection
+
+
+def block_attn_select(q, k, v, k_scale=None, v_scale=None, *, q_pos0: int, k_blocks: int, sm_scale: float,
+                      out=None, lse=None, block_idx=None, block_scores=None, want_scores: bool = True,
+                      workspace=None, stream=None):
+    """hs2_block_attn_select. Returns (out, lse, block_idx [B][n_q][k_blocks] int32,
+    block_scores [B][n_q][ceil(n_ctx/64)] fp32 or None)."""
+    B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if block_idx is None:
+        block_idx = torch.empty((B, n_q, k_blocks), dtype=torch.int32, device=dev)
+    if block_scores is None and want_scores:
+        block_scores = torch.empty((B, n_q, (n_ctx + BLOCK - 1) // BLOCK), dtype=torch.float32, device=dev)
+    kvdt = _KVDT[k.dtype]
+    ws = _workspace(workspace_size(OP_BLOCK_ATTN_SELECT, B, n_q, n_ctx, H, d, 0, 0, kvdt), dev, workspace)
+    rc = lib().hs2_block_attn_select(_ptr(q), _QDT[q.dtype], _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), kvdt,
+                                     B, n_q, q_pos0, n_ctx, H, d, BLOCK, k_blocks, sm_scale, _ptr(out), _ptr(lse),
+                                     _ptr(block_idx), _ptr(block_scores), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream))
+    _check("hs2_block_attn_select", rc)
+    return out, lse, block_idx, block_scores
+
+
+def block_sparse_attn(q, k, v, k_scale=None, v_scale=None, *, block_idx, q_pos0: int, window: int, gates,
+                      sm_scale: float, out=None, workspace=None, stream=None):
+    """hs2_block_sparse_attn. q [L][B][n_q][H][d]; block_idx [B][n_q][k_blocks];
+    gates [L][B][n_q][H][2] fp32. Returns out [L][B][n_q][H][d]."""
+    L, B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    k_blocks = block_idx.shape[-1]
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    qdt = _QDT[q.dtype]
+    ws = _workspace(workspace_size(OP_BLOCK_SPARSE_ATTN, B, n_q, n_ctx, H, d, window, k_blocks, qdt), dev,
+                    workspace)
+    rc = lib().hs2_block_sparse_attn(_ptr(q), qdt, L, _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _KVDT[k.dtype],
+                                     B, n_q, q_pos0, n_ctx, H, d, _ptr(block_idx), BLOCK, k_blocks, window,
+                                     _ptr(gates), sm_scale, _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                     _stream(stream))
+    _check("hs2_block_sparse_attn", rc)
+    return out
+

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhs2.so")
-SOURCES = ["hs2_api.cpp", "k_rows.hip", "k_decode.hip", "k_select.hip", "k_prefill.hip", "k_project.hip"]
+SOURCES = ["hs2_api.cpp", "k_rows.hip", "k_decode.hip", "k_select.hip", "k_prefill.hip", "k_project.hip",
+           "k_block.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

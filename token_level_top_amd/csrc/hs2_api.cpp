@@ -4,6 +4,7 @@
 #include "hs2.h"
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -172,11 +173,58 @@ PrefillWs prefill_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d
     return w;
 }
 
+// HySparse v1 block mode: the prefill working set without the per-token
+// candidate buffers, plus one rank key per (token, 64-token block)
+constexpr int kBlock = 64;
+struct BlockPfWs {
+    void* vt;
+    uint16_t* kc;
+    float* lse2;
+    uint64_t* keys;
+    int64_t n_ctx_pad, key_stride;
+    size_t bytes;
+};
+BlockPfWs block_pf_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int d, int kv_dtype) {
+    Carver c(base);
+    BlockPfWs w;
+    w.n_ctx_pad = (n_ctx + kVtPad - 1) / kVtPad * kVtPad;
+    w.key_stride = (n_ctx + kBlock - 1) / kBlock;
+    const size_t vt_el = kv_dtype == HS2_F32 ? 4 : 2;
+    w.vt = c.take<void>(vt_el * (size_t)B * d * w.n_ctx_pad);
+    w.kc = kv_dtype == HS2_FP8_E4M3 ? c.take<uint16_t>(2 * (size_t)B * n_ctx * d) : nullptr;
+    w.lse2 = c.take<float>(sizeof(float) * (size_t)B * n_q * H);
+    w.keys = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * n_q * w.key_stride);
+    w.bytes = c.used;
+    return w;
+}
+// the two-branch sparse layer: both branches' index rows, both branch outputs
+// (query type) and the gather kernel's split partials
+struct BlockSpWs {
+    int32_t *win, *blk;
+    void *ob, *ow;
+    float* part;
+    size_t bytes;
+};
+BlockSpWs block_sp_ws(void* base, int64_t n_tok, int H, int d, int q_dtype, int window, int k_blocks) {
+    Carver c(base);
+    BlockSpWs w;
+    w.win = c.take<int32_t>(sizeof(int32_t) * (size_t)n_tok * window);
+    w.blk = c.take<int32_t>(sizeof(int32_t) * (size_t)n_tok * k_blocks * kBlock);
+    w.ob = c.take<void>(esize(q_dtype) * (size_t)n_tok * H * d);
+    w.ow = c.take<void>(esize(q_dtype) * (size_t)n_tok * H * d);
+    // the split count is not monotone in the row count: size for both branches
+    const size_t pb = std::max(sparse_ws(nullptr, n_tok, window, H, d).bytes,
+                               sparse_ws(nullptr, n_tok, k_blocks * kBlock, H, d).bytes);
+    w.part = pb ? c.take<float>(pb) : nullptr;
+    w.bytes = c.used;
+    return w;
+}
+
 // ---- measurement hook: hipEvents around launches of selected kernel classes
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
     KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_PF_FINAL = 10, KC_FILL = 11,
-    KC_PROJECT = 12
+    KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14, KC_GATE = 15
 };
 struct TimedPair {
     int cls;
@@ -340,6 +388,14 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
         case HS2_OP_SELECT_TOPK:
             if (k_global < 1) return SIZE_MAX;
             return select_ws(nullptr, B, n_ctx).bytes;
+        case HS2_OP_BLOCK_ATTN_SELECT:
+            if (n_q <= 0 || H <= 0 || d <= 0 || !dtype_known(kv_dtype)) return SIZE_MAX;
+            return block_pf_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype).bytes;
+        case HS2_OP_BLOCK_SPARSE_ATTN:
+            if (n_q <= 0 || H <= 0 || d <= 0 || window < 1 || k_global < 1 || !dtype_known(kv_dtype))
+                return SIZE_MAX;
+            return block_sp_ws(nullptr, (int64_t)B * n_q, H, d, kv_dtype /* the query type */, window,
+                               k_global).bytes;
         default: return SIZE_MAX;
     }
 }
@@ -388,6 +444,105 @@ int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_la
     a.k_scale = fp8 ? k_scale : nullptr;
     a.v_scale = fp8 ? v_scale : nullptr;
     HS2_TRY(TIMED(KC_PROJECT, s, launch_kv_project(a, d, fp8, s)));
+    return HS2_OK;
+}
+
+int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void* v, const float* k_scale,
+                          const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t q_pos0, int64_t n_ctx,
+                          int H, int d, int block, int k_blocks, float sm_scale, void* out, float* lse,
+                          int32_t* block_idx, float* block_scores, void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    if (block < 1 || k_blocks < 1) return HS2_ERR_INVALID_ARG;
+    if (n_q <= 0 || q_pos0 < 0 || q_pos0 + n_q > n_ctx) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if ((n_ctx + kVtPad - 1) / kVtPad * kVtPad * (int64_t)d >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (!q || !out || !lse || !block_idx) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(block_idx) || !aligned16(block_scores))
+        return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    if (block != kBlock || k_blocks > 4096 / kBlock) return HS2_ERR_UNSUPPORTED;
+    const BlockPfWs need = block_pf_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const BlockPfWs w = block_pf_ws(workspace, B, n_q, n_ctx, H, d, kv_dtype);
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.kc = w.kc;
+    a.vt = w.vt;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.n_q = n_q;
+    a.q_pos0 = q_pos0;
+    a.n_ctx = n_ctx;
+    a.n_ctx_pad = w.n_ctx_pad;
+    a.B = B;
+    a.scale_log2 = sm_scale * kLog2eF;
+    a.out = out;
+    a.lse = lse;
+    a.lse2 = w.lse2;
+    a.block_scores = block_scores;
+    a.block_keys = w.keys;
+    a.block_stride = w.key_stride;
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
+    HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
+    HS2_TRY(TIMED(KC_BLOCK_SCORE, s, launch_block_score(a, H, d, kv_dtype, s)));
+    BlockArgs ba{};
+    ba.n_tok = (int64_t)B * n_q;
+    ba.n_q = n_q;
+    ba.q_pos0 = q_pos0;
+    ba.keys = w.keys;
+    ba.key_stride = w.key_stride;
+    ba.k_blocks = k_blocks;
+    ba.block_idx = block_idx;
+    HS2_TRY(TIMED(KC_BLOCK_SELECT, s, launch_block_select(ba, s)));
+    return HS2_OK;
+}
+
+int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                          const float* k_scale, const float* v_scale, int kv_dtype, int B, int64_t n_q,
+                          int64_t q_pos0, int64_t n_ctx, int H, int d, const int32_t* block_idx, int block,
+                          int k_blocks, int window, const float* gates, float sm_scale, void* out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    if (n_layers < 0 || block < 1 || k_blocks < 1 || window < 1) return HS2_ERR_INVALID_ARG;
+    if (n_q <= 0 || q_pos0 < 0 || q_pos0 + n_q > n_ctx) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if (n_layers > 0 && (!q || !out || !block_idx || !gates)) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(block_idx) || !aligned16(gates)) return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    if (block != kBlock || k_blocks > 4096 / kBlock || window > 4096) return HS2_ERR_UNSUPPORTED;
+    const int64_t n_tok = (int64_t)B * n_q;
+    const BlockSpWs need = block_sp_ws(nullptr, n_tok, H, d, q_dtype, window, k_blocks);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    if (n_layers == 0) return HS2_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const BlockSpWs w = block_sp_ws(workspace, n_tok, H, d, q_dtype, window, k_blocks);
+    BlockArgs ba{};
+    ba.n_tok = n_tok;
+    ba.n_q = n_q;
+    ba.q_pos0 = q_pos0;
+    ba.k_blocks = k_blocks;
+    ba.block_idx = const_cast<int32_t*>(block_idx);
+    ba.window = window;
+    ba.win_idx = w.win;
+    ba.blk_pos = w.blk;
+    HS2_TRY(TIMED(KC_BLOCK_SELECT, s, launch_block_expand(ba, s)));
+    const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
+    for (int l = 0; l < n_layers; ++l) {
+        const void* ql = static_cast<const char*>(q) + qstride * l;
+        int rc = run_sparse(ql, q_dtype, 1, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, w.blk,
+                            k_blocks * kBlock, sm_scale, w.ob, nullptr, w.part, s);
+        if (rc != HS2_OK) return rc;
+        rc = run_sparse(ql, q_dtype, 1, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, w.win, window,
+                        sm_scale, w.ow, nullptr, w.part, s);
+        if (rc != HS2_OK) return rc;
+        HS2_TRY(TIMED(KC_GATE, s, launch_gate_fuse(w.ob, w.ow, gates + (size_t)l * n_tok * H * 2,
+                                                   static_cast<char*>(out) + qstride * l, n_tok, H, d,
+                                                   q_dtype == HS2_BF16, s)));
+    }
     return HS2_OK;
 }
 

@@ -104,12 +104,36 @@ struct PrefillArgs {
     uint64_t* cand;         // [B*n_q][cand_cap] candidate keys
     int cand_cap;
     int32_t* indices;       // [B][n_q][window + k_global]
+    // block mode (HySparse v1 block scores): per (token, 64-key block)
+    float* block_scores;    // [B*n_q][block_stride] fp32, or nullptr
+    uint64_t* block_keys;   // [B*n_q][block_stride] rank keys (score bits << 32 | ~block)
+    int64_t block_stride;
 };
 hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
                           int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st);
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
 // pass 2 also writes the index rows (window + global part)
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+// block mode of pass 2: block scores and rank keys of every block up to the
+// last position of each workgroup's tokens
+hipError_t launch_block_score(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+
+// HySparse v1 block selection and the two-branch sparse layer
+struct BlockArgs {
+    int64_t n_tok, n_q, q_pos0;
+    const uint64_t* keys;   // [n_tok][key_stride] rank keys
+    int64_t key_stride;
+    int k_blocks;
+    int32_t* block_idx;     // [n_tok][k_blocks] ascending, -1 padded
+    int window;
+    int32_t* win_idx;       // [n_tok][window]
+    int32_t* blk_pos;       // [n_tok][k_blocks * 64]
+};
+hipError_t launch_block_select(const BlockArgs& a, hipStream_t st);
+hipError_t launch_block_expand(const BlockArgs& a, hipStream_t st);
+// out[t][h][:] = g[t][h][0] ob[t][h][:] + g[t][h][1] ow[t][h][:], q dtype (f32 or bf16)
+hipError_t launch_gate_fuse(const void* ob, const void* ow, const float* gates, void* out, int64_t n_tok, int H,
+                            int D, bool bf16, hipStream_t st);
 
 // KV Bridging projections: [J][2][d][hidden] bf16 weights applied to [T][hidden]
 // bf16 hidden states, out [J][T][d] (bf16 or e4m3 codes + [J][T] fp32 scales)

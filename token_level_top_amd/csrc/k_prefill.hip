@@ -1077,6 +1077,190 @@ void score_stream_kernel(PrefillArgs a) {
     }
 }
 
+// HySparse (v1) block scores: pass 2 without the per-token top-K. Each 64-key
+// LDS tile is one block; a token's block score is the sum over the tile's
+// causal keys of score_j, each formed exactly as in pass 2 (in-lane head sums
+// of 2^(s c - lse2 + 64)), reduced over the tile's 32 key lanes of each wave
+// half, scaled back by 2^-64 (exact for normal values) and written once per
+// (token, block) with its rank key. The store is held for one step and issued
+// after the next LDS tile store, so it never sits ahead of a tile load on vmcnt.
+template <int H, int D, int KV>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(score_stream_occupancy<H, D, KV>())))
+void block_score_kernel(PrefillArgs a) {
+    constexpr bool F32 = KV == DT_F32;
+    constexpr bool SCALED = KV == DT_FP8;
+    using T = PfTypes<F32>;
+    using LT = typename T::L;
+    using Stage = typename std::conditional<F32, TileStage<D, true, false>, ScoreStage<D, SCALED>>::type;
+    constexpr int VPL = T::VPL, KD = T::KD, NS = D / KD;
+    constexpr int KLD = Stage::KLD;
+    constexpr int TB = kPfRows / H;   // tokens per workgroup
+    constexpr int TW = 32 / H;        // tokens per wave
+    constexpr int NSC = 16 / H;       // scores per lane per 32-key block
+    static_assert(kPfBufs == 3, "the tile loop is unrolled over the three LDS buffers");
+
+    __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
+    __shared__ __attribute__((aligned(16))) float ks_lds[kPfBufs][kPfTile];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+    const int n_blk = (int)((a.n_q + TB - 1) / TB);
+    const int blk = n_blk - 1 - (int)blockIdx.x;
+    const int b = blockIdx.y;
+    const int64_t tok0 = (int64_t)blk * TB;
+    const int64_t wtok0 = tok0 + (int64_t)w * TW;
+    const int64_t p_max = a.q_pos0 + min<int64_t>(tok0 + TB, a.n_q) - 1;
+    auto slot_token = [](int u, int side) { return H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side); };
+    // key js + n is causal for slot u iff js <= pl_n[u]
+    int pl_n[NSC];
+#pragma unroll
+    for (int u = 0; u < NSC; ++u) {
+        const int64_t tk = wtok0 + slot_token(u, hh);
+        pl_n[u] = (tk < a.n_q ? (int)(a.q_pos0 + tk) : -1) - n;
+    }
+    const size_t row0 = (size_t)b * a.n_q;
+
+    LT qf[NS][VPL];
+    {
+        const int R = 32 * w + n;
+        const int64_t tk = tok0 + R / H;
+        const bool ok = tk < a.n_q;
+        const size_t qb = (((size_t)b * a.n_q + (size_t)(ok ? tk : 0)) * H + (R % H)) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int d0 = KD * s + VPL * hh;
+            if constexpr (F32) {
+                qf[s][0] = ok ? reinterpret_cast<const float*>(a.q)[qb + d0] : 0.f;
+            } else {
+                const u32x4 w4 = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qb + d0)
+                                    : u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(&qf[s][0]) = w4;
+            }
+        }
+    }
+    float lse_r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int64_t tk = min<int64_t>(tok0 + R / H, a.n_q - 1);
+        lse_r[i] = a.lse2[((size_t)b * a.n_q + (size_t)tk) * H + (R % H)];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
+        lse_r[i] = tok0 + R / H < a.n_q ? lse_r[i] - kScoreShift : INFINITY;
+    }
+    const LT* kg = SCALED ? reinterpret_cast<const LT*>(a.kc) + (size_t)b * a.n_ctx * D
+                          : reinterpret_cast<const LT*>(a.k) + (size_t)b * a.n_ctx * D;
+    const float* ksg = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
+    const int n_tiles = (int)(p_max / kPfTile) + 1;
+
+    auto qk = [&](int buf, int sub) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        const LT* krow = k_lds[buf] + (32 * sub + n) * KLD + VPL * hh;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = mfma32(&qf[s][0], krow + KD * s, acc);
+        return acc;
+    };
+    // causal token scores of one 32-key block, added into tacc
+    float tacc[NSC];
+    auto score = [&](const f32x16& sacc, int buf, int sub, int j0) {
+        const float c = SCALED ? ks_lds[buf][32 * sub + n] : a.scale_log2;
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
+            const int pi = H == 16 ? (i >> 3) : (i >> 2);
+            part[pi] = (H == 16 ? (i & 7) : (i & 3)) == 0 ? e : part[pi] + e;
+        }
+        float sc[NSC];
+        if constexpr (H == 16) {
+            sc[0] = halves_sum(part[0], part[1]);
+        } else if constexpr (H == 8) {
+            sc[0] = halves_sum(part[0], part[2]);
+            sc[1] = halves_sum(part[1], part[3]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sc[u] = part[u];
+        }
+        const int js = j0 + 32 * sub;
+#pragma unroll
+        for (int u = 0; u < NSC; ++u) tacc[u] += js <= pl_n[u] ? sc[u] : 0.f;
+    };
+    // the pending block score of each slot (lane n == 0 of each half holds it)
+    float pend_v[NSC];
+    int pend_t = -1;
+    auto flush = [&]() {
+        if (pend_t >= 0 && n == 0) {
+#pragma unroll
+            for (int u = 0; u < NSC; ++u) {
+                const int64_t tk = wtok0 + slot_token(u, hh);
+                if (tk < a.n_q) {
+                    const size_t at = (row0 + (size_t)tk) * (size_t)a.block_stride + (size_t)pend_t;
+                    const float v = pend_v[u] * 0x1p-64f;
+                    if (a.block_scores) a.block_scores[at] = v;
+                    a.block_keys[at] = ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)(~(uint32_t)pend_t);
+                }
+            }
+        }
+        pend_t = -1;
+    };
+    Stage stg;
+    auto stage_load = [&](int t) {
+        if constexpr (F32)
+            stg.load(kg, nullptr, (int64_t)t * kPfTile, a.n_ctx, a.n_ctx_pad);
+        else
+            stg.load(kg, ksg, t, (int)a.n_ctx);
+    };
+    auto stage_store = [&](auto bufc) {
+        constexpr int bb = decltype(bufc)::value;
+        if constexpr (F32)
+            stg.store(k_lds[bb], nullptr);
+        else
+            stg.store(k_lds[bb], ks_lds[bb], a.scale_log2);
+    };
+    auto step = [&](auto bufc, int t) {
+        constexpr int bb = decltype(bufc)::value;
+#pragma unroll
+        for (int u = 0; u < NSC; ++u) tacc[u] = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) score(qk(bb, sub), bb, sub, t * kPfTile);
+        // sum over the 32 key lanes of each half
+#pragma unroll
+        for (int u = 0; u < NSC; ++u) {
+            float v = tacc[u];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            v += __shfl_xor(v, 16);
+            tacc[u] = v;
+        }
+        if (t + 1 < n_tiles) stage_store(ic<(bb + 1) % kPfBufs>{});
+        flush();
+#pragma unroll
+        for (int u = 0; u < NSC; ++u) pend_v[u] = tacc[u];
+        pend_t = t;
+        __syncthreads();
+        if (t + 2 < n_tiles) stage_load(t + 2);
+    };
+    stage_load(0);
+    stage_store(ic<0>{});
+    __syncthreads();
+    if (n_tiles > 1) stage_load(1);
+    for (int t = 0; t < n_tiles; t += kPfBufs) {
+        step(ic<0>{}, t);
+        if (t + 1 >= n_tiles) break;
+        step(ic<1>{}, t + 1);
+        if (t + 2 >= n_tiles) break;
+        step(ic<2>{}, t + 2);
+    }
+    flush();
+}
+
 #ifndef HS2_PF_RB
 #define HS2_PF_RB 1
 #endif
@@ -1086,12 +1270,13 @@ void score_stream_kernel(PrefillArgs a) {
 #ifndef HS2_PF_PIPE
 #define HS2_PF_PIPE true
 #endif
+enum PfKernel { PF_FWD, PF_STREAM, PF_BLOCKS };
 template <int H, int D, int KV>
-static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
+static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st) {
     constexpr int TB = kPfRows / H;
     constexpr int kFwdTB = 32 * HS2_PF_NW * HS2_PF_RB / H;  // tokens per pass-1 workgroup (bf16 / FP8)
     dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
-    if (fwd) {
+    if (which == PF_FWD) {
         if constexpr (KV == DT_F32)
             hipLaunchKernelGGL((attn_fwd_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
         else
@@ -1099,13 +1284,15 @@ static hipError_t launch_pf(const PrefillArgs& a, bool fwd, hipStream_t st) {
                                dim3((unsigned)((a.n_q + kFwdTB - 1) / kFwdTB), (unsigned)a.B), dim3(64 * HS2_PF_NW), 0,
                                st, a);
     }
-    else
+    else if (which == PF_STREAM)
         hipLaunchKernelGGL((score_stream_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((block_score_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
     return hipGetLastError();
 }
 
 template <int H, int D>
-static hipError_t launch_pf_hd(const PrefillArgs& a, int kv, bool fwd, hipStream_t st) {
+static hipError_t launch_pf_hd(const PrefillArgs& a, int kv, PfKernel fwd, hipStream_t st) {
     switch (kv) {
         case DT_F32: return launch_pf<H, D, DT_F32>(a, fwd, st);
         case DT_BF16: return launch_pf<H, D, DT_BF16>(a, fwd, st);
@@ -1113,7 +1300,7 @@ static hipError_t launch_pf_hd(const PrefillArgs& a, int kv, bool fwd, hipStream
     }
 }
 
-static hipError_t launch_pf_any(const PrefillArgs& a, int H, int D, int kv, bool fwd, hipStream_t st) {
+static hipError_t launch_pf_any(const PrefillArgs& a, int H, int D, int kv, PfKernel fwd, hipStream_t st) {
     if (D == 64) {
         if (H == 4) return launch_pf_hd<4, 64>(a, kv, fwd, st);
         if (H == 8) return launch_pf_hd<8, 64>(a, kv, fwd, st);
@@ -1125,10 +1312,13 @@ static hipError_t launch_pf_any(const PrefillArgs& a, int H, int D, int kv, bool
 }
 
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
-    return launch_pf_any(a, H, D, kv, true, st);
+    return launch_pf_any(a, H, D, kv, PF_FWD, st);
 }
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
-    return launch_pf_any(a, H, D, kv, false, st);
+    return launch_pf_any(a, H, D, kv, PF_STREAM, st);
+}
+hipError_t launch_block_score(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
+    return launch_pf_any(a, H, D, kv, PF_BLOCKS, st);
 }
 
 }  // namespace hs2
