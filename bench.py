@@ -39,7 +39,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernel classes of the library's timing hook (include/hs2.h)
 KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
-      "prefill_final": 10, "fill": 11, "kv_project": 12}
+      "prefill_final": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14, "gate_fuse": 15}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
 KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "kv_project": "k_project.hip"}
 
@@ -58,8 +58,10 @@ def causal_pairs(wl) -> int:
     return wl.B * (n * p0 + n * (n + 1) // 2)
 
 
-def path_roofline_seconds(wl) -> float:
-    """Lower bound on one step from the method's algorithmic work (HBM or MFMA)."""
+def path_roofline_seconds(wl, blocks: bool = False) -> float:
+    """Lower bound on one step from the method's algorithmic work (HBM or MFMA).
+    blocks: the HySparse v1 variant, whose two branches attend to min(p+1, W)
+    and min(p+1, K) rows."""
     b = kv_bytes(wl.kv_dtype)
     sb = 4 if wl.kv_dtype == "fp8" else 0
     S = wl.window + wl.k_global
@@ -70,7 +72,11 @@ def path_roofline_seconds(wl) -> float:
     peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"] * 1e12
     full = 6 * wl.d * wl.H * causal_pairs(wl) / peak
     # every query attends to min(p+1, S) selected rows in each sparse layer
-    sel = sum(min(wl.q_pos0 + i + 1, S) for i in range(wl.n_q)) * wl.B
+    if blocks:
+        sel = sum(min(wl.q_pos0 + i + 1, wl.window) + min(wl.q_pos0 + i + 1, wl.k_global)
+                  for i in range(wl.n_q)) * wl.B
+    else:
+        sel = sum(min(wl.q_pos0 + i + 1, S) for i in range(wl.n_q)) * wl.B
     sparse = wl.n_sparse * 4 * wl.d * wl.H * sel / peak
     return full + sparse
 
@@ -103,7 +109,7 @@ def traffic_record(name: str, workload_name: str):
         return None
 
 
-def cpu_baseline(wl, x, seconds: float):
+def cpu_baseline(wl, x, seconds: float, blocks: bool = False):
     import numpy as np
     import oracle
     oracle.lib()
@@ -115,10 +121,18 @@ def cpu_baseline(wl, x, seconds: float):
     t0 = time.perf_counter()
     for r in order:
         r = int(r)
-        ref = oracle.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global,
-                                 x.sm_scale, [r])
-        for l in range(wl.n_sparse):
-            oracle.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["idx"], x.sm_scale, [r])
+        if blocks:
+            kb = wl.k_global // 64
+            ref = oracle.block_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, 64, kb, x.sm_scale, [r])
+            for l in range(wl.n_sparse):
+                oracle.block_sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["block_idx"], 64,
+                                    wl.window, np.full((wl.B * wl.n_q, wl.H, 2), 0.5), wl.q_pos0, x.sm_scale, [r])
+        else:
+            ref = oracle.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global,
+                                     x.sm_scale, [r])
+            for l in range(wl.n_sparse):
+                oracle.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["idx"], x.sm_scale,
+                              [r])
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -241,6 +255,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (extra steps)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB twice (reference for HBM counters)")
+    ap.add_argument("--hysparse-blocks", action="store_true",
+                    help="prefill workloads: the HySparse v1 block-level variant (64-token blocks, top 16, gated "
+                         "128-token window branch) in place of token-level selection")
     ap.add_argument("--kv-project", choices=["bf16", "fp8"], default=None,
                     help="instead of the attention path, time the KV Bridging projections with this cache type")
     args = ap.parse_args()
@@ -251,12 +268,16 @@ def main():
         return 2
     if args.kv_project:
         return bench_kv_project(args, args.kv_project)
+    blocks = args.hysparse_blocks
 
     import torch
     import token_level_top_amd as hs2
-    from hs2_inputs import make_inputs, workload
+    from hs2_inputs import make_gates, make_inputs, workload
 
     wl = workload(args.config)
+    if blocks and wl.decode:
+        print("--hysparse-blocks applies to the prefill workloads (1, 2, 4)", file=sys.stderr)
+        return 2
     log(f"workload {wl.name}: generating inputs on the host")
     t0 = time.perf_counter()
     x = make_inputs(wl)
@@ -280,6 +301,25 @@ def main():
         def step():
             hs2.decode_step(qf, qs, k, v, ks, vs, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale,
                             workspace=ws, **bufs)
+    elif blocks:
+        KB = wl.k_global // hs2.BLOCK
+        q = g(x.q)
+        qs = g(x.q_sparse)
+        ws_full = torch.empty(hs2.workspace_size(hs2.OP_BLOCK_ATTN_SELECT, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, 0, 0,
+                                                 kvdt), dtype=torch.uint8, device=dev)
+        ws_sp = torch.empty(hs2.workspace_size(hs2.OP_BLOCK_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d,
+                                               wl.window, KB, hs2._QDT[q.dtype]), dtype=torch.uint8, device=dev)
+        gates = g(make_gates(7, (wl.n_sparse, wl.B, wl.n_q, wl.H, 2)))
+        out = torch.empty_like(q)
+        lse = torch.empty((wl.B, wl.n_q, wl.H), device=dev)
+        bidx = torch.empty((wl.B, wl.n_q, KB), dtype=torch.int32, device=dev)
+        out_s = torch.empty_like(qs)
+
+        def step():
+            hs2.block_attn_select(q, k, v, ks, vs, q_pos0=wl.q_pos0, k_blocks=KB, sm_scale=x.sm_scale, out=out,
+                                  lse=lse, block_idx=bidx, want_scores=False, workspace=ws_full)
+            hs2.block_sparse_attn(qs, k, v, ks, vs, block_idx=bidx, q_pos0=wl.q_pos0, window=wl.window, gates=gates,
+                                  sm_scale=x.sm_scale, out=out_s, workspace=ws_sp)
     else:
         q = g(x.q)
         qs = g(x.q_sparse)
@@ -347,28 +387,30 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
             "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),
             "algorithmic_per_launch": units}
-    t_roof = path_roofline_seconds(wl)
-    res = {"metric": METRIC, "value": round(value, 2), "unit": "query tok/s", "n_gpus": 1, "steps": args.steps,
+    t_roof = path_roofline_seconds(wl, blocks)
+    metric = METRIC if not blocks else ("query tok/s, HySparse v1 block variant: full attn + 64-token block "
+                                        "top-16 + gated 128-token window branch")
+    res = {"metric": metric, "value": round(value, 2), "unit": "query tok/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
-           "config": {"workload": wl.name, "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
+           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else ""), "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,
            "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)}}
     if args.breakdown:
-        L.hs2_timing_enable(0xFFF)  # the attention path's classes (0..11)
+        L.hs2_timing_enable(0xFFFF if blocks else 0xFFF)
         for _ in range(3):
             step()
         torch.cuda.synchronize()
         L.hs2_timing_enable(0)
         ms, n = read_timing()
         names = {v_: k_ for k_, v_ in KC.items()}
-        res["breakdown_ms_per_step"] = {names[c]: round(ms[c] / 3, 4) for c in range(12) if n[c]}
+        res["breakdown_ms_per_step"] = {names[c]: round(ms[c] / 3, 4) for c in range(16) if n[c]}
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, blocks)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -76,6 +76,18 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// gfx950 transposing LDS read of 16-bit elements (ds_read_b64_tr_b16). Within
+// each group of 16 lanes, lane s supplies the address of 4 consecutive
+// elements (8 bytes, 8-byte aligned); lane l receives element l % 4 of the
+// runs supplied by lanes l / 4, 4 + l / 4, 8 + l / 4 and 12 + l / 4, in that
+// order (measured lane layout). Returned as two dwords of packed pairs.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
 // By value on purpose: clang's __builtin_bit_cast applied directly to an
 // ext_vector element (v[e]) reads element 0 whatever e is.
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }

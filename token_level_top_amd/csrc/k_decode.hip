@@ -39,7 +39,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     constexpr int RB = D * ESZ;           // bytes per cache row
     constexpr int NC = D / 32;            // MFMA k-steps over d
     constexpr int NDT = D / 16;           // output d tiles
-    constexpr int VLD = D + 8;            // LDS row stride of the V buffer (bf16 elements)
+    // LDS row stride of the V buffer (bf16 elements): rows 32 bytes past a
+    // multiple of 256, so the transposing fragment reads (8-byte runs of 8 rows
+    // per 32 lanes) touch 64 distinct banks
+    constexpr int VLD = D + 16;
     constexpr int VP = kDecBlock * RB / 16 / 64;  // 16-byte V pieces per lane per block
     static_assert(VP >= 1, "pieces");
     // K operand registers per lane per 16-key group and k-step: 8 elements
@@ -132,9 +135,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
             if constexpr (KV == DT_FP8) {
                 const u32x2 p0 = fp8x4_to_bf16x4(vr[buf][i][0]), p1 = fp8x4_to_bf16x4(vr[buf][i][1]);
                 const u32x2 p2 = fp8x4_to_bf16x4(vr[buf][i][2]), p3 = fp8x4_to_bf16x4(vr[buf][i][3]);
+                // odd rows write their upper half first: with an even number of
+                // 16-byte units per row, each store then covers even and odd units
                 u32x4* o = reinterpret_cast<u32x4*>(vl + row * VLD + 16 * cc);
-                o[0] = u32x4{p0[0], p0[1], p1[0], p1[1]};
-                o[1] = u32x4{p2[0], p2[1], p3[0], p3[1]};
+                const u32x4 lo{p0[0], p0[1], p1[0], p1[1]}, hi{p2[0], p2[1], p3[0], p3[1]};
+                const bool swap = (row & 1) != 0;
+                o[swap ? 1 : 0] = swap ? hi : lo;
+                o[swap ? 0 : 1] = swap ? lo : hi;
             } else {
                 *reinterpret_cast<u32x4*>(vl + row * VLD + 8 * cc) = vr[buf][i];
             }
@@ -230,15 +237,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
         pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
         const bf16x8 pbf = as_bf16x8(pb);
-        const uint16_t* vb = vl + (4 * g) * VLD;
+        // V^T fragment of d tile t (column 16t + hl, keys 4g..4g+3 then 16+4g..)
+        // by two transposing reads: lane hl of each 16-lane group supplies the 4
+        // d values 16t + 4(hl%4).. of key row 4g + hl/4
+        const uint16_t* vb = vl + (4 * g + (hl >> 2)) * VLD + 4 * (hl & 3);
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
-            const int dcol = 16 * t + hl;
-            u32x4 va;
-            va[0] = (uint32_t)vb[0 * VLD + dcol] | ((uint32_t)vb[1 * VLD + dcol] << 16);
-            va[1] = (uint32_t)vb[2 * VLD + dcol] | ((uint32_t)vb[3 * VLD + dcol] << 16);
-            va[2] = (uint32_t)vb[16 * VLD + dcol] | ((uint32_t)vb[17 * VLD + dcol] << 16);
-            va[3] = (uint32_t)vb[18 * VLD + dcol] | ((uint32_t)vb[19 * VLD + dcol] << 16);
+            const u32x2 lo = lds_read_tr16(vb + 16 * t), hi = lds_read_tr16(vb + 16 * VLD + 16 * t);
+            const u32x4 va{lo[0], lo[1], hi[0], hi[1]};
             o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pbf, o_acc[t], 0, 0, 0);
         }
     };
@@ -268,14 +274,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     l_run += __shfl_xor(l_run, 16);
     l_run += xor32(l_run);
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&v_lds[0][0]);  // [4 waves][16][D], then m, l
-    float* red_m = red + 4 * 16 * D;
+    // [4 waves][16][RS], then m, l; rows of RS = D + 4 floats (an odd number of
+    // 16-byte units), so the 16 head lanes of one 16-byte store hit 16 bank quads
+    constexpr int RS = D + 4;
+    float* red = reinterpret_cast<float*>(&v_lds[0][0]);
+    float* red_m = red + 4 * 16 * RS;
     float* red_l = red_m + 4 * 16;
-    static_assert(sizeof(v_lds) >= sizeof(float) * (4 * 16 * D + 128), "merge scratch");
+    static_assert(sizeof(v_lds) >= sizeof(float) * (4 * 16 * RS + 128), "merge scratch");
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[(w * 16 + hl) * D + 16 * t + 4 * g + i] = o_acc[t][i];
+        *reinterpret_cast<f32x4*>(&red[(w * 16 + hl) * RS + 16 * t + 4 * g]) = o_acc[t];
     if (g == 0) {
         red_m[w * 16 + hl] = m_run;
         red_l[w * 16 + hl] = l_run;
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         for (int ww = 0; ww < 4; ++ww) {
             const float f = fast_exp2(red_m[ww * 16 + h] - mm);
             ll += red_l[ww * 16 + h] * f;
-            oo += red[(ww * 16 + h) * D + dd] * f;
+            oo += red[(ww * 16 + h) * RS + dd] * f;
         }
         if (final_out) {
             const float o = ll > 0.f ? oo / ll : 0.f;

@@ -59,14 +59,19 @@ __device__ __forceinline__ u32x4 load_piece(const void* row, int cc) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(row) + cc * 16);
 }
 
+// FP8: the piece widens to two 16-byte halves; with `swap` (odd rows of a
+// tile whose row stride is an even number of 16-byte units) the upper half is
+// written first, so each of the two store instructions covers even and odd
+// units across a 16-lane group instead of colliding on the same banks.
 template <int KV>
-__device__ __forceinline__ void store_piece(typename RowsTypes<KV>::L* dst_row, int cc, u32x4 w) {
+__device__ __forceinline__ void store_piece(typename RowsTypes<KV>::L* dst_row, int cc, u32x4 w, bool swap = false) {
     if constexpr (KV == DT_FP8) {
         u32x2 a = fp8x4_to_bf16x4(w[0]), b = fp8x4_to_bf16x4(w[1]);
         u32x2 c = fp8x4_to_bf16x4(w[2]), e = fp8x4_to_bf16x4(w[3]);
         u32x4* o = reinterpret_cast<u32x4*>(dst_row + cc * 16);
-        o[0] = u32x4{a[0], a[1], b[0], b[1]};
-        o[1] = u32x4{c[0], c[1], e[0], e[1]};
+        const u32x4 lo{a[0], a[1], b[0], b[1]}, hi{c[0], c[1], e[0], e[1]};
+        o[swap ? 1 : 0] = swap ? hi : lo;
+        o[swap ? 0 : 1] = swap ? lo : hi;
     } else {
         constexpr int EPC = 16 / RowsTypes<KV>::ESZ;  // elements per 16-byte piece
         *reinterpret_cast<u32x4*>(dst_row + cc * EPC) = w;
@@ -78,7 +83,11 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     using T = RowsTypes<KV>;
     using LT = typename T::L;
     constexpr int VPL = T::VPL, KD = T::KD, PAD = T::PAD;
-    constexpr int LD = D + PAD;               // LDS row stride (elements)
+    constexpr int LD = D + PAD;               // K tile row stride (elements)
+    // V tile row stride: bf16 rows 32 bytes past a multiple of 256, so the
+    // transposing fragment reads (8-byte runs of 8 rows per 32 lanes) touch 64
+    // distinct banks
+    constexpr int VLD = KV == DT_F32 ? LD : D + 16;
     constexpr int RB = D * T::ESZ;            // global bytes per row
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int CPT = kRowsTile * CPR / kRowsThreads;
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     static_assert((kRowsTile * CPR) % kRowsThreads == 0, "tile chunks");
 
     __shared__ __attribute__((aligned(16))) LT k_lds[kRowsTile * LD];
-    __shared__ __attribute__((aligned(16))) LT v_lds[kRowsTile * LD];
+    __shared__ __attribute__((aligned(16))) LT v_lds[kRowsTile * VLD];
     __shared__ int pos_lds[kRowsTile];
     __shared__ float ksc_lds[kRowsTile];
     __shared__ float vsc_lds[kRowsTile];
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
             const int row = ch / CPR, cc = ch % CPR;
             const bool ok = (kvalid >> c) & 1u;
             store_piece<KV>(k_lds + row * LD, cc, ok ? kreg[c] : u32x4{0, 0, 0, 0});
-            store_piece<KV>(v_lds + row * LD, cc, ok ? vreg[c] : u32x4{0, 0, 0, 0});
+            store_piece<KV>(v_lds + row * VLD, cc, ok ? vreg[c] : u32x4{0, 0, 0, 0}, (row & 1) != 0);
         }
         if (tid < kRowsTile) {
             pos_lds[tid] = meta_p;
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
             for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float* vrow = v_lds + (32 * w + 16 * grp + 4 * g + i) * LD;
+                    const float* vrow = v_lds + (32 * w + 16 * grp + 4 * g + i) * VLD;
 #pragma unroll
                     for (int t = 0; t < NDT; ++t)
                         o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * t + hl], pr[grp][i], o_acc[t], 0,
@@ -296,15 +305,14 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
             pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
             pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
             const bf16x8 pbf = as_bf16x8(pb);
-            const uint16_t* vb = v_lds + (32 * w + 4 * g) * LD;
+            // V^T fragment of d tile t (column 16t + hl, rows 4g..4g+3 then
+            // 16+4g..16+4g+3) by two transposing reads: lane hl of each 16-lane
+            // group supplies the 4 d values 16t + 4(hl%4).. of row 4g + hl/4
+            const uint16_t* vb = v_lds + (32 * w + 4 * g + (hl >> 2)) * VLD + 4 * (hl & 3);
 #pragma unroll
             for (int t = 0; t < NDT; ++t) {
-                const int dcol = 16 * t + hl;
-                u32x4 va;
-                va[0] = (uint32_t)vb[0 * LD + dcol] | ((uint32_t)vb[1 * LD + dcol] << 16);
-                va[1] = (uint32_t)vb[2 * LD + dcol] | ((uint32_t)vb[3 * LD + dcol] << 16);
-                va[2] = (uint32_t)vb[16 * LD + dcol] | ((uint32_t)vb[17 * LD + dcol] << 16);
-                va[3] = (uint32_t)vb[18 * LD + dcol] | ((uint32_t)vb[19 * LD + dcol] << 16);
+                const u32x2 lo = lds_read_tr16(vb + 16 * t), hi = lds_read_tr16(vb + 16 * VLD + 16 * t);
+                const u32x4 va{lo[0], lo[1], hi[0], hi[1]};
                 o_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pbf, o_acc[t], 0, 0, 0);
             }
         }
@@ -316,14 +324,17 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     // ---- merge the 4 waves: per head m, l (summed over lane groups), O
     l_run += __shfl_xor(l_run, 16);
     l_run += xor32(l_run);
-    float* red = reinterpret_cast<float*>(k_lds);  // reuse: [4 waves][16 heads][D] O, then m, l
-    float* red_m = red + 4 * 16 * D;
+    // reuse the K tile: [4 waves][16 heads][RS] O, then m, l. Rows of RS = D + 4
+    // floats (an odd number of 16-byte units), so the 16 head lanes of one
+    // 16-byte store land on 16 different bank quads
+    constexpr int RS = D + 4;
+    float* red = reinterpret_cast<float*>(k_lds);
+    float* red_m = red + 4 * 16 * RS;
     float* red_l = red_m + 4 * 16;
-    static_assert(sizeof(k_lds) >= sizeof(float) * (4 * 16 * D + 128), "reduction scratch");
+    static_assert(sizeof(k_lds) >= sizeof(float) * (4 * 16 * RS + 128), "reduction scratch");
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[(w * 16 + hl) * D + 16 * t + 4 * g + i] = o_acc[t][i];
+        *reinterpret_cast<f32x4*>(&red[(w * 16 + hl) * RS + 16 * t + 4 * g]) = o_acc[t];
     if (g == 0) {
         red_m[w * 16 + hl] = m_run;
         red_l[w * 16 + hl] = l_run;
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         for (int ww = 0; ww < 4; ++ww) {
             const float f = fast_exp2(red_m[ww * 16 + h] - mm);
             ll += red_l[ww * 16 + h] * f;
-            oo += red[(ww * 16 + h) * D + dd] * f;
+            oo += red[(ww * 16 + h) * RS + dd] * f;
         }
         if (final_out) {
             const float o = ll > 0.f ? oo / ll : 0.f;
