@@ -267,3 +267,24 @@ def test_prefill_batched_and_head_shapes(hs2, orc, cfg, B, H, d, n_q, q_pos0, n_
                    x.sm_scale, rows)
     rows_close(so[0].reshape(B * n_q, H, d), s["out"], tol, "prefill sparse out")
     lse_close(sl[0].reshape(B * n_q, H), s["lse"], tol)
+
+
+def test_sparse_attn_beyond_65535_tokens(hs2, orc):
+    """More query tokens in one call than a grid's y dimension holds (65535):
+    the sparse layer's 1-D grid covers them all; sampled rows against the
+    oracle, including the last token."""
+    n = 70000
+    wl = workload(1).with_(B=1, n_q=n, q_pos0=0, n_ctx=n, n_needles=0, n_sparse=1)
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(1, 1, n, wl.H, wl.d, generator=g)
+    k = torch.randn(1, n, wl.d, generator=g)
+    v = torch.randn(1, n, wl.d, generator=g)
+    idx = torch.randint(0, n, (1, n, 8), generator=g, dtype=torch.int32)
+    idx[0, :, 7] = -1
+    say("sparse attention over", n, "tokens")
+    out, lse = hs2.sparse_attn(q.cuda(), k.cuda(), v.cuda(), indices=idx.cuda(), sm_scale=0.125)
+    torch.cuda.synchronize()
+    rows = [0, 65534, 65535, 65536, n - 1]
+    ref = orc.sparse(q[0].contiguous(), k, v, None, None, idx[0, rows].numpy(), 0.125, rows)
+    rows_close(out[0, 0, rows], ref["out"], RTOL["f32"], "sparse out")
+    lse_close(lse[0, 0, rows], ref["lse"], RTOL["f32"])

@@ -17,10 +17,10 @@ struct RowsArgs {
     const int32_t* idx;     // gather: [n_tok][n_rows] positions, -1 = empty
     int64_t n_ctx;
     int64_t n_rows;         // rows per token (gather: n_sel; contiguous: n_ctx)
-    int n_tok;              // query tokens (grid.y)
+    int n_tok;              // query tokens (grid: n_tok * n_split workgroups, splits adjacent)
     int n_q;                // tokens per sequence (token t reads sequence t / n_q)
     int rows_per_split;     // rows per workgroup (multiple of the 128-row tile)
-    int n_split;            // workgroups per token (grid.x)
+    int n_split;            // workgroups per token
     float scale_log2;       // sm_scale * log2(e)
     float* logits;          // contiguous + store: [B][n_ctx][H] base-2 logits
     float* part;            // n_split > 1: [n_tok][n_split][H*(D+2)] = m[H], l[H], O[H][D]

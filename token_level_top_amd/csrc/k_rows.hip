@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hl = lane & 15, g = lane >> 4;
-    const int tok = blockIdx.y, split = blockIdx.x;
+    // 1-D grid, the splits of one token adjacent (a y dimension would cap the
+    // token count at 65535)
+    const int tok = (int)(blockIdx.x / (uint32_t)a.n_split), split = (int)(blockIdx.x % (uint32_t)a.n_split);
     const int seq = tok / a.n_q;
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
     const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
 
 template <int H, int D, int KV, bool GATHER, bool STORE>
 static hipError_t launch_rows_t(const RowsArgs& a, hipStream_t st) {
-    dim3 grid(a.n_split, a.n_tok);
+    const dim3 grid((unsigned)((int64_t)a.n_split * a.n_tok));
     hipLaunchKernelGGL((rows_attn_kernel<H, D, KV, GATHER, STORE>), grid, dim3(kRowsThreads), 0, st, a);
     return hipGetLastError();
 }
