@@ -7,4 +7,5 @@ no selection. Both the CPU oracle's tests and the GPU path's tests/bench take
 their inputs from here, so the two sides always see bit-identical arrays.
 """
 from .configs import WORKLOADS, Workload, workload  # noqa: F401
-from .gen import Inputs, make_inputs, make_projection_inputs, make_gates, quantize_e4m3, checked_rows  # noqa: F401
+from .gen import (Inputs, IndexerInputs, make_inputs, make_projection_inputs, make_gates, make_indexer_inputs,  # noqa: F401
+                  quantize_e4m3, checked_rows)

@@ -229,3 +229,56 @@ def make_gates(seed: int, shape) -> torch.Tensor:
     g = np.random.Generator(np.random.Philox(np.random.SeedSequence([seed, 72])))
     z = g.standard_normal(size=shape)
     return torch.from_numpy((1.0 / (1.0 + np.exp(-z))).astype(np.float32))
+
+
+@dataclass
+class IndexerInputs:
+    qi: torch.Tensor       # [B][n_q][HI][dI] uint8 E4M3 codes
+    qs: torch.Tensor       # [B][n_q][HI] fp32 scales
+    w: torch.Tensor        # [B][n_q][HI] fp32 head weights (either sign)
+    ki: torch.Tensor       # [B][n_ctx][dI] uint8 E4M3 codes
+    ks: torch.Tensor       # [B][n_ctx] fp32 scales
+    needles: List[Tuple[int, int, int]] = field(default_factory=list)  # (flat query row, head, key position)
+
+
+def make_indexer_inputs(seed: int, B: int, n_q: int, q_pos0: int, n_ctx: int, HI: int, dI: int,
+                        n_needles: int = 0, window: int = 128, exact: bool = False) -> IndexerInputs:
+    """Light-indexer operands (streams 80..84 of SeedSequence([seed, stream])).
+
+    Default: queries and keys N(0,1), quantised per (token, head) and per key
+    row to E4M3 with scale amax/448; weights N(0, 1/HI), so a few are negative
+    per token. Needles: for a random query row and head with a positive
+    weight (its largest, and only where it is at least 0.5), the key at a random
+    candidate position (<= p - window) is set to 8*sqrt(dI) times the unit
+    direction of that head's query.
+    exact=True: codes of integers in [-2, 2], unit scales, weights k/8 with
+    integer k in [-8, 8]: every dot product and weighted sum is exact in fp32
+    and equal scores are common (ties then decide by position)."""
+    g = [np.random.Generator(np.random.Philox(np.random.SeedSequence([seed, s]))) for s in range(80, 85)]
+    if exact:
+        qv = torch.from_numpy(g[0].integers(-2, 3, size=(B, n_q, HI, dI)).astype(np.float32))
+        kv = torch.from_numpy(g[1].integers(-2, 3, size=(B, n_ctx, dI)).astype(np.float32))
+        w = torch.from_numpy(g[2].integers(-8, 9, size=(B, n_q, HI)).astype(np.float32) / 8.0)
+        qi = qv.to(torch.float8_e4m3fn).view(torch.uint8)
+        ki = kv.to(torch.float8_e4m3fn).view(torch.uint8)
+        return IndexerInputs(qi, torch.ones(B, n_q, HI), w, ki, torch.ones(B, n_ctx))
+    qv = torch.from_numpy(g[0].standard_normal(size=(B, n_q, HI, dI), dtype=np.float32))
+    kv = torch.from_numpy(g[1].standard_normal(size=(B, n_ctx, dI), dtype=np.float32))
+    w = torch.from_numpy(g[2].standard_normal(size=(B, n_q, HI), dtype=np.float32) / np.float32(math.sqrt(HI)))
+    needles = []
+    for _ in range(n_needles):
+        b = int(g[3].integers(0, B))
+        i = int(g[3].integers(0, n_q))
+        p = q_pos0 + i
+        if p - window < 0:
+            continue
+        h = int(torch.argmax(w[b, i]))
+        if w[b, i, h] < 0.5:
+            continue
+        j = int(g[4].integers(0, p - window + 1))
+        qd = qv[b, i, h]
+        kv[b, j] = 8.0 * math.sqrt(dI) * qd / qd.norm()
+        needles.append((b * n_q + i, h, j))
+    qi, qs = quantize_e4m3(qv)
+    ki, ks = quantize_e4m3(kv)
+    return IndexerInputs(qi.contiguous(), qs.contiguous(), w.contiguous(), ki.contiguous(), ks.contiguous(), needles)

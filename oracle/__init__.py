@@ -53,6 +53,9 @@ def lib():
         L.orc_kv_project.restype = _i
         L.orc_block_select.argtypes = [_p, _i64, _i64, _p, _i, _i, _p, _p]
         L.orc_block_select.restype = _i
+        L.orc_index_select.argtypes = [_p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _i, _i, _p, _i64, _p, _p,
+                                       _p]
+        L.orc_index_select.restype = _i
         L.orc_num_threads.restype = _i
         L.orc_set_threads.argtypes = [_i]
         _lib = L
@@ -233,4 +236,24 @@ def block_sparse(q, k, v, k_scale, v_scale, block_idx, block: int, window: int, 
     out = g[..., 0:1] * ob["out"] + g[..., 1:2] * ow["out"]
     return {"out": out, "out_blocks": ob["out"], "out_window": ow["out"], "lse_blocks": ob["lse"],
             "lse_window": ow["lse"], "win_idx": win, "blk_idx": blk}
+
+
+def index_select(qi, qs, w, ki, ks, q_pos0: int, window: int, k_global: int, rows: Sequence[int],
+                 want_scores: bool = False):
+    """Light-indexer scores and the window + top-k index rows for flat query
+    rows `rows`. qi [B][n_q][HI][dI] uint8 E4M3 codes, qs [B][n_q][HI] fp32,
+    w [B][n_q][HI] fp32, ki [B][n_ctx][dI] uint8 codes, ks [B][n_ctx] fp32."""
+    B, n_q, HI, dI = qi.shape
+    n_ctx = ki.shape[1]
+    rows_a = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = len(rows_a)
+    idx = np.zeros((n, window + k_global), np.int32)
+    kth = np.zeros((n,), np.float64)
+    sc = np.zeros((n, n_ctx), np.float64) if want_scores else None
+    rc = lib().orc_index_select(_ptr(qi.contiguous()), _ptr(qs.contiguous()), _ptr(w.contiguous()),
+                                _ptr(ki.contiguous()), _ptr(ks.contiguous()), B, n_q, q_pos0, n_ctx, HI, dI, window,
+                                k_global, _ptr(rows_a), n, _ptr(sc), _ptr(idx), _ptr(kth))
+    if rc != 0:
+        raise ValueError("oracle index_select: invalid arguments")
+    return {"idx": idx, "kth": kth, "scores": sc, "rows": rows_a}
 

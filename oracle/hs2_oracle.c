@@ -434,6 +434,77 @@ int orc_block_select(const double* scores, int64_t n_rows, int64_t stride, const
     return 0;
 }
 
+/*
+ * Light indexer scores and selection (IndexCache page, section 2.1, on the
+ * DeepSeek Sparse Attention indexer: a multi-head ReLU-gated dot product of
+ * the current query with every preceding token, few heads, FP8). Reading R26:
+ *   I_t(s) = sum_j w[t][j] * max(0, qs[t][j] * ks[s] * sum_c q[t][j][c] k[s][c])
+ * with FP8 E4M3 codes q [B][n_q][HI][dI] (scale qs per token and head) and one
+ * indexer key per position k [B][n_ctx][dI] (scale ks per position), weights
+ * w [B][n_q][HI] of either sign. The index row is the HySparse2 rule on these
+ * scores: the window, then the top k_global positions j <= p - window by
+ * (I desc, position asc).
+ *   scores [n_rows][n_ctx] (nullable): I for j <= p, -inf beyond
+ *   idx    [n_rows][window + k_global], kth [n_rows] (nullable): the score of
+ *          the last global position taken (-inf if none)
+ * Returns 0, or 1 on invalid arguments.
+ */
+int orc_index_select(const uint8_t* q, const float* qs, const float* w, const uint8_t* k, const float* ks,
+                     int B, int64_t n_q, int64_t q_pos0, int64_t n_ctx, int HI, int dI, int window, int k_global,
+                     const int64_t* rows, int64_t n_rows, double* scores, int32_t* idx, double* kth) {
+    if (B <= 0 || n_q <= 0 || n_ctx <= 0 || HI <= 0 || dI <= 0 || window < 1 || k_global < 0) return 1;
+    if (q_pos0 < 0 || q_pos0 + n_q > n_ctx) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= (int64_t)B * n_q) return 1;
+    const int S = window + k_global;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t row = rows[r], b = row / n_q, p = q_pos0 + row % n_q, n = p + 1;
+        double* qd = (double*)malloc(sizeof(double) * (size_t)HI * (size_t)dI);
+        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+        for (int t = 0; t < HI * dI; ++t) qd[t] = orc_e4m3_value(q[(size_t)row * HI * dI + (size_t)t]);
+        for (int64_t j = 0; j < n; ++j) {
+            const uint8_t* kr = k + ((size_t)b * (size_t)n_ctx + (size_t)j) * (size_t)dI;
+            double acc = 0.0;
+            for (int h = 0; h < HI; ++h) {
+                double dot = 0.0;
+                for (int c = 0; c < dI; ++c) dot += qd[h * dI + c] * orc_e4m3_value(kr[c]);
+                dot *= (double)qs[(size_t)row * HI + h] * (double)ks[(size_t)b * n_ctx + j];
+                acc += (double)w[(size_t)row * HI + h] * (dot > 0.0 ? dot : 0.0);
+            }
+            sc[j] = acc;
+        }
+        if (scores) {
+            double* dst = scores + (size_t)r * (size_t)n_ctx;
+            for (int64_t j = 0; j < n_ctx; ++j) dst[j] = j < n ? sc[j] : -INFINITY;
+        }
+        int32_t* dst = idx ? idx + (size_t)r * (size_t)S : NULL;
+        const int64_t nw = p + 1 < window ? p + 1 : window;
+        if (dst)
+            for (int t = 0; t < window; ++t) dst[t] = t < nw ? (int32_t)(p - nw + 1 + t) : -1;
+        int64_t n_cand = p - window + 1;
+        if (n_cand < 0) n_cand = 0;
+        const int64_t take = n_cand < k_global ? n_cand : k_global;
+        orc_cand* cand = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(n_cand > 0 ? n_cand : 1));
+        for (int64_t j = 0; j < n_cand; ++j) {
+            cand[j].s = sc[j];
+            cand[j].j = j;
+        }
+        qsort(cand, (size_t)n_cand, sizeof(orc_cand), orc_cand_cmp);
+        if (kth) kth[r] = take > 0 ? cand[take - 1].s : -INFINITY;
+        if (dst) {
+            int32_t* g = dst + window;
+            for (int64_t t = 0; t < take; ++t) g[t] = (int32_t)cand[t].j;
+            qsort(g, (size_t)take, sizeof(int32_t), orc_i32_cmp);
+            for (int64_t t = take; t < k_global; ++t) g[t] = -1;
+        }
+        free(cand);
+        free(sc);
+        free(qd);
+    }
+    return 0;
+}
+
 int orc_num_threads(void) { return omp_get_max_threads(); }
 void orc_set_threads(int n) {
     if (n > 0) omp_set_num_threads(n);

@@ -614,3 +614,84 @@ def test_block_sparse_reduces_to_full_attention(orc):
     # the window branch alone is attention over the last 128 positions
     assert (rb["win_idx"][3] == np.arange(1000 - 127, 1001)).all()
     assert (rb["win_idx"][1][:8] == np.arange(8)).all() and (rb["win_idx"][1][8:] == -1).all()
+
+
+# ----------------------------------------------------- light indexer (DSA-style)
+
+def _e4m3_codes(a):
+    return torch.tensor(a, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+def test_index_select_hand_example(orc):
+    """Two heads picking the two coordinates of 2-d keys, weights 1 and 1/2:
+    I(j) = relu(k_j[0]) + relu(k_j[1]) / 2, worked by hand; then window 2 and
+    the top candidates among j <= p - 2, ties to the lower position."""
+    qi = _e4m3_codes([[[[1, 0], [0, 1]]]])                    # [B=1][n_q=1][HI=2][dI=2]
+    ki = _e4m3_codes([[[2, 0], [0, 2], [1, 1], [-1, 2], [0, 0], [1, 0]]])
+    qs, ks = torch.ones(1, 1, 2), torch.ones(1, 6)
+    w = torch.tensor([[[1.0, 0.5]]])
+    r = orc.index_select(qi, qs, w, ki, ks, 5, 2, 2, [0], want_scores=True)
+    assert r["scores"][0].tolist() == [2.0, 1.0, 1.5, 1.0, 0.0, 1.0]
+    assert r["idx"][0].tolist() == [4, 5, 0, 2]
+    r = orc.index_select(qi, qs, w, ki, ks, 5, 2, 3, [0])       # 1 and 3 tie at 1: 1 wins
+    assert r["idx"][0].tolist() == [4, 5, 0, 1, 2]
+    w = torch.tensor([[[-1.0, 0.5]]])                           # I = -2, 1, -0.5, 1
+    r = orc.index_select(qi, qs, w, ki, ks, 5, 2, 2, [0], want_scores=True)
+    assert r["scores"][0][:4].tolist() == [-2.0, 1.0, -0.5, 1.0]
+    assert r["idx"][0].tolist() == [4, 5, 1, 3]
+    r = orc.index_select(qi, qs, w, ki, ks, 5, 2, 1, [0])
+    assert r["idx"][0].tolist() == [4, 5, 1]
+
+
+def test_index_select_scales_and_relu(orc):
+    """The scales multiply each head's dot product; a head whose dot product is
+    negative contributes nothing whatever its weight."""
+    qi = _e4m3_codes([[[[1, 1], [-1, -1]]]])
+    ki = _e4m3_codes([[[1, 2], [3, 0]]])
+    w = torch.tensor([[[2.0, -5.0]]])
+    r = orc.index_select(qi, torch.tensor([[[0.5, 1.0]]]), w, ki, torch.tensor([[4.0, 0.25]]), 1, 1, 1, [0],
+                         want_scores=True)
+    # head 0: 0.5 * scale_k * (k0 + k1), head 1: negative dot, relu -> 0
+    assert r["scores"][0].tolist() == [2.0 * 0.5 * 4.0 * 3.0, 2.0 * 0.5 * 0.25 * 3.0]
+
+
+def test_index_select_all_zero_scores_pick_lowest_positions(orc):
+    """Queries of +1 and keys of -1 everywhere: every dot product is negative,
+    every score 0 whatever the weights, so the global part is the first
+    k_global candidates."""
+    from hs2_inputs import make_indexer_inputs
+    x = make_indexer_inputs(3, 1, 4, 300, 304, 4, 64)
+    qi = _e4m3_codes(np.ones((1, 4, 4, 64)).tolist())
+    ki = _e4m3_codes((-np.ones((1, 304, 64))).tolist())
+    r = orc.index_select(qi, torch.ones(1, 4, 4), x.w, ki, torch.ones(1, 304), 300, 128, 16, [0, 3],
+                         want_scores=True)
+    assert (r["scores"][0, :301] == 0).all() and (r["scores"][1, :304] == 0).all()
+    assert r["idx"][0][128:].tolist() == list(range(16))
+    assert r["idx"][1][:128].tolist() == list(range(303 - 127, 304))
+
+
+def test_index_select_sign_and_order(orc):
+    """Negating the weights negates every score exactly, and the chosen set is
+    the plain sort of the scores (desc, position asc) over the candidates."""
+    from hs2_inputs import make_indexer_inputs
+    x = make_indexer_inputs(5, 1, 6, 500, 506, 8, 64)
+    rows = [0, 5]
+    a = orc.index_select(x.qi, x.qs, x.w, x.ki, x.ks, 500, 128, 40, rows, want_scores=True)
+    b = orc.index_select(x.qi, x.qs, (-x.w).contiguous(), x.ki, x.ks, 500, 128, 40, rows, want_scores=True)
+    for t, row in enumerate(rows):
+        p = 500 + row
+        assert np.array_equal(b["scores"][t, :p + 1], -a["scores"][t, :p + 1])
+        for r in (a, b):
+            s = r["scores"][t]
+            order = sorted(range(p - 128 + 1), key=lambda j: (-s[j], j))[:40]
+            assert r["idx"][t][128:].tolist() == sorted(order)
+
+
+def test_index_select_recovers_planted_needles(orc):
+    from hs2_inputs import make_indexer_inputs
+    x = make_indexer_inputs(11, 1, 64, 4032, 4096, 4, 64, n_needles=12)
+    rows = sorted({r for r, _, _ in x.needles})
+    r = orc.index_select(x.qi, x.qs, x.w, x.ki, x.ks, 4032, 128, 1024, rows)
+    where = {row: i for i, row in enumerate(rows)}
+    for row, h, j in x.needles:
+        assert j in r["idx"][where[row]][128:].tolist()
