@@ -78,7 +78,8 @@ typedef enum {
     HS2_OP_SPARSE_ATTN = 2,
     HS2_OP_SELECT_TOPK = 3,
     HS2_OP_BLOCK_ATTN_SELECT = 4,
-    HS2_OP_BLOCK_SPARSE_ATTN = 5
+    HS2_OP_BLOCK_SPARSE_ATTN = 5,
+    HS2_OP_INDEX_SELECT = 6
 } hs2_op;
 
 /* HS2_ABI_VERSION of the built library. */
@@ -92,7 +93,8 @@ const char* hs2_status_string(int status);
  * arguments are invalid). For HS2_OP_SELECT_TOPK pass B = rows, n_ctx = row
  * length and k_global = k; the other arguments are ignored. For
  * HS2_OP_BLOCK_SPARSE_ATTN pass window, k_global = k_blocks and, in place of
- * kv_dtype, the query type. Pure host code.
+ * kv_dtype, the query type. For HS2_OP_INDEX_SELECT pass d = the indexer
+ * head dimension dI. Pure host code.
  */
 size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int d, int window,
                           int k_global, int kv_dtype);
@@ -256,6 +258,33 @@ int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* 
                           size_t ws_bytes, void* stream);
 
 /*
+ * Light-indexer selection: index rows chosen by the DeepSeek Sparse Attention
+ * style indexer the IndexCache page describes (section 2.1: a multi-head
+ * ReLU-gated dot product of the query with every preceding token, few heads,
+ * FP8) instead of exact attention scores. For a query at position p:
+ *   I(j) = sum_h w[h] * max(0, q_scale[h] * k_scale[j] * <q[h], k[j]>)
+ * and the index row is the rule above on I: the window, then the k_global
+ * positions j <= p - window with the largest I, equal scores to the lower
+ * position. Scores may be negative (weights of either sign).
+ *   q_idx    [B][n_q][HI][dI] uint8  E4M3 codes of the indexer queries
+ *   q_scale  [B][n_q][HI]     fp32   per (token, head) scale, > 0
+ *   weights  [B][n_q][HI]     fp32   head weights
+ *   k_idx    [B][n_ctx][dI]   uint8  E4M3 codes of the indexer keys
+ *   k_scale  [B][n_ctx]       fp32   per position scale, > 0
+ *   indices  [B][n_q][window+k_global] int32  (layout above)
+ *   workspace >= hs2_workspace_size(HS2_OP_INDEX_SELECT, B, n_q, n_ctx, 0, dI,
+ *                0, 0, 0) bytes
+ * HI in {4, 8, 16}, dI in {64, 128}, window and k_global as for
+ * hs2_full_attn_select (else HS2_ERR_UNSUPPORTED). Products accumulate in
+ * fp32. With IndexCache reuse (section 3) the layers that skip the indexer
+ * pass these rows to hs2_sparse_attn.
+ */
+int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* weights,
+                     const uint8_t* k_idx, const float* k_scale, int B, int64_t n_q, int64_t q_pos0,
+                     int64_t n_ctx, int HI, int dI, int window, int k_global, int32_t* indices,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram
@@ -265,6 +294,8 @@ int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* 
  *   bit 10 prefill final selection     bit 11 buffer fills
  *   bit 12 KV Bridging projections     bit 13 block scores (block mode)
  *   bit 14 block choice / expansion    bit 15 two-branch gate fusion
+ * (the light indexer's scoring and selection report as bit 9, its key
+ * widening as bit 7)
  * hs2_timing_enable(mask): from now on every launch of a class in `mask` is
  * bracketed by two hipEvents recorded on its launch stream (0 disables).
  * hs2_timing_read(ms, launches): waits for the recorded events and adds, per

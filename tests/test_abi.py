@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -181,6 +181,29 @@ def test_block_variant_validation():
     assert call_sp(a15=16) == E.HS2_ERR_UNSUPPORTED
     assert call_sp(a2=-1) == E.HS2_ERR_INVALID_ARG
     assert hs2.workspace_size(E.OP_BLOCK_SPARSE_ATTN, 1, 100, 100, 16, 128, 128, 16, 1) > 0
+
+
+def test_index_select_validation():
+    L = hs2.lib()
+    E = hs2
+    # qi, qs, w, ki, ks, B, n_q, q_pos0, n_ctx, HI, dI, window, k_global, idx, ws, wsb, stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 100, 0, 100, 8, 128, 128, 1024, FAKE, None, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_index_select(*a)
+
+    assert call() == E.HS2_ERR_WORKSPACE
+    assert call(a9=6) == E.HS2_ERR_UNSUPPORTED                # indexer heads
+    assert call(a10=96) == E.HS2_ERR_UNSUPPORTED              # indexer head dim
+    assert call(a12=4096) == E.HS2_ERR_UNSUPPORTED            # k_global > 2048
+    assert call(a11=0) == E.HS2_ERR_INVALID_ARG
+    assert call(a1=None) == E.HS2_ERR_INVALID_ARG
+    assert call(a3=MIS) == E.HS2_ERR_INVALID_ARG
+    assert call(a7=1) == E.HS2_ERR_INVALID_ARG                 # q_pos0 + n_q > n_ctx
+    assert hs2.workspace_size(E.OP_INDEX_SELECT, 1, 32768, 32768, 0, 128, 0, 0, 0) >= 32768 * 4096 * 8
 
 
 def test_binding_refuses_host_tensors():

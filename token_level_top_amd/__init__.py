@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhs2.so")
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = range(5)
 HS2_F32, HS2_BF16, HS2_FP8_E4M3 = 0, 1, 2
 OP_FULL_ATTN_SELECT, OP_DECODE_STEP, OP_SPARSE_ATTN, OP_SELECT_TOPK = 0, 1, 2, 3
-OP_BLOCK_ATTN_SELECT, OP_BLOCK_SPARSE_ATTN = 4, 5
+OP_BLOCK_ATTN_SELECT, OP_BLOCK_SPARSE_ATTN, OP_INDEX_SELECT = 4, 5, 6
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
@@ -37,6 +37,7 @@ _SIGS = {
     "hs2_kv_project": ([_p, _i64, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
     "hs2_block_attn_select": ([_p, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _i, _i, _f, _p, _p,
                                _p, _p, _p, _sz, _p], _i),
+    "hs2_index_select": ([_p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
     "hs2_block_sparse_attn": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _p, _i, _i, _i,
                                _p, _f, _p, _p, _sz, _p], _i),
 }
@@ -262,4 +263,22 @@ def block_sparse_attn(q, k, v, k_scale=None, v_scale=None, *, block_idx, q_pos0:
                                      _stream(stream))
     _check("hs2_block_sparse_attn", rc)
     return out
+
+
+def index_select(q_idx, q_scale, weights, k_idx, k_scale, *, q_pos0: int, window: int, k_global: int,
+                 indices=None, workspace=None, stream=None):
+    """hs2_index_select. q_idx [B][n_q][HI][dI] uint8 E4M3 codes, q_scale and
+    weights [B][n_q][HI] fp32, k_idx [B][n_ctx][dI] uint8, k_scale [B][n_ctx].
+    Returns indices [B][n_q][window+k_global] int32."""
+    B, n_q, HI, dI = q_idx.shape
+    n_ctx = k_idx.shape[1]
+    dev = q_idx.device
+    if indices is None:
+        indices = torch.empty((B, n_q, window + k_global), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_size(OP_INDEX_SELECT, B, n_q, n_ctx, 0, dI, 0, 0, 0), dev, workspace)
+    rc = lib().hs2_index_select(_ptr(q_idx), _ptr(q_scale), _ptr(weights), _ptr(k_idx), _ptr(k_scale), B, n_q,
+                                q_pos0, n_ctx, HI, dI, window, k_global, _ptr(indices), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream))
+    _check("hs2_index_select", rc)
+    return indices
 

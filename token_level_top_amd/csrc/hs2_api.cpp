@@ -220,6 +220,21 @@ BlockSpWs block_sp_ws(void* base, int64_t n_tok, int H, int d, int q_dtype, int 
     return w;
 }
 
+// light indexer: the keys widened to bf16, the candidate buffers
+struct IndexWs {
+    uint16_t* kc;
+    uint64_t* cand;
+    size_t bytes;
+};
+IndexWs index_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int dI) {
+    Carver c(base);
+    IndexWs w;
+    w.kc = c.take<uint16_t>(2 * (size_t)B * n_ctx * dI);
+    w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * n_q * kPrefillCandCap);
+    w.bytes = c.used;
+    return w;
+}
+
 // ---- measurement hook: hipEvents around launches of selected kernel classes
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
@@ -391,6 +406,9 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
         case HS2_OP_BLOCK_ATTN_SELECT:
             if (n_q <= 0 || H <= 0 || d <= 0 || !dtype_known(kv_dtype)) return SIZE_MAX;
             return block_pf_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype).bytes;
+        case HS2_OP_INDEX_SELECT:
+            if (n_q <= 0 || d <= 0) return SIZE_MAX;
+            return index_ws(nullptr, B, n_q, n_ctx, d).bytes;
         case HS2_OP_BLOCK_SPARSE_ATTN:
             if (n_q <= 0 || H <= 0 || d <= 0 || window < 1 || k_global < 1 || !dtype_known(kv_dtype))
                 return SIZE_MAX;
@@ -543,6 +561,45 @@ int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* 
                                                    static_cast<char*>(out) + qstride * l, n_tok, H, d,
                                                    q_dtype == HS2_BF16, s)));
     }
+    return HS2_OK;
+}
+
+int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* weights, const uint8_t* k_idx,
+                     const float* k_scale, int B, int64_t n_q, int64_t q_pos0, int64_t n_ctx, int HI, int dI,
+                     int window, int k_global, int32_t* indices, void* workspace, size_t ws_bytes, void* stream) {
+    if (B <= 0 || n_q <= 0 || n_ctx <= 0 || n_ctx >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (q_pos0 < 0 || q_pos0 + n_q > n_ctx || HI <= 0 || dI <= 0) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    int ss = check_select_shape(window, k_global);
+    if (ss == HS2_ERR_INVALID_ARG) return ss;
+    if (!q_idx || !q_scale || !weights || !k_idx || !k_scale || !indices) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q_idx) || !aligned16(q_scale) || !aligned16(weights) || !aligned16(k_idx) ||
+        !aligned16(k_scale) || !aligned16(indices))
+        return HS2_ERR_INVALID_ARG;
+    if (ss != HS2_OK) return ss;
+    if ((HI != 4 && HI != 8 && HI != 16) || (dI != 64 && dI != 128)) return HS2_ERR_UNSUPPORTED;
+    const IndexWs need = index_ws(nullptr, B, n_q, n_ctx, dI);
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const IndexWs w = index_ws(workspace, B, n_q, n_ctx, dI);
+    HS2_TRY(TIMED(KC_PREP, s, launch_widen_fp8(k_idx, w.kc, (int64_t)B * n_ctx * dI, s)));
+    PrefillArgs a{};
+    a.q = q_idx;
+    a.kc = w.kc;
+    a.ks = k_scale;
+    a.n_q = n_q;
+    a.q_pos0 = q_pos0;
+    a.n_ctx = n_ctx;
+    a.B = B;
+    a.scale_log2 = 1.0f;  // key scales enter as they are
+    a.window = window;
+    a.k_global = k_global;
+    a.cand = w.cand;
+    a.cand_cap = kPrefillCandCap;
+    a.indices = indices;
+    a.idx_w = weights;
+    a.idx_qs = q_scale;
+    HS2_TRY(TIMED(KC_STREAM, s, launch_index_stream(a, HI, dI, s)));
     return HS2_OK;
 }
 

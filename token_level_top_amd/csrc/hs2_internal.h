@@ -108,6 +108,10 @@ struct PrefillArgs {
     float* block_scores;    // [B*n_q][block_stride] fp32, or nullptr
     uint64_t* block_keys;   // [B*n_q][block_stride] rank keys (score bits << 32 | ~block)
     int64_t block_stride;
+    // light-indexer form of pass 2: q holds E4M3 codes [B][n_q][H][D], kc the
+    // keys widened to bf16, ks their scales; per (token, head) weight and scale
+    const float* idx_w;     // [B][n_q][H]
+    const float* idx_qs;    // [B][n_q][H]
 };
 hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
                           int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st);
@@ -117,6 +121,10 @@ hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipSt
 // block mode of pass 2: block scores and rank keys of every block up to the
 // last position of each workgroup's tokens
 hipError_t launch_block_score(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+// light indexer: the streaming top-K of pass 2 over indexer scores (index rows)
+hipError_t launch_index_stream(const PrefillArgs& a, int H, int D, hipStream_t st);
+// E4M3 codes [n][d] -> bf16 [n][d] (exact)
+hipError_t launch_widen_fp8(const uint8_t* src, uint16_t* dst, int64_t n_elem, hipStream_t st);
 
 // HySparse v1 block selection and the two-branch sparse layer
 struct BlockArgs {

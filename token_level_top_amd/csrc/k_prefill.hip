@@ -818,7 +818,11 @@ struct ScoreStage {
 template <int B>
 using ic = std::integral_constant<int, B>;
 
-template <int H, int D, int KV>
+// IDX: the light-indexer form (R26 of the design notes): the same streaming
+// top-K over I_t(s) = sum_j w_tj relu(q_tj . k_s) with FP8 queries and keys,
+// the keys pre-widened to bf16 with their scales on the FP8 key-scale path,
+// and a per-row factor w * q_scale in place of the LSE.
+template <int H, int D, int KV, bool IDX>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(score_stream_occupancy<H, D, KV>())))
 void score_stream_kernel(PrefillArgs a) {
     constexpr bool F32 = KV == DT_F32;
@@ -854,17 +858,17 @@ void score_stream_kernel(PrefillArgs a) {
     // Score slot u of the lanes in half `side` belongs to token wtok0 + slot_token(u, side).
     auto slot_token = [](int u, int side) { return H == 16 ? side : (H == 8 ? 2 * side + u : 2 * u + side); };
     // Per slot: the lane's last candidate position minus n (so key j0 + n is a
-    // candidate iff j0 <= cl_n), the score bits of its token's threshold key
-    // (-1: none yet), and the candidate count of each half's token, which is
-    // the same on all lanes.
+    // candidate iff j0 <= cl_n), the rank word of its token's threshold key
+    // minus one (0: none yet; rank words are never 0), and the candidate count
+    // of each half's token, which is the same on all lanes.
     int cl_n[NSC];
-    int thr_hi[NSC];
+    uint32_t thr_k[NSC];
     uint32_t cnt[NSC][2];
 #pragma unroll
     for (int u = 0; u < NSC; ++u) {
         const int64_t tk = wtok0 + slot_token(u, hh);
         cl_n[u] = (tk < a.n_q ? (int)(a.q_pos0 + tk - W) : -1) - n;
-        thr_hi[u] = -1;
+        thr_k[u] = 0;
         cnt[u][0] = cnt[u][1] = 0;
     }
     const size_t row0 = (size_t)b * a.n_q;  // flat token index base
@@ -885,6 +889,12 @@ void score_stream_kernel(PrefillArgs a) {
             const int d0 = KD * s + VPL * hh;
             if constexpr (F32) {
                 qf[s][0] = ok ? reinterpret_cast<const float*>(a.q)[qb + d0] : 0.f;
+            } else if constexpr (IDX) {
+                // 8 E4M3 codes, widened exactly to bf16
+                const u32x2 c8 = ok ? *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + qb + d0)
+                                    : u32x2{0, 0};
+                const u32x2 lo = fp8x4_to_bf16x4(c8[0]), hi = fp8x4_to_bf16x4(c8[1]);
+                *reinterpret_cast<u32x4*>(&qf[s][0]) = u32x4{lo[0], lo[1], hi[0], hi[1]};
             } else {
                 const u32x4 w4 = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qb + d0)
                                     : u32x4{0, 0, 0, 0};
@@ -892,18 +902,26 @@ void score_stream_kernel(PrefillArgs a) {
             }
         }
     }
-    // base-2 LSE of the 16 rows this lane's accumulator holds: m = 8(i/4) + 4hh + i%4
+    // per row this lane's accumulator holds (m = 8(i/4) + 4hh + i%4): the base-2
+    // LSE, or (IDX) the factor w * q_scale of that (token, head)
     float lse_r[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {  // loads first (clamped addresses), selects after
         const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
         const int64_t tk = min<int64_t>(tok0 + R / H, a.n_q - 1);
-        lse_r[i] = a.lse2[((size_t)b * a.n_q + (size_t)tk) * H + (R % H)];
+        const size_t at = ((size_t)b * a.n_q + (size_t)tk) * H + (R % H);
+        if constexpr (IDX)
+            lse_r[i] = a.idx_w[at] * a.idx_qs[at];
+        else
+            lse_r[i] = a.lse2[at];
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int R = 32 * w + 8 * (i >> 2) + 4 * hh + (i & 3);
-        lse_r[i] = tok0 + R / H < a.n_q ? lse_r[i] - kScoreShift : INFINITY;
+        if constexpr (IDX)
+            lse_r[i] = tok0 + R / H < a.n_q ? lse_r[i] : 0.f;
+        else
+            lse_r[i] = tok0 + R / H < a.n_q ? lse_r[i] - kScoreShift : INFINITY;
     }
     const LT* kg = SCALED ? reinterpret_cast<const LT*>(a.kc) + (size_t)b * a.n_ctx * D
                           : reinterpret_cast<const LT*>(a.k) + (size_t)b * a.n_ctx * D;
@@ -947,13 +965,16 @@ void score_stream_kernel(PrefillArgs a) {
     // token scores of one S block, and the appends of keys that beat each
     // token's threshold key (held in pend_*[sub]). Keys arrive in ascending
     // position, so a key whose score bits equal the threshold's loses the tie.
+    // The 32-bit rank word is order-preserving for either sign: bits | 2^31 for
+    // a score >= 0 (every score of the exact form), ~bits below 0 (indexer).
     auto score = [&](const f32x16& sacc, int buf, int sub, int j0) {
         const float c = SCALED ? ks_lds[buf][32 * sub + n] : a.scale_log2;
         // head sums: accumulator i holds row 8(i/4) + 4hh + i%4 of the wave
         float part[4];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float e = fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
+            const float e = IDX ? lse_r[i] * fmaxf(sacc[i], 0.f)
+                                : fast_exp2(__builtin_fmaf(sacc[i], c, -lse_r[i]));
             const int pi = H == 16 ? (i >> 3) : (i >> 2);  // H=16: token i/8; H=8: token i/4; H=4: token 2(i/4)+hh
             part[pi] = (H == 16 ? (i & 7) : (i & 3)) == 0 ? e : part[pi] + e;
         }
@@ -970,8 +991,15 @@ void score_stream_kernel(PrefillArgs a) {
         const int js = j0 + 32 * sub;  // lane n holds key js + n
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
-            const uint32_t sb = __float_as_uint(sc[u]);  // a sum of exponentials: never negative
-            const bool take = (js <= cl_n[u]) & ((int)sb > thr_hi[u]);
+            uint32_t sb;
+            if constexpr (IDX) {
+                const float f = sc[u] * c + 0.f;  // the key's scale; -0 becomes +0
+                const uint32_t bits = __float_as_uint(f);
+                sb = f >= 0.f ? bits | 0x80000000u : ~bits;
+            } else {
+                sb = __float_as_uint(sc[u]) | 0x80000000u;  // a sum of exponentials: never negative
+            }
+            const bool take = (js <= cl_n[u]) & (sb > thr_k[u]);
             const uint64_t m = __ballot(take);
             pend_m[sub][u] = m;
             if (m) {
@@ -1005,7 +1033,7 @@ void score_stream_kernel(PrefillArgs a) {
                     uint32_t kept;
                     const uint64_t cut = trim_candidates(cbuf, cs, kglob, trim_keep, whist[w], &kept);
                     // a later key may still be needed if its score bits reach the cut's
-                    if (hh == side) thr_hi[u] = (int)(uint32_t)(cut >> 32) - 1;
+                    if (hh == side) thr_k[u] = (uint32_t)(cut >> 32) - 1u;
                     cnt[u][side] = __builtin_amdgcn_readfirstlane(kept);
                 }
             }
@@ -1285,7 +1313,7 @@ static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st
                                st, a);
     }
     else if (which == PF_STREAM)
-        hipLaunchKernelGGL((score_stream_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
+        hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false>), grid, dim3(kPfThreads), 0, st, a);
     else
         hipLaunchKernelGGL((block_score_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
     return hipGetLastError();
@@ -1319,6 +1347,24 @@ hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipSt
 }
 hipError_t launch_block_score(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
     return launch_pf_any(a, H, D, kv, PF_BLOCKS, st);
+}
+
+template <int H, int D>
+static hipError_t launch_index_stream_hd(const PrefillArgs& a, hipStream_t st) {
+    constexpr int TB = kPfRows / H;
+    const dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
+    hipLaunchKernelGGL((score_stream_kernel<H, D, DT_FP8, true>), grid, dim3(kPfThreads), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_index_stream(const PrefillArgs& a, int H, int D, hipStream_t st) {
+    if (D == 64) {
+        if (H == 4) return launch_index_stream_hd<4, 64>(a, st);
+        if (H == 8) return launch_index_stream_hd<8, 64>(a, st);
+        return launch_index_stream_hd<16, 64>(a, st);
+    }
+    if (H == 4) return launch_index_stream_hd<4, 128>(a, st);
+    if (H == 8) return launch_index_stream_hd<8, 128>(a, st);
+    return launch_index_stream_hd<16, 128>(a, st);
 }
 
 }  // namespace hs2
