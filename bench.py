@@ -109,7 +109,7 @@ def traffic_record(name: str, workload_name: str):
         return None
 
 
-def cpu_baseline(wl, x, seconds: float, blocks: bool = False):
+def cpu_baseline(wl, x, seconds: float, blocks: bool = False, xi=None):
     import numpy as np
     import oracle
     oracle.lib()
@@ -121,7 +121,12 @@ def cpu_baseline(wl, x, seconds: float, blocks: bool = False):
     t0 = time.perf_counter()
     for r in order:
         r = int(r)
-        if blocks:
+        if xi is not None:
+            ref = oracle.index_select(xi.qi, xi.qs, xi.w, xi.ki, xi.ks, wl.q_pos0, wl.window, wl.k_global, [r])
+            oracle.sparse(x.q.contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["idx"], x.sm_scale, [r])
+            for l in range(wl.n_sparse):
+                oracle.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, ref["idx"], x.sm_scale, [r])
+        elif blocks:
             kb = wl.k_global // 64
             ref = oracle.block_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, 64, kb, x.sm_scale, [r])
             for l in range(wl.n_sparse):
@@ -258,6 +263,11 @@ def main():
     ap.add_argument("--hysparse-blocks", action="store_true",
                     help="prefill workloads: the HySparse v1 block-level variant (64-token blocks, top 16, gated "
                          "128-token window branch) in place of token-level selection")
+    ap.add_argument("--indexer", action="store_true",
+                    help="prefill workloads: light-indexer selection (FP8 heads, see --indexer-*) in place of the full "
+                         "layer, its index rows shared IndexCache-style by 1 + n_sparse sparse layers")
+    ap.add_argument("--indexer-heads", type=int, default=8, help="indexer heads (4, 8 or 16)")
+    ap.add_argument("--indexer-dim", type=int, default=64, help="indexer head dimension (64 or 128)")
     ap.add_argument("--kv-project", choices=["bf16", "fp8"], default=None,
                     help="instead of the attention path, time the KV Bridging projections with this cache type")
     args = ap.parse_args()
@@ -269,14 +279,15 @@ def main():
     if args.kv_project:
         return bench_kv_project(args, args.kv_project)
     blocks = args.hysparse_blocks
+    indexer = args.indexer
 
     import torch
     import token_level_top_amd as hs2
-    from hs2_inputs import make_gates, make_inputs, workload
+    from hs2_inputs import make_gates, make_indexer_inputs, make_inputs, workload
 
     wl = workload(args.config)
-    if blocks and wl.decode:
-        print("--hysparse-blocks applies to the prefill workloads (1, 2, 4)", file=sys.stderr)
+    if (blocks or indexer) and wl.decode:
+        print("--hysparse-blocks and --indexer apply to the prefill workloads (1, 2, 4)", file=sys.stderr)
         return 2
     log(f"workload {wl.name}: generating inputs on the host")
     t0 = time.perf_counter()
@@ -301,6 +312,23 @@ def main():
         def step():
             hs2.decode_step(qf, qs, k, v, ks, vs, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale,
                             workspace=ws, **bufs)
+    elif indexer:
+        HI, DI = args.indexer_heads, args.indexer_dim
+        xi = make_indexer_inputs(2026, wl.B, wl.n_q, wl.q_pos0, wl.n_ctx, HI, DI, n_needles=16)
+        qi, qsc, qw, ki, ksc = (g(t) for t in (xi.qi, xi.qs, xi.w, xi.ki, xi.ks))
+        ws_i = torch.empty(hs2.workspace_size(hs2.OP_INDEX_SELECT, wl.B, wl.n_q, wl.n_ctx, 0, DI, 0, 0, 0),
+                           dtype=torch.uint8, device=dev)
+        qs_all = g(torch.cat([x.q.unsqueeze(0), x.q_sparse], 0))    # the F layer's queries, then the S layers'
+        nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
+        ws_sp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        idx = torch.empty((wl.B, wl.n_q, S), dtype=torch.int32, device=dev)
+        out_s = torch.empty_like(qs_all)
+
+        def step():
+            hs2.index_select(qi, qsc, qw, ki, ksc, q_pos0=wl.q_pos0, window=wl.window, k_global=wl.k_global,
+                             indices=idx, workspace=ws_i)
+            hs2.sparse_attn(qs_all, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, want_lse=False,
+                            workspace=ws_sp)
     elif blocks:
         KB = wl.k_global // hs2.BLOCK
         q = g(x.q)
@@ -361,6 +389,9 @@ def main():
     read_timing()
 
     dom, bound, units, unit = dominant(wl)
+    if indexer:  # the indexer pass: 2 * HI * dI flops per candidate pair, on the bf16 matrix cores
+        cand = sum(max(0, wl.q_pos0 + i - wl.window + 1) for i in range(wl.n_q)) * wl.B
+        dom, bound, units, unit = "score_stream", "mfma", 2 * args.indexer_heads * args.indexer_dim * cand, "TFLOP/s"
     L.hs2_timing_enable(1 << KC[dom])
     log(f"timing {args.steps} steps")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -388,13 +419,23 @@ def main():
             "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),
             "algorithmic_per_launch": units}
     t_roof = path_roofline_seconds(wl, blocks)
-    metric = METRIC if not blocks else ("query tok/s, HySparse v1 block variant: full attn + 64-token block "
-                                        "top-16 + gated 128-token window branch")
+    if indexer:
+        peak_b = MFMA_PEAK_TFLOPS["bf16"] * 1e12
+        sel = sum(min(wl.q_pos0 + i + 1, S) for i in range(wl.n_q)) * wl.B
+        t_roof = units / peak_b + (1 + wl.n_sparse) * 4 * wl.d * wl.H * sel / peak_b
+    metric = METRIC
+    if blocks:
+        metric = ("query tok/s, HySparse v1 block variant: full attn + 64-token block top-16 + gated 128-token "
+                  "window branch")
+    if indexer:
+        metric = (f"query tok/s, light-indexer selection ({args.indexer_heads} FP8 heads x {args.indexer_dim}) + "
+                  "IndexCache F + S x n_sparse sparse layers")
     res = {"metric": metric, "value": round(value, 2), "unit": "query tok/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
-           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else ""), "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
+           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else ""),
+                      "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,
@@ -410,7 +451,7 @@ def main():
         res["breakdown_ms_per_step"] = {names[c]: round(ms[c] / 3, 4) for c in range(16) if n[c]}
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, blocks)
+        res["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, blocks, xi if indexer else None)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
