@@ -260,6 +260,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (extra steps)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB twice (reference for HBM counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as replays of one captured HIP graph (the kernels and their order are the "
+                         "same; launch gaps go away); the per-kernel roofline timing stays eager")
     ap.add_argument("--hysparse-blocks", action="store_true",
                     help="prefill workloads: the HySparse v1 block-level variant (64-token blocks, top 16, gated "
                          "128-token window branch) in place of token-level selection")
@@ -404,6 +407,27 @@ def main():
     L.hs2_timing_enable(0)
     ms_total = e0.elapsed_time(e1)
     ms, n = read_timing()
+    ms_eager = ms_total / args.steps
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        log(f"timing {args.steps} graph replays")
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
     tokens = wl.B * wl.n_q
     value = tokens * args.steps / (ms_total / 1e3)
@@ -439,7 +463,10 @@ def main():
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,
-           "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)}}
+           "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)},
+           "launch": "hip_graph" if args.graph else "eager"}
+    if args.graph:
+        res["eager_ms_per_step"] = round(ms_eager, 4)
     if args.breakdown:
         L.hs2_timing_enable(0xFFFF if blocks else 0xFFF)
         for _ in range(3):
