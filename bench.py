@@ -58,19 +58,21 @@ def causal_pairs(wl) -> int:
     return wl.B * (n * p0 + n * (n + 1) // 2)
 
 
-def path_roofline_seconds(wl, blocks: bool = False) -> float:
+def path_roofline_seconds(wl, blocks: bool = False, h_full: int = 0) -> float:
     """Lower bound on one step from the method's algorithmic work (HBM or MFMA).
     blocks: the HySparse v1 variant, whose two branches attend to min(p+1, W)
-    and min(p+1, K) rows."""
+    and min(p+1, K) rows. h_full: query heads of the full layer when it has
+    fewer than the sparse layers (0: the same)."""
+    hf = h_full or wl.H
     b = kv_bytes(wl.kv_dtype)
     sb = 4 if wl.kv_dtype == "fp8" else 0
     S = wl.window + wl.k_global
     if wl.decode:
-        full = wl.B * wl.n_ctx * (2 * (wl.d * b + sb) + 2 * wl.H * 4 + 8) / (HBM_PEAK_GBS * 1e9)
+        full = wl.B * wl.n_ctx * (2 * (wl.d * b + sb) + 2 * hf * 4 + 8) / (HBM_PEAK_GBS * 1e9)
         sparse = wl.n_sparse * wl.B * S * 2 * (wl.d * b + sb) / (HBM_PEAK_GBS * 1e9)
         return full + sparse
     peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"] * 1e12
-    full = 6 * wl.d * wl.H * causal_pairs(wl) / peak
+    full = 6 * wl.d * hf * causal_pairs(wl) / peak
     # every query attends to min(p+1, S) selected rows in each sparse layer
     if blocks:
         sel = sum(min(wl.q_pos0 + i + 1, wl.window) + min(wl.q_pos0 + i + 1, wl.k_global)
@@ -263,6 +265,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of one captured HIP graph (the kernels and their order are the "
                          "same; launch gaps go away); the per-kernel roofline timing stays eager")
+    ap.add_argument("--full-heads", type=int, default=0,
+                    help="query heads of the full layer (4 or 8) when fewer than the sparse layers' 16 (asymmetric "
+                         "heads); 0: the same")
     ap.add_argument("--hysparse-blocks", action="store_true",
                     help="prefill workloads: the HySparse v1 block-level variant (64-token blocks, top 16, gated "
                          "128-token window branch) in place of token-level selection")
@@ -303,7 +308,29 @@ def main():
     kvdt = {"f32": hs2.HS2_F32, "bf16": hs2.HS2_BF16, "fp8": hs2.HS2_FP8_E4M3}[wl.kv_dtype]
     S = wl.window + wl.k_global
 
-    if wl.decode:
+    hf = args.full_heads or wl.H
+    if args.full_heads and (blocks or indexer):
+        print("--full-heads combines with the token-level path only", file=sys.stderr)
+        return 2
+    if wl.decode and args.full_heads:
+        qf = g(x.q[:, 0, :hf])
+        qs = g(x.q_sparse)                                   # [L][B][1][H][d]
+        ws = torch.empty(hs2.workspace_size(hs2.OP_DECODE_STEP, wl.B, 1, wl.n_ctx, hf, wl.d, wl.window,
+                                            wl.k_global, kvdt), dtype=torch.uint8, device=dev)
+        nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, 1, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
+        ws_sp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        bufs = dict(out_full=torch.empty_like(qf), lse_full=torch.empty((wl.B, hf), device=dev),
+                    indices=torch.empty((wl.B, S), dtype=torch.int32, device=dev))
+        idx3 = bufs["indices"].view(wl.B, 1, S)
+        out_s = torch.empty_like(qs)
+        lse_s = torch.empty((wl.n_sparse, wl.B, 1, wl.H), device=dev)
+
+        def step():
+            hs2.decode_step(qf, None, k, v, ks, vs, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale,
+                            workspace=ws, **bufs)
+            hs2.sparse_attn(qs, k, v, ks, vs, indices=idx3, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
+                            workspace=ws_sp)
+    elif wl.decode:
         qf = g(x.q[:, 0])
         qs = g(x.q_sparse[:, :, 0])
         ws = torch.empty(hs2.workspace_size(hs2.OP_DECODE_STEP, wl.B, 1, wl.n_ctx, wl.H, wl.d, wl.window,
@@ -352,14 +379,14 @@ def main():
             hs2.block_sparse_attn(qs, k, v, ks, vs, block_idx=bidx, q_pos0=wl.q_pos0, window=wl.window, gates=gates,
                                   sm_scale=x.sm_scale, out=out_s, workspace=ws_sp)
     else:
-        q = g(x.q)
+        q = g(x.q[:, :, :hf])
         qs = g(x.q_sparse)
-        ws_full = torch.empty(hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d,
+        ws_full = torch.empty(hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, wl.B, wl.n_q, wl.n_ctx, hf, wl.d,
                                                  wl.window, wl.k_global, kvdt), dtype=torch.uint8, device=dev)
         nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
         ws_sp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         out = torch.empty_like(q)
-        lse = torch.empty((wl.B, wl.n_q, wl.H), device=dev)
+        lse = torch.empty((wl.B, wl.n_q, hf), device=dev)
         idx = torch.empty((wl.B, wl.n_q, S), dtype=torch.int32, device=dev)
         out_s = torch.empty_like(qs)
         lse_s = torch.empty((wl.n_sparse, wl.B, wl.n_q, wl.H), device=dev)
@@ -391,7 +418,7 @@ def main():
     torch.cuda.synchronize()
     read_timing()
 
-    dom, bound, units, unit = dominant(wl)
+    dom, bound, units, unit = dominant(wl.with_(H=hf))
     if indexer:  # the indexer pass: 2 * HI * dI flops per candidate pair, on the bf16 matrix cores
         cand = sum(max(0, wl.q_pos0 + i - wl.window + 1) for i in range(wl.n_q)) * wl.B
         dom, bound, units, unit = "score_stream", "mfma", 2 * args.indexer_heads * args.indexer_dim * cand, "TFLOP/s"
@@ -442,7 +469,7 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
             "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),
             "algorithmic_per_launch": units}
-    t_roof = path_roofline_seconds(wl, blocks)
+    t_roof = path_roofline_seconds(wl, blocks, args.full_heads)
     if indexer:
         peak_b = MFMA_PEAK_TFLOPS["bf16"] * 1e12
         sel = sum(min(wl.q_pos0 + i + 1, S) for i in range(wl.n_q)) * wl.B
@@ -458,8 +485,9 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
-           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else ""),
-                      "B": wl.B, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
+           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else "")
+                      + (f"_full_heads{hf}" if args.full_heads else ""),
+                      "B": wl.B, "H_full": hf, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,

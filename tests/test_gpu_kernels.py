@@ -288,3 +288,40 @@ def test_sparse_attn_beyond_65535_tokens(hs2, orc):
     ref = orc.sparse(q[0].contiguous(), k, v, None, None, idx[0, rows].numpy(), 0.125, rows)
     rows_close(out[0, 0, rows], ref["out"], RTOL["f32"], "sparse out")
     lse_close(lse[0, 0, rows], ref["lse"], RTOL["f32"])
+
+
+@pytest.mark.parametrize("cfg,B,n_q,q_pos0,n_ctx,h_full", [
+    (2, 1, 300, 700, 1000, 4),      # prefill: 4 full-layer heads, 16 sparse-layer heads
+    (4, 1, 64, 3000, 3064, 8),      # FP8 cache, 8 full-layer heads
+    (3, 4, 1, 9999, 10000, 4),      # decode: decode step without sparse layers, then 16-head sparse layers
+])
+def test_asymmetric_heads_compose(hs2, orc, cfg, B, n_q, q_pos0, n_ctx, h_full):
+    """Fewer query heads in the full layer than in the sparse layers (the
+    HySparse2 page's future-work direction): the index rows of an h_full-head
+    full layer drive 16-head sparse layers."""
+    wl = workload(cfg).with_(B=B, n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, n_needles=2, n_sparse=2)
+    x = make_inputs(wl)
+    say("asymmetric heads", wl.name, B, n_q, q_pos0, n_ctx, h_full)
+    qf = x.q[:, :, :h_full].contiguous()
+    kv = (dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale))
+    if wl.decode:
+        r = hs2.decode_step(dev(qf[:, 0]), None, *kv, window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale)
+        idx = r["indices"].reshape(B, 1, -1)
+        out_f = r["out_full"].reshape(B, 1, h_full, wl.d)
+    else:
+        out_f, _, idx = hs2.full_attn_select(dev(qf), *kv, q_pos0=q_pos0, window=wl.window, k_global=wl.k_global,
+                                             sm_scale=x.sm_scale)
+    so, sl = hs2.sparse_attn(dev(x.q_sparse), *kv, indices=idx, sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    rows = list(range(B * n_q))
+    ref = orc.full_select(qf, x.k, x.v, x.k_scale, x.v_scale, q_pos0, wl.window, wl.k_global, x.sm_scale, rows,
+                          want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    rows_close(out_f.reshape(B * n_q, h_full, wl.d), ref["out"], tol, "full out")
+    g = idx.reshape(B * n_q, -1)
+    check_index_rows(g, ref["idx"], ref["scores"], ref["kth"], wl.window)
+    gi = to_np(g).astype(np.int32)
+    for l in range(2):
+        s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gi, x.sm_scale, rows)
+        rows_close(so[l].reshape(B * n_q, wl.H, wl.d), s["out"], tol, f"sparse out {l}")
+        lse_close(sl[l].reshape(B * n_q, wl.H), s["lse"], tol)
