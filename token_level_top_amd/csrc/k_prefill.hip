@@ -818,11 +818,20 @@ struct ScoreStage {
 template <int B>
 using ic = std::integral_constant<int, B>;
 
+// Threshold histograms of the streaming top-K: per token, 64 bins of the
+// 32-bit rank word (8 per octave of a score: the word shifted right by 20),
+// anchored 2 octaves below the token's latest trim cut.
+constexpr int kThrBins = 64;
+constexpr int kThrShift = 20;
+constexpr int kThrBelow = 16;
+
 // IDX: the light-indexer form (R26 of the design notes): the same streaming
 // top-K over I_t(s) = sum_j w_tj relu(q_tj . k_s) with FP8 queries and keys,
 // the keys pre-widened to bf16 with their scales on the FP8 key-scale path,
 // and a per-row factor w * q_scale in place of the LSE.
-template <int H, int D, int KV, bool IDX>
+// HIST: the streaming top-K also raises thresholds between trims from per-token
+// histograms (chosen by the launcher where it pays, see launch_score_stream).
+template <int H, int D, int KV, bool IDX, bool HIST>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(score_stream_occupancy<H, D, KV>())))
 void score_stream_kernel(PrefillArgs a) {
     constexpr bool F32 = KV == DT_F32;
@@ -835,11 +844,13 @@ void score_stream_kernel(PrefillArgs a) {
     constexpr int TB = kPfRows / H;   // tokens per workgroup
     constexpr int TW = 32 / H;        // tokens per wave
     constexpr int NSC = 16 / H;       // scores per lane per 32-key block
+    constexpr bool THR_HIST = HIST;
     static_assert(kPfBufs == 3, "the tile loop is unrolled over the three LDS buffers");
 
     __shared__ __attribute__((aligned(16))) LT k_lds[kPfBufs][kPfTile * KLD];
     __shared__ __attribute__((aligned(16))) float ks_lds[kPfBufs][kPfTile];  // FP8: k_scale * log2(e) * sm_scale
     __shared__ uint32_t whist[kPfWaves][kCompactScratchMem];
+    __shared__ uint32_t thist[kPfWaves][THR_HIST ? TW : 1][kThrBins];  // threshold histograms, one per token
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave addresses scalar
@@ -861,15 +872,23 @@ void score_stream_kernel(PrefillArgs a) {
     // candidate iff j0 <= cl_n), the rank word of its token's threshold key
     // minus one (0: none yet; rank words are never 0), and the candidate count
     // of each half's token, which is the same on all lanes.
+    // The threshold also rises between trims: tbase (per half's token, the same
+    // on all lanes; -1 until its first trim) anchors a histogram, rebuilt at
+    // every trim from the kept candidates and then fed by every append, so it
+    // counts exactly the candidates in the buffer. When at least k_global of
+    // them have rank words >= a bin's lower edge, no key below that edge can be
+    // among the token's top k_global, so the threshold moves up to the edge.
     int cl_n[NSC];
     uint32_t thr_k[NSC];
     uint32_t cnt[NSC][2];
+    int tbase[NSC][2];
 #pragma unroll
     for (int u = 0; u < NSC; ++u) {
         const int64_t tk = wtok0 + slot_token(u, hh);
         cl_n[u] = (tk < a.n_q ? (int)(a.q_pos0 + tk - W) : -1) - n;
         thr_k[u] = 0;
         cnt[u][0] = cnt[u][1] = 0;
+        tbase[u][0] = tbase[u][1] = -1;
     }
     const size_t row0 = (size_t)b * a.n_q;  // flat token index base
     const int cap = a.cand_cap;
@@ -1013,6 +1032,12 @@ void score_stream_kernel(PrefillArgs a) {
                 pend_hi[sub][u] = sb;
                 cnt[u][0] += plo;
                 cnt[u][1] += __popc(mhi);
+                const int tb = hh ? tbase[u][1] : tbase[u][0];
+                if (THR_HIST && take && tb >= 0) {  // tb stays -1 unless use_hist
+                    const int bin = min(max((int)(sb >> kThrShift) - tb, 0), kThrBins - 1);
+                    __hip_atomic_fetch_add(&thist[w][slot_token(u, hh)][bin], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WAVEFRONT);
+                }
             }
         }
     };
@@ -1020,7 +1045,11 @@ void score_stream_kernel(PrefillArgs a) {
     // they make no calls): a tile appends at most 64 keys per token, so any
     // buffer that could overflow within the next `tiles` tiles is trimmed
     // first, to a superset of its top k_global.
+    // the threshold rises every 4th room check (every 768 keys)
+    const bool use_hist = THR_HIST;
+    int room_checks = 0;
     auto make_room = [&](int tiles) {
+        const bool raise = use_hist && (room_checks++ & 3) == 0;
 #pragma unroll
         for (int u = 0; u < NSC; ++u) {
 #pragma unroll
@@ -1033,8 +1062,41 @@ void score_stream_kernel(PrefillArgs a) {
                     uint32_t kept;
                     const uint64_t cut = trim_candidates(cbuf, cs, kglob, trim_keep, whist[w], &kept);
                     // a later key may still be needed if its score bits reach the cut's
-                    if (hh == side) thr_k[u] = (uint32_t)(cut >> 32) - 1u;
+                    if (hh == side) thr_k[u] = max(thr_k[u], (uint32_t)(cut >> 32) - 1u);
                     cnt[u][side] = __builtin_amdgcn_readfirstlane(kept);
+                    if (use_hist) {
+                        // (re)anchor the histogram at this cut and count the kept keys
+                        const int base = (int)((uint32_t)(cut >> 32) >> kThrShift) - kThrBelow;
+                        tbase[u][side] = base;
+                        uint32_t* h = thist[w][slot_token(u, side)];
+                        h[lane] = 0;
+                        __builtin_amdgcn_wave_barrier();
+                        for (uint32_t i = (uint32_t)lane; i < cnt[u][side]; i += 64u) {
+                            const uint32_t hi = (uint32_t)(cbuf[i] >> 32);
+                            const int bin = min(max((int)(hi >> kThrShift) - base, 0), kThrBins - 1);
+                            __hip_atomic_fetch_add(&h[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                        }
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                }
+                if (raise && tbase[u][side] >= 0) {
+                    // raise the threshold to the highest bin edge with k_global
+                    // candidates at or above it (bin 0 also holds keys below its
+                    // edge, and an edge must fit the 32-bit rank word)
+                    const int tb = tbase[u][side];
+                    uint32_t v = thist[w][slot_token(u, side)][lane];
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const uint32_t o = __shfl_down(v, off);
+                        if (lane + off < 64) v += o;
+                    }
+                    const int e = tb + lane;
+                    const uint64_t ok = __ballot(v >= kglob && lane >= 1 && e >= 1 && e < (1 << (32 - kThrShift)));
+                    if (ok) {
+                        const int bb = 63 - __clzll((long long)ok);
+                        const uint32_t edge = (uint32_t)(tb + bb) << kThrShift;
+                        if (hh == side && edge - 1u > thr_k[u]) thr_k[u] = edge - 1u;
+                    }
                 }
             }
         }
@@ -1299,6 +1361,11 @@ void block_score_kernel(PrefillArgs a) {
 #define HS2_PF_PIPE true
 #endif
 enum PfKernel { PF_FWD, PF_STREAM, PF_BLOCKS };
+// Threshold histograms in the streaming top-K (measured): the pass at 32 Ki keys
+// per row drops 11-14 % with fewer than 16 heads or in the indexer form, while on
+// 256 Ki rows it costs more than it saves, and the 16-head forms (4 waves per
+// SIMD in 128 registers) spill with it. Used where no row has 64 Ki candidates.
+static bool hist_pays(const PrefillArgs& a) { return a.q_pos0 + a.n_q - a.window < 65536; }
 template <int H, int D, int KV>
 static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st) {
     constexpr int TB = kPfRows / H;
@@ -1312,8 +1379,16 @@ static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st
                                dim3((unsigned)((a.n_q + kFwdTB - 1) / kFwdTB), (unsigned)a.B), dim3(64 * HS2_PF_NW), 0,
                                st, a);
     }
-    else if (which == PF_STREAM)
-        hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false>), grid, dim3(kPfThreads), 0, st, a);
+    else if (which == PF_STREAM) {
+        if constexpr (H < 16) {
+            if (hist_pays(a))
+                hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, true>), grid, dim3(kPfThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, false>), grid, dim3(kPfThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, false>), grid, dim3(kPfThreads), 0, st, a);
+        }
+    }
     else
         hipLaunchKernelGGL((block_score_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
     return hipGetLastError();
@@ -1353,7 +1428,10 @@ template <int H, int D>
 static hipError_t launch_index_stream_hd(const PrefillArgs& a, hipStream_t st) {
     constexpr int TB = kPfRows / H;
     const dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
-    hipLaunchKernelGGL((score_stream_kernel<H, D, DT_FP8, true>), grid, dim3(kPfThreads), 0, st, a);
+    if (hist_pays(a))
+        hipLaunchKernelGGL((score_stream_kernel<H, D, DT_FP8, true, true>), grid, dim3(kPfThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((score_stream_kernel<H, D, DT_FP8, true, false>), grid, dim3(kPfThreads), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_index_stream(const PrefillArgs& a, int H, int D, hipStream_t st) {
