@@ -114,6 +114,7 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
     w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * kHistBins);
+    // directly after hist, so that one fill clears both
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * 2);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
     const int ss = sparse_splits(B, window + k_global);
@@ -144,6 +145,7 @@ SelectWs select_ws(void* base, int64_t rows, int64_t row_len) {
     Carver c(base);
     SelectWs w;
     w.hist = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * kHistBins);
+    // directly after hist, so that one fill clears both
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * 2);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)rows * kCandCap);
     w.bytes = c.used;
@@ -626,9 +628,9 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     a.out = out;
     a.out_stride = k;
     a.out_offset = 0;
-    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, rows * kHistBins, 0u, s)));
+    // histogram and candidate counters (adjacent in the workspace) start at zero
+    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, (w.thr + 2 * rows) - w.hist, 0u, s)));
     HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_hist(a, s)));
-    HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(a, s)));
     HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(a, s)));
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final(a, s)));
     return HS2_OK;
@@ -684,6 +686,9 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_rows_attn(a, H, d, kv_dtype, false, true, s)));
     else
         HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_decode_split(a, H, d, kv_dtype, s)));
+    // the score histogram and the candidate counters (adjacent in the
+    // workspace) start at zero: cleared by the combine kernel, else a fill
+    const int64_t n_zero = (w.thr + 2 * B) - w.hist;
     if (ns > 1) {
         CombineArgs c{};
         c.part = w.part;
@@ -692,12 +697,15 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         c.out = out_full;
         c.lse = lse_full;
         c.lse2 = w.lse2;
+        c.zero = w.hist;
+        c.n_zero = n_zero;
         HS2_TRY(TIMED(KC_COMBINE, s, launch_combine(c, H, d, q_dtype, s)));
+    } else {
+        HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, n_zero, 0u, s)));
     }
-    // 2. token scores + histogram of the candidates j <= n_ctx-1-window (+ threshold bin)
+    // 2. token scores + histogram of the candidates j <= n_ctx-1-window
     const int64_t n_cand = n_ctx - window > 0 ? n_ctx - window : 0;
     float* sc = scores ? scores : w.scores;
-    HS2_TRY(TIMED(KC_FILL, s, launch_fill_u32(w.hist, (int64_t)B * kHistBins, 0u, s)));
     ScoreArgs sa{};
     sa.logits = w.logits;
     sa.lse2 = w.lse2;
@@ -720,10 +728,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     se.out = indices;
     se.out_stride = n_sel;
     se.out_offset = window;
-    if (k_global > 0 && n_cand > 0) {
-        HS2_TRY(TIMED(KC_SEL_HIST, s, launch_select_threshold(se, s)));
-        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
-    }
+    if (k_global > 0 && n_cand > 0) HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     // 4. sparse layers reuse the indices and the cache
     if (n_sparse > 0)

@@ -35,6 +35,8 @@ struct CombineArgs {
     void* out;              // [n_tok][H][D]
     float* lse;             // nullable, natural log
     float* lse2;            // nullable, base 2
+    uint32_t* zero;         // nullable: n_zero words the kernel also clears (a later kernel's counters)
+    int64_t n_zero;
 };
 
 hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather, bool store_logits,
@@ -69,7 +71,7 @@ struct SelectArgs {
     const int32_t* n_cand;  // [rows] or nullptr
     int k;
     uint32_t* hist;         // [rows][kHistBins]
-    uint32_t* thr;          // [rows][2] threshold bin, candidate count
+    uint32_t* thr;          // [rows][2] (unused, candidate count); zeroed with hist
     uint64_t* cand;         // [rows][kCandCap] candidate rank keys (unordered)
     int32_t* out;           // [rows][out_stride]
     int64_t out_stride;
@@ -77,9 +79,8 @@ struct SelectArgs {
 };
 // hist zeroed; fills hist
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);
-// thr from the complete hist
-hipError_t launch_select_threshold(const SelectArgs& a, hipStream_t st);
-// candidates (scores in the threshold bin or above) appended to cand, counted in thr[2r+1]
+// from the complete hist, the candidates (scores in the bin of the k-th largest
+// or above) appended to cand and counted in thr[2r+1] (zeroed beforehand)
 hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st);
 hipError_t launch_select_final(const SelectArgs& a, hipStream_t st);
 // also writes the forced window of every row (all rows at position p_last) when window > 0

@@ -378,53 +378,88 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     }
 }
 
-// Merge split partials (m, l, O per head, base-2) into O, LSE.
-// Grid (token, head, d/32); a block is 32 output columns x 8 groups of splits,
-// so even hundreds of splits are read with 8-way parallelism per column.
+// Merge split partials (m, l, O per head, base-2) into O, LSE; the blocks also
+// clear a.zero[0, n_zero) when given (counters of a later kernel, saving a
+// fill launch). A thread owns
+// one quad of 4 output columns of the token's (head, d) row and folds splits
+// into a running (m, l, O), one 16-byte load of O per split.
+//  * G = 1 (few splits): 256 quads per block, every thread folds all splits;
+//    grid (token, ceil(H*D / 1024)).
+//  * G = 32 (many splits): 8 quads x 32 groups of splits per block, a thread
+//    folds every 32nd split, so hundreds of splits are read in a few rounds;
+//    the groups are merged by shuffles within each wave and through LDS
+//    across the waves; grid (token, H*D / 32).
 constexpr int kCombThreads = 256;
-template <int H, int D, int QT>
+constexpr int kCombFewSplits = 16;  // at most this many splits: G = 1
+__device__ __forceinline__ void merge_part(float& m, float& l, f32x4& o, float mb, float lb, const f32x4& ob) {
+    const float mn = fmaxf(m, mb);
+    const float fa = fast_exp2(m - mn), fb = fast_exp2(mb - mn);
+    l = l * fa + lb * fb;
+    o = o * fa + ob * fb;
+    m = mn;
+}
+template <int H, int D, int QT, int G>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
-    __shared__ float red_m[kCombThreads / 64];
-    __shared__ float red_o[8][32], red_l[8][32];
-    const int tok = blockIdx.x, h = blockIdx.y, d0 = 32 * blockIdx.z;
-    const int tid = threadIdx.x, dl = tid & 31, gs = tid >> 5;
+    constexpr int NW = kCombThreads / 64, Q = kCombThreads / G;
+    static_assert(G == 1 || G == 32, "group layouts");
+    const int tok = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (a.zero) {
+        const int64_t nthr = (int64_t)gridDim.x * gridDim.y * kCombThreads;
+        for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + tok) * kCombThreads + tid; i < a.n_zero; i += nthr)
+            a.zero[i] = 0u;
+    }
+    const int qi = tid % Q, gs = tid / Q;
+    const int col = 4 * (Q * (int)blockIdx.y + qi);  // first column of the quad in the (head, d) row
+    if (G == 1 && col >= H * D) return;               // whole waves (H * D is a multiple of 256)
+    const int h = col / D;
     const size_t rec = (size_t)H * (D + 2);
     const float* base = a.part + (size_t)tok * a.n_split * rec;
-    float mm = kNegBig;
-    for (int s = tid; s < a.n_split; s += kCombThreads) mm = fmaxf(mm, base[(size_t)s * rec + h]);
-    mm = wave_max(mm);
-    if ((tid & 63) == 0) red_m[tid >> 6] = mm;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kCombThreads / 64; ++w) mm = fmaxf(mm, red_m[w]);
-    float ll = 0.f, oo = 0.f;
+    // m starts finite (kNegBig): empty splits carry m = kNegBig, l = 0, O = 0
+    float m = kNegBig, l = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int s = gs; s < a.n_split; s += 8) {
+    for (int s = gs; s < a.n_split; s += G) {
         const float* r = base + (size_t)s * rec;
-        const float f = fast_exp2(r[h] - mm);
-        ll += r[H + h] * f;
-        oo += r[2 * H + h * D + d0 + dl] * f;
+        merge_part(m, l, o, r[h], r[H + h], *reinterpret_cast<const f32x4*>(r + 2 * H + col));
     }
-    red_o[gs][dl] = oo;
-    red_l[gs][dl] = ll;
-    __syncthreads();
-    if (gs == 0) {
+    if constexpr (G > 1) {
+        __shared__ f32x4 red_o[NW][Q];
+        __shared__ float red_m[NW], red_l[NW];
+        // lanes qi + Q g of a wave hold the same column quad
 #pragma unroll
-        for (int q = 1; q < 8; ++q) {
-            oo += red_o[q][dl];
-            ll += red_l[q][dl];
+        for (int off = Q; off < 64; off <<= 1) {
+            f32x4 ob;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[e] = __shfl_xor(o[e], off);
+            merge_part(m, l, o, __shfl_xor(m, off), __shfl_xor(l, off), ob);
         }
-        const float o = ll > 0.f ? oo / ll : 0.f;
-        const size_t oi = ((size_t)tok * H + h) * D + d0 + dl;
-        if constexpr (QT == DT_F32)
-            reinterpret_cast<float*>(a.out)[oi] = o;
-        else
-            reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_bits(o);
-        if (d0 == 0 && dl == 0) {
-            const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
-            if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
-            if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
+        if (lane < Q) red_o[w][lane] = o;
+        if (lane == 0) {
+            red_m[w] = m;
+            red_l[w] = l;
         }
+        __syncthreads();
+        if (tid >= Q) return;
+        m = red_m[0];
+        l = red_l[0];
+        o = red_o[0][tid];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) merge_part(m, l, o, red_m[q], red_l[q], red_o[q][tid]);
+    }
+    const size_t oi = (size_t)tok * H * D + col;
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = l > 0.f ? o[e] / l : 0.f;
+    if constexpr (QT == DT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = r;
+    } else {
+        const u32x2 b{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = b;
+    }
+    if (col % D == 0) {
+        const float lse2 = l > 0.f ? m + log2f(l) : -INFINITY;
+        if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
+        if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
     }
 }
 
@@ -463,14 +498,20 @@ hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather
     return launch_rows_hd<16, 128>(a, kv, gather, store_logits, st);
 }
 
+template <int H, int D, int G>
+static hipError_t launch_combine_hdg(const CombineArgs& a, int qt, hipStream_t st) {
+    constexpr int cols_per_block = 4 * (kCombThreads / G);
+    const dim3 grid((unsigned)a.n_tok, (unsigned)((H * D + cols_per_block - 1) / cols_per_block));
+    if (qt == DT_F32)
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32, G>), grid, dim3(kCombThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16, G>), grid, dim3(kCombThreads), 0, st, a);
+    return hipGetLastError();
+}
 template <int H, int D>
 static hipError_t launch_combine_hd(const CombineArgs& a, int qt, hipStream_t st) {
-    const dim3 grid((unsigned)a.n_tok, (unsigned)H, (unsigned)(D / 32));
-    if (qt == DT_F32)
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_F32>), grid, dim3(kCombThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((combine_kernel<H, D, DT_BF16>), grid, dim3(kCombThreads), 0, st, a);
-    return hipGetLastError();
+    if (a.n_split <= kCombFewSplits) return launch_combine_hdg<H, D, 1>(a, qt, st);
+    return launch_combine_hdg<H, D, 32>(a, qt, st);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_t st) {

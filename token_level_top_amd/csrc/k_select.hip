@@ -11,13 +11,15 @@
 //
 // Selection over a row of non-negative fp32 scores:
 //  1. histogram of the top 12 bits (8 exponent + 4 mantissa bits): many
-//     workgroups per row, LDS histograms merged with global atomics; then one
-//     workgroup per row finds the bin holding the k-th largest score;
-//  2. collect: many workgroups per row append the rank keys of the scores in
-//     that bin or above to the row's candidate list (one atomic per wave and
-//     64 scores; the list is unordered);
+//     workgroups per row, LDS histograms merged with global atomics (the
+//     histogram and the candidate counters start zeroed);
+//  2. collect: many workgroups per row each find the bin holding the k-th
+//     largest score from the histogram and append the rank keys of the scores
+//     in that bin or above to the row's candidate list (each workgroup reads
+//     its chunk once into registers and reserves room with one atomic; the
+//     list is unordered);
 //  3. final: one 1024-thread workgroup per row loads the candidates into LDS,
-//     finds the exact k-th largest key by 4-bit digit passes (per-wave LDS
+//     finds the exact k-th largest key by 8-bit digit passes (per-wave LDS
 //     histograms), gathers the positions of the keys at or above it and sorts
 //     them ascending (bitonic, in LDS). Rows whose candidates overflow the list
 //     fall back to an exact multi-pass radix select over the whole row.
@@ -57,81 +59,50 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h_lds, uint32_t* h_gl
     }
 }
 
-// Threshold bin: the largest b with (count of bins >= b) >= kk. Returns b and the
-// count of bins strictly above it. Called by all threads of a 256-thread block.
-__device__ void threshold_bin(const uint32_t* hist_glob, uint32_t kk, uint32_t* sh_scan, int* out_bin,
-                              uint32_t* out_above) {
-    constexpr int PER = kHistBins / kSelThreads;  // 16 bins per thread, thread t owns the t-th block from the top
-    const int t = threadIdx.x;
-    const int hi = kHistBins - 1 - PER * t;       // bins hi, hi-1, ..., hi-PER+1
+// Threshold bin of one row: the largest b with (count of bins >= b) >= kk
+// (1 <= kk <= the histogram's total). Called by all threads of a
+// kSelThreads block; thread t owns the 16 bins 4095-16t down to 4080-16t, a
+// wave scan of their sums plus the wave totals in LDS (`wave_tot`) find the
+// bin; two barriers.
+__device__ uint32_t row_threshold_bin(const uint32_t* hist_row, uint32_t kk, uint32_t* wave_tot, uint32_t* bin_sh) {
+    constexpr int PER = kHistBins / kSelThreads;
+    static_assert(PER == 16, "four 16-byte loads per thread");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int lo = kHistBins - PER * (t + 1);  // the thread's bins lo .. lo + 15
     uint32_t loc[PER];
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(hist_row + lo + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) loc[4 * q + e] = x[e];
+    }
     uint32_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        loc[i] = hist_glob[hi - i];
-        sum += loc[i];
+    for (int i = 0; i < PER; ++i) sum += loc[i];
+    uint32_t incl = sum;  // inclusive over the wave's lanes, i.e. from the top bin down
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
     }
-    sh_scan[t] = sum;
+    if (lane == 63) wave_tot[w] = incl;
+    if (t == 0) *bin_sh = 0;  // not reached when the histogram holds >= kk counts
     __syncthreads();
-    // inclusive prefix over threads (from the top bin down), Hillis-Steele
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-        const uint32_t v = t >= off ? sh_scan[t - off] : 0u;
-        __syncthreads();
-        sh_scan[t] += v;
-        __syncthreads();
-    }
-    const uint32_t before = t ? sh_scan[t - 1] : 0u;
+    uint32_t before = incl - sum;
+#pragma unroll
+    for (int q = 0; q < kSelThreads / 64; ++q) before += q < w ? wave_tot[q] : 0u;
     if (before < kk && before + sum >= kk) {
         uint32_t acc = before;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (acc + loc[i] >= kk) {
-                *out_bin = hi - i;
-                *out_above = acc;
+        for (int i = PER - 1; i >= 0; --i) {  // bins lo + 15 down to lo
+            acc += loc[i];
+            if (acc >= kk) {
+                *bin_sh = (uint32_t)(lo + i);
                 break;
             }
-            acc += loc[i];
         }
     }
     __syncthreads();
-}
-
-
-// One workgroup per row: the threshold bin of the complete histogram.
-// thr[0] = bin (kHistBins if nothing is to be selected), thr[1] = 0 (the
-// collect step counts its candidates there).
-__global__ __launch_bounds__(kSelThreads) void select_threshold_kernel(const uint32_t* hist, uint32_t* thr,
-                                                                        const int32_t* n_cand, int64_t row_len,
-                                                                        int k) {
-    __shared__ uint32_t scan[kSelThreads];
-    __shared__ int bin_sh;
-    __shared__ uint32_t above_sh;
-    const int64_t r = blockIdx.x;
-    const int64_t n = n_cand ? (int64_t)n_cand[r] : row_len;
-    const uint32_t kk = (uint32_t)min<int64_t>(k, n);
-    if (kk == 0) {
-        if (threadIdx.x == 0) {
-            thr[2 * r] = kHistBins;
-            thr[2 * r + 1] = 0;
-        }
-        return;
-    }
-    if (threadIdx.x == 0) {
-        bin_sh = 0;
-        above_sh = 0;
-    }
-    __syncthreads();
-    threshold_bin(hist + (size_t)r * kHistBins, kk, scan, &bin_sh, &above_sh);
-    if (threadIdx.x == 0) {
-        thr[2 * r] = (uint32_t)bin_sh;
-        thr[2 * r + 1] = 0;  // candidate counter of the collect step
-    }
-}
-
-hipError_t launch_select_threshold(const SelectArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(select_threshold_kernel, dim3((unsigned)a.rows), dim3(kSelThreads), 0, st, a.hist, a.thr,
-                       a.n_cand, a.row_len, a.k);
-    return hipGetLastError();
+    return *bin_sh;
 }
 
 // ---------------------------------------------------------------- decode score
@@ -200,59 +171,94 @@ hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ step 2: collect
-// grid (chunks of kSelChunk scores, rows). A workgroup counts its candidates
-// (LDS), reserves room with one global atomic, then writes them (its chunk is
-// read twice, the second time from cache). Candidates beyond kCandCap are
-// counted but not stored (the final step then selects over the whole row).
-__global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs a) {
-    __shared__ uint32_t wg_count, wg_base;
-    const int64_t r = blockIdx.y;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t n = row_cands(a, r);
-    const uint32_t tbin = a.thr[2 * r];
+// grid (chunks of kSelChunk scores, rows). Every thread loads its 32 scores of
+// the chunk into registers at once (8 x 16 bytes where the row is 16-byte
+// aligned, else 32 coalesced words), counts those in the threshold bin or
+// above, and takes its write offset from a wave scan, the wave totals in LDS
+// and one global atomic per workgroup; the rank keys are then stored from the
+// registers (the chunk is read once). Candidates beyond kCandCap are counted
+// but not stored (the final step then selects over the whole row).
+constexpr int kCollectPer = kSelChunk / kSelThreads;  // scores per thread
+static_assert(kCollectPer == 32, "one 32-bit take mask per thread");
+template <bool VEC>
+__device__ __forceinline__ int64_t collect_pos(int64_t j0, int t, int i) {
+    // VEC: 16-byte pieces, piece q = i / 4 of thread t at j0 + 4 t + 4 kSelThreads q
+    return VEC ? j0 + 4 * t + 4 * kSelThreads * (i >> 2) + (i & 3) : j0 + t + (int64_t)kSelThreads * i;
+}
+template <bool VEC>
+__device__ __forceinline__ void collect_row_chunk(const SelectArgs& a, int64_t r, int64_t n, uint32_t kk,
+                                                  uint32_t* wave_tot, uint32_t* sh) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
     const int64_t j0 = (int64_t)blockIdx.x * kSelChunk, j1 = min<int64_t>(j0 + kSelChunk, n);
-    if (threadIdx.x == 0) wg_count = 0;
-    __syncthreads();
-    uint32_t c = 0;
-    const bool vec = ((r * a.row_stride) & 3) == 0;  // rows 16-byte aligned: 4 scores per load
-    if (vec) {
-        for (int64_t j = j0 + 4 * threadIdx.x; j < j1; j += 4 * kSelThreads) {
-            if (j + 4 <= j1) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(s + j);
+    float v[kCollectPer];
+    if constexpr (VEC) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) c += score_bin(v[e]) >= tbin ? 1u : 0u;
+        for (int q = 0; q < kCollectPer / 4; ++q) {
+            const int64_t j = collect_pos<true>(j0, t, 4 * q);
+            if (j + 4 <= j1) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(s + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
             } else {
-                for (int64_t jj = j; jj < j1; ++jj) c += score_bin(s[jj]) >= tbin ? 1u : 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * q + e] = j + e < j1 ? s[j + e] : 0.f;
             }
         }
     } else {
-        for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) c += score_bin(s[j]) >= tbin ? 1u : 0u;
-    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-    if (lane == 0 && c) atomicAdd(&wg_count, c);
-    __syncthreads();
-    if (wg_count == 0) return;
-    if (threadIdx.x == 0) {
-        wg_base = atomicAdd(&a.thr[2 * r + 1], wg_count);
-        wg_count = 0;  // reused as the running offset of the writes
+        for (int i = 0; i < kCollectPer; ++i) {
+            const int64_t j = collect_pos<false>(j0, t, i);
+            v[i] = j < j1 ? s[j] : 0.f;
+        }
     }
-    __syncthreads();
-    const uint32_t base = wg_base;
-    for (int64_t jb = j0 + 64 * w; jb < j1; jb += kSelThreads) {
-        const int64_t j = jb + lane;
-        const float v = j < j1 ? s[j] : 0.f;
-        const bool take = j < j1 && score_bin(v) >= tbin;
-        const uint64_t m = __ballot(take);
-        if (m == 0) continue;
-        uint32_t off = 0;
-        if (lane == 0) off = atomicAdd(&wg_count, (uint32_t)__popcll(m));
-        off = __shfl(off, 0);
-        const uint32_t at = base + off + __popcll(m & ((1ull << lane) - 1ull));
-        if (take && at < (uint32_t)kCandCap) cand[at] = rank_key(v, (uint32_t)j);
+    // the threshold bin, while the score loads are in flight
+    const uint32_t tbin = row_threshold_bin(a.hist + (size_t)r * kHistBins, kk, wave_tot, sh);
+    uint32_t take = 0;
+#pragma unroll
+    for (int i = 0; i < kCollectPer; ++i)
+        if (collect_pos<VEC>(j0, t, i) < j1 && score_bin(v[i]) >= tbin) take |= 1u << i;
+    const uint32_t c = (uint32_t)__popc(take);
+    // inclusive scan of the counts over the wave
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
     }
+    if (lane == 63) wave_tot[w] = incl;  // the threshold's reads of wave_tot ended at its last barrier
+    __syncthreads();
+    uint32_t wave_off = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < kSelThreads / 64; ++q) {
+        const uint32_t x = wave_tot[q];
+        wave_off += q < w ? x : 0u;
+        total += x;
+    }
+    if (total == 0) return;  // uniform over the workgroup
+    if (t == 0) sh[1] = atomicAdd(&a.thr[2 * r + 1], total);
+    __syncthreads();
+    uint32_t at = sh[1] + wave_off + incl - c;
+#pragma unroll
+    for (int i = 0; i < kCollectPer; ++i) {  // static indices keep v in registers
+        if ((take >> i) & 1u) {
+            if (at < (uint32_t)kCandCap) cand[at] = rank_key(v[i], (uint32_t)collect_pos<VEC>(j0, t, i));
+            ++at;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs a) {
+    __shared__ uint32_t wave_tot[kSelThreads / 64], sh[2];
+    const int64_t r = blockIdx.y;
+    const int64_t n = row_cands(a, r);
+    const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
+    if (kk == 0) return;  // nothing to select in this row
+    if (((r * a.row_stride) & 3) == 0)  // rows 16-byte aligned: 4 scores per load
+        collect_row_chunk<true>(a, r, n, kk, wave_tot, sh);
+    else
+        collect_row_chunk<false>(a, r, n, kk, wave_tot, sh);
 }
 
 hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st) {
