@@ -55,7 +55,37 @@ def test_select_topk_bit_exact(hs2, orc):
     assert np.array_equal(to_np(got), ref)
 
 
-@pytest.mark.parametrize("L,k", [(131072, 1024), (300, 256), (9000, 2048), (70000, 1)])
+def test_select_topk_bin_ranking_paths(hs2, orc):
+    """The final step's branches: keys of the threshold bin ranked directly
+    (random rows), more than 512 keys in that bin without overflowing the
+    candidate list (digit search; 1500 exact ties straddle the k-th), every
+    candidate kept (700 equal scores, n_cand = 700), rows not 16-byte aligned
+    (odd row length: scalar loads), and a row of more than 1024 chunks of 8192
+    (positions sorted instead of placed by runs)."""
+    rng = np.random.default_rng(11)
+    rows, L, k = 4, 20001, 1024
+    s = (rng.random((rows, L), dtype=np.float32) * 0.5).astype(np.float32)
+    hi = rng.choice(L, 2000, replace=False)
+    s[0, hi[:500]] = 0.9 + 0.09 * rng.random(500, dtype=np.float32)
+    s[0, hi[500:]] = np.float32(0.75)
+    s[1, :] = np.float32(0.3)
+    s[3] = rng.standard_exponential(L).astype(np.float32)
+    n_cand = np.array([L, 700, L, L - 3], np.int32)
+    say("select_topk bin paths", rows, L, k)
+    got = hs2.select_topk(torch.from_numpy(s).cuda(), k, torch.from_numpy(n_cand).cuda())
+    torch.cuda.synchronize()
+    ref = orc.select_scores_f32(s, n_cand.astype(np.int64), k)
+    assert np.array_equal(to_np(got), ref)
+    Lx = 8192 * 1025 + 1
+    sx = rng.random((1, Lx), dtype=np.float32)
+    say("select_topk long row", Lx)
+    got = hs2.select_topk(torch.from_numpy(sx).cuda(), k)
+    torch.cuda.synchronize()
+    ref = orc.select_scores_f32(sx, [Lx], k)
+    assert np.array_equal(to_np(got), ref)
+
+
+@pytest.mark.parametrize("L,k", [(131072, 1024), (300, 256), (9000, 2048), (70000, 1), (9001, 1024)])
 def test_select_topk_shapes(hs2, orc, L, k):
     rng = np.random.default_rng(L + k)
     rows = 5

@@ -99,9 +99,11 @@ int sparse_splits(int64_t n_tok, int n_sel) {
     const int rps = sparse_rows_per_split(n_tok, n_sel);
     return (n_sel + rps - 1) / rps;
 }
+// chunks of a selection row (one collect workgroup each)
+int64_t select_chunks(int64_t row_len) { return (row_len + kSelChunk - 1) / kSelChunk; }
 struct DecodeWs {
     float *logits, *part, *lse2, *scores, *spart;
-    uint32_t *hist, *thr;
+    uint32_t *hist, *thr, *runs;
     uint64_t* cand;
     size_t bytes;
 };
@@ -117,6 +119,7 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     // directly after hist, so that one fill clears both
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)B * 2);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)B * kCandCap);
+    w.runs = c.take<uint32_t>(sizeof(uint32_t) * 2 * (size_t)B * (size_t)select_chunks(n_ctx));
     const int ss = sparse_splits(B, window + k_global);
     w.spart = ss > 1 ? c.take<float>(sizeof(float) * (size_t)B * ss * H * (d + 2)) : nullptr;
     w.bytes = c.used;
@@ -137,7 +140,7 @@ SparseWs sparse_ws(void* base, int64_t n_tok, int n_sel, int H, int d) {
 }
 
 struct SelectWs {
-    uint32_t *hist, *thr;
+    uint32_t *hist, *thr, *runs;
     uint64_t* cand;
     size_t bytes;
 };
@@ -148,6 +151,7 @@ SelectWs select_ws(void* base, int64_t rows, int64_t row_len) {
     // directly after hist, so that one fill clears both
     w.thr = c.take<uint32_t>(sizeof(uint32_t) * (size_t)rows * 2);
     w.cand = c.take<uint64_t>(sizeof(uint64_t) * (size_t)rows * kCandCap);
+    w.runs = c.take<uint32_t>(sizeof(uint32_t) * 2 * (size_t)rows * (size_t)select_chunks(row_len));
     w.bytes = c.used;
     return w;
 }
@@ -625,6 +629,8 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     a.hist = w.hist;
     a.thr = w.thr;
     a.cand = w.cand;
+    a.runs = w.runs;
+    a.runs_stride = select_chunks(row_len);
     a.out = out;
     a.out_stride = k;
     a.out_offset = 0;
@@ -725,6 +731,8 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     se.hist = w.hist;
     se.thr = w.thr;
     se.cand = w.cand;
+    se.runs = w.runs;
+    se.runs_stride = select_chunks(n_cand);
     se.out = indices;
     se.out_stride = n_sel;
     se.out_offset = window;

@@ -48,6 +48,7 @@ hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStrea
 // ---- selection ------------------------------------------------------------
 constexpr int kHistBins = 4096;      // top 12 bits of a non-negative fp32 (bits 30..19)
 constexpr int kCandCap = 4096;       // candidates the final wave holds in registers
+constexpr int kSelChunk = 8192;      // scores per workgroup in the histogram and collect steps
 
 // decode: score_j = sum_h exp2(logit2[j][h] - lse2[h]) for j < n_ctx; writes
 // scores [B][n_ctx] and the histogram of candidates j < n_cand.
@@ -71,8 +72,10 @@ struct SelectArgs {
     const int32_t* n_cand;  // [rows] or nullptr
     int k;
     uint32_t* hist;         // [rows][kHistBins]
-    uint32_t* thr;          // [rows][2] (unused, candidate count); zeroed with hist
-    uint64_t* cand;         // [rows][kCandCap] candidate rank keys (unordered)
+    uint32_t* thr;          // [rows][2] threshold bin, candidate count; zeroed with hist
+    uint64_t* cand;         // [rows][kCandCap] candidate rank keys, one position-ordered run per chunk
+    uint32_t* runs;         // [rows][runs_stride][2] (first slot, count) of each chunk's run
+    int64_t runs_stride;    // chunks per row: ceil(row_len / kSelChunk)
     int32_t* out;           // [rows][out_stride]
     int64_t out_stride;
     int out_offset;         // first column written in each out row

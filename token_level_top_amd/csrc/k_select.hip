@@ -18,11 +18,15 @@
 //     in that bin or above to the row's candidate list (each workgroup reads
 //     its chunk once into registers and reserves room with one atomic; the
 //     list is unordered);
-//  3. final: one 1024-thread workgroup per row loads the candidates into LDS,
-//     finds the exact k-th largest key by 8-bit digit passes (per-wave LDS
-//     histograms), gathers the positions of the keys at or above it and sorts
-//     them ascending (bitonic, in LDS). Rows whose candidates overflow the list
-//     fall back to an exact multi-pass radix select over the whole row.
+//  3. final: one 1024-thread workgroup per row loads the candidates into LDS;
+//     those above the threshold bin are kept, those in it are ranked among
+//     themselves by direct comparison (by 8-bit digit passes over all keys,
+//     per-wave LDS histograms, when more than kRankMax share the bin); an
+//     exclusive scan of the kept flags in slot order plus the kept counts of
+//     the chunks' position-ordered runs give every kept position its output
+//     slot, so no sort is needed (rows of more than kFinThreads chunks sort
+//     the positions instead). Rows whose candidates overflow the list fall
+//     back to an exact multi-pass radix select over the whole row.
 // The 64-bit rank key (score bits, complemented position) makes every key
 // distinct, so the result is unique.
 #include "hs2_device.h"
@@ -32,7 +36,6 @@
 namespace hs2 {
 
 constexpr int kSelThreads = 256;
-constexpr int kSelChunk = 8192;      // scores per workgroup in steps 1 and 2
 constexpr int kFinThreads = 1024;
 
 __device__ __forceinline__ uint32_t score_bits(float s) { return __float_as_uint(s) & 0x7FFFFFFFu; }
@@ -172,93 +175,124 @@ hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st) {
 
 // ------------------------------------------------------------ step 2: collect
 // grid (chunks of kSelChunk scores, rows). Every thread loads its 32 scores of
-// the chunk into registers at once (8 x 16 bytes where the row is 16-byte
-// aligned, else 32 coalesced words), counts those in the threshold bin or
-// above, and takes its write offset from a wave scan, the wave totals in LDS
-// and one global atomic per workgroup; the rank keys are then stored from the
-// registers (the chunk is read once). Candidates beyond kCandCap are counted
-// but not stored (the final step then selects over the whole row).
+// the chunk into registers at once (piece q = 0..7 of thread t holds positions
+// j0 + 1024 q + 4 t + 0..3: 16-byte loads where the row is 16-byte aligned),
+// finds the row's threshold bin meanwhile, and takes the candidates (scores in
+// that bin or above). Their slots follow position order, i.e. (piece, thread,
+// element): per piece a wave scan of the counts (two pieces per 32-bit word)
+// and the wave totals in LDS; one global atomic per workgroup reserves the
+// chunk's run, recorded in `runs` as (first slot, count). The chunk is read
+// once. Candidates beyond kCandCap are counted but not stored (the final step
+// then selects over the whole row).
 constexpr int kCollectPer = kSelChunk / kSelThreads;  // scores per thread
-static_assert(kCollectPer == 32, "one 32-bit take mask per thread");
-template <bool VEC>
+static_assert(kCollectPer == 32, "one 32-bit take mask per thread, 8 pieces of 4");
 __device__ __forceinline__ int64_t collect_pos(int64_t j0, int t, int i) {
-    // VEC: 16-byte pieces, piece q = i / 4 of thread t at j0 + 4 t + 4 kSelThreads q
-    return VEC ? j0 + 4 * t + 4 * kSelThreads * (i >> 2) + (i & 3) : j0 + t + (int64_t)kSelThreads * i;
+    return j0 + 4 * kSelThreads * (i >> 2) + 4 * t + (i & 3);
 }
 template <bool VEC>
 __device__ __forceinline__ void collect_row_chunk(const SelectArgs& a, int64_t r, int64_t n, uint32_t kk,
-                                                  uint32_t* wave_tot, uint32_t* sh) {
+                                                  uint32_t* wave_tot, uint32_t (*wave_pk)[4], uint32_t* sh) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
     const int64_t j0 = (int64_t)blockIdx.x * kSelChunk, j1 = min<int64_t>(j0 + kSelChunk, n);
     float v[kCollectPer];
-    if constexpr (VEC) {
 #pragma unroll
-        for (int q = 0; q < kCollectPer / 4; ++q) {
-            const int64_t j = collect_pos<true>(j0, t, 4 * q);
-            if (j + 4 <= j1) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(s + j);
+    for (int q = 0; q < kCollectPer / 4; ++q) {
+        const int64_t j = collect_pos(j0, t, 4 * q);
+        if (VEC && j + 4 <= j1) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(s + j);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-            } else {
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * q + e] = j + e < j1 ? s[j + e] : 0.f;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kCollectPer; ++i) {
-            const int64_t j = collect_pos<false>(j0, t, i);
-            v[i] = j < j1 ? s[j] : 0.f;
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = j + e < j1 ? s[j + e] : 0.f;
         }
     }
     // the threshold bin, while the score loads are in flight
     const uint32_t tbin = row_threshold_bin(a.hist + (size_t)r * kHistBins, kk, wave_tot, sh);
+    if (blockIdx.x == 0 && t == 0) a.thr[2 * r] = tbin;
     uint32_t take = 0;
 #pragma unroll
     for (int i = 0; i < kCollectPer; ++i)
-        if (collect_pos<VEC>(j0, t, i) < j1 && score_bin(v[i]) >= tbin) take |= 1u << i;
-    const uint32_t c = (uint32_t)__popc(take);
-    // inclusive scan of the counts over the wave
-    uint32_t incl = c;
+        if (collect_pos(j0, t, i) < j1 && score_bin(v[i]) >= tbin) take |= 1u << i;
+    // per piece q the count of taken scores, two pieces per word (16 bits each,
+    // at most 4 * 64 per wave); inclusive scans over the wave
+    uint32_t pk[4], inc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        pk[p] = (uint32_t)__popc((take >> (8 * p)) & 0xFu) | ((uint32_t)__popc((take >> (8 * p + 4)) & 0xFu) << 16);
+        inc[p] = pk[p];
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) wave_tot[w] = incl;  // the threshold's reads of wave_tot ended at its last barrier
-    __syncthreads();
-    uint32_t wave_off = 0, total = 0;
 #pragma unroll
-    for (int q = 0; q < kSelThreads / 64; ++q) {
-        const uint32_t x = wave_tot[q];
-        wave_off += q < w ? x : 0u;
-        total += x;
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t y = __shfl_up(inc[p], o);
+            if (lane >= o) inc[p] += y;
+        }
     }
-    if (total == 0) return;  // uniform over the workgroup
-    if (t == 0) sh[1] = atomicAdd(&a.thr[2 * r + 1], total);
-    __syncthreads();
-    uint32_t at = sh[1] + wave_off + incl - c;
+    if (lane == 63) {
 #pragma unroll
-    for (int i = 0; i < kCollectPer; ++i) {  // static indices keep v in registers
-        if ((take >> i) & 1u) {
-            if (at < (uint32_t)kCandCap) cand[at] = rank_key(v[i], (uint32_t)collect_pos<VEC>(j0, t, i));
-            ++at;
+        for (int p = 0; p < 4; ++p) wave_pk[w][p] = inc[p];
+    }
+    __syncthreads();
+    // slot of piece q of this thread within the chunk's run: all earlier
+    // pieces, then this piece in earlier waves, then earlier lanes of the wave
+    uint32_t off[kCollectPer / 4], total = 0;
+#pragma unroll
+    for (int q = 0; q < kCollectPer / 4; ++q) {
+        const int p = q >> 1, sh16 = 16 * (q & 1);
+        uint32_t tot_q = 0, before = 0;
+#pragma unroll
+        for (int ww = 0; ww < kSelThreads / 64; ++ww) {
+            const uint32_t x = (wave_pk[ww][p] >> sh16) & 0xFFFFu;
+            tot_q += x;
+            before += ww < w ? x : 0u;
+        }
+        off[q] = total + before + ((inc[p] >> sh16) & 0xFFFFu) - ((pk[p] >> sh16) & 0xFFFFu);
+        total += tot_q;
+    }
+    uint32_t* run = a.runs + ((size_t)r * (size_t)a.runs_stride + blockIdx.x) * 2;
+    if (total == 0) {  // uniform over the workgroup
+        if (t == 0) {
+            run[0] = 0u;
+            run[1] = 0u;
+        }
+        return;
+    }
+    if (t == 0) {
+        const uint32_t base = atomicAdd(&a.thr[2 * r + 1], total);
+        sh[1] = base;
+        run[0] = base;
+        run[1] = total;
+    }
+    __syncthreads();
+    const uint32_t base = sh[1];
+#pragma unroll
+    for (int q = 0; q < kCollectPer / 4; ++q) {  // static indices keep v in registers
+        uint32_t at = base + off[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            if ((take >> i) & 1u) {
+                if (at < (uint32_t)kCandCap) cand[at] = rank_key(v[i], (uint32_t)collect_pos(j0, t, i));
+                ++at;
+            }
         }
     }
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_collect_kernel(SelectArgs a) {
-    __shared__ uint32_t wave_tot[kSelThreads / 64], sh[2];
+    __shared__ uint32_t wave_tot[kSelThreads / 64], wave_pk[kSelThreads / 64][4], sh[2];
     const int64_t r = blockIdx.y;
     const int64_t n = row_cands(a, r);
     const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
-    if (kk == 0) return;  // nothing to select in this row
+    if (kk == 0) return;  // nothing to select in this row (the final step reads no run)
     if (((r * a.row_stride) & 3) == 0)  // rows 16-byte aligned: 4 scores per load
-        collect_row_chunk<true>(a, r, n, kk, wave_tot, sh);
+        collect_row_chunk<true>(a, r, n, kk, wave_tot, wave_pk, sh);
     else
-        collect_row_chunk<false>(a, r, n, kk, wave_tot, sh);
+        collect_row_chunk<false>(a, r, n, kk, wave_tot, wave_pk, sh);
 }
 
 hipError_t launch_select_collect(const SelectArgs& a, hipStream_t st) {
@@ -530,25 +564,32 @@ __device__ void block_sort_positions(int32_t* v, int32_t* tmp, int n) {
     __syncthreads();
 }
 
+// In-bin ranking: keys in the threshold bin are ranked among themselves by
+// direct comparison when there are at most this many (else the digit search).
+constexpr int kRankMax = 512;
+static_assert(kRankMax <= kFinThreads, "one in-bin key per thread");
+
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a, int window, int64_t p_last) {
     __shared__ uint64_t keys[kCandCap];
     __shared__ int32_t pos[2048];
     __shared__ uint32_t hist[256 * (kFinThreads / 64)];
     __shared__ uint32_t ctl[20];
     __shared__ uint64_t red[kFinThreads / 64];
-    __shared__ uint32_t scratch[1024];  // the whole-row fallback
+    __shared__ uint32_t scratch[1024];  // the whole-row fallback; scan scratch
+    static_assert(256 * (kFinThreads / 64) >= kCandCap, "hist holds one flag / offset per candidate");
     const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
     int32_t* out = a.out + (size_t)r * (size_t)a.out_stride;
     // forced window (decode rows all sit at p_last)
     if (window > 0) {
         const int64_t nw = min<int64_t>(window, p_last + 1);
-        for (int t = threadIdx.x; t < window; t += blockDim.x)
+        for (int t = tid; t < window; t += blockDim.x)
             out[t] = t < nw ? (int32_t)(p_last - nw + 1 + t) : -1;
     }
     out += a.out_offset;
     const int64_t n = row_cands(a, r);
     const uint32_t kk = (uint32_t)min<int64_t>(a.k, n);
-    for (int t = threadIdx.x + kk; t < a.k; t += blockDim.x) out[t] = -1;
+    for (int t = tid + kk; t < a.k; t += blockDim.x) out[t] = -1;
     if (kk == 0) return;
     const uint32_t nc = a.thr[2 * r + 1];
     if (nc > (uint32_t)kCandCap) {
@@ -556,29 +597,124 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
         return;
     }
     const uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    for (uint32_t i = threadIdx.x; i < nc; i += blockDim.x) keys[i] = cand[i];
-    if (threadIdx.x == 0) ctl[3] = 0;
+    for (uint32_t i = tid; i < nc; i += blockDim.x) keys[i] = cand[i];
+    if (tid == 0) {
+        ctl[3] = 0;
+        ctl[4] = 0;
+    }
+    const int64_t n_chunks = (n + kSelChunk - 1) / kSelChunk;
+    if (n_chunks > kFinThreads) {
+        // very long rows: k-th key by digits, then a sort of the positions
+        __syncthreads();
+        const uint64_t T = kk < nc ? block_kth_key(keys, nc, kk, hist, ctl, red) : 0ull;
+        for (uint32_t ib = 0; ib < nc; ib += blockDim.x) {
+            const uint32_t i = ib + tid;
+            const uint64_t k = i < nc ? keys[i] : 0ull;
+            const bool keep = i < nc && k >= T;
+            const uint64_t m = __ballot(keep);
+            if (m == 0) continue;
+            uint32_t off = 0;
+            if ((tid & 63) == 0) off = atomicAdd(&ctl[3], (uint32_t)__popcll(m));
+            off = __shfl(off, 0);
+            if (keep) pos[off + __popcll(m & ((1ull << (tid & 63)) - 1ull))] = (int32_t)key_pos(k);
+        }
+        int np = 1;
+        while (np < (int)kk) np <<= 1;
+        __syncthreads();
+        for (int i = (int)kk + tid; i < np; i += blockDim.x) pos[i] = 0x7FFFFFFF;
+        __syncthreads();
+        block_sort_positions(pos, reinterpret_cast<int32_t*>(keys), np);
+        for (uint32_t i = tid; i < kk; i += blockDim.x) out[i] = pos[i];
+        return;
+    }
+    // Keys above the threshold bin are all kept (fewer than kk of them); of the
+    // nb keys in the bin the need = kk - (nc - nb) largest are kept.
+    const uint32_t tbin = a.thr[2 * r];
+    uint64_t* inb_key = reinterpret_cast<uint64_t*>(pos);  // pos[0, 1024): kRankMax keys
+    uint32_t* inb_idx = reinterpret_cast<uint32_t*>(pos + 1024);
     __syncthreads();
-    const uint64_t T = kk < nc ? block_kth_key(keys, nc, kk, hist, ctl, red) : 0ull;
-    // positions of the keys >= T (exactly kk of them), then ascending order
     for (uint32_t ib = 0; ib < nc; ib += blockDim.x) {
-        const uint32_t i = ib + threadIdx.x;
+        const uint32_t i = ib + tid;
         const uint64_t k = i < nc ? keys[i] : 0ull;
-        const bool keep = i < nc && k >= T;
-        const uint64_t m = __ballot(keep);
+        const bool in_bin = i < nc && (uint32_t)(k >> 51) == tbin;
+        const uint64_t m = __ballot(in_bin);
         if (m == 0) continue;
         uint32_t off = 0;
-        if ((threadIdx.x & 63) == 0) off = atomicAdd(&ctl[3], (uint32_t)__popcll(m));
-        off = __shfl(off, 0);
-        if (keep) pos[off + __popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull))] = (int32_t)key_pos(k);
+        if ((tid & 63) == 0) off = atomicAdd(&ctl[4], (uint32_t)__popcll(m));
+        off = __shfl(off, 0) + __popcll(m & ((1ull << (tid & 63)) - 1ull));
+        if (in_bin && off < (uint32_t)kRankMax) {
+            inb_key[off] = k;
+            inb_idx[off] = i;
+        }
     }
-    int np = 1;
-    while (np < (int)kk) np <<= 1;
     __syncthreads();
-    for (int i = (int)kk + threadIdx.x; i < np; i += blockDim.x) pos[i] = 0x7FFFFFFF;
+    const uint32_t nb = ctl[4];
+    // flags in hist[0, nc): 1 = kept
+    if (nb <= (uint32_t)kRankMax) {
+        const uint32_t need = kk - (nc - nb);
+        bool kept = false;
+        if (tid < (int)nb) {
+            const uint64_t kq = inb_key[tid];
+            uint32_t rank = 0;  // keys are distinct: rank = number of larger ones
+            for (uint32_t j = 0; j < nb; ++j) rank += inb_key[j] > kq ? 1u : 0u;
+            kept = rank < need;
+        }
+        for (uint32_t i = tid; i < nc; i += blockDim.x) hist[i] = (uint32_t)(keys[i] >> 51) > tbin ? 1u : 0u;
+        __syncthreads();
+        if (tid < (int)nb) hist[inb_idx[tid]] = kept ? 1u : 0u;
+    } else {
+        // the digit search (hist as its scratch) needs kk < nc; kk == nc keeps every key
+        const uint64_t T = kk < nc ? block_kth_key(keys, nc, kk, hist, ctl, red) : 0ull;
+        for (uint32_t i = tid; i < nc; i += blockDim.x) hist[i] = keys[i] >= T ? 1u : 0u;
+    }
     __syncthreads();
-    block_sort_positions(pos, reinterpret_cast<int32_t*>(keys), np);
-    for (uint32_t i = threadIdx.x; i < kk; i += blockDim.x) out[i] = pos[i];
+    // kept keys before each candidate in slot order (exclusive scan, four
+    // consecutive slots per thread), the flag kept in bit 31
+    {
+        uint32_t f[4], loc = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t i = 4 * tid + e;
+            f[e] = i < nc ? hist[i] : 0u;
+            loc += f[e];
+        }
+        uint32_t tot;
+        uint32_t x = block_excl_scan(loc, scratch, &tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t i = 4 * tid + e;
+            if (i < nc) hist[i] = x | (f[e] << 31);
+            x += f[e];
+        }
+    }
+    __syncthreads();
+    // runs are position-ordered per chunk: a kept key's output slot is the kept
+    // count of the earlier chunks plus its kept rank within its own run
+    int32_t* chunk_off = pos;  // the in-bin lists are no longer needed
+    {
+        uint32_t kc = 0, eb = 0;
+        if (tid < n_chunks) {
+            const uint32_t* run = a.runs + ((size_t)r * (size_t)a.runs_stride + tid) * 2;
+            const uint32_t rb = run[0], rc = run[1];
+            if (rc) {
+                eb = hist[rb] & 0x7FFFFFFFu;
+                const uint32_t ee = rb + rc < nc ? hist[rb + rc] & 0x7FFFFFFFu : kk;
+                kc = ee - eb;
+            }
+        }
+        uint32_t tot;
+        const uint32_t before = block_excl_scan(kc, scratch, &tot);
+        if (tid < n_chunks) chunk_off[tid] = (int32_t)before - (int32_t)eb;
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < nc; i += blockDim.x) {
+        const uint32_t h = hist[i];
+        if (h >> 31) {
+            const uint32_t p = key_pos(keys[i]);
+            const int32_t o = chunk_off[p / kSelChunk] + (int32_t)(h & 0x7FFFFFFFu);
+            if (o >= 0 && o < (int32_t)kk) out[o] = (int32_t)p;  // always true; keeps a slip inside the row
+        }
+    }
 }
 
 hipError_t launch_select_final_w(const SelectArgs& a, int window, int64_t p_last, hipStream_t st) {
