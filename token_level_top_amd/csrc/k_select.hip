@@ -17,7 +17,7 @@
 //     largest score from the histogram and append the rank keys of the scores
 //     in that bin or above to the row's candidate list (each workgroup reads
 //     its chunk once into registers and reserves room with one atomic; the
-//     list is unordered);
+//     list is one position-ordered run per chunk, the runs in any order);
 //  3. final: one 1024-thread workgroup per row loads the candidates into LDS;
 //     those above the threshold bin are kept, those in it are ranked among
 //     themselves by direct comparison (by 8-bit digit passes over all keys,
