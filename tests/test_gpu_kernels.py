@@ -213,6 +213,17 @@ def test_prefill_and_decode_are_deterministic(hs2):
                              sm_scale=x.sm_scale)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+    # decode over 7 selection chunks per row: the chunks' candidate runs land in
+    # whatever order their atomics resolve, the results may not depend on it
+    wd = workload(3).with_(B=4, n_ctx=50000, q_pos0=49999, n_needles=4, n_sparse=2)
+    xd = make_inputs(wd)
+    say("determinism decode", wd.name, wd.B, wd.n_ctx)
+    runs = [hs2.decode_step(dev(xd.q[:, 0]), dev(xd.q_sparse[:, :, 0]), dev(xd.k), dev(xd.v), window=128,
+                            k_global=1024, sm_scale=xd.sm_scale, want_scores=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for key in ("indices", "scores", "out_full", "lse_full", "out_sparse", "lse_sparse"):
+            assert torch.equal(r[key], runs[0][key]), key
 
 
 @pytest.mark.parametrize("cfg", [2, 4])
