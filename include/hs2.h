@@ -49,6 +49,10 @@
  *    0 <= k_global <= 2048, window + k_global <= 4096, n_ctx < 2^31,
  *    0 <= q_pos0, q_pos0 + n_q <= n_ctx (query i sits at position q_pos0+i and
  *    its own key/value are already in the cache). Others: HS2_ERR_UNSUPPORTED.
+ *  - Batch limits: B <= 65535 sequences for hs2_full_attn_select,
+ *    hs2_decode_step, hs2_block_attn_select and hs2_index_select, and
+ *    rows <= 65535 for hs2_select_topk (one launch dimension each); larger
+ *    values return HS2_ERR_UNSUPPORTED before anything is enqueued.
  */
 #ifndef HS2_H
 #define HS2_H
@@ -128,15 +132,17 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
  * the other on `stream`.
  *   q        [n_layers][B][n_q][H][d]   q_dtype
  *   k, v, k_scale, v_scale              as for hs2_full_attn_select
- *   indices  [B][n_q][n_sel]  int32     entries in [-1, n_ctx); -1 = empty
+ *   indices  [B][n_q][n_sel]  int32     positions; an entry outside [0, n_ctx)
+ *                                       (-1 by convention) is empty: skipped
  *   out      [n_layers][B][n_q][H][d]   q_dtype
  *   lse      [n_layers][B][n_q][H]      fp32, may be NULL (not written);
  *                                       a row with no valid index gets O = 0
  *                                       and LSE = -inf
  *   workspace >= hs2_workspace_size(HS2_OP_SPARSE_ATTN, B, n_q, n_ctx, H, d,
  *                n_sel, 0, kv_dtype) bytes (the window argument carries n_sel)
- * 1 <= n_sel <= 4096. Index values are not range-checked on the host; an
- * out-of-range entry is undefined behaviour.
+ * 1 <= n_sel <= 4096. Index values are range-checked by the kernel as it
+ * gathers (an entry outside [0, n_ctx) is skipped like -1, never read), not on
+ * the host; duplicate entries are attended to as often as they appear.
  */
 int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
                     const float* k_scale, const float* v_scale, int kv_dtype, int B, int64_t n_q,

@@ -210,3 +210,22 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         hs2.select_topk(torch.zeros(2, 10), 3)
+
+
+def test_batch_limits_of_the_launch_grid():
+    """Sequences (and selection rows) ride on a launch's second grid
+    dimension: more than 65535 is refused on the host, before any enqueue."""
+    L = hs2.lib()
+    E = hs2
+    big = 65536
+    assert _full(B=big, n_q=1, n_ctx=10) == E.HS2_ERR_UNSUPPORTED
+    assert _full(B=65535, n_q=1, n_ctx=10) == E.HS2_ERR_WORKSPACE   # the limit itself is accepted
+    assert _decode(B=big) == E.HS2_ERR_UNSUPPORTED
+    assert _decode(B=65535) == E.HS2_ERR_WORKSPACE
+    assert L.hs2_select_topk(FAKE, big, 100, None, 8, FAKE, None, 0, None) == E.HS2_ERR_UNSUPPORTED
+    assert L.hs2_select_topk(FAKE, 65535, 100, None, 8, FAKE, None, 0, None) == E.HS2_ERR_WORKSPACE
+    idx_args = [FAKE, FAKE, FAKE, FAKE, FAKE, big, 1, 0, 100, 8, 128, 128, 1024, FAKE, None, 0, None]
+    assert L.hs2_index_select(*idx_args) == E.HS2_ERR_UNSUPPORTED
+    sel = [FAKE, 1, FAKE, FAKE, None, None, 1, big, 1, 0, 100, 16, 128, 64, 16, 0.1, FAKE, FAKE, FAKE, None,
+           None, 0, None]
+    assert L.hs2_block_attn_select(*sel) == E.HS2_ERR_UNSUPPORTED

@@ -1,8 +1,9 @@
 """GPU parity at the five workloads' full sizes, through the same C-ABI calls
 and shapes the benchmark times. The oracle checks sampled rows: every
 sequence of the decode workloads, all rows of the tiny prefill, 512 seeded
-rows (all needle rows + uniform rows) of the 32k prefill and 64 rows of the
-256k chunked prefill."""
+rows (all needle rows + uniform rows) of the 32k prefill and 512 seeded rows
+(the 32 cluster-target rows + 480 uniform rows) of the 256k chunked prefill.
+Needle recovery runs at every workload's full shape."""
 import sys
 
 import numpy as np
@@ -35,6 +36,17 @@ def g(t):
     return None if t is None else t.cuda().contiguous()
 
 
+def oracle_rows(orc, x, wl, rows, chunk=64):
+    """The oracle's full layer on `rows`, in chunks (a progress line each)."""
+    parts = []
+    for c0 in range(0, len(rows), chunk):
+        part = rows[c0:c0 + chunk]
+        parts.append(orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global,
+                                     x.sm_scale, part, want_scores=True))
+        say(f"  oracle rows {c0 + len(part)} of {len(rows)}")
+    return {k: np.concatenate([p[k] for p in parts]) for k in ("out", "lse", "idx", "kth", "scores")}
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_decode_full_size(hs2, orc, cfg):
     wl = workload(cfg)
@@ -46,24 +58,24 @@ def test_decode_full_size(hs2, orc, cfg):
     torch.cuda.synchronize()
     rows = list(range(wl.B))
     say("oracle on", len(rows), "sequences")
-    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
-                          rows, want_scores=True)
+    ref = oracle_rows(orc, x, wl, rows, chunk=16)
     tol = RTOL[wl.kv_dtype]
     rows_close(r["out_full"], ref["out"], tol, "decode out")
-    lse_close(r["lse_full"], ref["lse"], tol)
+    lse_close(r["lse_full"], ref["lse"], tol, "decode lse")
     sc = to_np(r["scores"]).astype(np.float64)
     rel = np.abs(sc - ref["scores"]) / ref["scores"].max(axis=1, keepdims=True)
+    say(f"  score vector: worst error relative to the row maximum {rel.max():.3e} (tol 2e-3)")
     assert rel.max() < 2e-3, rel.max()
-    ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
-    say(f"  overlap mean {ov:.5f} min {mn:.5f} swaps {sw}")
+    check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
     gidx = to_np(r["indices"]).astype(np.int32)
     for l in range(wl.n_sparse):
         s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
-        rows_close(r["out_sparse"][l], s["out"], tol, "decode sparse out")
-        lse_close(r["lse_sparse"][l], s["lse"], tol)
+        rows_close(r["out_sparse"][l], s["out"], tol, f"decode sparse layer {l} out")
+        lse_close(r["lse_sparse"][l], s["lse"], tol, f"decode sparse layer {l} lse")
 
 
-@pytest.mark.parametrize("cfg,n_uniform,n_target", [(1, 2048, None), (2, 256, None), (4, 32, 32)])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,n_uniform,n_target", [(1, 2048, None), (2, 256, None), (4, 480, 32)])
 def test_prefill_full_size(hs2, orc, cfg, n_uniform, n_target):
     wl = workload(cfg)
     say("generate", wl.name)
@@ -76,19 +88,17 @@ def test_prefill_full_size(hs2, orc, cfg, n_uniform, n_target):
     so, sl = hs2.sparse_attn(g(x.q_sparse), g(x.k), g(x.v), g(x.k_scale), g(x.v_scale), indices=idx,
                              sm_scale=x.sm_scale)
     torch.cuda.synchronize()
-    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
-                          rows, want_scores=True)
+    ref = oracle_rows(orc, x, wl, rows)
     tol = RTOL[wl.kv_dtype]
     ri = torch.tensor(rows)
     rows_close(out[0, ri], ref["out"], tol, "prefill out")
-    lse_close(lse[0, ri], ref["lse"], tol)
-    ov, mn, sw = check_index_rows(idx[0, ri], ref["idx"], ref["scores"], ref["kth"], wl.window)
-    say(f"  overlap mean {ov:.5f} min {mn:.5f} swaps {sw}")
+    lse_close(lse[0, ri], ref["lse"], tol, "prefill lse")
+    check_index_rows(idx[0, ri], ref["idx"], ref["scores"], ref["kth"], wl.window)
     gidx = to_np(idx[0, ri]).astype(np.int32)
     for l in range(wl.n_sparse):
         s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
-        rows_close(so[l, 0, ri], s["out"], tol, "prefill sparse out")
-        lse_close(sl[l, 0, ri], s["lse"], tol)
+        rows_close(so[l, 0, ri], s["out"], tol, f"prefill sparse layer {l} out")
+        lse_close(sl[l, 0, ri], s["lse"], tol, f"prefill sparse layer {l} lse")
     # every index row of the whole launch is well formed (window, order, causality)
     full = to_np(idx[0]).astype(np.int64)
     p = wl.q_pos0 + np.arange(wl.n_q)
@@ -105,27 +115,35 @@ def test_prefill_full_size(hs2, orc, cfg, n_uniform, n_target):
     assert (np.where(valid, glb, -1).max(axis=1)[has] <= (p - wl.window)[has]).all()
     d = np.diff(np.where(valid, glb, np.iinfo(np.int64).max), axis=1)
     assert (d[valid[:, 1:]] > 0).all()
+    say(f"  all {wl.n_q} index rows well formed")
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_needle_recovery(hs2, orc, cfg):
-    """Planted needles are recovered by the GPU's selection: the literal
-    3*q/|q| needles at the tiny workload's shape, and needles three times a
-    typical key norm at the 32k prefill and the 128k decode shapes."""
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_needle_recovery(hs2, cfg):
+    """Planted needles are recovered by the GPU's selection at every
+    workload's full shape: the literal 3*q/|q| needles at the tiny workload,
+    needles three times a typical key norm elsewhere -- 256 rows of the 32k
+    prefill (one needle each; a 512-row tail of queries), 32 per sequence of
+    the 128k decode, 32 clusters of 8 identical FP8 keys in the 256k chunked
+    prefill (every key of a cluster ties with the others), 64 per sequence by
+    depth in the 1M FP8 decode."""
     wl = workload(cfg)
     if cfg == 2:
         wl = wl.with_(n_q=512, q_pos0=32768 - 512)
     norm = "R18a" if cfg == 1 else "R18b"
     x = make_inputs(wl, needle_norm=norm)
     say("needles", wl.name, norm, len(x.needles))
+    kv = (g(x.k), g(x.v), g(x.k_scale), g(x.v_scale))
     if wl.decode:
-        r = hs2.decode_step(g(x.q[:, 0]), g(x.q_sparse[:, :, 0]), g(x.k), g(x.v), window=wl.window,
-                            k_global=wl.k_global, sm_scale=x.sm_scale)
+        r = hs2.decode_step(g(x.q[:, 0]), g(x.q_sparse[:, :, 0]), *kv, window=wl.window, k_global=wl.k_global,
+                            sm_scale=x.sm_scale)
         idx = to_np(r["indices"])[:, None, :]
     else:
-        _, _, ii = hs2.full_attn_select(g(x.q), g(x.k), g(x.v), q_pos0=wl.q_pos0, window=wl.window,
-                                        k_global=wl.k_global, sm_scale=x.sm_scale)
+        _, _, ii = hs2.full_attn_select(g(x.q), *kv, q_pos0=wl.q_pos0, window=wl.window, k_global=wl.k_global,
+                                        sm_scale=x.sm_scale)
         idx = to_np(ii)
     torch.cuda.synchronize()
+    keys = sum(n.length for n in x.needles)
     hit = sum(all((n.j + t) in idx[n.b, n.i, wl.window:] for t in range(n.length)) for n in x.needles)
+    say(f"  {hit} of {len(x.needles)} needles ({keys} planted keys) recovered")
     assert hit == len(x.needles), f"{hit} of {len(x.needles)} needles recovered"

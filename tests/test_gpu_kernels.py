@@ -366,3 +366,34 @@ def test_asymmetric_heads_compose(hs2, orc, cfg, B, n_q, q_pos0, n_ctx, h_full):
         s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gi, x.sm_scale, rows)
         rows_close(so[l].reshape(B * n_q, wl.H, wl.d), s["out"], tol, f"sparse out {l}")
         lse_close(sl[l].reshape(B * n_q, wl.H), s["lse"], tol)
+
+
+@pytest.mark.parametrize("cfg,n_q", [(2, 5), (4, 1100)])
+def test_sparse_out_of_range_entries_are_skipped(hs2, orc, cfg, n_q):
+    """Index entries outside [0, n_ctx) (past the end, or negative other than
+    -1) are skipped like -1: the result equals the oracle on the same rows with
+    those entries emptied, and the in-range neighbours are unaffected."""
+    n_ctx, n_sel = 3000, 1152
+    wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=n_ctx - n_q, n_ctx=n_ctx, n_needles=0, needles="none",
+                             n_sparse=1)
+    x = make_inputs(wl)
+    rng = np.random.default_rng(11 + n_q)
+    idx = _rand_index_rows(rng, n_q, n_sel, n_ctx, 0)
+    bad = idx.copy()
+    for t in range(n_q):
+        slots = rng.choice(n_sel, size=8, replace=False)
+        bad[t, slots] = rng.choice([n_ctx, n_ctx + 1, 2 ** 31 - 1, -2, -(2 ** 31), 10 * n_ctx], size=8)
+    clean = np.where((bad >= 0) & (bad < n_ctx), bad, -1).astype(np.int32)
+    say("sparse with out-of-range entries", wl.name, n_q)
+    out, lse = hs2.sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale),
+                               indices=torch.from_numpy(bad).reshape(1, n_q, n_sel).cuda(), sm_scale=x.sm_scale)
+    ref_o, ref_l = hs2.sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale),
+                                   indices=torch.from_numpy(clean).reshape(1, n_q, n_sel).cuda(),
+                                   sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    rows = list(range(n_q))
+    r = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, clean, x.sm_scale, rows)
+    empty = (clean < 0).all(axis=1)
+    rows_close(out[0, 0][~torch.from_numpy(empty)], r["out"][~empty], RTOL[wl.kv_dtype], "sparse out")
+    lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype])

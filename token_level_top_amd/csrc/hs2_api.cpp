@@ -61,6 +61,9 @@ int check_common(int q_dtype, int kv_dtype, const void* k, const void* v, const 
     return HS2_OK;
 }
 
+// Sequences (or selection rows) ride on a launch's second grid dimension.
+constexpr int64_t kMaxGridY = 65535;
+
 int check_select_shape(int window, int k_global) {
     if (window < 1 || k_global < 0) return HS2_ERR_INVALID_ARG;
     if (k_global > 2048 || window + k_global > 4096) return HS2_ERR_UNSUPPORTED;
@@ -485,7 +488,7 @@ int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void*
     if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(block_idx) || !aligned16(block_scores))
         return HS2_ERR_INVALID_ARG;
     if (st != HS2_OK) return st;
-    if (block != kBlock || k_blocks > 4096 / kBlock) return HS2_ERR_UNSUPPORTED;
+    if (block != kBlock || k_blocks > 4096 / kBlock || B > kMaxGridY) return HS2_ERR_UNSUPPORTED;
     const BlockPfWs need = block_pf_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -583,7 +586,7 @@ int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* we
         !aligned16(k_scale) || !aligned16(indices))
         return HS2_ERR_INVALID_ARG;
     if (ss != HS2_OK) return ss;
-    if ((HI != 4 && HI != 8 && HI != 16) || (dI != 64 && dI != 128)) return HS2_ERR_UNSUPPORTED;
+    if ((HI != 4 && HI != 8 && HI != 16) || (dI != 64 && dI != 128) || B > kMaxGridY) return HS2_ERR_UNSUPPORTED;
     const IndexWs need = index_ws(nullptr, B, n_q, n_ctx, dI);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -614,7 +617,7 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     if (!scores || !out || rows < 1 || row_len < 1 || k < 1) return HS2_ERR_INVALID_ARG;
     if (rows >= (int64_t(1) << 31) || row_len >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
     if (!aligned16(scores) || !aligned16(out) || !aligned16(n_cand)) return HS2_ERR_INVALID_ARG;
-    if (k > 2048) return HS2_ERR_UNSUPPORTED;
+    if (k > 2048 || rows > kMaxGridY) return HS2_ERR_UNSUPPORTED;
     const SelectWs need = select_ws(nullptr, rows, row_len);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -659,6 +662,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         return HS2_ERR_INVALID_ARG;
     if (st != HS2_OK) return st;
     if (ss != HS2_OK) return ss;
+    if (B > kMaxGridY) return HS2_ERR_UNSUPPORTED;
     const DecodeWs need = decode_ws(nullptr, B, n_ctx, H, d, window, k_global);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -760,6 +764,7 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
     if (st != HS2_OK) return st;
     if (ss != HS2_OK) return ss;
+    if (B > kMaxGridY) return HS2_ERR_UNSUPPORTED;
     const PrefillWs need = prefill_ws(nullptr, B, n_q, n_ctx, H, d, kv_dtype);
     if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);

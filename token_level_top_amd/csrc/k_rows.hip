@@ -139,11 +139,17 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
 #pragma unroll
     for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
 
-    // Row position of tile row `row` (tile starting at t0), -1 if empty.
+    // Row position of tile row `row` (tile starting at t0), -1 if empty. A
+    // gathered index outside [0, n_ctx) counts as empty, so a caller's bad
+    // entry never turns into an address outside the sequence's cache rows.
     auto row_pos = [&](int64_t t0, int row) -> int {
         const int64_t r = t0 + row;
         if (r >= r_end) return -1;
-        return GATHER ? idx_lds[(r - r_begin) % kIdxChunk] : (int)r;
+        if constexpr (GATHER) {
+            const int p = idx_lds[(r - r_begin) % kIdxChunk];
+            return (uint32_t)p < (uint32_t)a.n_ctx ? p : -1;
+        }
+        return (int)r;
     };
     // stage index entries [c0, c0 + kIdxChunk) of the split (GATHER)
     auto stage_idx = [&](int64_t c0) {
