@@ -151,6 +151,24 @@ int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, con
                     void* stream);
 
 /*
+ * hs2_sparse_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same layers, kernels and results, with the split partials kept in a
+ * library-owned device array (8 MiB per GPU, held until the process ends)
+ * instead of a caller workspace. Arguments, layouts and errors as for
+ * hs2_sparse_attn, without the workspace. It calls no allocating routine;
+ * the first call on a device looks the array up (hipGetSymbolAddress).
+ * Shapes whose partials need more than 8 MiB return HS2_ERR_UNSUPPORTED
+ * (none with the library's split policy: at most 4.1 MiB). The array of the
+ * current device is used, so `stream` must belong to it, and calls that
+ * overlap in time on one GPU (other streams or threads) race on the array.
+ */
+int hs2_sparse_attn_noalloc(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                            const float* k_scale, const float* v_scale, int kv_dtype, int B,
+                            int64_t n_q, int64_t n_ctx, int H, int d, const int32_t* indices,
+                            int n_sel, float sm_scale, void* out, float* lse, void* stream);
+
+/*
  * One decode step of a hybrid block: for every sequence the newest token
  * (position n_ctx-1, already in the cache) runs the full layer with
  * selection, then n_sparse sparse layers reuse the indices.

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -229,3 +229,25 @@ def test_batch_limits_of_the_launch_grid():
     sel = [FAKE, 1, FAKE, FAKE, None, None, 1, big, 1, 0, 100, 16, 128, 64, 16, 0.1, FAKE, FAKE, FAKE, None,
            None, 0, None]
     assert L.hs2_block_attn_select(*sel) == E.HS2_ERR_UNSUPPORTED
+
+
+def test_sparse_attn_noalloc_validation():
+    """The no-allocation variant checks its arguments like hs2_sparse_attn
+    (no workspace) before it touches the device."""
+    L = hs2.lib()
+    E = hs2
+    # q, qdt, n_layers, k, v, ks, vs, kvdt, B, n_q, n_ctx, H, d, idx, n_sel, scale, out, lse, stream
+    args = [FAKE, 1, 2, FAKE, FAKE, None, None, 1, 64, 1, 5000, 16, 128, FAKE, 1152, 0.1, FAKE, None, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_sparse_attn_noalloc(*a)
+
+    assert call(a14=0) == E.HS2_ERR_INVALID_ARG
+    assert call(a14=5000) == E.HS2_ERR_UNSUPPORTED
+    assert call(a13=None) == E.HS2_ERR_INVALID_ARG
+    assert call(a0=MIS) == E.HS2_ERR_INVALID_ARG
+    assert call(a11=12) == E.HS2_ERR_UNSUPPORTED
+    assert call(a2=0) == E.HS2_OK              # no layers: nothing enqueued, no device touched

@@ -33,6 +33,8 @@ _SIGS = {
                          _p, _sz, _p], _i),
     "hs2_decode_step": ([_p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _f, _p, _p,
                          _p, _p, _p, _p, _p, _sz, _p], _i),
+    "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
+                                 _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
     "hs2_kv_project": ([_p, _i64, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p], _i),
     "hs2_block_attn_select": ([_p, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _i, _i, _f, _p, _p,
@@ -151,6 +153,24 @@ def sparse_attn(q, k, v, k_scale=None, v_scale=None, *, indices, sm_scale: float
                                B, n_q, n_ctx, H, d, _ptr(indices), n_sel, sm_scale, _ptr(out), _ptr(lse),
                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check("hs2_sparse_attn", rc)
+    return out, lse
+
+
+def sparse_attn_noalloc(q, k, v, k_scale=None, v_scale=None, *, indices, sm_scale: float, out=None, lse=None,
+                        want_lse: bool = True, stream=None):
+    """hs2_sparse_attn_noalloc: sparse_attn without a workspace (the library's
+    per-GPU scratch array holds the split partials). Same shapes and returns."""
+    L, B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    n_sel = indices.shape[-1]
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((L, B, n_q, H), dtype=torch.float32, device=dev)
+    rc = lib().hs2_sparse_attn_noalloc(_ptr(q), _QDT[q.dtype], L, _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                                       _KVDT[k.dtype], B, n_q, n_ctx, H, d, _ptr(indices), n_sel, sm_scale,
+                                       _ptr(out), _ptr(lse), _stream(stream))
+    _check("hs2_sparse_attn_noalloc", rc)
     return out, lse
 
 

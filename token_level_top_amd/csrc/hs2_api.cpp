@@ -357,6 +357,37 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
 
 }  // namespace
 
+namespace hs2 {
+
+int sparse_attn_check(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* k_scale,
+                      const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+                      const int32_t* indices, int n_sel, float sm_scale, const void* out, const float* lse) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    if (n_layers < 0 || n_q <= 0 || n_sel < 1 || n_sel > 4096) return n_sel > 4096 ? HS2_ERR_UNSUPPORTED
+                                                                                   : HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if (n_layers > 0 && (!q || !out || !indices)) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
+    return st;
+}
+
+size_t sparse_attn_scratch_bytes(int B, int64_t n_q, int n_sel, int H, int d) {
+    return sparse_ws(nullptr, (int64_t)B * n_q, n_sel, H, d).bytes;
+}
+
+int sparse_attn_enqueue(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* k_scale,
+                        const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+                        const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* scratch,
+                        hipStream_t stream) {
+    if (n_layers == 0) return HS2_OK;
+    const SparseWs w = sparse_ws(scratch, (int64_t)B * n_q, n_sel, H, d);
+    return run_sparse(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, indices, n_sel,
+                      sm_scale, out, lse, w.part, stream);
+}
+
+}  // namespace hs2
+
 extern "C" {
 
 int hs2_abi_version(void) { return HS2_ABI_VERSION; }
@@ -431,20 +462,13 @@ int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, con
                     const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
                     const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* workspace,
                     size_t ws_bytes, void* stream) {
-    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
-    if (st == HS2_ERR_INVALID_ARG) return st;
-    if (n_layers < 0 || n_q <= 0 || n_sel < 1 || n_sel > 4096) return n_sel > 4096 ? HS2_ERR_UNSUPPORTED
-                                                                                   : HS2_ERR_INVALID_ARG;
-    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
-    if (n_layers > 0 && (!q || !out || !indices)) return HS2_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
+    const int st = hs2::sparse_attn_check(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H,
+                                          d, indices, n_sel, sm_scale, out, lse);
     if (st != HS2_OK) return st;
-    const SparseWs need = sparse_ws(nullptr, (int64_t)B * n_q, n_sel, H, d);
-    if (need.bytes > 0 && (!workspace || ws_bytes < need.bytes || !aligned16(workspace))) return HS2_ERR_WORKSPACE;
-    if (n_layers == 0) return HS2_OK;
-    const SparseWs w = sparse_ws(workspace, (int64_t)B * n_q, n_sel, H, d);
-    return run_sparse(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, indices, n_sel,
-                      sm_scale, out, lse, w.part, static_cast<hipStream_t>(stream));
+    const size_t need = hs2::sparse_attn_scratch_bytes(B, n_q, n_sel, H, d);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return HS2_ERR_WORKSPACE;
+    return hs2::sparse_attn_enqueue(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d,
+                                    indices, n_sel, sm_scale, out, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
 int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_layers, int d, int kv_dtype,

@@ -161,4 +161,17 @@ struct ProjectArgs {
 };
 hipError_t launch_kv_project(const ProjectArgs& a, int D, bool fp8, hipStream_t st);
 
+// ---- host layer pieces shared by the entry points that run sparse layers
+// (hs2_api.cpp): argument checks of hs2_sparse_attn (all but the workspace),
+// the scratch bytes its split partials need, and the enqueue itself over a
+// given scratch region (device memory of at least that many bytes).
+int sparse_attn_check(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* k_scale,
+                      const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+                      const int32_t* indices, int n_sel, float sm_scale, const void* out, const float* lse);
+size_t sparse_attn_scratch_bytes(int B, int64_t n_q, int n_sel, int H, int d);
+int sparse_attn_enqueue(const void* q, int q_dtype, int n_layers, const void* k, const void* v, const float* k_scale,
+                        const float* v_scale, int kv_dtype, int B, int64_t n_q, int64_t n_ctx, int H, int d,
+                        const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* scratch,
+                        hipStream_t stream);
+
 }  // namespace hs2
