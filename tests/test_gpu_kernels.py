@@ -115,6 +115,9 @@ def _rand_index_rows(rng, n_tok, n_sel, n_ctx, fill):
     (4, 6, 5000, 1152, 0),         # fp8 KV, split path
     (2, 1100, 2000, 200, 0),       # bf16, one workgroup per token (no split)
     (2, 1030, 6000, 2300, 0),      # bf16, no split, index rows longer than one LDS index chunk
+    (2, 40, 9000, 4096, 0),        # bf16, split path, the longest index rows
+    (4, 3, 3000, 2300, 2300),      # FP8, 18 splits per token
+    (4, 1023, 5000, 1152, 0),      # FP8, one workgroup per token (no split)
 ])
 def test_sparse_matches_oracle(hs2, orc, cfg, n_q, n_ctx, n_sel, fill):
     wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=n_ctx - n_q, n_ctx=n_ctx, n_needles=0, needles="none",
@@ -396,4 +399,27 @@ def test_sparse_out_of_range_entries_are_skipped(hs2, orc, cfg, n_q):
     r = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, clean, x.sm_scale, rows)
     empty = (clean < 0).all(axis=1)
     rows_close(out[0, 0][~torch.from_numpy(empty)], r["out"][~empty], RTOL[wl.kv_dtype], "sparse out")
+    lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype])
+
+
+@pytest.mark.parametrize("cfg,H,d,n_q,n_sel", [(2, 4, 64, 9, 384), (2, 8, 128, 17, 1152), (4, 8, 64, 5, 700),
+                                               (4, 4, 128, 33, 1152)])
+def test_sparse_few_tokens_head_shapes(hs2, orc, cfg, H, d, n_q, n_sel):
+    """Sparse layers for few query tokens (the split path and its combine) at
+    every head count and head dimension instantiated, bf16 and FP8 caches,
+    ragged index rows."""
+    n_ctx = 4000
+    wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=n_ctx - n_q, n_ctx=n_ctx, H=H, d=d, n_needles=0,
+                             needles="none", n_sparse=1)
+    x = make_inputs(wl)
+    rng = np.random.default_rng(n_q * 13 + H + d)
+    idx = _rand_index_rows(rng, n_q, n_sel, n_ctx, 0)
+    say("sparse few tokens", wl.name, H, d, n_q, n_sel)
+    out, lse = hs2.sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale),
+                               indices=torch.from_numpy(idx).reshape(1, n_q, n_sel).cuda(), sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    r = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, idx, x.sm_scale, list(range(n_q)))
+    empty = (idx < 0).all(axis=1)
+    rows_close(out[0, 0][~torch.from_numpy(empty)], r["out"][~empty], RTOL[wl.kv_dtype], "sparse out")
+    assert (to_np(out[0, 0])[empty] == 0).all()
     lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype])
