@@ -39,7 +39,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernel classes of the library's timing hook (include/hs2.h)
 KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
-      "prefill_final": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14, "gate_fuse": 15}
+      "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14, "gate_fuse": 15}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
 KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "kv_project": "k_project.hip"}
 
@@ -271,6 +271,8 @@ def main():
     ap.add_argument("--hysparse-blocks", action="store_true",
                     help="prefill workloads: the HySparse v1 block-level variant (64-token blocks, top 16, gated "
                          "128-token window branch) in place of token-level selection")
+    ap.add_argument("--window-sharing", action="store_true",
+                    help="prefill: sparse layers with the window shared per query block (hs2_sparse_attn_window)")
     ap.add_argument("--indexer", action="store_true",
                     help="prefill workloads: light-indexer selection (FP8 heads, see --indexer-*) in place of the full "
                          "layer, its index rows shared IndexCache-style by 1 + n_sparse sparse layers")
@@ -294,8 +296,13 @@ def main():
     from hs2_inputs import make_gates, make_indexer_inputs, make_inputs, workload
 
     wl = workload(args.config)
-    if (blocks or indexer) and wl.decode:
-        print("--hysparse-blocks and --indexer apply to the prefill workloads (1, 2, 4)", file=sys.stderr)
+    if (blocks or indexer or args.window_sharing) and wl.decode:
+        print("--hysparse-blocks, --indexer and --window-sharing apply to the prefill workloads (1, 2, 4)",
+              file=sys.stderr)
+        return 2
+    if args.window_sharing and (blocks or indexer or wl.kv_dtype == "f32"):
+        print("--window-sharing applies to the token-level path with a bf16 or FP8 cache (workloads 2, 4)",
+              file=sys.stderr)
         return 2
     log(f"workload {wl.name}: generating inputs on the host")
     t0 = time.perf_counter()
@@ -383,7 +390,11 @@ def main():
         qs = g(x.q_sparse)
         ws_full = torch.empty(hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, wl.B, wl.n_q, wl.n_ctx, hf, wl.d,
                                                  wl.window, wl.k_global, kvdt), dtype=torch.uint8, device=dev)
-        nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
+        if args.window_sharing:
+            nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN_WINDOW, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, wl.window,
+                                     wl.k_global, kvdt)
+        else:
+            nws = hs2.workspace_size(hs2.OP_SPARSE_ATTN, wl.B, wl.n_q, wl.n_ctx, wl.H, wl.d, S, 0, kvdt)
         ws_sp = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         out = torch.empty_like(q)
         lse = torch.empty((wl.B, wl.n_q, hf), device=dev)
@@ -394,8 +405,12 @@ def main():
         def step():
             hs2.full_attn_select(q, k, v, ks, vs, q_pos0=wl.q_pos0, window=wl.window, k_global=wl.k_global,
                                  sm_scale=x.sm_scale, out=out, lse=lse, indices=idx, workspace=ws_full)
-            hs2.sparse_attn(qs, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
-                            workspace=ws_sp)
+            if args.window_sharing:
+                hs2.sparse_attn_window(qs, k, v, ks, vs, indices=idx, q_pos0=wl.q_pos0, window=wl.window,
+                                       sm_scale=x.sm_scale, out=out_s, lse=lse_s, workspace=ws_sp)
+            else:
+                hs2.sparse_attn(qs, k, v, ks, vs, indices=idx, sm_scale=x.sm_scale, out=out_s, lse=lse_s,
+                                workspace=ws_sp)
 
     copy_calibration(args.copy_calibration_mib, dev)
 
@@ -486,7 +501,8 @@ def main():
            "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
            "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else "")
-                      + (f"_full_heads{hf}" if args.full_heads else ""),
+                      + (f"_full_heads{hf}" if args.full_heads else "")
+                      + ("_window_sharing" if args.window_sharing and not wl.decode else ""),
                       "B": wl.B, "H_full": hf, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},

@@ -83,7 +83,8 @@ typedef enum {
     HS2_OP_SELECT_TOPK = 3,
     HS2_OP_BLOCK_ATTN_SELECT = 4,
     HS2_OP_BLOCK_SPARSE_ATTN = 5,
-    HS2_OP_INDEX_SELECT = 6
+    HS2_OP_INDEX_SELECT = 6,
+    HS2_OP_SPARSE_ATTN_WINDOW = 7
 } hs2_op;
 
 /* HS2_ABI_VERSION of the built library. */
@@ -98,7 +99,8 @@ const char* hs2_status_string(int status);
  * length and k_global = k; the other arguments are ignored. For
  * HS2_OP_BLOCK_SPARSE_ATTN pass window, k_global = k_blocks and, in place of
  * kv_dtype, the query type. For HS2_OP_INDEX_SELECT pass d = the indexer
- * head dimension dI. Pure host code.
+ * head dimension dI. For HS2_OP_SPARSE_ATTN_WINDOW the size does not depend
+ * on n_ctx or on the first query's position. Pure host code.
  */
 size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int d, int window,
                           int k_global, int kv_dtype);
@@ -149,6 +151,39 @@ int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, con
                     int64_t n_ctx, int H, int d, const int32_t* indices, int n_sel,
                     float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
                     void* stream);
+
+/*
+ * The sparse layers of hs2_sparse_attn for index rows laid out as the full
+ * layer writes them (a window part, then a global part), with the window
+ * shared across a block of consecutive queries (the HySparse2 page, section
+ * "전제와 한계", names cheaper sparse layers as future work): consecutive
+ * tokens' windows overlap in all but one position, so instead of gathering
+ * each token's window rows again, one dense pass per block of 256/H
+ * consecutive queries reads the band of window + 256/H - 1 keys once and
+ * computes every row's window attention from it; the gathered global part is
+ * then merged with it by the log-sum-exp rule. The result is the softmax over
+ * the union, as hs2_sparse_attn computes it over the whole row.
+ *   q        [n_layers][B][n_q][H][d]   q_dtype; query i at position q_pos0 + i
+ *   k, v, k_scale, v_scale              as for hs2_full_attn_select
+ *   indices  [B][n_q][window + k_global] int32: entries [0, window) are not
+ *            read (the window of a query at p is max(0, p-window+1) .. p,
+ *            whatever they hold); entries [window, window + k_global) are
+ *            the global positions, which must lie at or below p - window
+ *            (as hs2_full_attn_select, hs2_decode_step and hs2_index_select
+ *            write them); an entry outside [0, n_ctx) is skipped
+ *   out, lse as for hs2_sparse_attn
+ *   workspace >= hs2_workspace_size(HS2_OP_SPARSE_ATTN_WINDOW, B, n_q, n_ctx,
+ *                H, d, window, k_global, kv_dtype) bytes
+ * bf16 or FP8 caches (fp32: HS2_ERR_UNSUPPORTED); window and k_global as for
+ * hs2_full_attn_select; 0 <= q_pos0, q_pos0 + n_q <= n_ctx; d * n_ctx < 2^31.
+ * The window pass multiplies P by V as pass 1 of the full layer does (an FP8
+ * V in the bf16 rounding of code x v_scale).
+ */
+int hs2_sparse_attn_window(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                           const float* k_scale, const float* v_scale, int kv_dtype, int B,
+                           int64_t n_q, int64_t q_pos0, int64_t n_ctx, int H, int d,
+                           const int32_t* indices, int window, int k_global, float sm_scale,
+                           void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * hs2_sparse_attn for callers that cannot allocate device memory (code under
@@ -315,7 +350,7 @@ int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* we
  *   bit 4 selection candidates         bit 5 selection final
  *   bit 6 sparse-layer attention       bit 7 prefill K/V preparation
  *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
- *   bit 10 prefill final selection     bit 11 buffer fills
+ *   bit 10 window pass (window sharing) bit 11 buffer fills
  *   bit 12 KV Bridging projections     bit 13 block scores (block mode)
  *   bit 14 block choice / expansion    bit 15 two-branch gate fusion
  * (the light indexer's scoring and selection report as bit 9, its key

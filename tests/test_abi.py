@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -38,7 +38,14 @@ def test_workspace_sizes():
     assert ws(hs2.OP_SPARSE_ATTN, 1, 4096, 5000, 16, 128, 1152, 0, hs2.HS2_BF16) == 0   # no split
     assert ws(hs2.OP_SPARSE_ATTN, 64, 1, 5000, 16, 128, 1152, 0, hs2.HS2_BF16) > 0
     with pytest.raises(ValueError):
-        ws(7, 1, 1, 1, 16, 128, 128, 1024, 1)
+        ws(8, 1, 1, 1, 16, 128, 128, 1024, 1)
+    # the window-sharing sparse layers: band copies of n_q + window + 62 rows
+    # (rounded to 64) whatever n_ctx is, plus one partial record per token
+    w1 = ws(hs2.OP_SPARSE_ATTN_WINDOW, 1, 8192, 262144, 16, 128, 128, 1024, hs2.HS2_FP8_E4M3)
+    w2 = ws(hs2.OP_SPARSE_ATTN_WINDOW, 1, 8192, 9000, 16, 128, 128, 1024, hs2.HS2_FP8_E4M3)
+    assert w1 == w2 and w1 >= 8192 * 16 * 130 * 4 + 2 * (2 * 8384 * 128)
+    with pytest.raises(ValueError):
+        ws(hs2.OP_SPARSE_ATTN_WINDOW, 1, 10, 100, 16, 128, 0, 1024, 1)   # window < 1
 
 
 def _full(**kw):
@@ -251,3 +258,30 @@ def test_sparse_attn_noalloc_validation():
     assert call(a0=MIS) == E.HS2_ERR_INVALID_ARG
     assert call(a11=12) == E.HS2_ERR_UNSUPPORTED
     assert call(a2=0) == E.HS2_OK              # no layers: nothing enqueued, no device touched
+
+
+def test_sparse_attn_window_validation():
+    L = hs2.lib()
+    E = hs2
+    # q, qdt, n_layers, k, v, ks, vs, kvdt, B, n_q, q_pos0, n_ctx, H, d, idx, window, k_global, scale, out, lse,
+    # ws, wsb, stream
+    args = [FAKE, 1, 2, FAKE, FAKE, None, None, 1, 1, 100, 900, 1000, 16, 128, FAKE, 128, 1024, 0.1, FAKE, None,
+            None, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_sparse_attn_window(*a)
+
+    assert call() == E.HS2_ERR_WORKSPACE
+    assert call(a10=901) == E.HS2_ERR_INVALID_ARG            # q_pos0 + n_q > n_ctx
+    assert call(a10=-1) == E.HS2_ERR_INVALID_ARG
+    assert call(a15=0) == E.HS2_ERR_INVALID_ARG              # window
+    assert call(a16=-1) == E.HS2_ERR_INVALID_ARG
+    assert call(a16=4096) == E.HS2_ERR_UNSUPPORTED           # k_global > 2048
+    assert call(a14=None) == E.HS2_ERR_INVALID_ARG           # indices needed when k_global > 0
+    assert call(a0=MIS) == E.HS2_ERR_INVALID_ARG
+    assert call(a1=0, a7=0) == E.HS2_ERR_UNSUPPORTED         # fp32 cache
+    assert call(a8=65536) == E.HS2_ERR_UNSUPPORTED           # batch limit
+    assert call(a2=0) == E.HS2_ERR_WORKSPACE                 # no layers, but still no workspace

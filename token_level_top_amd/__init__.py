@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhs2.so")
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = range(5)
 HS2_F32, HS2_BF16, HS2_FP8_E4M3 = 0, 1, 2
 OP_FULL_ATTN_SELECT, OP_DECODE_STEP, OP_SPARSE_ATTN, OP_SELECT_TOPK = 0, 1, 2, 3
-OP_BLOCK_ATTN_SELECT, OP_BLOCK_SPARSE_ATTN, OP_INDEX_SELECT = 4, 5, 6
+OP_BLOCK_ATTN_SELECT, OP_BLOCK_SPARSE_ATTN, OP_INDEX_SELECT, OP_SPARSE_ATTN_WINDOW = 4, 5, 6, 7
 
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
@@ -33,6 +33,8 @@ _SIGS = {
                          _p, _sz, _p], _i),
     "hs2_decode_step": ([_p, _p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i, _i, _i, _i, _f, _p, _p,
                          _p, _p, _p, _p, _p, _sz, _p], _i),
+    "hs2_sparse_attn_window": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _p, _i, _i, _f, _p,
+                                _p, _p, _sz, _p], _i),
     "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
                                  _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
@@ -153,6 +155,29 @@ def sparse_attn(q, k, v, k_scale=None, v_scale=None, *, indices, sm_scale: float
                                B, n_q, n_ctx, H, d, _ptr(indices), n_sel, sm_scale, _ptr(out), _ptr(lse),
                                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check("hs2_sparse_attn", rc)
+    return out, lse
+
+
+def sparse_attn_window(q, k, v, k_scale=None, v_scale=None, *, indices, q_pos0: int, window: int, sm_scale: float,
+                       out=None, lse=None, want_lse: bool = True, workspace=None, stream=None):
+    """hs2_sparse_attn_window: sparse layers over full-layer index rows
+    [B][n_q][window + k_global] with the window shared per query block.
+    q [L][B][n_q][H][d]. Returns (out [L][B][n_q][H][d], lse [L][B][n_q][H] or None)."""
+    L, B, n_q, H, d = q.shape
+    n_ctx = k.shape[1]
+    k_global = indices.shape[-1] - window
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((L, B, n_q, H), dtype=torch.float32, device=dev)
+    kvdt = _KVDT[k.dtype]
+    ws = _workspace(workspace_size(OP_SPARSE_ATTN_WINDOW, B, n_q, n_ctx, H, d, window, k_global, kvdt), dev,
+                    workspace)
+    rc = lib().hs2_sparse_attn_window(_ptr(q), _QDT[q.dtype], L, _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), kvdt,
+                                      B, n_q, q_pos0, n_ctx, H, d, _ptr(indices), window, k_global, sm_scale,
+                                      _ptr(out), _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
+                                      _stream(stream))
+    _check("hs2_sparse_attn_window", rc)
     return out, lse
 
 

@@ -244,10 +244,40 @@ IndexWs index_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int dI) {
     return w;
 }
 
+// window-sharing sparse layers: V^T (and the widened FP8 K) of the cache rows
+// the window pass reaches -- from j_lo, the first query's window start rounded
+// down to 64, ld rows, at most n_q + window + 62 rounded up to 64 whatever
+// q_pos0 is -- and the partial records: [n_tok][H (d+2)] merged by the gather
+// kernel, or with split gathers [n_tok][n_split + 1][H (d+2)] (the window's
+// record last) merged by the combine
+struct WinWs {
+    void* vt;
+    uint16_t* kc;
+    float* rec;
+    int64_t j_lo, ld;
+    int n_split;
+    size_t bytes;
+};
+WinWs win_ws(void* base, int B, int64_t n_q, int64_t q_pos0, int H, int d, int window, int k_global, int kv_dtype) {
+    Carver c(base);
+    WinWs w;
+    const int64_t n_tok = (int64_t)B * n_q;
+    const int64_t first = q_pos0 - window + 1 > 0 ? q_pos0 - window + 1 : 0;
+    w.j_lo = first / kVtPad * kVtPad;
+    w.ld = (n_q + window + 62 + kVtPad - 1) / kVtPad * kVtPad;
+    w.n_split = k_global > 0 ? sparse_splits(n_tok, k_global) : 1;
+    w.vt = c.take<void>(2 * (size_t)B * d * w.ld);
+    w.kc = kv_dtype == HS2_FP8_E4M3 ? c.take<uint16_t>(2 * (size_t)B * w.ld * d) : nullptr;
+    const int recs = w.n_split > 1 ? w.n_split + 1 : 1;
+    w.rec = c.take<float>(sizeof(float) * (size_t)n_tok * recs * H * (d + 2));
+    w.bytes = c.used;
+    return w;
+}
+
 // ---- measurement hook: hipEvents around launches of selected kernel classes
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
-    KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_PF_FINAL = 10, KC_FILL = 11,
+    KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_WINDOW = 10, KC_FILL = 11,
     KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14, KC_GATE = 15
 };
 struct TimedPair {
@@ -449,6 +479,9 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
         case HS2_OP_INDEX_SELECT:
             if (n_q <= 0 || d <= 0) return SIZE_MAX;
             return index_ws(nullptr, B, n_q, n_ctx, d).bytes;
+        case HS2_OP_SPARSE_ATTN_WINDOW:
+            if (n_q <= 0 || H <= 0 || d <= 0 || window < 1 || k_global < 0 || !dtype_known(kv_dtype)) return SIZE_MAX;
+            return win_ws(nullptr, B, n_q, 0, H, d, window, k_global, kv_dtype).bytes;
         case HS2_OP_BLOCK_SPARSE_ATTN:
             if (n_q <= 0 || H <= 0 || d <= 0 || window < 1 || k_global < 1 || !dtype_known(kv_dtype))
                 return SIZE_MAX;
@@ -469,6 +502,98 @@ int hs2_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, con
     if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return HS2_ERR_WORKSPACE;
     return hs2::sparse_attn_enqueue(q, q_dtype, n_layers, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d,
                                     indices, n_sel, sm_scale, out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+int hs2_sparse_attn_window(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
+                           const float* k_scale, const float* v_scale, int kv_dtype, int B, int64_t n_q,
+                           int64_t q_pos0, int64_t n_ctx, int H, int d, const int32_t* indices, int window,
+                           int k_global, float sm_scale, void* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    int st = check_common(q_dtype, kv_dtype, k, v, k_scale, v_scale, B, n_ctx, H, d, sm_scale);
+    if (st == HS2_ERR_INVALID_ARG) return st;
+    int ss = check_select_shape(window, k_global);
+    if (ss == HS2_ERR_INVALID_ARG) return ss;
+    if (n_layers < 0 || n_q <= 0 || q_pos0 < 0 || q_pos0 + n_q > n_ctx) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)B * n_q >= (int64_t(1) << 31) / 2) return HS2_ERR_INVALID_ARG;
+    if (n_layers > 0 && (!q || !out || (k_global > 0 && !indices))) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(indices)) return HS2_ERR_INVALID_ARG;
+    if (st != HS2_OK) return st;
+    if (ss != HS2_OK) return ss;
+    if (kv_dtype == HS2_F32 || B > kMaxGridY) return HS2_ERR_UNSUPPORTED;
+    const WinWs need = win_ws(nullptr, B, n_q, q_pos0, H, d, window, k_global, kv_dtype);
+    // 32-bit element offsets inside the window pass's copies
+    if (need.ld * (int64_t)d >= (int64_t(1) << 31) || n_ctx * (int64_t)d >= (int64_t(1) << 31))
+        return HS2_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    if (n_layers == 0) return HS2_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const WinWs w = win_ws(workspace, B, n_q, q_pos0, H, d, window, k_global, kv_dtype);
+    const int64_t n_tok = (int64_t)B * n_q;
+    const int ns = w.n_split;
+    const size_t rec = (size_t)H * (d + 2);
+    const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, w.j_lo, w.ld, w.ld, d, w.kc, w.vt,
+                                             s)));
+    for (int l = 0; l < n_layers; ++l) {
+        const void* ql = static_cast<const char*>(q) + qstride * l;
+        void* ol = static_cast<char*>(out) + qstride * l;
+        float* ll = lse ? lse + (size_t)n_tok * H * l : nullptr;
+        // 1. the window part: one dense band per query block
+        PrefillArgs pa{};
+        pa.q = ql;
+        pa.k = k;
+        pa.kc = w.kc;
+        pa.vt = w.vt;
+        pa.ks = k_scale;
+        pa.vs = v_scale;
+        pa.n_q = n_q;
+        pa.q_pos0 = q_pos0;
+        pa.n_ctx = n_ctx;
+        pa.n_ctx_pad = w.ld;
+        pa.kv_off = w.j_lo;
+        pa.kc_rows = w.ld;
+        pa.B = B;
+        pa.scale_log2 = sm_scale * kLog2eF;
+        pa.window = window;
+        pa.win_rec = ns > 1 ? w.rec + (size_t)ns * rec : w.rec;
+        pa.win_stride = (int64_t)(ns > 1 ? ns + 1 : 1) * (int64_t)rec;
+        HS2_TRY(TIMED(KC_WINDOW, s, launch_window_attn(pa, H, d, kv_dtype, s)));
+        // 2. the global part, gathered, merged with the window's record
+        RowsArgs a{};
+        a.q = ql;
+        a.k = k;
+        a.v = v;
+        a.ks = k_scale;
+        a.vs = v_scale;
+        a.idx = indices ? indices + window : nullptr;
+        a.idx_stride = window + k_global;
+        a.n_ctx = n_ctx;
+        a.n_rows = k_global;
+        a.n_tok = (int)n_tok;
+        a.n_q = (int)n_q;
+        a.n_split = ns;
+        a.rows_per_split = k_global > 0 ? sparse_rows_per_split(n_tok, k_global) : kTile;
+        a.scale_log2 = sm_scale * kLog2eF;
+        if (ns > 1) {
+            a.part = w.rec;
+            a.part_stride = ns + 1;
+        } else {
+            a.out = ol;
+            a.lse = ll;
+            a.win_rec = w.rec;
+        }
+        HS2_TRY(TIMED(KC_SPARSE, s, launch_rows_attn(a, H, d, kv_dtype, true, false, s)));
+        if (ns > 1) {
+            CombineArgs c{};
+            c.part = w.rec;
+            c.n_tok = (int)n_tok;
+            c.n_split = ns + 1;
+            c.out = ol;
+            c.lse = ll;
+            HS2_TRY(TIMED(KC_COMBINE, s, launch_combine(c, H, d, q_dtype, s)));
+        }
+    }
+    return HS2_OK;
 }
 
 int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_layers, int d, int kv_dtype,
@@ -536,7 +661,7 @@ int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void*
     a.block_scores = block_scores;
     a.block_keys = w.keys;
     a.block_stride = w.key_stride;
-    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, 0, w.n_ctx_pad, n_ctx, d, w.kc, w.vt, s)));
     HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
     HS2_TRY(TIMED(KC_BLOCK_SCORE, s, launch_block_score(a, H, d, kv_dtype, s)));
     BlockArgs ba{};
@@ -814,7 +939,7 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     a.cand = w.cand;
     a.cand_cap = kPrefillCandCap;
     a.indices = indices;
-    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, w.n_ctx_pad, d, w.kc, w.vt, s)));
+    HS2_TRY(TIMED(KC_PREP, s, launch_prep_kv(k, v, v_scale, kv_dtype, B, n_ctx, 0, w.n_ctx_pad, n_ctx, d, w.kc, w.vt, s)));
     HS2_TRY(TIMED(KC_FWD, s, launch_attn_fwd(a, H, d, kv_dtype, s)));
     HS2_TRY(TIMED(KC_STREAM, s, launch_score_stream(a, H, d, kv_dtype, s)));
     return HS2_OK;

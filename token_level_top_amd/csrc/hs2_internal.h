@@ -27,6 +27,14 @@ struct RowsArgs {
     void* out;              // n_split == 1: [n_tok][H][D] in the query type
     float* lse;             // n_split == 1: [n_tok][H] natural log, nullable
     float* lse2;            // n_split == 1: [n_tok][H] base 2, nullable
+    // gather: entries between consecutive tokens' index rows (0: n_rows)
+    int64_t idx_stride;
+    // n_split > 1: partial records between consecutive tokens (0: n_split)
+    int part_stride;
+    // n_split == 1, nullable: a partial record (m[H], l[H], O[H][D], base 2)
+    // per token, at win_rec + token * H * (D + 2), merged into the result
+    // (the window pass of the window-sharing sparse layers)
+    const float* win_rec;
 };
 
 struct CombineArgs {
@@ -116,10 +124,23 @@ struct PrefillArgs {
     // keys widened to bf16, ks their scales; per (token, head) weight and scale
     const float* idx_w;     // [B][n_q][H]
     const float* idx_qs;    // [B][n_q][H]
+    // window pass of the window-sharing sparse layers (launch_window_attn):
+    // vt and kc hold cache rows kv_off.. only (vt columns and kc rows are
+    // relative to kv_off; kc has kc_rows rows per sequence), and each
+    // (token, head) row attends to positions max(0, p - window + 1) .. p; the
+    // result is written as a partial record (m, l, O unnormalised, base 2) per
+    // token at win_rec + token * win_stride floats: m[H], l[H], O[H][D]
+    int64_t kv_off, kc_rows;
+    float* win_rec;
+    int64_t win_stride;
 };
+// rows j_lo .. j_lo + ld - 1 of every sequence (ld a multiple of 64): V^T into vt
+// [B][D][ld] (column j - j_lo), FP8 K widened into kc [B][kc_rows][D] (row j - j_lo)
 hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
-                          int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st);
+                          int64_t j_lo, int64_t ld, int64_t kc_rows, int D, uint16_t* kc, void* vt, hipStream_t st);
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
+// the window pass (bf16 / FP8 caches): pass 1 over each row's window only
+hipError_t launch_window_attn(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
 // pass 2 also writes the index rows (window + global part)
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st);
 // block mode of pass 2: block scores and rank keys of every block up to the

@@ -71,20 +71,26 @@ __device__ __forceinline__ f32x16 mfma32(const float* a, const float* b, f32x16 
 }
 
 // ------------------------------------------------------------------ prep_kv
-// grid (n_ctx_pad / 64, B), 256 threads. V^T[b][d][j] for j < n_ctx_pad (0 past
-// n_ctx); FP8: kc[b][j][d] = bf16(code value), exact.
+// grid (ld / 64, B), 256 threads, over cache rows j = j_lo .. j_lo + ld - 1 (the
+// full layer: j_lo = 0, ld = n_ctx padded to 64; the window pass of the
+// window-sharing sparse layers: the rows its query blocks can reach).
+// V^T[b][d][j - j_lo] (ld columns; 0 past n_ctx); FP8: kc[b][j - j_lo][d] =
+// bf16(code value), exact, kc_rows rows per sequence (rows past n_ctx are not
+// written).
 template <int D, int KV>
 __global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void* v, const float* vs, int64_t n_ctx,
-                                                      int64_t n_ctx_pad, uint16_t* kc, void* vt) {
+                                                      int64_t j_lo, int64_t ld, int64_t kc_rows, uint16_t* kc,
+                                                      void* vt) {
     constexpr bool F32 = KV == DT_F32;
     using LT = typename PfTypes<F32>::L;
     __shared__ LT tile[kPfTile][D + 1];
     const int b = blockIdx.y;
-    const int64_t j0 = (int64_t)blockIdx.x * kPfTile;
+    const int64_t r0 = (int64_t)blockIdx.x * kPfTile;  // first column of this block in the copy
     const size_t base = (size_t)b * (size_t)n_ctx;
+    const size_t kc_base = (size_t)b * (size_t)kc_rows;
     for (int e = threadIdx.x; e < kPfTile * D; e += 256) {
         const int r = e / D, c = e % D;
-        const int64_t j = j0 + r;
+        const int64_t j = j_lo + r0 + r;
         LT val = 0;
         if (j < n_ctx) {
             const size_t gi = (base + (size_t)j) * D + c;
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void*
                 fp8x4_to_f32(code, f);
                 val = f32_to_bf16_bits(f[0] * vs[base + (size_t)j]);
                 const uint32_t kcode = reinterpret_cast<const uint8_t*>(k)[gi];
-                kc[gi] = (uint16_t)(fp8x4_to_bf16x4(kcode)[0] & 0xFFFFu);
+                kc[(kc_base + (size_t)(j - j_lo)) * D + c] = (uint16_t)(fp8x4_to_bf16x4(kcode)[0] & 0xFFFFu);
             }
         }
         tile[r][c] = val;
@@ -107,20 +113,20 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(const void* k, const void*
     // bf16 V^T: within every 16 keys the middle two quads are swapped (keys
     // 0-3 8-11 4-7 12-15), so that the 8 keys one lane of the PV MFMA takes
     // are one contiguous 16-byte piece
-    LT* out = reinterpret_cast<LT*>(vt) + (size_t)b * D * (size_t)n_ctx_pad;
+    LT* out = reinterpret_cast<LT*>(vt) + (size_t)b * D * (size_t)ld;
     for (int e = threadIdx.x; e < kPfTile * D; e += 256) {
         const int c = e / kPfTile, r = e % kPfTile;
         const int q = (r >> 2) & 3;
         const int slot = F32 ? r : (r & ~15) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2) | (r & 3);
-        out[(size_t)c * n_ctx_pad + j0 + slot] = tile[r][c];
+        out[(size_t)c * ld + r0 + slot] = tile[r][c];
     }
 }
 
-hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx,
-                          int64_t n_ctx_pad, int D, uint16_t* kc, void* vt, hipStream_t st) {
-    dim3 grid((unsigned)(n_ctx_pad / kPfTile), (unsigned)B);
+hipError_t launch_prep_kv(const void* k, const void* v, const float* vs, int kv, int B, int64_t n_ctx, int64_t j_lo,
+                          int64_t ld, int64_t kc_rows, int D, uint16_t* kc, void* vt, hipStream_t st) {
+    dim3 grid((unsigned)(ld / kPfTile), (unsigned)B);
 #define HS2_PREP(DD, KK) \
-    hipLaunchKernelGGL((prep_kv_kernel<DD, KK>), grid, dim3(256), 0, st, k, v, vs, n_ctx, n_ctx_pad, kc, vt)
+    hipLaunchKernelGGL((prep_kv_kernel<DD, KK>), grid, dim3(256), 0, st, k, v, vs, n_ctx, j_lo, ld, kc_rows, kc, vt)
     if (D == 64) {
         if (kv == DT_F32) HS2_PREP(64, DT_F32);
         else if (kv == DT_BF16) HS2_PREP(64, DT_BF16);
@@ -458,6 +464,9 @@ struct PipeStage {
     static constexpr int VPT = WITH_V ? (VCH + NT - 1) / NT : 0;
     u32x4 kr[KPT], vr[VPT > 0 ? VPT : 1];
     f32x4 cr;
+    // first cache row held by the K buffer and by the V^T copy (0 unless they
+    // hold a row range only)
+    int k_off = 0, v_off = 0;
 
     // Tile t: K rows 64t.. (clamped into the cache; rows past the end are
     // masked by causality), V^T columns 64t.. of the zero-padded copy, and
@@ -469,12 +478,12 @@ struct PipeStage {
         for (int i = 0; i < KPT; ++i) {
             const int ch = min(tid + NT * i, KCH - 1), row = ch / (D / 8), cc = ch % (D / 8);
             const int j = min(j0 + row, n_ctx - 1);
-            kr[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)(j * D + cc * 8));
+            kr[i] = *reinterpret_cast<const u32x4*>(kb + (uint32_t)((j - k_off) * D + cc * 8));
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int ch = min(tid + NT * i, VCH - 1), d = ch / (kPfTile / 8), cc = ch % (kPfTile / 8);
-            vr[i] = *reinterpret_cast<const u32x4*>(vtb + (uint32_t)(d * n_ctx_pad + j0 + cc * 8));
+            vr[i] = *reinterpret_cast<const u32x4*>(vtb + (uint32_t)(d * n_ctx_pad + j0 - v_off + cc * 8));
         }
         if constexpr (SCALED) {
             if (tid < kPfTile / 4) {
@@ -502,11 +511,15 @@ struct PipeStage {
     }
 };
 
-template <int H, int D, int KV, int RB, int NW, bool PIPE>
+template <int H, int D, int KV, int RB, int NW, bool PIPE, bool WIN = false>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     // NW waves of RB 32-row blocks each: 32 NW RB (token, head) rows per
     // workgroup; every K or V^T fragment read from LDS feeds RB MFMAs. PIPE
     // issues the QK^T MFMAs of the next block beside the current softmax.
+    // WIN: the window pass of the window-sharing sparse layers -- each row
+    // attends to positions max(0, p - window + 1) .. p only, so a workgroup's
+    // 256/H consecutive tokens share one dense band of window + 256/H - 1
+    // keys; the result is a partial record (m, l, O) per token.
     constexpr bool SCALED = KV == DT_FP8;
     constexpr int NT = 64 * NW;
     using Stage = PipeStage<D, SCALED, NT>;
@@ -547,11 +560,14 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
             qf[r][s] = row_ok[r] ? w4 : u32x4{0, 0, 0, 0};
         }
     }
-    const uint16_t* kb = (SCALED ? a.kc : reinterpret_cast<const uint16_t*>(a.k)) + (size_t)b * a.n_ctx * D;
+    // (the FP8 K copy holds kc_rows rows per sequence, n_ctx unless set)
+    const uint16_t* kb = SCALED ? a.kc + (size_t)b * (size_t)(a.kc_rows ? a.kc_rows : a.n_ctx) * D
+                                : reinterpret_cast<const uint16_t*>(a.k) + (size_t)b * a.n_ctx * D;
     const uint16_t* vtb = reinterpret_cast<const uint16_t*>(a.vt) + (size_t)b * D * a.n_ctx_pad;
     const float* ksb = SCALED ? a.ks + (size_t)b * a.n_ctx : nullptr;
     const int n_ctx = (int)a.n_ctx, n_ctx_pad = (int)a.n_ctx_pad;
     const float scale_log2 = a.scale_log2;
+    const int W = a.window;
 
     float m_run[RB], l_run[RB];
     f32x16 o_acc[RB][NDT];
@@ -566,7 +582,10 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     }
 
     const int n_tiles = (int)((p_max + kPfTile) / kPfTile);
-    const int n_full = min<int>(n_tiles, (int)((p_min + 1) / kPfTile));  // tiles needing no causal mask
+    // first tile: 0, or (WIN) the tile of the block's lowest window position
+    const int T0 = WIN ? (int)(max<int64_t>(0, p_min - W + 1) / kPfTile) : 0;
+    // tiles needing no mask (WIN: every tile is masked)
+    const int n_full = WIN ? T0 : min<int>(n_tiles, (int)((p_min + 1) / kPfTile));
 
     // S^T blocks of keys 32*sub.. of an LDS tile (M) x each row block (N)
     auto qk = [&](int buf, int sub, f32x16* acc) {
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     // holds key 32*sub + 8(i/4) + 4hh + i%4; keys with 8(i/4) + i%4 > rel are
     // masked.
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-    auto softmax = [&](const f32x16& s, int r, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+    auto softmax = [&](const f32x16& s, int r, int buf, int sub, int rel, int lo, u32x4* pb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         float c[16];
         if constexpr (SCALED) {
@@ -607,7 +626,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
         for (int i = 0; i < 16; ++i) {
             p[i] = fast_exp2(__builtin_fmaf(s[i], c[i], -m_run[r]));
             if constexpr (MASK) {
-                if (32 * sub + 8 * (i >> 2) + (i & 3) > rel) p[i] = 0.f;
+                const int kk = 32 * sub + 8 * (i >> 2) + (i & 3);
+                if (kk > rel || (WIN && kk < lo)) p[i] = 0.f;
             }
         }
         float ps = 0.f;
@@ -623,7 +643,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     };
     // rare: some term of the block exceeded 2^kLazy (or this is the row's first
     // block); raise m_run to the block's row maximum, rescale, redo the block
-    auto settle = [&](float& ps, const f32x16& s, int r, int buf, int sub, int rel, u32x4* pb, auto mask_tag) {
+    auto settle = [&](float& ps, const f32x16& s, int r, int buf, int sub, int rel, int lo, u32x4* pb,
+                      auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         if (__ballot(!(ps <= kPsumMax))) {
             float mx = -INFINITY;
@@ -632,7 +653,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
                 const int kk = 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
                 const float ci = SCALED ? c_lds[buf][kk] : scale_log2;
                 float v = s[i] * ci;
-                if (MASK && 32 * sub + 8 * (i >> 2) + (i & 3) > rel) v = -INFINITY;
+                const int kr = 32 * sub + 8 * (i >> 2) + (i & 3);
+                if (MASK && (kr > rel || (WIN && kr < lo))) v = -INFINITY;
                 mx = fmaxf(mx, v);
             }
             mx = fmaxf(mx, xor32(mx));
@@ -642,7 +664,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
             l_run[r] *= alpha;
 #pragma unroll
             for (int t = 0; t < NDT; ++t) o_acc[r][t] *= alpha;
-            ps = softmax(s, r, buf, sub, rel, pb, mask_tag);
+            ps = softmax(s, r, buf, sub, rel, lo, pb, mask_tag);
         }
         l_run[r] += ps;
     };
@@ -659,19 +681,24 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
                     o_acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pb[r][c]), o_acc[r][t], 0, 0, 0);
             }
     };
-    auto softmax_all = [&](f32x16* s, int buf, int sub, const int* rel, u32x4 (*pb)[2], auto mask_tag) {
+    auto softmax_all = [&](f32x16* s, int buf, int sub, const int* rel, const int* lo, u32x4 (*pb)[2],
+                           auto mask_tag) {
         float ps[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) ps[r] = softmax(s[r], r, buf, sub, rel[r], pb[r], mask_tag);
+        for (int r = 0; r < RB; ++r) ps[r] = softmax(s[r], r, buf, sub, rel[r], lo[r], pb[r], mask_tag);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) settle(ps[r], s[r], r, buf, sub, rel[r], pb[r], mask_tag);
+        for (int r = 0; r < RB; ++r) settle(ps[r], s[r], r, buf, sub, rel[r], lo[r], pb[r], mask_tag);
     };
 
     Stage stg;
-    stg.load(kb, vtb, ksb, 0, n_ctx, n_ctx_pad);
+    if constexpr (WIN) {
+        stg.k_off = SCALED ? (int)a.kv_off : 0;
+        stg.v_off = (int)a.kv_off;
+    }
+    stg.load(kb, vtb, ksb, T0, n_ctx, n_ctx_pad);
     stg.store(k_lds[0], v_lds[0], c_lds[0], scale_log2);
     __syncthreads();
-    if (n_tiles > 1) stg.load(kb, vtb, ksb, 1, n_ctx, n_ctx_pad);
+    if (T0 + 1 < n_tiles) stg.load(kb, vtb, ksb, T0 + 1, n_ctx, n_ctx_pad);
     f32x16 s_cur[RB], s_nxt[RB];
     if constexpr (PIPE) qk(0, 0, s_cur);
     int buf = 0, nbuf = 1;  // LDS buffers of tiles T and T+1
@@ -679,17 +706,20 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     //         [S(2T+2) | softmax 2T+1] [PV 2T+1]
     auto tile = [&](int T, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        int rel[RB];
+        int rel[RB], lo[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int r = 0; r < RB; ++r) {
             rel[r] = MASK ? (int)min<int64_t>(my_p[r] - (int64_t)kPfTile * T, kPfTile) - 4 * hh : 0;
+            // WIN: keys of the tile below the row's window start
+            lo[r] = WIN ? (int)max<int64_t>(my_p[r] - W + 1 - (int64_t)kPfTile * T, -kPfTile) - 4 * hh : 0;
+        }
         u32x4 pb[RB][2];
         if constexpr (!PIPE) {
             // one block at a time; more waves per SIMD hide the latencies
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
                 qk(buf, sub, s_cur);
-                softmax_all(s_cur, buf, sub, rel, pb, mask_tag);
+                softmax_all(s_cur, buf, sub, rel, lo, pb, mask_tag);
                 pv(buf, sub, pb);
             }
             if (T + 1 < n_tiles) stg.store(k_lds[nbuf], v_lds[nbuf], c_lds[nbuf], scale_log2);
@@ -700,18 +730,18 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
             return;
         }
         qk(buf, 1, s_nxt);
-        softmax_all(s_cur, buf, 0, rel, pb, mask_tag);
+        softmax_all(s_cur, buf, 0, rel, lo, pb, mask_tag);
         pv(buf, 0, pb);
         if (T + 1 < n_tiles) stg.store(k_lds[nbuf], v_lds[nbuf], c_lds[nbuf], scale_log2);
         __syncthreads();
         if (T + 2 < n_tiles) stg.load(kb, vtb, ksb, T + 2, n_ctx, n_ctx_pad);
         qk(nbuf, 0, s_cur);  // after the last tile this reads a stale buffer; unused
-        softmax_all(s_nxt, buf, 1, rel, pb, mask_tag);
+        softmax_all(s_nxt, buf, 1, rel, lo, pb, mask_tag);
         pv(buf, 1, pb);
         buf = nbuf;
         nbuf = nbuf == kPfBufs - 1 ? 0 : nbuf + 1;
     };
-    int T = 0;
+    int T = T0;
     for (; T < n_full; ++T) tile(T, std::integral_constant<bool, false>{});
     for (; T < n_tiles; ++T) tile(T, std::integral_constant<bool, true>{});
 
@@ -719,7 +749,22 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         const float l_tot = l_run[r] + xor32(l_run[r]);
-        if (row_ok[r]) {
+        if (WIN && row_ok[r]) {
+            // partial record of the token: m[H], l[H], O[H][D] (unnormalised)
+            float* rec = a.win_rec + ((size_t)b * a.n_q + (size_t)my_tok[r]) * (size_t)a.win_stride;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    const int d0 = 32 * t + 8 * (i >> 2) + 4 * hh;
+                    const f32x4 o4 = {o_acc[r][t][i], o_acc[r][t][i + 1], o_acc[r][t][i + 2], o_acc[r][t][i + 3]};
+                    *reinterpret_cast<f32x4*>(rec + 2 * H + my_head[r] * D + d0) = o4;
+                }
+            if (hh == 0) {
+                rec[my_head[r]] = m_run[r];
+                rec[H + my_head[r]] = l_tot;
+            }
+        } else if (row_ok[r]) {
             const float inv = 1.f / l_tot;
             const size_t ob = (((size_t)b * a.n_q + (size_t)my_tok[r]) * H + my_head[r]) * D;
 #pragma unroll
@@ -1416,6 +1461,30 @@ static hipError_t launch_pf_any(const PrefillArgs& a, int H, int D, int kv, PfKe
 
 hipError_t launch_attn_fwd(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
     return launch_pf_any(a, H, D, kv, PF_FWD, st);
+}
+
+template <int H, int D>
+static hipError_t launch_window_hd(const PrefillArgs& a, int kv, hipStream_t st) {
+    constexpr int TB = 32 * HS2_PF_NW * HS2_PF_RB / H;
+    const dim3 grid((unsigned)((a.n_q + TB - 1) / TB), (unsigned)a.B);
+    if (kv == DT_FP8)
+        hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, DT_FP8, HS2_PF_RB, HS2_PF_NW, HS2_PF_PIPE, true>), grid,
+                           dim3(64 * HS2_PF_NW), 0, st, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_pipe_kernel<H, D, DT_BF16, HS2_PF_RB, HS2_PF_NW, HS2_PF_PIPE, true>), grid,
+                           dim3(64 * HS2_PF_NW), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_window_attn(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
+    if (kv == DT_F32) return hipErrorInvalidValue;
+    if (D == 64) {
+        if (H == 4) return launch_window_hd<4, 64>(a, kv, st);
+        if (H == 8) return launch_window_hd<8, 64>(a, kv, st);
+        return launch_window_hd<16, 64>(a, kv, st);
+    }
+    if (H == 4) return launch_window_hd<4, 128>(a, kv, st);
+    if (H == 8) return launch_window_hd<8, 128>(a, kv, st);
+    return launch_window_hd<16, 128>(a, kv, st);
 }
 hipError_t launch_score_stream(const PrefillArgs& a, int H, int D, int kv, hipStream_t st) {
     return launch_pf_any(a, H, D, kv, PF_STREAM, st);

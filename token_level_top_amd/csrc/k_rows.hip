@@ -114,7 +114,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
     const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
     const size_t kv_base = (size_t)seq * (size_t)a.n_ctx;
-    const int32_t* idx_row = GATHER ? a.idx + (size_t)tok * (size_t)a.n_rows : nullptr;
+    const int32_t* idx_row =
+        GATHER ? a.idx + (size_t)tok * (size_t)(a.idx_stride ? a.idx_stride : a.n_rows) : nullptr;
 
     // query fragment (B operand of S^T = K Q^T): head hl, d = KD*s + VPL*g + [0, VPL)
     LT qf[NS][VPL];
@@ -349,17 +350,26 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     }
     __syncthreads();
     const bool final_out = a.n_split == 1;
+    // a partial record to merge in (the window pass), n_split == 1 only
+    const float* wr = final_out && a.win_rec ? a.win_rec + (size_t)tok * (size_t)(H * (D + 2)) : nullptr;
     for (int e = tid; e < H * D; e += kRowsThreads) {
         const int h = e / D, dd = e % D;
         float mm = kNegBig;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww * 16 + h]);
+        const float m_w = wr ? wr[h] : kNegBig;
+        mm = fmaxf(mm, m_w);
         float ll = 0.f, oo = 0.f;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
             const float f = fast_exp2(red_m[ww * 16 + h] - mm);
             ll += red_l[ww * 16 + h] * f;
             oo += red[(ww * 16 + h) * RS + dd] * f;
+        }
+        if (wr) {
+            const float f = fast_exp2(m_w - mm);
+            ll += wr[H + h] * f;
+            oo += wr[2 * H + e] * f;
         }
         if (final_out) {
             const float o = ll > 0.f ? oo / ll : 0.f;
@@ -374,7 +384,8 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
                 if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
             }
         } else {
-            float* rec = a.part + ((size_t)tok * a.n_split + split) * (size_t)(H * (D + 2));
+            float* rec = a.part + ((size_t)tok * (a.part_stride ? a.part_stride : a.n_split) + split) *
+                                      (size_t)(H * (D + 2));
             rec[2 * H + e] = oo;
             if (dd == 0) {
                 rec[h] = mm;
