@@ -423,3 +423,33 @@ def test_sparse_few_tokens_head_shapes(hs2, orc, cfg, H, d, n_q, n_sel):
     rows_close(out[0, 0][~torch.from_numpy(empty)], r["out"][~empty], RTOL[wl.kv_dtype], "sparse out")
     assert (to_np(out[0, 0])[empty] == 0).all()
     lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype])
+
+
+@pytest.mark.parametrize("H,q_pos0", [(16, 70000), (4, 30000)])
+def test_streaming_topk_repeatable_under_many_trims(hs2, orc, H, q_pos0):
+    """Rows with tens of thousands of candidates, so each token's candidate
+    buffer is trimmed several times while its keys stream in (16 heads at
+    >= 64 Ki candidates: the form without threshold histograms; 4 heads below
+    it: the form with them). Six calls, each on a workspace filled with fresh
+    random bytes, must give identical index rows, and they must pass the
+    oracle's index-set rule."""
+    n_q = 96
+    wl = workload(2).with_(H=H, n_q=n_q, q_pos0=q_pos0, n_ctx=q_pos0 + n_q, n_needles=4)
+    x = make_inputs(wl)
+    kv = (dev(x.k), dev(x.v), None, None)
+    nws = hs2.workspace_size(hs2.OP_FULL_ATTN_SELECT, 1, n_q, wl.n_ctx, H, wl.d, 128, 1024, hs2.HS2_BF16)
+    gen = torch.Generator(device="cuda").manual_seed(H)
+    say("streaming top-k repeatability", H, q_pos0)
+    runs = []
+    for rep in range(6):
+        ws = torch.randint(0, 256, (nws,), dtype=torch.uint8, device="cuda", generator=gen)
+        _, _, idx = hs2.full_attn_select(dev(x.q), *kv, q_pos0=q_pos0, window=128, k_global=1024,
+                                         sm_scale=x.sm_scale, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append(idx.clone())
+    for rep in range(1, 6):
+        bad = (runs[rep] != runs[0]).any(dim=-1).nonzero()
+        assert len(bad) == 0, f"call {rep} differs from call 0 in rows {bad[:8].tolist()}"
+    rows = list(range(0, n_q, 6))
+    ref = orc.full_select(x.q, x.k, x.v, None, None, q_pos0, 128, 1024, x.sm_scale, rows, want_scores=True)
+    check_index_rows(runs[0][0, rows], ref["idx"], ref["scores"], ref["kth"], 128)

@@ -127,6 +127,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 
+// s_waitcnt vmcnt(0): returns once every vector memory operation this wave has
+// issued -- loads and stores, global and buffer -- has completed (the lgkm and
+// export counters are left alone). A workgroup-scope fence does not emit this
+// wait (one CU's vector memory operations are kept in order), so code that
+// reads back what the same wave just stored uses it to make the order explicit.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // 64-bit ranking key of a (score, position) pair: larger key = better.
 // Scores are >= 0, so their IEEE bits order like the values (-0 maps to +0);
 // the low word is the complemented position, so among equal scores the lower

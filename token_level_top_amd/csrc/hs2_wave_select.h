@@ -46,6 +46,7 @@ __device__ __noinline__ uint64_t wave_topk_ordered(const uint64_t* src, uint32_t
     const uint32_t lane = lane_id();
     // the wave's own earlier appends must be complete before they are read back
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wait_vmem();
     uint64_t key[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
@@ -262,7 +263,10 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
                                                   int32_t* pos_out, uint64_t* buf, uint32_t max_keep = 0,
                                                   uint32_t* kept = nullptr) {
     const uint32_t lane = lane_id();
+    // every store this wave issued to the list (appends, an earlier compaction)
+    // has completed before the first key is read back
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wait_vmem();
     // fn(key, valid) over every key, U per lane at a time (clamped loads)
     auto each = [&](auto fn) {
         for (uint32_t base = 0; base < cnt; base += 64u * U) {
@@ -382,6 +386,7 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
     });
     if (wr > limit) wr = limit;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    wait_vmem();
     if (kept) *kept = wr;
     return T;
 }
