@@ -294,30 +294,52 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     }
     __syncthreads();
     const bool final_out = a.n_split == 1;
-    for (int e = tid; e < H * D; e += kDecThreads) {
-        const int h = e / D, dd = e % D;
-        float mm = kNegBig;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww * 16 + h]);
-        float ll = 0.f, oo = 0.f;
+    // 16 threads per head, each owning DQ consecutive d values (vector reads
+    // and writes, the wave factors formed once)
+    constexpr int DQ = D / 16;
+    const int h = tid >> 4, q = tid & 15, d0 = DQ * q;
+    if (h < H) {
+        float mw[4], mm = kNegBig;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-            const float f = fast_exp2(red_m[ww * 16 + h] - mm);
+            mw[ww] = red_m[ww * 16 + h];
+            mm = fmaxf(mm, mw[ww]);
+        }
+        float ll = 0.f;
+        f32x4 oo[DQ / 4];
+#pragma unroll
+        for (int j = 0; j < DQ / 4; ++j) oo[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float f = fast_exp2(mw[ww] - mm);
             ll += red_l[ww * 16 + h] * f;
-            oo += red[(ww * 16 + h) * RS + dd] * f;
+#pragma unroll
+            for (int j = 0; j < DQ / 4; ++j)
+                oo[j] += *reinterpret_cast<const f32x4*>(&red[(ww * 16 + h) * RS + d0 + 4 * j]) * f;
         }
         if (final_out) {
-            const float o = ll > 0.f ? oo / ll : 0.f;
-            reinterpret_cast<uint16_t*>(a.out)[((size_t)seq * H + h) * D + dd] = f32_to_bf16_bits(o);
-            if (dd == 0) {
+            const float inv = ll > 0.f ? 1.f / ll : 0.f;
+            uint32_t pk[DQ / 2];
+#pragma unroll
+            for (int j = 0; j < DQ / 4; ++j) {
+                pk[2 * j] = pack_bf16x2(oo[j][0] * inv, oo[j][1] * inv);
+                pk[2 * j + 1] = pack_bf16x2(oo[j][2] * inv, oo[j][3] * inv);
+            }
+            uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)seq * H + h) * D + d0;
+            if constexpr (DQ == 8)
+                *reinterpret_cast<u32x4*>(op) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            else
+                *reinterpret_cast<u32x2*>(op) = u32x2{pk[0], pk[1]};
+            if (q == 0) {
                 const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
                 if (a.lse) a.lse[(size_t)seq * H + h] = lse2 * kLn2;
                 if (a.lse2) a.lse2[(size_t)seq * H + h] = lse2;
             }
         } else {
             float* rec = a.part + ((size_t)seq * a.n_split + split) * (size_t)(H * (D + 2));
-            rec[2 * H + e] = oo;
-            if (dd == 0) {
+#pragma unroll
+            for (int j = 0; j < DQ / 4; ++j) *reinterpret_cast<f32x4*>(rec + 2 * H + h * D + d0 + 4 * j) = oo[j];
+            if (q == 0) {
                 rec[h] = mm;
                 rec[H + h] = ll;
             }
