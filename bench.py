@@ -39,7 +39,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernel classes of the library's timing hook (include/hs2.h)
 KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
-      "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14, "gate_fuse": 15}
+      "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
 KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "kv_project": "k_project.hip"}
 

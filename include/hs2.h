@@ -98,7 +98,7 @@ const char* hs2_status_string(int status);
  * arguments are invalid). For HS2_OP_SELECT_TOPK pass B = rows, n_ctx = row
  * length and k_global = k; the other arguments are ignored. For
  * HS2_OP_BLOCK_SPARSE_ATTN pass window, k_global = k_blocks and, in place of
- * kv_dtype, the query type. For HS2_OP_INDEX_SELECT pass d = the indexer
+ * kv_dtype, the query type (the size is 0). For HS2_OP_INDEX_SELECT pass d = the indexer
  * head dimension dI. For HS2_OP_SPARSE_ATTN_WINDOW the size does not depend
  * on n_ctx or on the first query's position. Pure host code.
  */
@@ -304,10 +304,11 @@ int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void*
  *   block_idx [B][n_q][k_blocks] int32  as written by hs2_block_attn_select
  *   gates    [n_layers][B][n_q][H][2]   fp32
  *   out      [n_layers][B][n_q][H][d]   q_dtype
- *   workspace >= hs2_workspace_size(HS2_OP_BLOCK_SPARSE_ATTN, B, n_q, n_ctx,
- *                H, d, window, k_blocks, q_dtype) bytes
- * block must be 64, 1 <= k_blocks <= 64, 1 <= window <= 4096. With bf16
- * queries each branch's output is rounded to bf16 before the fusion.
+ *   workspace, ws_bytes   unused (hs2_workspace_size(HS2_OP_BLOCK_SPARSE_ATTN,
+ *                ...) returns 0): each layer is one launch that computes both
+ *                branches and their gated sum
+ * block must be 64, 1 <= k_blocks <= 64, 1 <= window <= 4096. The branches
+ * are fused in fp32 and the sum is rounded once to the query type.
  */
 int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* k, const void* v,
                           const float* k_scale, const float* v_scale, int kv_dtype, int B,
@@ -352,7 +353,7 @@ int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* we
  *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
  *   bit 10 window pass (window sharing) bit 11 buffer fills
  *   bit 12 KV Bridging projections     bit 13 block scores (block mode)
- *   bit 14 block choice / expansion    bit 15 two-branch gate fusion
+ *   bit 14 block choice                bit 15 (unused)
  * (the light indexer's scoring and selection report as bit 9, its key
  * widening as bit 7)
  * hs2_timing_enable(mask): from now on every launch of a class in `mask` is

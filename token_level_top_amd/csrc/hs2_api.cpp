@@ -206,29 +206,6 @@ BlockPfWs block_pf_ws(void* base, int B, int64_t n_q, int64_t n_ctx, int H, int 
     w.bytes = c.used;
     return w;
 }
-// the two-branch sparse layer: both branches' index rows, both branch outputs
-// (query type) and the gather kernel's split partials
-struct BlockSpWs {
-    int32_t *win, *blk;
-    void *ob, *ow;
-    float* part;
-    size_t bytes;
-};
-BlockSpWs block_sp_ws(void* base, int64_t n_tok, int H, int d, int q_dtype, int window, int k_blocks) {
-    Carver c(base);
-    BlockSpWs w;
-    w.win = c.take<int32_t>(sizeof(int32_t) * (size_t)n_tok * window);
-    w.blk = c.take<int32_t>(sizeof(int32_t) * (size_t)n_tok * k_blocks * kBlock);
-    w.ob = c.take<void>(esize(q_dtype) * (size_t)n_tok * H * d);
-    w.ow = c.take<void>(esize(q_dtype) * (size_t)n_tok * H * d);
-    // the split count is not monotone in the row count: size for both branches
-    const size_t pb = std::max(sparse_ws(nullptr, n_tok, window, H, d).bytes,
-                               sparse_ws(nullptr, n_tok, k_blocks * kBlock, H, d).bytes);
-    w.part = pb ? c.take<float>(pb) : nullptr;
-    w.bytes = c.used;
-    return w;
-}
-
 // light indexer: the keys widened to bf16, the candidate buffers
 struct IndexWs {
     uint16_t* kc;
@@ -278,7 +255,7 @@ WinWs win_ws(void* base, int B, int64_t n_q, int64_t q_pos0, int H, int d, int w
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
     KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_WINDOW = 10, KC_FILL = 11,
-    KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14, KC_GATE = 15
+    KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14
 };
 struct TimedPair {
     int cls;
@@ -485,8 +462,7 @@ size_t hs2_workspace_size(int op, int B, int64_t n_q, int64_t n_ctx, int H, int 
         case HS2_OP_BLOCK_SPARSE_ATTN:
             if (n_q <= 0 || H <= 0 || d <= 0 || window < 1 || k_global < 1 || !dtype_known(kv_dtype))
                 return SIZE_MAX;
-            return block_sp_ws(nullptr, (int64_t)B * n_q, H, d, kv_dtype /* the query type */, window,
-                               k_global).bytes;
+            return 0;  // one fused launch per layer, no workspace
         default: return SIZE_MAX;
     }
 }
@@ -690,34 +666,31 @@ int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* 
     if (!aligned16(q) || !aligned16(out) || !aligned16(block_idx) || !aligned16(gates)) return HS2_ERR_INVALID_ARG;
     if (st != HS2_OK) return st;
     if (block != kBlock || k_blocks > 4096 / kBlock || window > 4096) return HS2_ERR_UNSUPPORTED;
-    const int64_t n_tok = (int64_t)B * n_q;
-    const BlockSpWs need = block_sp_ws(nullptr, n_tok, H, d, q_dtype, window, k_blocks);
-    if (!workspace || ws_bytes < need.bytes || !aligned16(workspace)) return HS2_ERR_WORKSPACE;
+    (void)workspace;
+    (void)ws_bytes;  // the fused layer needs no workspace
     if (n_layers == 0) return HS2_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const BlockSpWs w = block_sp_ws(workspace, n_tok, H, d, q_dtype, window, k_blocks);
-    BlockArgs ba{};
-    ba.n_tok = n_tok;
-    ba.n_q = n_q;
-    ba.q_pos0 = q_pos0;
-    ba.k_blocks = k_blocks;
-    ba.block_idx = const_cast<int32_t*>(block_idx);
-    ba.window = window;
-    ba.win_idx = w.win;
-    ba.blk_pos = w.blk;
-    HS2_TRY(TIMED(KC_BLOCK_SELECT, s, launch_block_expand(ba, s)));
+    const int64_t n_tok = (int64_t)B * n_q;
     const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
+    // one launch per layer: window branch, block branch, gated sum
     for (int l = 0; l < n_layers; ++l) {
-        const void* ql = static_cast<const char*>(q) + qstride * l;
-        int rc = run_sparse(ql, q_dtype, 1, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, w.blk,
-                            k_blocks * kBlock, sm_scale, w.ob, nullptr, w.part, s);
-        if (rc != HS2_OK) return rc;
-        rc = run_sparse(ql, q_dtype, 1, k, v, k_scale, v_scale, kv_dtype, B, n_q, n_ctx, H, d, w.win, window,
-                        sm_scale, w.ow, nullptr, w.part, s);
-        if (rc != HS2_OK) return rc;
-        HS2_TRY(TIMED(KC_GATE, s, launch_gate_fuse(w.ob, w.ow, gates + (size_t)l * n_tok * H * 2,
-                                                   static_cast<char*>(out) + qstride * l, n_tok, H, d,
-                                                   q_dtype == HS2_BF16, s)));
+        RowsArgs a{};
+        a.q = static_cast<const char*>(q) + qstride * l;
+        a.k = k;
+        a.v = v;
+        a.ks = k_scale;
+        a.vs = v_scale;
+        a.n_ctx = n_ctx;
+        a.n_tok = (int)n_tok;
+        a.n_q = (int)n_q;
+        a.scale_log2 = sm_scale * kLog2eF;
+        a.out = static_cast<char*>(out) + qstride * l;
+        a.blk_idx = block_idx;
+        a.k_blocks = k_blocks;
+        a.win = window;
+        a.q_pos0 = q_pos0;
+        a.gates = gates + (size_t)l * n_tok * H * 2;
+        HS2_TRY(TIMED(KC_SPARSE, s, launch_block_branches(a, H, d, kv_dtype, s)));
     }
     return HS2_OK;
 }

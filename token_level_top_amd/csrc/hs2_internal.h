@@ -35,6 +35,15 @@ struct RowsArgs {
     // per token, at win_rec + token * H * (D + 2), merged into the result
     // (the window pass of the window-sharing sparse layers)
     const float* win_rec;
+    // two-branch (HySparse v1) layer, launch_block_branches: rows [0, win) of a
+    // token are its window max(0, p-win+1)..p, rows from win rounded up to 128
+    // the positions <= p of its k_blocks 64-token blocks blk_idx[token][.]
+    // (-1 = none); each branch has its own softmax and the output is
+    // gates[token][h][0] O_blocks + gates[token][h][1] O_window (no LSE)
+    const int32_t* blk_idx;
+    int k_blocks, win;
+    int64_t q_pos0;
+    const float* gates;
 };
 
 struct CombineArgs {
@@ -50,6 +59,9 @@ struct CombineArgs {
 hipError_t launch_rows_attn(const RowsArgs& a, int H, int D, int kv, bool gather, bool store_logits,
                             hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_t st);
+// the HySparse v1 two-branch sparse layer in one launch (one workgroup per
+// token; n_rows, n_split and rows_per_split are set by the launcher)
+hipError_t launch_block_branches(const RowsArgs& a, int H, int D, int kv, hipStream_t st);
 // decode full layer over a contiguous cache range, bf16 or FP8 cache (logits always stored)
 hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStream_t st);
 
@@ -151,22 +163,15 @@ hipError_t launch_index_stream(const PrefillArgs& a, int H, int D, hipStream_t s
 // E4M3 codes [n][d] -> bf16 [n][d] (exact)
 hipError_t launch_widen_fp8(const uint8_t* src, uint16_t* dst, int64_t n_elem, hipStream_t st);
 
-// HySparse v1 block selection and the two-branch sparse layer
+// HySparse v1 block selection
 struct BlockArgs {
     int64_t n_tok, n_q, q_pos0;
     const uint64_t* keys;   // [n_tok][key_stride] rank keys
     int64_t key_stride;
     int k_blocks;
     int32_t* block_idx;     // [n_tok][k_blocks] ascending, -1 padded
-    int window;
-    int32_t* win_idx;       // [n_tok][window]
-    int32_t* blk_pos;       // [n_tok][k_blocks * 64]
 };
 hipError_t launch_block_select(const BlockArgs& a, hipStream_t st);
-hipError_t launch_block_expand(const BlockArgs& a, hipStream_t st);
-// out[t][h][:] = g[t][h][0] ob[t][h][:] + g[t][h][1] ow[t][h][:], q dtype (f32 or bf16)
-hipError_t launch_gate_fuse(const void* ob, const void* ow, const float* gates, void* out, int64_t n_tok, int H,
-                            int D, bool bf16, hipStream_t st);
 
 // KV Bridging projections: [J][2][d][hidden] bf16 weights applied to [T][hidden]
 // bf16 hidden states, out [J][T][d] (bf16 or e4m3 codes + [J][T] fp32 scales)

@@ -78,8 +78,16 @@ __device__ __forceinline__ void store_piece(typename RowsTypes<KV>::L* dst_row, 
     }
 }
 
-template <int H, int D, int KV, bool GATHER, bool STORE_LOGITS>
-__global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
+// BLOCKS: the HySparse v1 two-branch layer (window rows first, then the rows
+// of the chosen 64-token blocks, computed from the block ids; the window
+// branch is merged across the waves when its last tile is done and kept in
+// registers, and the gated sum of the two branches is the output).
+// bf16 / FP8 caches are held to two waves per SIMD (the registers of the
+// prefetched tile and, in block mode, of the window branch's output would
+// otherwise push the allocator past 256 and halve the waves in flight).
+template <int H, int D, int KV, bool GATHER, bool STORE_LOGITS, bool BLOCKS = false>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(KV == DT_F32 ? 1 : 2)))
+void rows_attn_kernel(RowsArgs a) {
     using T = RowsTypes<KV>;
     using LT = typename T::L;
     constexpr int VPL = T::VPL, KD = T::KD, PAD = T::PAD;
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     __shared__ float vsc_lds[kRowsTile];
     // gathered rows: the index row is staged here kIdxChunk entries at a time, so
     // a tile's K/V loads never wait behind the load of their own indices
-    __shared__ int idx_lds[GATHER ? kIdxChunk : 1];
+    __shared__ int idx_lds[GATHER ? kIdxChunk : BLOCKS ? 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hl = lane & 15, g = lane >> 4;
@@ -143,9 +151,25 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
     // Row position of tile row `row` (tile starting at t0), -1 if empty. A
     // gathered index outside [0, n_ctx) counts as empty, so a caller's bad
     // entry never turns into an address outside the sequence's cache rows.
+    // BLOCKS: the token's position, its window, and where its block rows start
+    const int p_tok = BLOCKS ? (int)(a.q_pos0 + tok % a.n_q) : 0;  // (n_ctx < 2^31)
+    const int w_pad = BLOCKS ? (a.win + kRowsTile - 1) / kRowsTile * kRowsTile : 0;
+    if constexpr (BLOCKS) {
+        if (tid < a.k_blocks) idx_lds[tid] = a.blk_idx[(size_t)tok * a.k_blocks + tid];
+        __syncthreads();
+    }
     auto row_pos = [&](int64_t t0, int row) -> int {
         const int64_t r = t0 + row;
         if (r >= r_end) return -1;
+        if constexpr (BLOCKS) {
+            // window row r, or row f of the block rows (block f / 64); no branch,
+            // so the caller's loads issue back to back
+            const int rr = (int)r;
+            const int jw = p_tok - a.win + 1 + rr;
+            const int f = max(rr - w_pad, 0), c = idx_lds[f >> 6];
+            const int jb = c * 64 + (f & 63);
+            return rr < w_pad ? (rr < a.win && jw >= 0 ? jw : -1) : (c >= 0 && jb <= p_tok ? jb : -1);
+        }
         if constexpr (GATHER) {
             const int p = idx_lds[(r - r_begin) % kIdxChunk];
             return (uint32_t)p < (uint32_t)a.n_ctx ? p : -1;
@@ -209,6 +233,35 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
                     }
         }
     };
+    // Wave merge scratch (reuses the K tile): [4 waves][16 heads][RS] O, then m,
+    // l. Rows of RS = D + 4 floats (an odd number of 16-byte units), so the 16
+    // head lanes of one 16-byte store land on 16 different bank quads. In the
+    // merge each thread owns one head and DQ consecutive d values.
+    constexpr int RS = D + 4;
+    constexpr int DQ = D / 16;
+    float* red = reinterpret_cast<float*>(k_lds);
+    float* red_m = red + 4 * 16 * RS;
+    float* red_l = red_m + 4 * 16;
+    static_assert(sizeof(k_lds) >= sizeof(float) * (4 * 16 * RS + 128), "reduction scratch");
+    const int mh = tid >> 4, mq = tid & 15, md0 = DQ * mq;
+    // BLOCKS: the window branch's normalised output, this thread's slice
+    float ow[BLOCKS ? DQ : 1];
+#pragma unroll
+    for (int j = 0; j < (BLOCKS ? DQ : 1); ++j) ow[j] = 0.f;
+    // the waves' running (m, l, O) into the scratch (then a barrier)
+    auto to_scratch = [&]() {
+        float lr = l_run + __shfl_xor(l_run, 16);
+        lr += xor32(lr);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+            *reinterpret_cast<f32x4*>(&red[(w * 16 + hl) * RS + 16 * t + 4 * g]) = o_acc[t];
+        if (g == 0) {
+            red_m[w * 16 + hl] = m_run;
+            red_l[w * 16 + hl] = lr;
+        }
+        __syncthreads();
+    };
+
     if (r_begin < r_end) {
         stage_idx(0);
         prefetch(r_begin);
@@ -326,36 +379,46 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
             }
         }
         __syncthreads();
+        if constexpr (BLOCKS) {
+            if (t0 + kRowsTile == w_pad) {
+                // the window branch is complete: its normalised output goes to
+                // registers, and the block branch starts from an empty state
+                to_scratch();
+                if (mh < H) {
+                    float mm = kNegBig;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww * 16 + mh]);
+                    float ll = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        const float f = fast_exp2(red_m[ww * 16 + mh] - mm);
+                        ll += red_l[ww * 16 + mh] * f;
+#pragma unroll
+                        for (int j = 0; j < DQ; ++j) ow[j] += red[(ww * 16 + mh) * RS + md0 + j] * f;
+                    }
+                    const float inv = ll > 0.f ? 1.f / ll : 0.f;
+#pragma unroll
+                    for (int j = 0; j < DQ; ++j) ow[j] *= inv;
+                }
+                __syncthreads();  // the scratch is the next tile's K buffer
+                m_run = kNegBig;
+                l_run = 0.f;
+#pragma unroll
+                for (int t = 0; t < NDT; ++t) o_acc[t] = f32x4{0, 0, 0, 0};
+            }
+        }
     }
 
     flush_logits();
 
     // ---- merge the 4 waves: per head m, l (summed over lane groups), O
-    l_run += __shfl_xor(l_run, 16);
-    l_run += xor32(l_run);
-    // reuse the K tile: [4 waves][16 heads][RS] O, then m, l. Rows of RS = D + 4
-    // floats (an odd number of 16-byte units), so the 16 head lanes of one
-    // 16-byte store land on 16 different bank quads
-    constexpr int RS = D + 4;
-    float* red = reinterpret_cast<float*>(k_lds);
-    float* red_m = red + 4 * 16 * RS;
-    float* red_l = red_m + 4 * 16;
-    static_assert(sizeof(k_lds) >= sizeof(float) * (4 * 16 * RS + 128), "reduction scratch");
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-        *reinterpret_cast<f32x4*>(&red[(w * 16 + hl) * RS + 16 * t + 4 * g]) = o_acc[t];
-    if (g == 0) {
-        red_m[w * 16 + hl] = m_run;
-        red_l[w * 16 + hl] = l_run;
-    }
-    __syncthreads();
+    to_scratch();
     const bool final_out = a.n_split == 1;
     // a partial record to merge in (the window pass), n_split == 1 only
     const float* wr = final_out && a.win_rec ? a.win_rec + (size_t)tok * (size_t)(H * (D + 2)) : nullptr;
     // 16 threads per head, each owning DQ consecutive d values: the wave
     // factors are formed once per thread and every read and write is a vector
-    constexpr int DQ = D / 16;
-    const int h = tid >> 4, q = tid & 15, d0 = DQ * q;
+    const int h = mh, q = mq, d0 = md0;
     if (h < H) {
         float mw[4], mm = kNegBig;
 #pragma unroll
@@ -387,23 +450,34 @@ __global__ __launch_bounds__(kRowsThreads) void rows_attn_kernel(RowsArgs a) {
         if (final_out) {
             const float inv = ll > 0.f ? 1.f / ll : 0.f;
             const size_t oi = ((size_t)tok * H + h) * D + d0;
+            if constexpr (BLOCKS) {
+                // out = g0 O_blocks + g1 O_window
+                const float g0 = a.gates[((size_t)tok * H + h) * 2], g1 = a.gates[((size_t)tok * H + h) * 2 + 1];
+#pragma unroll
+                for (int j = 0; j < DQ / 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oo[j][e] = g0 * (oo[j][e] * inv) + g1 * ow[4 * j + e];
+            } else {
+#pragma unroll
+                for (int j = 0; j < DQ / 4; ++j) oo[j] *= inv;
+            }
             if constexpr (KV == DT_F32) {
 #pragma unroll
                 for (int j = 0; j < DQ / 4; ++j)
-                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi + 4 * j) = oo[j] * inv;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi + 4 * j) = oo[j];
             } else {
                 uint32_t pk[DQ / 2];
 #pragma unroll
                 for (int j = 0; j < DQ / 4; ++j) {
-                    pk[2 * j] = pack_bf16x2(oo[j][0] * inv, oo[j][1] * inv);
-                    pk[2 * j + 1] = pack_bf16x2(oo[j][2] * inv, oo[j][3] * inv);
+                    pk[2 * j] = pack_bf16x2(oo[j][0], oo[j][1]);
+                    pk[2 * j + 1] = pack_bf16x2(oo[j][2], oo[j][3]);
                 }
                 if constexpr (DQ == 8)
                     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + oi) = u32x4{pk[0], pk[1], pk[2], pk[3]};
                 else
                     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = u32x2{pk[0], pk[1]};
             }
-            if (q == 0) {
+            if (!BLOCKS && q == 0) {
                 const float lse2 = ll > 0.f ? mm + log2f(ll) : -INFINITY;
                 if (a.lse) a.lse[(size_t)tok * H + h] = lse2 * kLn2;
                 if (a.lse2) a.lse2[(size_t)tok * H + h] = lse2;
@@ -511,6 +585,36 @@ static hipError_t launch_rows_t(const RowsArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)a.n_split * a.n_tok));
     hipLaunchKernelGGL((rows_attn_kernel<H, D, KV, GATHER, STORE>), grid, dim3(kRowsThreads), 0, st, a);
     return hipGetLastError();
+}
+
+template <int H, int D, int KV>
+static hipError_t launch_branches_hdk(const RowsArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((rows_attn_kernel<H, D, KV, false, false, true>), dim3((unsigned)a.n_tok), dim3(kRowsThreads), 0,
+                       st, a);
+    return hipGetLastError();
+}
+template <int H, int D>
+static hipError_t launch_branches_hd(const RowsArgs& a, int kv, hipStream_t st) {
+    switch (kv) {
+        case DT_F32: return launch_branches_hdk<H, D, DT_F32>(a, st);
+        case DT_BF16: return launch_branches_hdk<H, D, DT_BF16>(a, st);
+        default: return launch_branches_hdk<H, D, DT_FP8>(a, st);
+    }
+}
+hipError_t launch_block_branches(const RowsArgs& a_in, int H, int D, int kv, hipStream_t st) {
+    if (a_in.k_blocks < 1 || a_in.k_blocks > 64) return hipErrorInvalidValue;
+    RowsArgs a = a_in;
+    a.n_split = 1;
+    a.n_rows = (int64_t)(a.win + kRowsTile - 1) / kRowsTile * kRowsTile + 64 * (int64_t)a.k_blocks;
+    a.rows_per_split = (int)a.n_rows;
+    if (D == 64) {
+        if (H == 4) return launch_branches_hd<4, 64>(a, kv, st);
+        if (H == 8) return launch_branches_hd<8, 64>(a, kv, st);
+        return launch_branches_hd<16, 64>(a, kv, st);
+    }
+    if (H == 4) return launch_branches_hd<4, 128>(a, kv, st);
+    if (H == 8) return launch_branches_hd<8, 128>(a, kv, st);
+    return launch_branches_hd<16, 128>(a, kv, st);
 }
 
 template <int H, int D, int KV>
