@@ -164,6 +164,52 @@ def copy_calibration(mib: int, dev) -> None:
     del src, dst
 
 
+def gather_probe(args) -> int:
+    """Attainable random-row gather rate on this GPU, the reference the sparse
+    layers' row rate is read against (a sparse layer gathers a K row and a V
+    row per index entry, so its row rate is twice its index rate):
+    hs2_probe_gather reads 8192 x 1152 rows at random positions -- as fast as
+    the memory system returns them, nothing else done with them -- out of a
+    source of 16 MiB (the 32k prefill's K + V, which the memory-side cache
+    holds) and of 64 MiB, 256-byte rows (bf16, d = 128) and 128-byte rows with
+    a 4-byte scale each (FP8). hipEvents around each launch, median of steps."""
+    import torch
+    import token_level_top_amd as hs2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(11)
+    n_idx = 8192 * 1152
+    res = {"metric": "random-row gather rate (reference for the sparse layers)", "unit": "G rows/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "rows_per_launch": n_idx,
+           "cases": []}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sink = torch.empty(524288, dtype=torch.int32, device=dev)
+    for mib in (16, 64):
+        for row_bytes, with_scale in ((256, False), (128, True)):
+            n_rows = mib * 1024 * 1024 // row_bytes
+            src = torch.randint(0, 255, (n_rows, row_bytes), dtype=torch.uint8, device=dev, generator=g)
+            scale = torch.rand(n_rows, device=dev, generator=g) if with_scale else None
+            idx = torch.randint(0, n_rows, (n_idx,), dtype=torch.int32, device=dev, generator=g)
+            for _ in range(args.warmup):
+                hs2.probe_gather(src, idx, scale, sink)
+            times = []
+            for _ in range(args.steps):
+                e0.record()
+                hs2.probe_gather(src, idx, scale, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
+            rb = row_bytes + (4 if with_scale else 0)
+            res["cases"].append({"source_mib": mib, "row_bytes": rb, "ms": round(ms, 4),
+                                 "g_rows_per_s": round(n_idx / (ms / 1e3) / 1e9, 2),
+                                 "gathered_gb_per_s": round(n_idx * rb / (ms / 1e3) / 1e9, 1)})
+            log(f"gather probe {mib} MiB source, {rb}-byte rows: {ms:.3f} ms")
+            del src, idx, scale
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_kv_project(args, cache: str) -> int:
     """KV Bridging projections alone (hs2_kv_project): the hidden state of a
     32768-token prefill chunk, hidden 2048 (the pages' model width), projected
@@ -280,6 +326,9 @@ def main():
     ap.add_argument("--indexer-dim", type=int, default=64, help="indexer head dimension (64 or 128)")
     ap.add_argument("--kv-project", choices=["bf16", "fp8"], default=None,
                     help="instead of the attention path, time the KV Bridging projections with this cache type")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="instead of the attention path, measure the attainable random-row gather rate (a reference "
+                         "for the sparse layers)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -288,6 +337,8 @@ def main():
         return 2
     if args.kv_project:
         return bench_kv_project(args, args.kv_project)
+    if args.gather_probe:
+        return gather_probe(args)
     blocks = args.hysparse_blocks
     indexer = args.indexer
 

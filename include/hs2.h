@@ -345,6 +345,20 @@ int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* we
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Measurement probe (not part of the computation): the rate at which the GPU
+ * gathers rows from random positions, the reference the sparse layers' row
+ * rate is read against. Enqueues one kernel that reads row idx[i] of src
+ * ([n_rows][row_bytes], row_bytes 128 or 256) for every i < n_idx, and
+ * scale[idx[i]] when scale is not NULL, folding what it read into sink (at
+ * least 524288 words, contents meaningless); an index outside [0, n_rows)
+ * reads row 0. Time it with events on `stream`. Device pointers, 16-byte
+ * aligned; n_rows < 2^31.
+ */
+int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float* scale,
+                     const int32_t* idx, int64_t n_idx, uint32_t* sink, int64_t sink_words,
+                     void* stream);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -285,3 +285,21 @@ def test_sparse_attn_window_validation():
     assert call(a1=0, a7=0) == E.HS2_ERR_UNSUPPORTED         # fp32 cache
     assert call(a8=65536) == E.HS2_ERR_UNSUPPORTED           # batch limit
     assert call(a2=0) == E.HS2_ERR_WORKSPACE                 # no layers, but still no workspace
+
+
+def test_probe_gather_validation():
+    L = hs2.lib()
+    # src, n_rows, row_bytes, scale, idx, n_idx, sink, sink_words, stream
+    args = [FAKE, 1000, 256, None, FAKE, 5000, FAKE, 524288, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_probe_gather(*a)
+
+    assert call(a2=192) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a0=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a0=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a1=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a7=100) == hs2.HS2_ERR_INVALID_ARG          # sink too small for the grid

@@ -35,6 +35,7 @@ _SIGS = {
                          _p, _p, _p, _p, _p, _sz, _p], _i),
     "hs2_sparse_attn_window": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _p, _i, _i, _f, _p,
                                 _p, _p, _sz, _p], _i),
+    "hs2_probe_gather": ([_p, _i64, _i, _p, _p, _i64, _p, _i64, _p], _i),
     "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
                                  _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
@@ -179,6 +180,17 @@ def sparse_attn_window(q, k, v, k_scale=None, v_scale=None, *, indices, q_pos0: 
                                       _stream(stream))
     _check("hs2_sparse_attn_window", rc)
     return out, lse
+
+
+def probe_gather(src, idx, scale=None, sink=None, stream=None):
+    """hs2_probe_gather: src [n_rows][row_bytes] uint8 (128 or 256 bytes a row),
+    idx [n_idx] int32, scale [n_rows] fp32 or None. Returns the sink tensor."""
+    n_rows, row_bytes = src.shape
+    sink = torch.empty(524288, dtype=torch.int32, device=src.device) if sink is None else sink
+    rc = lib().hs2_probe_gather(_ptr(src), n_rows, row_bytes, _ptr(scale), _ptr(idx), idx.numel(), _ptr(sink),
+                                sink.numel(), _stream(stream))
+    _check("hs2_probe_gather", rc)
+    return sink
 
 
 def sparse_attn_noalloc(q, k, v, k_scale=None, v_scale=None, *, indices, sm_scale: float, out=None, lse=None,

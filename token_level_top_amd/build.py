@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhs2.so")
 SOURCES = ["hs2_api.cpp", "k_rows.hip", "k_decode.hip", "k_select.hip", "k_prefill.hip", "k_project.hip",
-           "k_block.hip", "k_index.hip", "hs2_noalloc.hip"]
+           "k_block.hip", "k_index.hip", "k_probe.hip", "hs2_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

@@ -61,6 +61,9 @@ int check_common(int q_dtype, int kv_dtype, const void* k, const void* v, const 
     return HS2_OK;
 }
 
+// workgroups of the gather probe (enough to fill the chip several times over)
+constexpr int64_t kProbeBlocks = 2048;
+
 // Sequences (or selection rows) ride on a launch's second grid dimension.
 constexpr int64_t kMaxGridY = 65535;
 
@@ -569,6 +572,19 @@ int hs2_sparse_attn_window(const void* q, int q_dtype, int n_layers, const void*
             HS2_TRY(TIMED(KC_COMBINE, s, launch_combine(c, H, d, q_dtype, s)));
         }
     }
+    return HS2_OK;
+}
+
+int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float* scale, const int32_t* idx,
+                     int64_t n_idx, uint32_t* sink, int64_t sink_words, void* stream) {
+    if (!src || !idx || !sink || n_rows < 1 || n_idx < 1 || n_rows >= (int64_t(1) << 31)) return HS2_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(scale) || !aligned16(idx) || !aligned16(sink)) return HS2_ERR_INVALID_ARG;
+    if (row_bytes != 128 && row_bytes != 256) return HS2_ERR_UNSUPPORTED;
+    const int64_t rows_per_step = 8 * (256 / (row_bytes / 16));
+    const int64_t blocks = std::min<int64_t>(kProbeBlocks, (n_idx + rows_per_step - 1) / rows_per_step);
+    if (sink_words < blocks * 256) return HS2_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HS2_TRY(launch_probe_gather(src, n_rows, scale, row_bytes, idx, n_idx, sink, (int)blocks, s));
     return HS2_OK;
 }
 

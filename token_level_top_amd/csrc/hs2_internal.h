@@ -200,4 +200,9 @@ int sparse_attn_enqueue(const void* q, int q_dtype, int n_layers, const void* k,
                         const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* scratch,
                         hipStream_t stream);
 
+// measurement probe: n_idx random-row gathers (row_bytes 128 or 256, with a
+// per-row fp32 scale when scale is given), folded into sink[n_blocks * 256]
+hipError_t launch_probe_gather(const void* src, int64_t n_rows, const float* scale, int row_bytes, const int32_t* idx,
+                               int64_t n_idx, uint32_t* sink, int n_blocks, hipStream_t st);
+
 }  // namespace hs2
