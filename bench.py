@@ -41,7 +41,8 @@ KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
       "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
-KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "kv_project": "k_project.hip"}
+KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "score_stream": "k_prefill.hip",
+        "kv_project": "k_project.hip"}
 
 
 def log(*a):
@@ -530,7 +531,10 @@ def main():
     else:
         achieved = units / kavg_s / 1e12
         peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"]
-    tr = traffic_record(dom, wl.name)
+    wname = (wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else "")
+             + (f"_full_heads{hf}" if args.full_heads else "")
+             + ("_window_sharing" if args.window_sharing and not wl.decode else ""))
+    tr = traffic_record(dom, wname)
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
             "kernel": dom, "kernel_ms": round(kavg_s * 1e3, 4),
@@ -551,10 +555,7 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if wl.q_dtype == "f32" else "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V with planted needles)",
-           "config": {"workload": wl.name + ("_hysparse_blocks" if blocks else "") + ("_indexer" if indexer else "")
-                      + (f"_full_heads{hf}" if args.full_heads else "")
-                      + ("_window_sharing" if args.window_sharing and not wl.decode else ""),
-                      "B": wl.B, "H_full": hf, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
+           "config": {"workload": wname, "B": wl.B, "H_full": hf, "n_q": wl.n_q, "q_pos0": wl.q_pos0, "n_ctx": wl.n_ctx,
                       "H": wl.H, "d": wl.d, "kv_storage": wl.kv_dtype, "window": wl.window,
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,
