@@ -165,6 +165,51 @@ def copy_calibration(mib: int, dev) -> None:
     del src, dst
 
 
+def mfma_probe(args) -> int:
+    """Attainable dense bf16 matrix-core rate on this GPU, the ceiling the
+    MFMA-bound kernels are read against: hs2_probe_mfma issues nothing but
+    v_mfma_f32_32x32x16_bf16 on register operands (8 independent chains a
+    wave), one workgroup a CU, with one and with two waves on each SIMD, on
+    constant operands (the sink checked against its exact value) and on
+    N(0,1) bf16 operands (the matrix cores' power draw, and so the clock they
+    hold, depends on the operand bits). hipEvents around each launch, median
+    of steps."""
+    import torch
+    import token_level_top_amd as hs2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_blocks, iters = 1024, 2000
+    res = {"metric": "dense bf16 MFMA rate (attainable ceiling)", "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "instruction": "v_mfma_f32_32x32x16_bf16",
+           "peak": MFMA_PEAK_TFLOPS["bf16"], "cases": []}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gen = torch.Generator(device=dev).manual_seed(13)
+    normal_ops = torch.randn(64, 16, device=dev, generator=gen).to(torch.bfloat16)
+    for operands in ("constant", "normal"):
+        ops = normal_ops if operands == "normal" else None
+        for wps in (1, 2):
+            sink = torch.empty(n_blocks * 256 * wps, dtype=torch.float32, device=dev)
+            for _ in range(args.warmup):
+                hs2.probe_mfma(wps, n_blocks, iters, 1.0, ops, sink)
+            times = []
+            for _ in range(args.steps):
+                e0.record()
+                hs2.probe_mfma(wps, n_blocks, iters, 1.0, ops, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            if ops is None and not bool((sink == 128.0 * iters).all()):
+                raise RuntimeError("MFMA probe sink holds a wrong value")
+            ms = sorted(times)[len(times) // 2]
+            flops = n_blocks * 4 * wps * iters * 8 * 32768
+            tf = flops / (ms / 1e3) / 1e12
+            res["cases"].append({"operands": operands, "waves_per_simd": wps, "ms": round(ms, 4),
+                                 "tflops": round(tf, 1), "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)})
+            log(f"MFMA probe, {operands} operands, {wps} wave(s) per SIMD: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def gather_probe(args) -> int:
     """Attainable random-row gather rate on this GPU, the reference the sparse
     layers' row rate is read against (a sparse layer gathers a K row and a V
@@ -327,6 +372,8 @@ def main():
     ap.add_argument("--indexer-dim", type=int, default=64, help="indexer head dimension (64 or 128)")
     ap.add_argument("--kv-project", choices=["bf16", "fp8"], default=None,
                     help="instead of the attention path, time the KV Bridging projections with this cache type")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="measure the attainable dense bf16 MFMA rate (hs2_probe_mfma) instead of the path")
     ap.add_argument("--gather-probe", action="store_true",
                     help="instead of the attention path, measure the attainable random-row gather rate (a reference "
                          "for the sparse layers)")
@@ -340,6 +387,8 @@ def main():
         return bench_kv_project(args, args.kv_project)
     if args.gather_probe:
         return gather_probe(args)
+    if args.mfma_probe:
+        return mfma_probe(args)
     blocks = args.hysparse_blocks
     indexer = args.indexer
 

@@ -359,6 +359,29 @@ int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float
                      void* stream);
 
 /*
+ * Measurement probe (not part of the computation): the dense bf16
+ * matrix-core rate the GPU sustains, the attainable ceiling the MFMA-bound
+ * kernels are read against. Enqueues one kernel of n_blocks workgroups of
+ * 4 * waves_per_simd waves (waves_per_simd 1 or 2: one or two waves on each
+ * SIMD of a CU, one workgroup a CU); every wave issues iters rounds of 8
+ * independent v_mfma_f32_32x32x16_bf16 (32768 flops each) on register
+ * operands, so the launch does n_blocks * 4 * waves_per_simd * iters * 8 *
+ * 32768 flops. ops NULL: A all `one`, B all `one`/16, and every thread
+ * writes 128 * iters * one^2 to its sink word (exact when `one` is a power of
+ * two and that stays below 2^24). ops not NULL (64 * 16 bf16 values, device
+ * memory): lane l of every wave takes the eight A values ops[16 l .. 16 l + 7]
+ * (A row l % 32, k = 8 (l / 32) .. + 7) and the eight B values
+ * ops[16 l + 8 .. 16 l + 15] (B column l % 32, same k), and every thread
+ * writes the sum over its 8 x 16 accumulators; the matrix cores' power draw,
+ * and so the clock they hold, depends on the operand bits. sink: at least
+ * n_blocks * 256 * waves_per_simd floats, device memory. Pointers 16-byte
+ * aligned; 1 <= n_blocks <= 65535, 1 <= iters <= 2^20. Time it with events
+ * on `stream`.
+ */
+int hs2_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const uint16_t* ops, float* sink,
+                   int64_t sink_words, void* stream);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram

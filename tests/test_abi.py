@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -303,3 +303,27 @@ def test_probe_gather_validation():
     assert call(a0=MIS) == hs2.HS2_ERR_INVALID_ARG
     assert call(a1=0) == hs2.HS2_ERR_INVALID_ARG
     assert call(a7=100) == hs2.HS2_ERR_INVALID_ARG          # sink too small for the grid
+
+
+def test_probe_mfma_validation():
+    L = hs2.lib()
+    # waves_per_simd, n_blocks, iters, one, ops, sink, sink_words, stream
+    args = [1, 1024, 100, 1.0, None, FAKE, 1024 * 256, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_probe_mfma(*a)
+
+    assert call(a0=3) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a0=0) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a1=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a1=65536) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a2=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a2=(1 << 20) + 1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a5=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a5=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a4=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a6=1024 * 256 - 1) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a0=2) == hs2.HS2_ERR_INVALID_ARG            # two waves a SIMD need twice the sink

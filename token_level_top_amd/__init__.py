@@ -36,6 +36,7 @@ _SIGS = {
     "hs2_sparse_attn_window": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i64, _i, _i, _p, _i, _i, _f, _p,
                                 _p, _p, _sz, _p], _i),
     "hs2_probe_gather": ([_p, _i64, _i, _p, _p, _i64, _p, _i64, _p], _i),
+    "hs2_probe_mfma": ([_i, _i, _i, _f, _p, _p, _i64, _p], _i),
     "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
                                  _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
@@ -190,6 +191,21 @@ def probe_gather(src, idx, scale=None, sink=None, stream=None):
     rc = lib().hs2_probe_gather(_ptr(src), n_rows, row_bytes, _ptr(scale), _ptr(idx), idx.numel(), _ptr(sink),
                                 sink.numel(), _stream(stream))
     _check("hs2_probe_gather", rc)
+    return sink
+
+
+def probe_mfma(waves_per_simd: int, n_blocks: int, iters: int, one: float = 1.0, ops=None, sink=None,
+               stream=None):
+    """hs2_probe_mfma: ops None (constant operands) or [64, 16] bf16 (lane l's A
+    fragment in ops[l, :8], its B fragment in ops[l, 8:]). Returns the sink
+    tensor (n_blocks * 256 * waves_per_simd floats)."""
+    n = n_blocks * 256 * waves_per_simd
+    sink = torch.empty(n, dtype=torch.float32, device="cuda") if sink is None else sink
+    if ops is not None:
+        assert ops.dtype == torch.bfloat16 and ops.numel() == 64 * 16 and ops.is_contiguous()
+    rc = lib().hs2_probe_mfma(waves_per_simd, n_blocks, iters, one, _ptr(ops), _ptr(sink), sink.numel(),
+                              _stream(stream))
+    _check("hs2_probe_mfma", rc)
     return sink
 
 

@@ -588,6 +588,17 @@ int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float
     return HS2_OK;
 }
 
+int hs2_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const uint16_t* ops, float* sink,
+                   int64_t sink_words, void* stream) {
+    if (waves_per_simd != 1 && waves_per_simd != 2) return HS2_ERR_UNSUPPORTED;
+    if (n_blocks < 1 || n_blocks > 65535 || iters < 1 || iters > (1 << 20) || !sink || !aligned16(sink) ||
+        !aligned16(ops))
+        return HS2_ERR_INVALID_ARG;
+    if (sink_words < (int64_t)n_blocks * 256 * waves_per_simd) return HS2_ERR_INVALID_ARG;
+    HS2_TRY(launch_probe_mfma(waves_per_simd, n_blocks, iters, one, ops, sink, static_cast<hipStream_t>(stream)));
+    return HS2_OK;
+}
+
 int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_layers, int d, int kv_dtype,
                    void* k_out, void* v_out, float* k_scale, float* v_scale, void* stream) {
     if (T < 0 || hidden <= 0 || n_layers < 0) return HS2_ERR_INVALID_ARG;

@@ -200,6 +200,11 @@ int sparse_attn_enqueue(const void* q, int q_dtype, int n_layers, const void* k,
                         const int32_t* indices, int n_sel, float sm_scale, void* out, float* lse, void* scratch,
                         hipStream_t stream);
 
+// measurement probe: n_blocks workgroups of 4 waves_per_simd waves, each wave
+// iters x 8 dense v_mfma_f32_32x32x16_bf16 on register operands (constant, or
+// per lane from ops)
+hipError_t launch_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const uint16_t* ops, float* sink,
+                             hipStream_t st);
 // measurement probe: n_idx random-row gathers (row_bytes 128 or 256, with a
 // per-row fp32 scale when scale is given), folded into sink[n_blocks * 256]
 hipError_t launch_probe_gather(const void* src, int64_t n_rows, const float* scale, int row_bytes, const int32_t* idx,
