@@ -216,18 +216,14 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
 constexpr int kDmaKC = 32;                          // hidden elements per stage
 constexpr int kDmaStageElems = 256 * kDmaKC;        // per operand and stage
 
-#ifndef HS2_PROJ_WAVES
-#define HS2_PROJ_WAVES 8
-#endif
+constexpr int kDmaWaves = 8;
+
 template <int D, bool FP8OUT>
-__global__ __launch_bounds__(64 * HS2_PROJ_WAVES) __attribute__((amdgpu_waves_per_eu(HS2_PROJ_WAVES / 4,
-                                                                                      HS2_PROJ_WAVES / 4)))
+__global__ __launch_bounds__(64 * kDmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kv_project_dma_kernel(ProjectArgs a) {
-    constexpr int NWV = HS2_PROJ_WAVES;
-    // NWV = 4: one wave per SIMD, 128 x 128 per wave; NWV = 8: two, 128 x 64
-    constexpr int WN = 512 / NWV;                   // tokens per wave
-    constexpr int NM = 4, NB = WN / 32;
-    constexpr int LPT = 16 / NWV;                   // load instructions per operand, wave and stage
+    constexpr int WN = 64;                          // tokens per wave
+    constexpr int NM = 4, NB = WN / 32;             // 128 x 64 per wave
+    constexpr int LPT = 2;                          // load instructions per operand, wave and stage
     constexpr int HPW = 128 / D;                    // heads per wave
     __shared__ __attribute__((aligned(16))) uint16_t w0[kDmaStageElems], w1[kDmaStageElems], w2[kDmaStageElems],
         w3[kDmaStageElems];
@@ -307,20 +303,10 @@ void kv_project_dma_kernel(ProjectArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        // (literal counts: the builtin takes no dependent constant)
-        if constexpr (NB == 4)
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        else
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NM * NB - NM - NB, 0);
     };
-    // vmcnt <= the two younger stages' loads (2 LPT each: 16 or 8), lgkmcnt 0
-    // (the immediates are literals: the builtin takes no dependent constant)
-    auto wait_open = [&]() {
-        if constexpr (LPT == 4)
-            __builtin_amdgcn_s_waitcnt(0x4070);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0078);
-    };
+    // vmcnt <= the two younger stages' loads (2 LPT = 4 each), lgkmcnt 0
+    auto wait_open = [&]() { __builtin_amdgcn_s_waitcnt(0x0078); };
     // stage c's buffers are open (its loads landed for every wave) and set 0
     // holds its first step's fragments: refill the stage read before, read the
     // second step's fragments under the first step's MFMAs, then open stage
@@ -425,11 +411,11 @@ hipError_t launch_kv_project(const ProjectArgs& a, int D, bool fp8, hipStream_t 
         const int64_t n_tb = (a.T + kProjTokens - 1) / kProjTokens;
         const dim3 grid((unsigned)(n_tb * (2 * a.n_layers * D / 256)));
         if (D == 64) {
-            if (fp8) hipLaunchKernelGGL((kv_project_dma_kernel<64, true>), grid, dim3(64 * HS2_PROJ_WAVES), 0, st, a);
-            else hipLaunchKernelGGL((kv_project_dma_kernel<64, false>), grid, dim3(64 * HS2_PROJ_WAVES), 0, st, a);
+            if (fp8) hipLaunchKernelGGL((kv_project_dma_kernel<64, true>), grid, dim3(64 * kDmaWaves), 0, st, a);
+            else hipLaunchKernelGGL((kv_project_dma_kernel<64, false>), grid, dim3(64 * kDmaWaves), 0, st, a);
         } else {
-            if (fp8) hipLaunchKernelGGL((kv_project_dma_kernel<128, true>), grid, dim3(64 * HS2_PROJ_WAVES), 0, st, a);
-            else hipLaunchKernelGGL((kv_project_dma_kernel<128, false>), grid, dim3(64 * HS2_PROJ_WAVES), 0, st, a);
+            if (fp8) hipLaunchKernelGGL((kv_project_dma_kernel<128, true>), grid, dim3(64 * kDmaWaves), 0, st, a);
+            else hipLaunchKernelGGL((kv_project_dma_kernel<128, false>), grid, dim3(64 * kDmaWaves), 0, st, a);
         }
         return hipGetLastError();
     }
