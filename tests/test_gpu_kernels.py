@@ -402,6 +402,29 @@ def test_sparse_out_of_range_entries_are_skipped(hs2, orc, cfg, n_q):
     lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype])
 
 
+@pytest.mark.parametrize("cfg,n_q", [(2, 3), (2, 300), (4, 40)])
+def test_sparse_duplicate_entries_count_each_time(hs2, orc, cfg, n_q):
+    """An index row may name a position more than once (the ABI attends to it
+    as often as it appears, as the oracle does): rows drawn with replacement
+    from a few hundred positions, so most positions repeat, against the oracle;
+    few tokens take the split path, many the one-workgroup path."""
+    n_ctx, n_sel = 3000, 1152
+    wl = workload(cfg).with_(B=1, n_q=n_q, q_pos0=n_ctx - n_q, n_ctx=n_ctx, n_needles=0, needles="none",
+                             n_sparse=1)
+    x = make_inputs(wl)
+    rng = np.random.default_rng(29 + n_q)
+    pool = rng.choice(n_ctx, size=300, replace=False)
+    idx = np.sort(rng.choice(pool, size=(n_q, n_sel), replace=True), axis=1).astype(np.int32)
+    idx[:, -5:] = -1
+    say("sparse with duplicate entries", wl.name, n_q)
+    out, lse = hs2.sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale),
+                               indices=torch.from_numpy(idx).reshape(1, n_q, n_sel).cuda(), sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    r = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, idx, x.sm_scale, list(range(n_q)))
+    rows_close(out[0, 0], r["out"], RTOL[wl.kv_dtype], "sparse out (duplicates)")
+    lse_close(lse[0, 0], r["lse"], RTOL[wl.kv_dtype], "sparse lse (duplicates)")
+
+
 @pytest.mark.parametrize("cfg,H,d,n_q,n_sel", [(2, 4, 64, 9, 384), (2, 8, 128, 17, 1152), (4, 8, 64, 5, 700),
                                                (4, 4, 128, 33, 1152)])
 def test_sparse_few_tokens_head_shapes(hs2, orc, cfg, H, d, n_q, n_sel):

@@ -695,3 +695,18 @@ def test_index_select_recovers_planted_needles(orc):
     where = {row: i for i, row in enumerate(rows)}
     for row, h, j in x.needles:
         assert j in r["idx"][where[row]][128:].tolist()
+
+
+def test_sparse_duplicate_entry_is_counted_twice(orc):
+    """A position listed twice gets two softmax terms: over the row [j, j] the
+    weights are 1/2 each, so O = v_j and LSE = s_j + ln 2 (closed form)."""
+    g = torch.Generator().manual_seed(3)
+    H, d, n_ctx = 2, 4, 8
+    q = torch.randn(1, 1, H, d, generator=g)
+    k = torch.randn(1, n_ctx, d, generator=g)
+    v = torch.randn(1, n_ctx, d, generator=g)
+    j, sm = 5, 0.5
+    r = orc.sparse(q, k, v, None, None, np.array([[j, j, -1]], np.int32), sm, [0])
+    s_j = sm * (q[0, 0].double() @ k[0, j].double()).numpy()          # [H]
+    np.testing.assert_allclose(r["out"][0], np.broadcast_to(v[0, j].double().numpy(), (H, d)), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"][0], s_j + np.log(2.0), rtol=0, atol=1e-12)
