@@ -382,6 +382,17 @@ int hs2_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const
                    int64_t sink_words, void* stream);
 
 /*
+ * Test hook (not part of the computation): with `on` nonzero, the kernels
+ * launched by later calls (from any thread) deal their workgroups' work in
+ * the reverse of the usual order — the prefill passes, the sparse and decode
+ * attention kernels, the selection's candidate collection and the KV
+ * projection — so that a test can check that no result depends on the order
+ * in which workgroups run or on which of them run together. Every result is
+ * required to be bit-identical either way. Returns HS2_OK.
+ */
+int hs2_test_reverse_grid(int on);
+
+/*
  * Measurement hook (not part of the computation). Kernel classes, one bit each:
  *   bit 0 decode split-K attention     bit 1 decode/sparse partial combine
  *   bit 2 decode token scores          bit 3 selection histogram

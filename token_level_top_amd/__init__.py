@@ -37,6 +37,7 @@ _SIGS = {
                                 _p, _p, _sz, _p], _i),
     "hs2_probe_gather": ([_p, _i64, _i, _p, _p, _i64, _p, _i64, _p], _i),
     "hs2_probe_mfma": ([_i, _i, _i, _f, _p, _p, _i64, _p], _i),
+    "hs2_test_reverse_grid": ([_i], _i),
     "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
                                  _p], _i),
     "hs2_select_topk": ([_p, _i64, _i64, _p, _i, _p, _p, _sz, _p], _i),
@@ -207,6 +208,12 @@ def probe_mfma(waves_per_simd: int, n_blocks: int, iters: int, one: float = 1.0,
                               _stream(stream))
     _check("hs2_probe_mfma", rc)
     return sink
+
+
+def set_reverse_grid(on: bool) -> None:
+    """hs2_test_reverse_grid: later calls' kernels deal their work in reverse
+    order (a test hook; results must not change)."""
+    _check("hs2_test_reverse_grid", lib().hs2_test_reverse_grid(1 if on else 0))
 
 
 def sparse_attn_noalloc(q, k, v, k_scale=None, v_scale=None, *, indices, sm_scale: float, out=None, lse=None,

@@ -17,6 +17,9 @@ namespace {
 
 using namespace hs2;
 
+// test hook (hs2_test_reverse_grid): kernels deal their grids in reverse order
+std::atomic<int> g_rev{0};
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -330,6 +333,7 @@ int run_sparse(const void* q, int q_dtype, int n_layers, const void* k, const vo
     const size_t qstride = (size_t)n_tok * H * d * esize(q_dtype);
     for (int l0 = 0; l0 < n_layers; ++l0) {
         RowsArgs a{};
+        a.rev = g_rev.load(std::memory_order_relaxed);
         a.q = static_cast<const char*>(q) + qstride * l0;
         a.k = k;
         a.v = v;
@@ -519,6 +523,7 @@ int hs2_sparse_attn_window(const void* q, int q_dtype, int n_layers, const void*
         float* ll = lse ? lse + (size_t)n_tok * H * l : nullptr;
         // 1. the window part: one dense band per query block
         PrefillArgs pa{};
+        pa.rev = g_rev.load(std::memory_order_relaxed);
         pa.q = ql;
         pa.k = k;
         pa.kc = w.kc;
@@ -539,6 +544,7 @@ int hs2_sparse_attn_window(const void* q, int q_dtype, int n_layers, const void*
         HS2_TRY(TIMED(KC_WINDOW, s, launch_window_attn(pa, H, d, kv_dtype, s)));
         // 2. the global part, gathered, merged with the window's record
         RowsArgs a{};
+        a.rev = g_rev.load(std::memory_order_relaxed);
         a.q = ql;
         a.k = k;
         a.v = v;
@@ -588,6 +594,11 @@ int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float
     return HS2_OK;
 }
 
+int hs2_test_reverse_grid(int on) {
+    g_rev.store(on ? 1 : 0, std::memory_order_relaxed);
+    return HS2_OK;
+}
+
 int hs2_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const uint16_t* ops, float* sink,
                    int64_t sink_words, void* stream) {
     if (waves_per_simd != 1 && waves_per_simd != 2) return HS2_ERR_UNSUPPORTED;
@@ -613,6 +624,7 @@ int hs2_kv_project(const void* h, int64_t T, int hidden, const void* w, int n_la
     if (fp8 && (!aligned16(k_scale) || !aligned16(v_scale))) return HS2_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProjectArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.h = h;
     a.w = w;
     a.T = T;
@@ -646,6 +658,7 @@ int hs2_block_attn_select(const void* q, int q_dtype, const void* k, const void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     const BlockPfWs w = block_pf_ws(workspace, B, n_q, n_ctx, H, d, kv_dtype);
     PrefillArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.q = q;
     a.k = k;
     a.kc = w.kc;
@@ -702,6 +715,7 @@ int hs2_block_sparse_attn(const void* q, int q_dtype, int n_layers, const void* 
     // one launch per layer: window branch, block branch, gated sum
     for (int l = 0; l < n_layers; ++l) {
         RowsArgs a{};
+        a.rev = g_rev.load(std::memory_order_relaxed);
         a.q = static_cast<const char*>(q) + qstride * l;
         a.k = k;
         a.v = v;
@@ -742,6 +756,7 @@ int hs2_index_select(const uint8_t* q_idx, const float* q_scale, const float* we
     const IndexWs w = index_ws(workspace, B, n_q, n_ctx, dI);
     HS2_TRY(TIMED(KC_PREP, s, launch_widen_fp8(k_idx, w.kc, (int64_t)B * n_ctx * dI, s)));
     PrefillArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.q = q_idx;
     a.kc = w.kc;
     a.ks = k_scale;
@@ -772,6 +787,7 @@ int hs2_select_topk(const float* scores, int64_t rows, int64_t row_len, const in
     hipStream_t s = static_cast<hipStream_t>(stream);
     const SelectWs w = select_ws(workspace, rows, row_len);
     SelectArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.scores = scores;
     a.rows = rows;
     a.row_stride = row_len;
@@ -821,6 +837,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     // 1. full layer, split over the cache: logits + partial (m, l, O)
     const int ns = decode_splits(B, n_ctx);
     RowsArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.q = q_full;
     a.k = k;
     a.v = v;
@@ -876,6 +893,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     HS2_TRY(TIMED(KC_SCORE, s, launch_decode_score(sa, B, s)));
     // 3. window + top-k_global, in position order
     SelectArgs se{};
+    se.rev = g_rev.load(std::memory_order_relaxed);
     se.scores = sc;
     se.rows = B;
     se.row_stride = n_ctx;
@@ -919,6 +937,7 @@ int hs2_full_attn_select(const void* q, int q_dtype, const void* k, const void* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PrefillWs w = prefill_ws(workspace, B, n_q, n_ctx, H, d, kv_dtype);
     PrefillArgs a{};
+    a.rev = g_rev.load(std::memory_order_relaxed);
     a.q = q;
     a.k = k;
     a.kc = w.kc;

@@ -44,6 +44,7 @@ struct RowsArgs {
     int k_blocks, win;
     int64_t q_pos0;
     const float* gates;
+    int rev;                // test hook: deal the grid in reverse order (0: normal)
 };
 
 struct CombineArgs {
@@ -99,6 +100,7 @@ struct SelectArgs {
     int32_t* out;           // [rows][out_stride]
     int64_t out_stride;
     int out_offset;         // first column written in each out row
+    int rev;                // test hook: deal the grid in reverse order (0: normal)
 };
 // hist zeroed; fills hist
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);
@@ -145,6 +147,7 @@ struct PrefillArgs {
     int64_t kv_off, kc_rows;
     float* win_rec;
     int64_t win_stride;
+    int rev;                // test hook: deal the grid in reverse order (0: normal)
 };
 // rows j_lo .. j_lo + ld - 1 of every sequence (ld a multiple of 64): V^T into vt
 // [B][D][ld] (column j - j_lo), FP8 K widened into kc [B][kc_rows][D] (row j - j_lo)
@@ -184,6 +187,7 @@ struct ProjectArgs {
     void* v_out;
     float* k_scale;
     float* v_scale;
+    int rev;                // test hook: deal the grid in reverse order (0: normal)
 };
 hipError_t launch_kv_project(const ProjectArgs& a, int D, bool fp8, hipStream_t st);
 

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps block addresses scalar
     const int hl = lane & 15, g = lane >> 4;
-    const int seq = blockIdx.y, split = blockIdx.x;
+    const int seq = blockIdx.y, split = a.rev ? (int)(gridDim.x - 1u - blockIdx.x) : (int)blockIdx.x;
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
     const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
     // wave w takes blocks w, w+4, w+8, ...: the workgroup reads (and writes logits

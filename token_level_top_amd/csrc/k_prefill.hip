@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_fwd_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int n_blk = (int)((a.n_q + TB - 1) / TB);
-    const int blk = n_blk - 1 - (int)blockIdx.x;  // longest rows first
+    const int blk = a.rev ? (int)blockIdx.x : n_blk - 1 - (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y;
     const int64_t tok0 = (int64_t)blk * TB;
     const int R = 32 * w + n;                      // this lane's (token, head) row in the block
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_pipe_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int n_blk = (int)((a.n_q + TB - 1) / TB);
-    const int blk = n_blk - 1 - (int)blockIdx.x;  // longest rows first
+    const int blk = a.rev ? (int)blockIdx.x : n_blk - 1 - (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y;
     const int64_t tok0 = (int64_t)blk * TB;
     const int64_t p_min = a.q_pos0 + tok0;
@@ -901,7 +901,7 @@ void score_stream_kernel(PrefillArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave addresses scalar
     const int n = lane & 31, hh = lane >> 5;
     const int n_blk = (int)((a.n_q + TB - 1) / TB);
-    const int blk = n_blk - 1 - (int)blockIdx.x;
+    const int blk = a.rev ? (int)blockIdx.x : n_blk - 1 - (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y;
     const int64_t tok0 = (int64_t)blk * TB;
     const int64_t wtok0 = tok0 + (int64_t)w * TW;  // first token of this wave
@@ -1241,7 +1241,7 @@ void block_score_kernel(PrefillArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
     const int n_blk = (int)((a.n_q + TB - 1) / TB);
-    const int blk = n_blk - 1 - (int)blockIdx.x;
+    const int blk = a.rev ? (int)blockIdx.x : n_blk - 1 - (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y;
     const int64_t tok0 = (int64_t)blk * TB;
     const int64_t wtok0 = tok0 + (int64_t)w * TW;

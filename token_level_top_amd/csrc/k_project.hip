@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kProjThreads * NH) void kv_project_kernel(ProjectAr
     const int head = w >> 2, tg = w & 3;
     const int n = lane & 31, hh = lane >> 5;
     // XCD-aware placement (see the header comment)
-    const uint32_t n_wg = gridDim.x, bid = blockIdx.x, full = n_wg & ~7u;
+    const uint32_t n_wg = gridDim.x, bid = a.rev ? n_wg - 1u - blockIdx.x : blockIdx.x, full = n_wg & ~7u;
     const uint32_t logical = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
     const int n_groups = 2 * a.n_layers / NH;
     const int tb = (int)(logical / (uint32_t)n_groups);
@@ -235,7 +235,7 @@ void kv_project_dma_kernel(ProjectArgs a) {
     const int wm = w & 1, wn = w >> 1;
     const int n = lane & 31, hh = lane >> 5;
     // XCD-aware placement (see the file's header comment)
-    const uint32_t n_wg = gridDim.x, bid = blockIdx.x, full = n_wg & ~7u;
+    const uint32_t n_wg = gridDim.x, bid = a.rev ? n_wg - 1u - blockIdx.x : blockIdx.x, full = n_wg & ~7u;
     const uint32_t logical = bid < full ? (bid & 7u) * (full >> 3) + (bid >> 3) : bid;
     const int n_groups = 2 * a.n_layers * D / 256;
     const int tb = (int)(logical / (uint32_t)n_groups);

@@ -117,7 +117,8 @@ void rows_attn_kernel(RowsArgs a) {
     const int hl = lane & 15, g = lane >> 4;
     // 1-D grid, the splits of one token adjacent (a y dimension would cap the
     // token count at 65535)
-    const int tok = (int)(blockIdx.x / (uint32_t)a.n_split), split = (int)(blockIdx.x % (uint32_t)a.n_split);
+    const uint32_t bx = a.rev ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
+    const int tok = (int)(bx / (uint32_t)a.n_split), split = (int)(bx % (uint32_t)a.n_split);
     const int seq = tok / a.n_q;
     const int64_t r_begin = (int64_t)split * a.rows_per_split;
     const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a) 
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     const int64_t n = row_cands(a, r);
-    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
+    const int64_t j0 = (int64_t)(a.rev ? gridDim.x - 1u - blockIdx.x : blockIdx.x) * kSelChunk;
     const int64_t j1 = min<int64_t>(j0 + kSelChunk, n);
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) atomicAdd(&hist[score_bin(s[j])], 1u);
@@ -195,7 +195,8 @@ __device__ __forceinline__ void collect_row_chunk(const SelectArgs& a, int64_t r
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float* s = a.scores + (size_t)r * (size_t)a.row_stride;
     uint64_t* cand = a.cand + (size_t)r * kCandCap;
-    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk, j1 = min<int64_t>(j0 + kSelChunk, n);
+    const uint32_t chunk = a.rev ? gridDim.x - 1u - blockIdx.x : blockIdx.x;
+    const int64_t j0 = (int64_t)chunk * kSelChunk, j1 = min<int64_t>(j0 + kSelChunk, n);
     float v[kCollectPer];
 #pragma unroll
     for (int q = 0; q < kCollectPer / 4; ++q) {
@@ -211,7 +212,7 @@ __device__ __forceinline__ void collect_row_chunk(const SelectArgs& a, int64_t r
     }
     // the threshold bin, while the score loads are in flight
     const uint32_t tbin = row_threshold_bin(a.hist + (size_t)r * kHistBins, kk, wave_tot, sh);
-    if (blockIdx.x == 0 && t == 0) a.thr[2 * r] = tbin;
+    if (chunk == 0 && t == 0) a.thr[2 * r] = tbin;
     uint32_t take = 0;
 #pragma unroll
     for (int i = 0; i < kCollectPer; ++i)
@@ -253,7 +254,7 @@ __device__ __forceinline__ void collect_row_chunk(const SelectArgs& a, int64_t r
         off[q] = total + before + ((inc[p] >> sh16) & 0xFFFFu) - ((pk[p] >> sh16) & 0xFFFFu);
         total += tot_q;
     }
-    uint32_t* run = a.runs + ((size_t)r * (size_t)a.runs_stride + blockIdx.x) * 2;
+    uint32_t* run = a.runs + ((size_t)r * (size_t)a.runs_stride + chunk) * 2;
     if (total == 0) {  // uniform over the workgroup
         if (t == 0) {
             run[0] = 0u;
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     __shared__ uint64_t red[kFinThreads / 64];
     __shared__ uint32_t scratch[1024];  // the whole-row fallback; scan scratch
     static_assert(256 * (kFinThreads / 64) >= kCandCap, "hist holds one flag / offset per candidate");
-    const int64_t r = blockIdx.x;
+    const int64_t r = a.rev ? (int64_t)(gridDim.x - 1u - blockIdx.x) : (int64_t)blockIdx.x;
     const int tid = threadIdx.x;
     int32_t* out = a.out + (size_t)r * (size_t)a.out_stride;
     // forced window (decode rows all sit at p_last)
