@@ -45,6 +45,13 @@ KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "score
         "kv_project": "k_project.hip"}
 
 
+def device_name() -> str:
+    """The GPU the line was measured on (name and ISA)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return f"{p.name} ({getattr(p, 'gcnArchName', '?')}, {p.multi_processor_count} CUs)"
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -609,7 +616,7 @@ def main():
                       "k_global": wl.k_global, "n_sparse": wl.n_sparse},
            "roofline": roof,
            "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms_step, 4)},
-           "launch": "hip_graph" if args.graph else "eager"}
+           "launch": "hip_graph" if args.graph else "eager", "device": device_name()}
     if args.graph:
         res["eager_ms_per_step"] = round(ms_eager, 4)
     if args.breakdown:
