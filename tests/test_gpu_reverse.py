@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from hs2_inputs import make_gates, make_inputs, make_projection_inputs, workload
+from hs2_inputs import make_gates, make_indexer_inputs, make_inputs, make_projection_inputs, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,26 @@ def test_block_variant(hs2):
     gates = dev(make_gates(7, (2, 1, wl.n_q, wl.H, 2)))
     both_orders(hs2, lambda: (hs2.block_sparse_attn(dev(x.q_sparse), dev(x.k), dev(x.v), block_idx=bidx, q_pos0=0,
                                                     window=128, gates=gates, sm_scale=x.sm_scale),))
+
+
+@pytest.mark.parametrize("cfg,n_q,q_pos0,n_ctx", [(2, 1100, 900, 2000), (4, 300, 2700, 3000)])
+def test_window_sharing(hs2, cfg, n_q, q_pos0, n_ctx):
+    wl = workload(cfg).with_(n_q=n_q, q_pos0=q_pos0, n_ctx=n_ctx, n_needles=2, n_sparse=2)
+    x = make_inputs(wl)
+    kv = (dev(x.k), dev(x.v), dev(x.k_scale), dev(x.v_scale))
+    _, _, idx = hs2.full_attn_select(dev(x.q), *kv, q_pos0=q_pos0, window=wl.window, k_global=wl.k_global,
+                                     sm_scale=x.sm_scale)
+    say("reverse grid: window sharing", wl.name, n_q)
+    both_orders(hs2, lambda: hs2.sparse_attn_window(dev(x.q_sparse), *kv, indices=idx, q_pos0=q_pos0,
+                                                    window=wl.window, sm_scale=x.sm_scale))
+
+
+@pytest.mark.parametrize("B,n_q,q_pos0,n_ctx,HI,dI,kg", [
+    (1, 600, 2400, 3000, 8, 64, 1024),      # threshold histograms
+    (2, 20, 66000, 66020, 16, 128, 2048),   # 64 Ki candidates or more: superset trims
+])
+def test_index_select(hs2, B, n_q, q_pos0, n_ctx, HI, dI, kg):
+    x = make_indexer_inputs(11, B, n_q, q_pos0, n_ctx, HI, dI, n_needles=4)
+    say("reverse grid: light indexer", B, n_q, n_ctx, HI, kg)
+    both_orders(hs2, lambda: (hs2.index_select(x.qi.cuda(), x.qs.cuda(), x.w.cuda(), x.ki.cuda(), x.ks.cuda(),
+                                               q_pos0=q_pos0, window=128, k_global=kg),))
