@@ -9,9 +9,13 @@
 // softmax per head, accumulate P V, and store the base-2 logits (the token score
 // needs the final LSE, which is only known once every split is done).
 //
-// Layout of the work: a workgroup owns `rows_per_split` keys of one sequence;
-// its 4 waves take interleaved blocks of 32 keys (so the workgroup streams one
-// contiguous region) with no workgroup barrier until the final merge.
+// Layout of the work: the n_split workgroups of a sequence deal its keys out
+// in 128-key chunks, split s taking chunks s, s + n_split, s + 2 n_split, ...,
+// and the 4 waves of a workgroup take the four 32-key blocks of each chunk, with
+// no workgroup barrier until the final merge. The workgroups of one sequence
+// that run together therefore sweep one contiguous stretch of it (measured
+// 1-5 % faster than each workgroup streaming a contiguous region of its own,
+// most with many splits per sequence).
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: 16 keys on M, the heads on N. The
 //    A operand (K rows) comes straight from HBM into registers: for k-step c the
 //    lane group g reads d = 32c + 8g .. +7 of its key row, so one load
@@ -57,13 +61,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps block addresses scalar
     const int hl = lane & 15, g = lane >> 4;
     const int seq = blockIdx.y, split = a.rev ? (int)(gridDim.x - 1u - blockIdx.x) : (int)blockIdx.x;
-    const int64_t r_begin = (int64_t)split * a.rows_per_split;
-    const int64_t r_end = min<int64_t>(r_begin + a.rows_per_split, a.n_rows);
-    // wave w takes blocks w, w+4, w+8, ...: the workgroup reads (and writes logits
-    // for) one contiguous region that advances 128 keys at a time
-    constexpr int64_t kStride = 4 * kDecBlock;
-    const int64_t w_begin = r_begin + w * kDecBlock;
-    const int nb = w_begin < r_end ? (int)((r_end - w_begin + kStride - 1) / kStride) : 0;
+    const int64_t r_end = a.n_rows;
+    // block n of wave w: keys blk_j(n) .. +31, in chunk n n_split + split
+    constexpr int64_t kChunk = 4 * kDecBlock;
+    const int64_t c_stride = kChunk * a.n_split, s0 = (int64_t)split * kChunk;
+    auto blk_j = [&](int n) -> int64_t { return (int64_t)n * c_stride + s0 + w * kDecBlock; };
+    int nb = 0;
+    if (s0 < r_end) {
+        const int64_t c_cnt = (r_end - s0 + c_stride - 1) / c_stride;  // chunks of the split
+        nb = (int)c_cnt - ((c_cnt - 1) * c_stride + s0 + w * kDecBlock < r_end ? 0 : 1);
+    }
     const size_t kv_base = (size_t)seq * (size_t)a.n_ctx;
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + kv_base * RB;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + kv_base * RB;
@@ -91,17 +98,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     // Two blocks are in flight per wave: while block n is computed, the loads
     // of blocks n+1 and n+2 are outstanding (block n+2's as soon as block n's
     // QK^T MFMAs have read its K registers). Loads go through a descriptor
-    // whose range ends at the split's last row, so rows past it read as zero
-    // (their logits are masked) and no row index needs clamping.
+    // whose range ends at the block's last row inside the sequence, so rows
+    // past the sequence read as zero (their logits are masked) and no row index
+    // needs clamping.
     // K: lane (row hl of group grp, g) reads elements 32c + 8g .. +7 of key row
     // j + 16*grp + hl for every k-step c. V: lane reads pieces lane + 64*i of the
     // block's rows (contiguous in the cache).
     KPiece kr[2][2][NC];
     u32x4 vr[2][VP];
     float ksr[2] = {0.f, 0.f}, vsr[2] = {0.f, 0.f};
-    const int n_split_rows = (int)(r_end - r_begin);
-    // rows of the split at and after row j (0 past its end: every access then misses the range)
-    auto rows_left = [&](int64_t j) -> uint32_t { return (uint32_t)max(0, n_split_rows - (int)(j - r_begin)); };
+    // rows of block j inside the sequence (0 past its end: every access then misses the range)
+    auto rows_left = [&](int64_t j) -> uint32_t {
+        return (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - j));
+    };
     // bf16 K/V stream through non-temporal loads (each byte is read once): the
     // split kernel at 64 x 128k runs 0.943 -> 0.900 ms; with FP8 rows (8-byte K
     // pieces) the same hint measured slower (0.263 -> 0.286 ms at 4 x 1M)
@@ -158,14 +167,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         }
     };
     // logits of the previous block: staged [32][H] in LDS, written as 16-B
-    // streaming stores through a descriptor ending at the split's last row
-    // (before the first block its range is empty). Every load and store of the
+    // streaming stores through a descriptor ending at the block's last row
+    // inside the sequence (before the first block its range is empty). Every load and store of the
     // loop is issued unconditionally, so the compiler's waits on the loads of
     // the next block count exactly the operations issued after them.
     int64_t pend_j = r_end;
     auto flush_logits = [&]() {
         const auto rl = raw_buffer(a.logits + (kv_base + (size_t)pend_j) * H,
-                                   (uint32_t)max<int64_t>(0, r_end - pend_j) * (uint32_t)(H * 4));
+                                   (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * 4));
 #pragma unroll
         for (int p = lane; p < kDecBlock * H / 4; p += 64)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(lgl + 4 * p)),
@@ -257,16 +266,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     // lies past the split: its loads read zeros, its logits are all masked
     // (no change to m, l, O) and its stores are dropped.
     auto step = [&](int buf, int n) {
-        const int64_t j = w_begin + (int64_t)n * kStride;
+        const int64_t j = blk_j(n);
         flush_logits();
         f32x4 sacc[2];
         scores(buf, sacc);
-        load_block(buf, j + 2 * kStride);
+        load_block(buf, blk_j(n + 2));
         finish(sacc, j);
         stage_v(buf ^ 1);
     };
-    load_block(0, w_begin);
-    load_block(1, w_begin + kStride);
+    load_block(0, blk_j(0));
+    load_block(1, blk_j(1));
     stage_v(0);
     for (int n = 0; n < nb; n += 2) {
         step(0, n);
