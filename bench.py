@@ -225,7 +225,10 @@ def gather_probe(args) -> int:
     the memory system returns them, nothing else done with them -- out of a
     source of 16 MiB (the 32k prefill's K + V, which the memory-side cache
     holds) and of 64 MiB, 256-byte rows (bf16, d = 128) and 128-byte rows with
-    a 4-byte scale each (FP8). hipEvents around each launch, median of steps."""
+    a 4-byte scale each (FP8). The 256-byte cases are also read as runs of 64
+    consecutive rows at random 64-row-aligned starts, the access pattern of the
+    block-level variant's sparse layer (64-token blocks). hipEvents around each
+    launch, median of steps."""
     import torch
     import token_level_top_amd as hs2
     dev = torch.device("cuda:0")
@@ -238,11 +241,12 @@ def gather_probe(args) -> int:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     sink = torch.empty(524288, dtype=torch.int32, device=dev)
     for mib in (16, 64):
-        for row_bytes, with_scale in ((256, False), (128, True)):
+        for row_bytes, with_scale, run in ((256, False, 1), (128, True, 1), (256, False, 64)):
             n_rows = mib * 1024 * 1024 // row_bytes
             src = torch.randint(0, 255, (n_rows, row_bytes), dtype=torch.uint8, device=dev, generator=g)
             scale = torch.rand(n_rows, device=dev, generator=g) if with_scale else None
-            idx = torch.randint(0, n_rows, (n_idx,), dtype=torch.int32, device=dev, generator=g)
+            starts = torch.randint(0, n_rows // run, (n_idx // run,), device=dev, generator=g) * run
+            idx = (starts[:, None] + torch.arange(run, device=dev)[None, :]).reshape(-1).to(torch.int32).contiguous()
             for _ in range(args.warmup):
                 hs2.probe_gather(src, idx, scale, sink)
             times = []
@@ -254,10 +258,10 @@ def gather_probe(args) -> int:
                 times.append(e0.elapsed_time(e1))
             ms = sorted(times)[len(times) // 2]
             rb = row_bytes + (4 if with_scale else 0)
-            res["cases"].append({"source_mib": mib, "row_bytes": rb, "ms": round(ms, 4),
+            res["cases"].append({"source_mib": mib, "row_bytes": rb, "run_rows": run, "ms": round(ms, 4),
                                  "g_rows_per_s": round(n_idx / (ms / 1e3) / 1e9, 2),
                                  "gathered_gb_per_s": round(n_idx * rb / (ms / 1e3) / 1e9, 1)})
-            log(f"gather probe {mib} MiB source, {rb}-byte rows: {ms:.3f} ms")
+            log(f"gather probe {mib} MiB source, {rb}-byte rows in runs of {run}: {ms:.3f} ms")
             del src, idx, scale
     print(json.dumps(res), flush=True)
     return 0
