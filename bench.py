@@ -217,6 +217,46 @@ def mfma_probe(args) -> int:
     return 0
 
 
+def stream_probe(args) -> int:
+    """Attainable streaming rate on this GPU, the reference the decode split
+    kernel is read against: hs2_probe_stream reads a 4 GiB source once (the
+    64 x 128k bf16 cache's K + V) in 4 KiB chunks dealt round-robin over 2048
+    workgroups (the split kernel's grid), with no writes and with a 4 KiB copy
+    written after every 8 chunks read (the split kernel's 64 bytes of logits
+    per 512 bytes of K and V). hipEvents around each launch, median of steps."""
+    import torch
+    import token_level_top_amd as hs2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src_bytes = 64 * 131072 * 512
+    src = torch.empty(src_bytes, dtype=torch.uint8, device=dev)
+    src.view(torch.int32).random_(0, 1 << 30, generator=torch.Generator(device=dev).manual_seed(5))
+    dst = torch.empty(src_bytes // 8, dtype=torch.uint8, device=dev)
+    res = {"metric": "streaming HBM rate (reference for the decode split kernel)", "unit": "TB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "src_bytes": src_bytes, "cases": []}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_blocks = 2048
+    sink = torch.empty(n_blocks * 256, dtype=torch.int32, device=dev)
+    for rpw in (0, 8):
+        d = dst if rpw else None
+        for _ in range(args.warmup):
+            hs2.probe_stream(src, d, rpw, n_blocks, sink)
+        times = []
+        for _ in range(args.steps):
+            e0.record()
+            hs2.probe_stream(src, d, rpw, n_blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        moved = src_bytes + (src_bytes // rpw if rpw else 0)
+        res["cases"].append({"reads_per_write": rpw, "n_blocks": n_blocks, "ms": round(ms, 4),
+                             "bytes_moved": moved, "tb_per_s": round(moved / (ms / 1e3) / 1e12, 3)})
+        log(f"stream probe, {'no writes' if not rpw else f'one write per {rpw} reads'}: {ms:.3f} ms")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def gather_probe(args) -> int:
     """Attainable random-row gather rate on this GPU, the reference the sparse
     layers' row rate is read against (a sparse layer gathers a K row and a V
@@ -385,6 +425,9 @@ def main():
                     help="instead of the attention path, time the KV Bridging projections with this cache type")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="measure the attainable dense bf16 MFMA rate (hs2_probe_mfma) instead of the path")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="instead of the attention path, measure the attainable streaming rate (a reference for the "
+                         "decode split kernel)")
     ap.add_argument("--gather-probe", action="store_true",
                     help="instead of the attention path, measure the attainable random-row gather rate (a reference "
                          "for the sparse layers)")
@@ -398,6 +441,8 @@ def main():
         return bench_kv_project(args, args.kv_project)
     if args.gather_probe:
         return gather_probe(args)
+    if args.stream_probe:
+        return stream_probe(args)
     if args.mfma_probe:
         return mfma_probe(args)
     blocks = args.hysparse_blocks

@@ -359,6 +359,28 @@ int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float
                      void* stream);
 
 /*
+ * Measurement probe (not part of the computation): the rate at which the GPU
+ * streams memory once, the reference the decode split kernel (K and V read
+ * once, a logit row written per key) is read against. Enqueues one kernel of
+ * n_blocks workgroups of 256 threads. src (src_bytes, a multiple of 4096) is
+ * read in 4 KiB chunks dealt round-robin: workgroup g reads chunks g,
+ * g + n_blocks, g + 2 n_blocks, ... (its t-th chunk is g + n_blocks t), each
+ * thread 16 bytes of a chunk, with non-temporal loads. With
+ * reads_per_write = R > 0, after its t-th chunk for every t with (t + 1) a
+ * multiple of R, workgroup g copies that chunk to chunk g + n_blocks ((t + 1)
+ * / R - 1) of dst, if that chunk lies inside dst_bytes (a multiple of 4096),
+ * with non-temporal stores; R = 0 writes nothing (dst may be NULL). Every
+ * thread folds what it read into its sink word (n_blocks * 256 words at
+ * least): the XOR of all sink words is the XOR of all 32-bit words of src.
+ * Time it with events on `stream`. Device pointers, 16-byte aligned;
+ * R in {0, 1, 2, 4, 8} (else HS2_ERR_UNSUPPORTED), dst_bytes < 2^32,
+ * 1 <= n_blocks <= 65536.
+ */
+int hs2_probe_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes,
+                     int reads_per_write, int n_blocks, uint32_t* sink, int64_t sink_words,
+                     void* stream);
+
+/*
  * Measurement probe (not part of the computation): the dense bf16
  * matrix-core rate the GPU sustains, the attainable ceiling the MFMA-bound
  * kernels are read against. Enqueues one kernel of n_blocks workgroups of

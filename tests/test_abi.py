@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     L = hs2.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -327,3 +327,31 @@ def test_probe_mfma_validation():
     assert call(a4=MIS) == hs2.HS2_ERR_INVALID_ARG
     assert call(a6=1024 * 256 - 1) == hs2.HS2_ERR_INVALID_ARG
     assert call(a0=2) == hs2.HS2_ERR_INVALID_ARG            # two waves a SIMD need twice the sink
+
+
+def test_probe_stream_validation():
+    L = hs2.lib()
+    # src, src_bytes, dst, dst_bytes, reads_per_write, n_blocks, sink, sink_words, stream
+    args = [FAKE, 1 << 20, FAKE, 1 << 17, 8, 64, FAKE, 64 * 256, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.hs2_probe_stream(*a)
+
+    assert call(a0=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a0=MIS) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a1=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a1=4097) == hs2.HS2_ERR_INVALID_ARG          # whole 4 KiB chunks
+    assert call(a3=100) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a2=None) == hs2.HS2_ERR_INVALID_ARG          # writes need dst
+    assert call(a3=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a4=-1) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a4=3) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a4=16) == hs2.HS2_ERR_UNSUPPORTED
+    assert call(a3=1 << 32) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a5=0) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a5=65537) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a6=None) == hs2.HS2_ERR_INVALID_ARG
+    assert call(a7=64 * 256 - 1) == hs2.HS2_ERR_INVALID_ARG  # sink too small for the grid

@@ -13,6 +13,11 @@ values fixed by their definitions (include/hs2.h):
     long as no row is read twice: n_idx is a multiple of the kernel's step
     (16 rows x 8 in flight for 256-byte rows, 32 x 8 for 128-byte rows).
     An index outside [0, n_rows) reads row 0.
+  * hs2_probe_stream: the XOR of all sink words equals the XOR of every
+    32-bit word of src (each 4 KiB chunk read once), and dst chunk
+    g + G w holds a copy of src chunk g + G (R (w + 1) - 1) where that chunk
+    exists (G workgroups, R reads per write), the rest of dst and a guard band
+    past it untouched.
 """
 import sys
 
@@ -81,3 +86,36 @@ def test_probe_gather_xor(row_bytes, with_scale):
     if with_scale:
         want ^= np.bitwise_xor.reduce(scale.numpy().view(np.uint32)[rows])
     assert got == want, (hex(got), hex(want))
+
+
+@pytest.mark.parametrize("n_chunks,n_dst,n_blocks,rpw", [(16387, 2100, 300, 8), (1000, 1200, 64, 1),
+                                                         (5000, 100, 256, 4), (3001, 700, 7, 2), (777, 0, 100, 0)])
+def test_probe_stream_exact(n_chunks, n_dst, n_blocks, rpw):
+    say(f"probe_stream chunks={n_chunks} dst={n_dst} blocks={n_blocks} rpw={rpw}")
+    g = torch.Generator().manual_seed(n_chunks + rpw)
+    src = torch.randint(0, 256, (n_chunks * 4096,), dtype=torch.uint8, generator=g)
+    guard = 16
+    dst = torch.full(((n_dst + guard) * 4096,), 0xA5, dtype=torch.uint8, device="cuda") if rpw else None
+    src_d = src.cuda()
+    sink = torch.empty(n_blocks * 256, dtype=torch.int32, device="cuda")
+    if rpw:
+        rc = hs2.lib().hs2_probe_stream(src_d.data_ptr(), src_d.numel(), dst.data_ptr(), n_dst * 4096, rpw, n_blocks,
+                                        sink.data_ptr(), sink.numel(), None)
+    else:
+        rc = hs2.lib().hs2_probe_stream(src_d.data_ptr(), src_d.numel(), None, 0, 0, n_blocks, sink.data_ptr(),
+                                        sink.numel(), None)
+    assert rc == hs2.HS2_OK
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want, f"XOR of sink {got:#x} != XOR of src {want:#x}"
+    if rpw:
+        d = dst.cpu().numpy().reshape(-1, 4096)
+        sc = src.numpy().reshape(-1, 4096)
+        dc = np.arange(n_dst)
+        from_chunk = dc % n_blocks + n_blocks * (rpw * (dc // n_blocks + 1) - 1)
+        written = from_chunk < n_chunks
+        assert np.array_equal(d[:n_dst][written], sc[from_chunk[written]]), "copied chunks differ"
+        assert (d[:n_dst][~written] == 0xA5).all(), "a chunk with no source chunk was written"
+        assert (d[n_dst:] == 0xA5).all(), "guard band past dst_bytes written"
+        say(f"  {int(written.sum())} of {n_dst} dst chunks copied, guard band intact")

@@ -26,7 +26,7 @@ RES = os.path.join(ROOT, "token_level_top_amd", "_build", "resource_usage.json")
 NO_SCRATCH = {"decode_split_kernel", "decode_score_kernel", "rows_attn_kernel", "combine_kernel",
               "attn_fwd_pipe_kernel", "kv_project_dma_kernel", "kv_project_kernel", "select_collect_kernel",
               "select_hist_kernel", "select_final_kernel", "block_select_kernel", "prep_kv_kernel",
-              "widen_fp8_kernel", "fill_u32_kernel", "probe_gather_kernel", "probe_mfma_kernel"}
+              "widen_fp8_kernel", "fill_u32_kernel", "probe_gather_kernel", "probe_mfma_kernel", "probe_stream_kernel"}
 BOUNDED_SCRATCH = {"score_stream_kernel": 48, "block_score_kernel": 48, "attn_fwd_kernel": 48}
 
 

@@ -37,6 +37,7 @@ _SIGS = {
                                 _p, _p, _sz, _p], _i),
     "hs2_probe_gather": ([_p, _i64, _i, _p, _p, _i64, _p, _i64, _p], _i),
     "hs2_probe_mfma": ([_i, _i, _i, _f, _p, _p, _i64, _p], _i),
+    "hs2_probe_stream": ([_p, _i64, _p, _i64, _i, _i, _p, _i64, _p], _i),
     "hs2_test_reverse_grid": ([_i], _i),
     "hs2_sparse_attn_noalloc": ([_p, _i, _i, _p, _p, _p, _p, _i, _i, _i64, _i64, _i, _i, _p, _i, _f, _p, _p,
                                  _p], _i),
@@ -192,6 +193,16 @@ def probe_gather(src, idx, scale=None, sink=None, stream=None):
     rc = lib().hs2_probe_gather(_ptr(src), n_rows, row_bytes, _ptr(scale), _ptr(idx), idx.numel(), _ptr(sink),
                                 sink.numel(), _stream(stream))
     _check("hs2_probe_gather", rc)
+    return sink
+
+
+def probe_stream(src, dst=None, reads_per_write: int = 0, n_blocks: int = 2048, sink=None, stream=None):
+    """hs2_probe_stream: src and dst uint8 tensors (sizes multiples of 4096).
+    Returns the sink tensor (n_blocks * 256 words)."""
+    sink = torch.empty(n_blocks * 256, dtype=torch.int32, device=src.device) if sink is None else sink
+    rc = lib().hs2_probe_stream(_ptr(src), src.numel(), _ptr(dst), 0 if dst is None else dst.numel(),
+                                reads_per_write, n_blocks, _ptr(sink), sink.numel(), _stream(stream))
+    _check("hs2_probe_stream", rc)
     return sink
 
 

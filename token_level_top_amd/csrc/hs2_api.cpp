@@ -594,6 +594,22 @@ int hs2_probe_gather(const void* src, int64_t n_rows, int row_bytes, const float
     return HS2_OK;
 }
 
+int hs2_probe_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, int reads_per_write,
+                     int n_blocks, uint32_t* sink, int64_t sink_words, void* stream) {
+    if (!src || !sink || !aligned16(src) || !aligned16(sink)) return HS2_ERR_INVALID_ARG;
+    if (src_bytes < 4096 || src_bytes % 4096 != 0 || dst_bytes < 0 || dst_bytes % 4096 != 0) return HS2_ERR_INVALID_ARG;
+    if (dst_bytes >= (int64_t(1) << 32) || n_blocks < 1 || n_blocks > 65536) return HS2_ERR_INVALID_ARG;
+    if (reads_per_write != 0 && reads_per_write != 1 && reads_per_write != 2 && reads_per_write != 4 &&
+        reads_per_write != 8)
+        return HS2_ERR_UNSUPPORTED;
+    if (reads_per_write > 0 && (!dst || !aligned16(dst) || dst_bytes == 0)) return HS2_ERR_INVALID_ARG;
+    if (sink_words < (int64_t)n_blocks * 256) return HS2_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HS2_TRY(launch_probe_stream(src, src_bytes, dst, reads_per_write > 0 ? dst_bytes : 0, reads_per_write, n_blocks,
+                                sink, s));
+    return HS2_OK;
+}
+
 int hs2_test_reverse_grid(int on) {
     g_rev.store(on ? 1 : 0, std::memory_order_relaxed);
     return HS2_OK;

@@ -211,6 +211,8 @@ hipError_t launch_probe_mfma(int waves_per_simd, int n_blocks, int iters, float 
                              hipStream_t st);
 // measurement probe: n_idx random-row gathers (row_bytes 128 or 256, with a
 // per-row fp32 scale when scale is given), folded into sink[n_blocks * 256]
+hipError_t launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, int rpw, int n_blocks,
+                               uint32_t* sink, hipStream_t st);
 hipError_t launch_probe_gather(const void* src, int64_t n_rows, const float* scale, int row_bytes, const int32_t* idx,
                                int64_t n_idx, uint32_t* sink, int n_blocks, hipStream_t st);
 

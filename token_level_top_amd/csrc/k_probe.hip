@@ -100,6 +100,94 @@ __global__ __launch_bounds__(64 * NW) void probe_mfma_kernel(int iters, float on
     sink[(size_t)blockIdx.x * (64 * NW) + threadIdx.x] = t;
 }
 
+// Streaming probe: the rate at which this GPU streams memory once, the
+// reference the decode split kernel is read against (one pass over the cache,
+// a 64-byte logit row written for every 512 bytes of bf16 K and V read). src
+// is read in 4 KiB chunks dealt to the workgroups round-robin, every thread 16
+// bytes of a chunk, with non-temporal loads; after every RPW-th chunk a
+// workgroup reads it writes that chunk, as is, to its next chunk of dst (same
+// round-robin order) with a non-temporal store. Two groups of eight chunks are
+// in flight: a group's loads are issued before the previous group's stores
+// and fold, so that (loads and stores share one counter) waiting for a group
+// never waits for a store. The loop body has no branches, so the compiler's
+// waits stay exact: loads and stores go through descriptors whose range ends
+// at the last chunk (of src, of dst), so a chunk past the end reads as zero
+// (folding it changes nothing) and a store that is not wanted is sent out of
+// range and dropped. What was read is folded into one word per thread.
+constexpr int kStreamChunk = 4096;
+constexpr int kStreamGroup = 8;
+constexpr uint32_t kStreamNoStore = 0xFFFFFFF0u;  // past every descriptor's range
+
+template <int RPW>
+__global__ __launch_bounds__(256) void probe_stream_kernel(const uint8_t* src, int64_t n_chunks, uint8_t* dst,
+                                                           int64_t n_dst, uint32_t* sink) {
+    static_assert(RPW == 0 || kStreamGroup % RPW == 0, "writes at fixed slots of a group");
+    const int tid = threadIdx.x;
+    const int64_t G = gridDim.x, g = blockIdx.x;
+    const uint32_t gstride = (uint32_t)G * kStreamChunk;  // bytes between a workgroup's chunks (< 2^28)
+    const auto rd = raw_buffer(dst, (uint32_t)n_dst * kStreamChunk);
+    uint32_t acc = 0;
+    // chunk t of this workgroup is g + G t
+    auto load = [&](u32x4* v, int64_t t0) {
+        const int64_t c0 = g + G * t0;
+        const int64_t left = c0 < n_chunks ? n_chunks - c0 : 0;  // chunks from c0 on
+        // wave-uniform by construction; said so, so that the descriptor stays scalar
+        const uint64_t base = (uint64_t)(src + (size_t)(c0 < n_chunks ? c0 : 0) * kStreamChunk);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+        const uint32_t left_c = (uint32_t)(left < 1048575 ? left : 1048575);  // chunks the range covers (< 2^20)
+        const uint32_t rng = __builtin_amdgcn_readfirstlane(left_c * (uint32_t)kStreamChunk);
+        const auto rs = raw_buffer(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), rng);
+#pragma unroll
+        for (int u = 0; u < kStreamGroup; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, gstride * u + 16 * tid, 0, 2);  // range-checked offset
+        __builtin_amdgcn_sched_barrier(0);  // nothing of the previous group's fold moves above these loads
+    };
+    auto finish = [&](const u32x4* v, int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < kStreamGroup; ++u) {
+            acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+            if constexpr (RPW > 0) {
+                if ((u + 1) % RPW == 0) {
+                    const int64_t t = t0 + u, dc = g + G * ((t + 1) / RPW - 1);
+                    const bool ok = g + G * t < n_chunks && dc < n_dst;
+                    const uint32_t off = ok ? (uint32_t)dc * kStreamChunk + 16 * tid : kStreamNoStore;
+                    __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, off, 0, 2);
+                }
+            }
+        }
+    };
+    // this workgroup's chunk count, in whole pairs of groups: the loop has no
+    // early exit, so no load can be sunk below a branch and lose its place
+    const int64_t mine = g < n_chunks ? (n_chunks - g + G - 1) / G : 0;
+    const int64_t n_t = (mine + 2 * kStreamGroup - 1) / (2 * kStreamGroup) * (2 * kStreamGroup);
+    u32x4 va[kStreamGroup], vb[kStreamGroup];
+    load(va, 0);
+    for (int64_t t0 = 0; t0 < n_t; t0 += 2 * kStreamGroup) {
+        load(vb, t0 + kStreamGroup);
+        finish(va, t0);
+        load(va, t0 + 2 * kStreamGroup);
+        finish(vb, t0 + kStreamGroup);
+    }
+    sink[(size_t)g * 256 + tid] = acc;
+}
+
+hipError_t launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, int rpw, int n_blocks,
+                               uint32_t* sink, hipStream_t st) {
+    const auto s = reinterpret_cast<const uint8_t*>(src);
+    const auto d = reinterpret_cast<uint8_t*>(dst);
+    const int64_t nc = src_bytes / kStreamChunk, nd = dst_bytes / kStreamChunk;
+    const dim3 grid((unsigned)n_blocks), block(256);
+    switch (rpw) {
+        case 0: hipLaunchKernelGGL(probe_stream_kernel<0>, grid, block, 0, st, s, nc, d, nd, sink); break;
+        case 1: hipLaunchKernelGGL(probe_stream_kernel<1>, grid, block, 0, st, s, nc, d, nd, sink); break;
+        case 2: hipLaunchKernelGGL(probe_stream_kernel<2>, grid, block, 0, st, s, nc, d, nd, sink); break;
+        case 4: hipLaunchKernelGGL(probe_stream_kernel<4>, grid, block, 0, st, s, nc, d, nd, sink); break;
+        default: hipLaunchKernelGGL(probe_stream_kernel<8>, grid, block, 0, st, s, nc, d, nd, sink); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_probe_mfma(int waves_per_simd, int n_blocks, int iters, float one, const uint16_t* ops, float* sink,
                              hipStream_t st) {
     if (waves_per_simd == 1)
