@@ -864,6 +864,9 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     a.n_tok = B;
     a.n_q = 1;
     a.n_split = ns;
+    // the fp32 form streams one contiguous region of rows_per_split keys per
+    // split; the bf16 / FP8 split kernel deals the keys to the same n_split
+    // workgroups in 128-key chunks
     a.rows_per_split = decode_rows_per_split(B, n_ctx);
     a.scale_log2 = sm_scale * kLog2eF;
     a.logits = w.logits;
