@@ -66,6 +66,13 @@ def causal_pairs(wl) -> int:
     return wl.B * (n * p0 + n * (n + 1) // 2)
 
 
+def logit_bytes(wl, h: int) -> float:
+    """Bytes per key of the decode logits between the split and score kernels:
+    fp32 for fp32 caches, else a 16-bit code per head plus the fp32 maxima of
+    each 32-key block (h/8 bytes a key)."""
+    return 4 * h if wl.kv_dtype == "f32" else 2 * h + h / 8
+
+
 def path_roofline_seconds(wl, blocks: bool = False, h_full: int = 0) -> float:
     """Lower bound on one step from the method's algorithmic work (HBM or MFMA).
     blocks: the HySparse v1 variant, whose two branches attend to min(p+1, W)
@@ -76,7 +83,8 @@ def path_roofline_seconds(wl, blocks: bool = False, h_full: int = 0) -> float:
     sb = 4 if wl.kv_dtype == "fp8" else 0
     S = wl.window + wl.k_global
     if wl.decode:
-        full = wl.B * wl.n_ctx * (2 * (wl.d * b + sb) + 2 * hf * 4 + 8) / (HBM_PEAK_GBS * 1e9)
+        # K + V read once, the logits written and read once, the score written and read once
+        full = wl.B * wl.n_ctx * (2 * (wl.d * b + sb) + 2 * logit_bytes(wl, hf) + 8) / (HBM_PEAK_GBS * 1e9)
         sparse = wl.n_sparse * wl.B * S * 2 * (wl.d * b + sb) / (HBM_PEAK_GBS * 1e9)
         return full + sparse
     peak = MFMA_PEAK_TFLOPS["f32" if wl.q_dtype == "f32" else "bf16"] * 1e12
@@ -96,8 +104,8 @@ def dominant(wl):
     if wl.decode:
         b = kv_bytes(wl.kv_dtype)
         sb = 4 if wl.kv_dtype == "fp8" else 0
-        per_key = 2 * (wl.d * b + sb) + 4 * wl.H          # K + V rows read, fp32 logits written
-        return "decode_split_attn", "hbm", wl.B * wl.n_ctx * per_key, "GB/s"
+        per_key = 2 * (wl.d * b + sb) + logit_bytes(wl, wl.H)  # K + V rows read, logits written
+        return "decode_split_attn", "hbm", int(wl.B * wl.n_ctx * per_key), "GB/s"
     return "attn_fwd", "mfma", 4 * wl.d * wl.H * causal_pairs(wl), "TFLOP/s"
 
 

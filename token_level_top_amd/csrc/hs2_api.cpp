@@ -120,7 +120,9 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     Carver c(base);
     DecodeWs w;
     const int ns = decode_splits(B, n_ctx);
-    w.logits = c.take<float>(sizeof(float) * (size_t)B * n_ctx * H);
+    // fp32 logits, or (bf16 / FP8 caches) the 16-bit codes followed by the
+    // 32-key block maxima: 2 n_ctx H bytes + 4 ceil(n_ctx / 32) H, never more
+    w.logits = c.take<float>(sizeof(float) * (size_t)B * n_ctx * H + 64 * (size_t)B * H);
     w.part = ns > 1 ? c.take<float>(sizeof(float) * (size_t)B * ns * H * (d + 2)) : nullptr;
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
     w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
@@ -869,7 +871,18 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     // workgroups in 128-key chunks
     a.rows_per_split = decode_rows_per_split(B, n_ctx);
     a.scale_log2 = sm_scale * kLog2eF;
-    a.logits = w.logits;
+    // fp32 caches keep fp32 logits; the bf16 / FP8 split kernel writes 16-bit
+    // codes and 32-key block maxima into the same region (2.125 H bytes a key)
+    uint16_t* lcode = nullptr;
+    float* lmax = nullptr;
+    if (kv_dtype == HS2_F32) {
+        a.logits = w.logits;
+    } else {
+        lcode = reinterpret_cast<uint16_t*>(w.logits);
+        lmax = reinterpret_cast<float*>(w.logits) + ((size_t)B * n_ctx * H * 2 + 15) / 16 * 4;
+        a.lcode = lcode;
+        a.lmax = lmax;
+    }
     if (ns > 1) {
         a.part = w.part;
     } else {
@@ -902,7 +915,9 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     const int64_t n_cand = n_ctx - window > 0 ? n_ctx - window : 0;
     float* sc = scores ? scores : w.scores;
     ScoreArgs sa{};
-    sa.logits = w.logits;
+    sa.logits = kv_dtype == HS2_F32 ? w.logits : nullptr;
+    sa.lcode = lcode;
+    sa.lmax = lmax;
     sa.lse2 = w.lse2;
     sa.scores = sc;
     sa.hist = w.hist;

@@ -53,6 +53,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kScoreShift = 64.0f;
 constexpr float kScoreUnshift = 5.421010862427522e-20f;  // 2^-64
 
+// Decode logit codes: c = round(kCodeScale (M - x)) in [0, 65535] for a base-2
+// logit x below its block maximum M; the logit is read back as M - c / kCodeScale.
+constexpr float kCodeScale = 2048.0f;
+constexpr float kCodeUnscale = 1.0f / 2048.0f;
+
 // Four OCP E4M3FN codes (one dword) -> four floats, exact (hardware convert).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
     auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);

@@ -22,7 +22,11 @@ struct RowsArgs {
     int rows_per_split;     // rows per workgroup (multiple of the 128-row tile)
     int n_split;            // workgroups per token
     float scale_log2;       // sm_scale * log2(e)
-    float* logits;          // contiguous + store: [B][n_ctx][H] base-2 logits
+    float* logits;          // contiguous + store (fp32 cache): [B][n_ctx][H] base-2 logits
+    // decode split kernel (bf16 / FP8 cache): the logits as 16-bit codes below
+    // the maximum of their 32-key block and head, and those maxima
+    uint16_t* lcode;        // [B][n_ctx][H]
+    float* lmax;            // [B][ceil(n_ctx / 32)][H] base 2
     float* part;            // n_split > 1: [n_tok][n_split][H*(D+2)] = m[H], l[H], O[H][D]
     void* out;              // n_split == 1: [n_tok][H][D] in the query type
     float* lse;             // n_split == 1: [n_tok][H] natural log, nullable
@@ -74,7 +78,9 @@ constexpr int kSelChunk = 8192;      // scores per workgroup in the histogram an
 // decode: score_j = sum_h exp2(logit2[j][h] - lse2[h]) for j < n_ctx; writes
 // scores [B][n_ctx] and the histogram of candidates j < n_cand.
 struct ScoreArgs {
-    const float* logits;    // [B][n_ctx][H] base 2
+    const float* logits;    // [B][n_ctx][H] base 2 (fp32 cache), or NULL:
+    const uint16_t* lcode;  // [B][n_ctx][H] codes below the block maxima
+    const float* lmax;      // [B][ceil(n_ctx / 32)][H] block maxima, base 2
     const float* lse2;      // [B][H]
     float* scores;          // [B][n_ctx]
     uint32_t* hist;         // [B][kHistBins], zeroed by the caller

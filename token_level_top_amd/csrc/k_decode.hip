@@ -6,8 +6,14 @@
 //
 // For one query token per sequence the work is a stream over the cache:
 // read each key and value row once, form the H logits of the key, keep an online
-// softmax per head, accumulate P V, and store the base-2 logits (the token score
-// needs the final LSE, which is only known once every split is done).
+// softmax per head, accumulate P V, and keep the base-2 logits for the token
+// score, which needs the final LSE (only known once every split is done).
+// The logits are kept as 16-bit codes: for each 32-key block and head the
+// block maximum M (fp32) and per key c = round(2048 (M - x)), clamped to
+// 65535; the score kernel forms 2^(M - c/2048 - LSE), within a factor
+// 2^(+-1/4096) (relative 1.7e-4) of the exact term, or below 2^-32 of the
+// block's largest term where clamped. That is 2.125 H bytes a key instead of
+// 4 H, written once and read once.
 //
 // Layout of the work: the n_split workgroups of a sequence deal its keys out
 // in 128-key chunks, split s taking chunks s, s + n_split, s + 2 n_split, ...,
@@ -23,8 +29,9 @@
 //    blocks n+1 and n+2 are in flight while block n is computed.
 //  * O^T = V^T P^T: V rows go through a wave-private LDS buffer (the MFMA needs
 //    8 keys of one column per lane), FP8 codes widened to bf16 exactly on the way.
-//  * Logits are staged in LDS and written one block later as 16-byte stores, so
-//    the stores never sit in the same wait as the loads the next block needs.
+//  * Logit codes are staged in LDS and written one block later as 16-byte
+//    stores (the block maxima beside them), so the stores never sit in the same
+//    wait as the loads the next block needs.
 #include <type_traits>
 
 #include "hs2_device.h"
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     using KPiece = typename std::conditional<KV == DT_FP8, u32x2, u32x4>::type;
 
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][kDecBlock * VLD];
-    __shared__ __attribute__((aligned(16))) float lg_lds[4][kDecBlock * H];
+    __shared__ __attribute__((aligned(16))) uint16_t lg_lds[4][kDecBlock * H];
     __shared__ float vs_lds[4][kDecBlock];
     __shared__ float ks_lds[4][kDecBlock];
 
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + kv_base * RB;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + kv_base * RB;
     uint16_t* vl = v_lds[w];
-    float* lgl = lg_lds[w];
+    uint16_t* lgl = lg_lds[w];
 
     // query fragment (B operand): head hl, k-step c, slots d = 32c + 8g .. +7
     u32x4 qf[NC];
@@ -166,19 +173,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
             }
         }
     };
-    // logits of the previous block: staged [32][H] in LDS, written as 16-B
-    // streaming stores through a descriptor ending at the block's last row
-    // inside the sequence (before the first block its range is empty). Every load and store of the
-    // loop is issued unconditionally, so the compiler's waits on the loads of
-    // the next block count exactly the operations issued after them.
+    // logit codes of the previous block: staged [32][H] in LDS, written as
+    // 16-B streaming stores through a descriptor ending at the block's last row
+    // inside the sequence (before the first block its range is empty), and the
+    // block's H maxima (every lane stores its head's; lanes of one head store
+    // the same value, heads >= H fall outside the range). Every load and store
+    // of the loop is issued unconditionally, so the compiler's waits on the
+    // loads of the next block count exactly the operations issued after them.
     int64_t pend_j = r_end;
+    float pend_mx = 0.f;
+    const int64_t n_blk = (a.n_ctx + kDecBlock - 1) / kDecBlock;  // code blocks per sequence
     auto flush_logits = [&]() {
-        const auto rl = raw_buffer(a.logits + (kv_base + (size_t)pend_j) * H,
-                                   (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * 4));
+        const bool any = pend_j < r_end;
+        const auto rl = raw_buffer(a.lcode + (kv_base + (size_t)pend_j) * H,
+                                   (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * 2));
+        constexpr int NP = kDecBlock * H * 2 / 16;  // 16-byte pieces of a block's codes
 #pragma unroll
-        for (int p = lane; p < kDecBlock * H / 4; p += 64)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(lgl + 4 * p)),
-                                                   rl, 16 * p, 0, 2);
+        for (int p = lane; p < NP; p += 64)
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lgl + 8 * p), rl, 16 * p, 0, 2);
+        const auto rm = raw_buffer(a.lmax + ((size_t)seq * n_blk + (size_t)(any ? pend_j / kDecBlock : 0)) * H,
+                                   any ? (uint32_t)(H * 4) : 0u);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pend_mx), rm, 4 * hl, 0, 2);
     };
 
     // S^T for the two 16-key groups of a block
@@ -217,11 +232,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
                 if (tail && j + key >= r_end) v = -INFINITY;
                 x[grp][i] = v;
                 mx = fmaxf(mx, v);
-                if (hl < H) lgl[key * H + hl] = v;
             }
         pend_j = j;
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, xor32(mx));
+        // codes below the block maximum of head hl (a masked key, or a block
+        // with every key masked, gives NaN or +inf, and fminf then the clamp)
+        pend_mx = mx;
+        if (hl < H) {
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lgl[(16 * grp + 4 * g + i) * H + hl] =
+                        (uint16_t)(uint32_t)fminf((mx - x[grp][i]) * kCodeScale + 0.5f, 65535.f);
+        }
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;

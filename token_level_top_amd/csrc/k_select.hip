@@ -137,14 +137,75 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
     flush_hist(hist, a.hist + (size_t)b * kHistBins);
 }
 
+// The same from the 16-bit logit codes of the bf16 / FP8 split kernel: term h
+// of key j is 2^(M_h - c_hj / 2048 - LSE_h) with M_h the maximum of head h over
+// the 32-key block of j. A thread reads its key's H codes (2H contiguous bytes)
+// and the block's maxima (shared by the 32 threads of the block).
+template <int H>
+__global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArgs a) {
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ float l2[H];
+    const int b = blockIdx.y;
+    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0;
+    if (threadIdx.x < H) l2[threadIdx.x] = a.lse2[(size_t)b * H + threadIdx.x] - kScoreShift;
+    __syncthreads();
+    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
+    const int64_t j1 = min<int64_t>(j0 + kSelChunk, a.n_ctx);
+    const int64_t n_blk = (a.n_ctx + 31) / 32;
+    const uint16_t* lc = a.lcode + (size_t)b * (size_t)a.n_ctx * H;
+    const float* lm = a.lmax + (size_t)b * (size_t)n_blk * H;
+    constexpr int NW = H / 2;  // 32-bit words of codes per key
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) {
+        uint32_t cw[NW];
+        if constexpr (H == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(lc + (size_t)j * H);
+            cw[0] = v[0];
+            cw[1] = v[1];
+        } else {
+#pragma unroll
+            for (int c = 0; c < NW / 4; ++c) {
+                const u32x4 v = reinterpret_cast<const u32x4*>(lc + (size_t)j * H)[c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cw[4 * c + i] = v[i];
+            }
+        }
+        const f32x4* mrow = reinterpret_cast<const f32x4*>(lm + (size_t)(j >> 5) * H);
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < H / 4; ++c) {
+            const f32x4 m = mrow[c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * c + i;
+                const uint32_t code = (cw[h >> 1] >> (16 * (h & 1))) & 0xffffu;
+                s += fast_exp2(fmaf((float)code, -kCodeUnscale, m[i] - l2[h]));
+            }
+        }
+        s *= kScoreUnshift;  // exact power-of-two rescale to the true score
+        a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
+        if (j < a.n_cand) atomicAdd(&hist[score_bin(s)], 1u);
+    }
+    __syncthreads();
+    flush_hist(hist, a.hist + (size_t)b * kHistBins);
+}
+
 hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st) {
     dim3 grid((unsigned)((a.n_ctx + kSelChunk - 1) / kSelChunk), (unsigned)B);
-    if (a.H == 4)
-        hipLaunchKernelGGL(decode_score_kernel<4>, grid, dim3(kSelThreads), 0, st, a);
-    else if (a.H == 8)
-        hipLaunchKernelGGL(decode_score_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL(decode_score_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
+    if (a.logits) {
+        if (a.H == 4)
+            hipLaunchKernelGGL(decode_score_kernel<4>, grid, dim3(kSelThreads), 0, st, a);
+        else if (a.H == 8)
+            hipLaunchKernelGGL(decode_score_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL(decode_score_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
+    } else {
+        if (a.H == 4)
+            hipLaunchKernelGGL(decode_score_code_kernel<4>, grid, dim3(kSelThreads), 0, st, a);
+        else if (a.H == 8)
+            hipLaunchKernelGGL(decode_score_code_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL(decode_score_code_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 
