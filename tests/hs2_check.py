@@ -55,6 +55,40 @@ def rows_close(got, ref, rtol: float, what: str = "out") -> float:
     return worst
 
 
+# Decode token scores. The fp32-cache path keeps fp32 logits: relative 1e-5 of
+# the row maximum. The bf16 / FP8 split kernel hands the logits to the score
+# kernel as 16-bit codes c = round(2048 (M - x)) below the maximum M of the
+# key's 32-key block and head (x, M base-2 logits), so every term
+# 2^(x - LSE) is read back within a factor 2^(+-1/4096), relative 1.7e-4, and a
+# term clamped at c = 65535 is below 2^-32 of its block's largest term.
+# Bound per score: 2.5e-4 of itself (the code rounding plus fp32 arithmetic)
+# plus 1e-8 of the row maximum (clamped terms).
+SCORE_CODE_REL = 2.5e-4
+SCORE_CODE_ABS = 1e-8
+
+
+def decode_scores_close(got, ref, kv_dtype: str, what: str = "score vector") -> float:
+    """Checks a decode score vector [B][n_ctx] against the oracle's; returns
+    the worst error as a fraction of the allowed error."""
+    g = to_np(got).astype(np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    rowmax = np.maximum(r.max(axis=-1, keepdims=True), 1e-300)
+    if kv_dtype == "f32":
+        allow = 1e-5 * rowmax + 0 * r
+    else:
+        allow = SCORE_CODE_REL * r + SCORE_CODE_ABS * rowmax
+    err = np.abs(g - r)
+    frac = err / allow
+    worst = float(frac.max()) if frac.size else 0.0
+    rel = float((err / np.maximum(r, 1e-300)).max()) if r.size else 0.0
+    if worst > 1.0:
+        i = np.unravel_index(np.argmax(frac), frac.shape)
+        raise AssertionError(f"{what}: worst entry {i}: got {g[i]:.9e} ref {r[i]:.9e} ({worst:.2f} of the bound)")
+    _say(f"{what}: {g.size} scores, worst error {worst:.3f} of the bound (largest relative error {rel:.3e})")
+    return worst
+
+
 def lse_close(got, ref, rtol: float, what: str = "lse") -> float:
     """|dLSE| <= rtol (absolute). Entries that are -inf on both sides (empty
     rows) agree. Returns the worst |dLSE|."""
