@@ -29,6 +29,8 @@
 //     back to an exact multi-pass radix select over the whole row.
 // The 64-bit rank key (score bits, complemented position) makes every key
 // distinct, so the result is unique.
+#include <type_traits>
+
 #include "hs2_device.h"
 #include "hs2_internal.h"
 #include "hs2_wave_select.h"
@@ -139,51 +141,62 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
 
 // The same from the 16-bit logit codes of the bf16 / FP8 split kernel: term h
 // of key j is 2^(M_h - c_hj / 2048 - LSE_h) with M_h the maximum of head h over
-// the 32-key block of j. A thread reads its key's H codes (2H contiguous bytes)
-// and the block's maxima (shared by the 32 threads of the block).
+// the 32-key block of j. The chunk's block maxima, less the LSE, are staged in
+// LDS first; then every thread takes keys j0 + 256 i + t, loading the 2H code
+// bytes of kBatch keys before it forms their scores (consecutive threads read
+// consecutive keys).
 template <int H>
 __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArgs a) {
+    constexpr int kBatch = 8;
+    constexpr int NBLK = kSelChunk / 32;  // 32-key blocks of a chunk
     __shared__ uint32_t hist[kHistBins];
-    __shared__ float l2[H];
-    const int b = blockIdx.y;
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0;
-    if (threadIdx.x < H) l2[threadIdx.x] = a.lse2[(size_t)b * H + threadIdx.x] - kScoreShift;
-    __syncthreads();
+    __shared__ __attribute__((aligned(16))) float ml[NBLK * H];  // M_h - LSE_h + kScoreShift per block
+    const int b = blockIdx.y, tid = threadIdx.x;
+    for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
     const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
     const int64_t j1 = min<int64_t>(j0 + kSelChunk, a.n_ctx);
     const int64_t n_blk = (a.n_ctx + 31) / 32;
+    const int nb = (int)((j1 - j0 + 31) / 32);
+    {
+        const float* lm = a.lmax + ((size_t)b * (size_t)n_blk + (size_t)(j0 / 32)) * H;
+        const float* l2 = a.lse2 + (size_t)b * H;
+        for (int e = tid; e < nb * H / 4; e += kSelThreads) {
+            const f32x4 m = reinterpret_cast<const f32x4*>(lm)[e];
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = m[i] - (l2[(4 * e + i) % H] - kScoreShift);
+            reinterpret_cast<f32x4*>(ml)[e] = v;
+        }
+    }
+    __syncthreads();
     const uint16_t* lc = a.lcode + (size_t)b * (size_t)a.n_ctx * H;
-    const float* lm = a.lmax + (size_t)b * (size_t)n_blk * H;
-    constexpr int NW = H / 2;  // 32-bit words of codes per key
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads) {
-        uint32_t cw[NW];
-        if constexpr (H == 4) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(lc + (size_t)j * H);
-            cw[0] = v[0];
-            cw[1] = v[1];
-        } else {
+    using Piece = typename std::conditional<H == 4, u32x2, u32x4>::type;
+    constexpr int NPC = H == 4 ? 1 : H / 8;  // pieces per key
+    for (int64_t jb = j0; jb < j1; jb += (int64_t)kBatch * kSelThreads) {
+        Piece cw[kBatch][NPC];
 #pragma unroll
-            for (int c = 0; c < NW / 4; ++c) {
-                const u32x4 v = reinterpret_cast<const u32x4*>(lc + (size_t)j * H)[c];
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t j = min<int64_t>(jb + (int64_t)i * kSelThreads + tid, j1 - 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) cw[4 * c + i] = v[i];
-            }
+            for (int c = 0; c < NPC; ++c) cw[i][c] = reinterpret_cast<const Piece*>(lc + (size_t)j * H)[c];
         }
-        const f32x4* mrow = reinterpret_cast<const f32x4*>(lm + (size_t)(j >> 5) * H);
-        float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < H / 4; ++c) {
-            const f32x4 m = mrow[c];
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t j = jb + (int64_t)i * kSelThreads + tid;
+            if (j >= j1) break;
+            const float* mrow = ml + (int)((j - j0) >> 5) * H;
+            float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 4 * c + i;
-                const uint32_t code = (cw[h >> 1] >> (16 * (h & 1))) & 0xffffu;
-                s += fast_exp2(fmaf((float)code, -kCodeUnscale, m[i] - l2[h]));
+            for (int h = 0; h < H; ++h) {
+                constexpr int WPP = sizeof(Piece) / 4;  // 32-bit words per piece
+                const uint32_t word = cw[i][(h / 2) / WPP][(h / 2) % WPP];
+                const uint32_t code = (word >> (16 * (h & 1))) & 0xffffu;
+                s += fast_exp2(fmaf((float)code, -kCodeUnscale, mrow[h]));
             }
+            s *= kScoreUnshift;  // exact power-of-two rescale to the true score
+            a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
+            if (j < a.n_cand) atomicAdd(&hist[score_bin(s)], 1u);
         }
-        s *= kScoreUnshift;  // exact power-of-two rescale to the true score
-        a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
-        if (j < a.n_cand) atomicAdd(&hist[score_bin(s)], 1u);
     }
     __syncthreads();
     flush_hist(hist, a.hist + (size_t)b * kHistBins);
