@@ -216,6 +216,12 @@ int hs2_sparse_attn_noalloc(const void* q, int q_dtype, int n_layers, const void
  *   scores   [B][n_ctx] fp32           may be NULL; else score_j for every j
  *   workspace >= hs2_workspace_size(HS2_OP_DECODE_STEP, B, 1, n_ctx, H, d,
  *                window, k_global, kv_dtype) bytes
+ * With a bf16 or FP8 cache the logits pass from the attention kernel to the
+ * score kernel as 16-bit codes below the maximum of their 32-key block and
+ * head (resolution 2^-10 in the base-2 exponent, clamped 64 below it): every
+ * term of a score is within a factor 2^(+-1/2048) (relative 3.4e-4) of its
+ * exact value, or below 2^-64 of its block's largest term; the selection is
+ * made on these scores. An fp32 cache keeps fp32 logits.
  */
 int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n_sparse,
                     const void* k, const void* v, const float* k_scale, const float* v_scale,

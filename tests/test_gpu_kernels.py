@@ -175,6 +175,48 @@ def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
         lse_close(r["lse_sparse"][l], s["lse"], tol)
 
 
+@pytest.mark.parametrize("B,n_ctx", [(2, 5003), (1, 20000)])
+def test_decode_peaked_attention_logit_codes_clamp(hs2, orc, B, n_ctx):
+    """Softmax scale 12/sqrt(d) on N(0,1) bf16 inputs: base-2 logits with a
+    spread of about 17, so a 32-key block of one head spans more than 64 in the
+    exponent and the decode kernel's 16-bit logit codes clamp. The score vector
+    stays within its bound (relative 4e-4, clamped terms below 2^-64 of the
+    block maximum) and the index rows within the swap rule, although the
+    K-th score is many orders of magnitude below the largest."""
+    wl = workload(3).with_(B=B, n_q=1, q_pos0=n_ctx - 1, n_ctx=n_ctx, n_sparse=1, needles="decode",
+                           n_needles=8, decode=True)
+    x = make_inputs(wl)
+    sm = 12.0 / math.sqrt(wl.d)
+    # the case must clamp: some (block, head) spans more than 64 base-2 units
+    qf = x.q[:, 0].to(torch.float64)                      # [B][H][d]
+    kf = x.k.to(torch.float64)                            # [B][n_ctx][d]
+    lg = torch.einsum("bhd,bjd->bjh", qf, kf) * (sm * math.log2(math.e))
+    nb = n_ctx // 32
+    blk = lg[:, :nb * 32].reshape(B, nb, 32, wl.H)
+    span = (blk.max(dim=2).values - blk.min(dim=2).values).max().item()
+    say(f"peaked decode B={B} n_ctx={n_ctx}: widest block span {span:.1f} (codes clamp beyond 64)")
+    assert span > 64.0, span
+    r = hs2.decode_step(dev(x.q[:, 0]).contiguous(), dev(x.q_sparse[:, :, 0]).contiguous(), dev(x.k), dev(x.v),
+                        dev(x.k_scale), dev(x.v_scale), window=wl.window, k_global=wl.k_global,
+                        sm_scale=sm, want_scores=True)
+    torch.cuda.synchronize()
+    rows = list(range(B))
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, sm,
+                          rows, want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    rows_close(r["out_full"], ref["out"], tol, "peaked decode out")
+    lse_close(r["lse_full"], ref["lse"], tol)
+    decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype, "peaked score vector")
+    sc = np.asarray(ref["scores"], dtype=np.float64)
+    say(f"  K-th score / largest score: {float((np.asarray(ref['kth']) / sc.max(axis=1)).min()):.3e}")
+    ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
+    gidx = to_np(r["indices"]).astype(np.int32)
+    s = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, sm, rows)
+    rows_close(r["out_sparse"][0], s["out"], tol, "peaked decode sparse out")
+    lse_close(r["lse_sparse"][0], s["lse"], tol)
+
+
 # ----------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("cfg,n_q,q_pos0,n_ctx,kg", [

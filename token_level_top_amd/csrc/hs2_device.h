@@ -54,9 +54,10 @@ constexpr float kScoreShift = 64.0f;
 constexpr float kScoreUnshift = 5.421010862427522e-20f;  // 2^-64
 
 // Decode logit codes: c = round(kCodeScale (M - x)) in [0, 65535] for a base-2
-// logit x below its block maximum M; the logit is read back as M - c / kCodeScale.
-constexpr float kCodeScale = 2048.0f;
-constexpr float kCodeUnscale = 1.0f / 2048.0f;
+// logit x below its block maximum M; the logit is read back as M - c / kCodeScale
+// (resolution 2^-10, range 64).
+constexpr float kCodeScale = 1024.0f;
+constexpr float kCodeUnscale = 1.0f / 1024.0f;
 
 // Four OCP E4M3FN codes (one dword) -> four floats, exact (hardware convert).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {

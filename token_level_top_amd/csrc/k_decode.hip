@@ -9,10 +9,12 @@
 // softmax per head, accumulate P V, and keep the base-2 logits for the token
 // score, which needs the final LSE (only known once every split is done).
 // The logits are kept as 16-bit codes: for each 32-key block and head the
-// block maximum M (fp32) and per key c = round(2048 (M - x)), clamped to
-// 65535; the score kernel forms 2^(M - c/2048 - LSE), within a factor
-// 2^(+-1/4096) (relative 1.7e-4) of the exact term, or below 2^-32 of the
-// block's largest term where clamped. That is 2.125 H bytes a key instead of
+// block maximum M (fp32) and per key c = round(1024 (M - x)), clamped to
+// 65535 (64 below M); the score kernel forms 2^(M - c/1024 - LSE), within a
+// factor 2^(+-1/2048) (relative 3.4e-4) of the exact term, or below 2^-64 of
+// the block's largest term where clamped. The wide range keeps a clamped term
+// negligible against any score fp32 can rank, also when a block holds a term
+// many orders of magnitude above its neighbours (peaked attention). That is 2.125 H bytes a key instead of
 // 4 H, written once and read once.
 //
 // Layout of the work: the n_split workgroups of a sequence deal its keys out

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
 }
 
 // The same from the 16-bit logit codes of the bf16 / FP8 split kernel: term h
-// of key j is 2^(M_h - c_hj / 2048 - LSE_h) with M_h the maximum of head h over
+// of key j is 2^(M_h - c_hj / 1024 - LSE_h) with M_h the maximum of head h over
 // the 32-key block of j. The chunk's block maxima, less the LSE, are staged in
 // LDS first; then every thread takes keys j0 + 256 i + t, loading the 2H code
 // bytes of kBatch keys before it forms their scores (consecutive threads read
