@@ -39,7 +39,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernel classes of the library's timing hook (include/hs2.h)
 KC = {"decode_split_attn": 0, "combine": 1, "decode_score": 2, "select_hist": 3, "select_collect": 4,
       "select_final": 5, "sparse_attn": 6, "prep_kv": 7, "attn_fwd": 8, "score_stream": 9,
-      "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14}
+      "window_pass": 10, "fill": 11, "kv_project": 12, "block_score": 13, "block_select": 14,
+      "decode_rescore": 15}
 # kernel source file each priced kernel lives in (for the traffic record's freshness check)
 KSRC = {"decode_split_attn": "k_decode.hip", "attn_fwd": "k_prefill.hip", "score_stream": "k_prefill.hip",
         "kv_project": "k_project.hip"}
@@ -67,10 +68,11 @@ def causal_pairs(wl) -> int:
 
 
 def logit_bytes(wl, h: int) -> float:
-    """Bytes per key of the decode logits between the split and score kernels:
-    fp32 for fp32 caches, else a 16-bit code per head plus the fp32 maxima of
-    each 32-key block (h/8 bytes a key)."""
-    return 4 * h if wl.kv_dtype == "f32" else 2 * h + h / 8
+    """Bytes per key of the decode logits between the split and score kernels
+    in the timed step (no score vector requested): fp32 for fp32 caches, else
+    an 8-bit code per head plus the fp32 maxima of each 32-key block (h/8
+    bytes a key)."""
+    return 4 * h if wl.kv_dtype == "f32" else h + h / 8
 
 
 def path_roofline_seconds(wl, blocks: bool = False, h_full: int = 0) -> float:
@@ -677,7 +679,7 @@ def main():
     if args.graph:
         res["eager_ms_per_step"] = round(ms_eager, 4)
     if args.breakdown:
-        L.hs2_timing_enable(0xFFFF if blocks else 0xFFF)
+        L.hs2_timing_enable(0xFFFF if blocks else 0xFFF | 1 << KC["decode_rescore"])
         for _ in range(3):
             step()
         torch.cuda.synchronize()

@@ -221,7 +221,13 @@ int hs2_sparse_attn_noalloc(const void* q, int q_dtype, int n_layers, const void
  * head (resolution 2^-10 in the base-2 exponent, clamped 64 below it): every
  * term of a score is within a factor 2^(+-1/2048) (relative 3.4e-4) of its
  * exact value, or below 2^-64 of its block's largest term; the selection is
- * made on these scores. An fp32 cache keeps fp32 logits.
+ * made on these scores. Without `scores` the logits are kept as 8-bit codes
+ * (resolution 2^-4, clamped 16 below the block maximum): from them every score
+ * is bounded within a factor 2^(+-1/32), every key whose upper bound reaches
+ * the k_global-th largest lower bound is kept as a candidate, and the
+ * candidates' exact scores are recomputed from their key rows (fp32 logits)
+ * for the selection; the indices then follow the exact scores. An fp32 cache
+ * keeps fp32 logits.
  */
 int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n_sparse,
                     const void* k, const void* v, const float* k_scale, const float* v_scale,
@@ -429,7 +435,7 @@ int hs2_test_reverse_grid(int on);
  *   bit 8 prefill pass 1 (attention)   bit 9 prefill pass 2 (score stream)
  *   bit 10 window pass (window sharing) bit 11 buffer fills
  *   bit 12 KV Bridging projections     bit 13 block scores (block mode)
- *   bit 14 block choice                bit 15 (unused)
+ *   bit 14 block choice                bit 15 decode candidate rescore
  * (the light indexer's scoring and selection report as bit 9, its key
  * widening as bit 7)
  * hs2_timing_enable(mask): from now on every launch of a class in `mask` is

@@ -69,6 +69,24 @@ def test_decode_full_size(hs2, orc, cfg):
         s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
         rows_close(r["out_sparse"][l], s["out"], tol, f"decode sparse layer {l} out")
         lse_close(r["lse_sparse"][l], s["lse"], tol, f"decode sparse layer {l} lse")
+    # the step as timed (no score vector: 8-bit logit codes, bounds, exact
+    # rescoring of the candidates), against the same oracle rows
+    say("decode step without the score vector")
+    r8 = hs2.decode_step(g(x.q[:, 0]), g(x.q_sparse[:, :, 0]), g(x.k), g(x.v), g(x.k_scale), g(x.v_scale),
+                         window=wl.window, k_global=wl.k_global, sm_scale=x.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(r8["out_full"], r["out_full"]) and torch.equal(r8["lse_full"], r["lse_full"])
+    ov, mn, sw = check_index_rows(r8["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  8-bit codes: overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
+    same = to_np(r8["indices"]) == gidx
+    if not same.all():
+        gidx8 = to_np(r8["indices"]).astype(np.int32)
+        for l in range(wl.n_sparse):
+            s = orc.sparse(x.q_sparse[l].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx8, x.sm_scale, rows)
+            rows_close(r8["out_sparse"][l], s["out"], tol, f"decode (8-bit codes) sparse layer {l} out")
+    else:
+        for l in range(wl.n_sparse):
+            assert torch.equal(r8["out_sparse"][l], r["out_sparse"][l])
 
 
 @pytest.mark.timeout(900)

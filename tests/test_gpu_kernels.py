@@ -148,14 +148,18 @@ def test_sparse_matches_oracle(hs2, orc, cfg, n_q, n_ctx, n_sel, fill):
     (3, 2, 700, 1),         # fewer candidates than k_global
     (3, 2, 3000, 9),        # nine sparse layers, one launch and combine each
 ])
-def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
+@pytest.mark.parametrize("want_scores", [True, False])
+def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse, want_scores):
+    """want_scores: the score vector is returned (bf16 / FP8: 16-bit logit
+    codes); without it the step runs as timed (8-bit codes, score bounds and
+    exact rescoring of the candidates)."""
     wl = workload(cfg).with_(B=B, n_q=1, q_pos0=n_ctx - 1, n_ctx=n_ctx, n_sparse=n_sparse, needles="decode",
                              n_needles=8 if n_ctx > 2000 else 0, decode=True)
     x = make_inputs(wl)
-    say("decode", wl.name, B, n_ctx)
+    say("decode", wl.name, B, n_ctx, "with" if want_scores else "without", "the score vector")
     r = hs2.decode_step(dev(x.q[:, 0]).contiguous(), dev(x.q_sparse[:, :, 0]).contiguous(), dev(x.k), dev(x.v),
                         dev(x.k_scale), dev(x.v_scale), window=wl.window, k_global=wl.k_global,
-                        sm_scale=x.sm_scale, want_scores=True)
+                        sm_scale=x.sm_scale, want_scores=want_scores)
     torch.cuda.synchronize()
     rows = list(range(B))
     ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
@@ -164,7 +168,8 @@ def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
     rows_close(r["out_full"], ref["out"], tol, "decode out")
     lse_close(r["lse_full"], ref["lse"], tol)
     # token scores: fp32 logits (fp32 cache) or the 16-bit logit codes
-    decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype)
+    if want_scores:
+        decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype)
     ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
     say(f"  overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
     # sparse layers, judged on the GPU's own index set
@@ -175,8 +180,9 @@ def test_decode_step_matches_oracle(hs2, orc, cfg, B, n_ctx, n_sparse):
         lse_close(r["lse_sparse"][l], s["lse"], tol)
 
 
+@pytest.mark.parametrize("want_scores", [True, False])
 @pytest.mark.parametrize("B,n_ctx", [(2, 5003), (1, 20000)])
-def test_decode_peaked_attention_logit_codes_clamp(hs2, orc, B, n_ctx):
+def test_decode_peaked_attention_logit_codes_clamp(hs2, orc, B, n_ctx, want_scores):
     """Softmax scale 12/sqrt(d) on N(0,1) bf16 inputs: base-2 logits with a
     spread of about 17, so a 32-key block of one head spans more than 64 in the
     exponent and the decode kernel's 16-bit logit codes clamp. The score vector
@@ -198,7 +204,7 @@ def test_decode_peaked_attention_logit_codes_clamp(hs2, orc, B, n_ctx):
     assert span > 64.0, span
     r = hs2.decode_step(dev(x.q[:, 0]).contiguous(), dev(x.q_sparse[:, :, 0]).contiguous(), dev(x.k), dev(x.v),
                         dev(x.k_scale), dev(x.v_scale), window=wl.window, k_global=wl.k_global,
-                        sm_scale=sm, want_scores=True)
+                        sm_scale=sm, want_scores=want_scores)
     torch.cuda.synchronize()
     rows = list(range(B))
     ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, sm,
@@ -206,7 +212,8 @@ def test_decode_peaked_attention_logit_codes_clamp(hs2, orc, B, n_ctx):
     tol = RTOL[wl.kv_dtype]
     rows_close(r["out_full"], ref["out"], tol, "peaked decode out")
     lse_close(r["lse_full"], ref["lse"], tol)
-    decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype, "peaked score vector")
+    if want_scores:
+        decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype, "peaked score vector")
     sc = np.asarray(ref["scores"], dtype=np.float64)
     say(f"  K-th score / largest score: {float((np.asarray(ref['kth']) / sc.max(axis=1)).min()):.3e}")
     ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
@@ -261,12 +268,15 @@ def test_prefill_and_decode_are_deterministic(hs2):
     wd = workload(3).with_(B=4, n_ctx=50000, q_pos0=49999, n_needles=4, n_sparse=2)
     xd = make_inputs(wd)
     say("determinism decode", wd.name, wd.B, wd.n_ctx)
-    runs = [hs2.decode_step(dev(xd.q[:, 0]), dev(xd.q_sparse[:, :, 0]), dev(xd.k), dev(xd.v), window=128,
-                            k_global=1024, sm_scale=xd.sm_scale, want_scores=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    for r in runs[1:]:
-        for key in ("indices", "scores", "out_full", "lse_full", "out_sparse", "lse_sparse"):
-            assert torch.equal(r[key], runs[0][key]), key
+    for ws in (True, False):
+        runs = [hs2.decode_step(dev(xd.q[:, 0]), dev(xd.q_sparse[:, :, 0]), dev(xd.k), dev(xd.v), window=128,
+                                k_global=1024, sm_scale=xd.sm_scale, want_scores=ws) for _ in range(3)]
+        torch.cuda.synchronize()
+        for r in runs[1:]:
+            for key in ("indices", "scores", "out_full", "lse_full", "out_sparse", "lse_sparse"):
+                if key == "scores" and not ws:
+                    continue
+                assert torch.equal(r[key], runs[0][key]), key
 
 
 @pytest.mark.parametrize("cfg", [2, 4])

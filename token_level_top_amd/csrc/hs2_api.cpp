@@ -263,7 +263,7 @@ WinWs win_ws(void* base, int B, int64_t n_q, int64_t q_pos0, int H, int d, int w
 enum KClass {
     KC_DECODE_ROWS = 0, KC_COMBINE = 1, KC_SCORE = 2, KC_SEL_HIST = 3, KC_SEL_COLLECT = 4, KC_SEL_FINAL = 5,
     KC_SPARSE = 6, KC_PREP = 7, KC_FWD = 8, KC_STREAM = 9, KC_WINDOW = 10, KC_FILL = 11,
-    KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14
+    KC_PROJECT = 12, KC_BLOCK_SCORE = 13, KC_BLOCK_SELECT = 14, KC_RESCORE = 15
 };
 struct TimedPair {
     int cls;
@@ -871,15 +871,19 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     // workgroups in 128-key chunks
     a.rows_per_split = decode_rows_per_split(B, n_ctx);
     a.scale_log2 = sm_scale * kLog2eF;
-    // fp32 caches keep fp32 logits; the bf16 / FP8 split kernel writes 16-bit
-    // codes and 32-key block maxima into the same region (2.125 H bytes a key)
-    uint16_t* lcode = nullptr;
+    // fp32 caches keep fp32 logits. The bf16 / FP8 split kernel writes codes
+    // and 32-key block maxima into the same region: 16-bit codes when the
+    // caller asks for the score vector (every score within relative 3.4e-4),
+    // else 8-bit codes (H + H/8 bytes a key), from which the selection bounds
+    // every score and recomputes the exact scores of its candidates.
+    const int code_bytes = scores ? 2 : 1;
+    void* lcode = nullptr;
     float* lmax = nullptr;
     if (kv_dtype == HS2_F32) {
         a.logits = w.logits;
     } else {
-        lcode = reinterpret_cast<uint16_t*>(w.logits);
-        lmax = reinterpret_cast<float*>(w.logits) + ((size_t)B * n_ctx * H * 2 + 15) / 16 * 4;
+        lcode = w.logits;
+        lmax = reinterpret_cast<float*>(w.logits) + ((size_t)B * n_ctx * H * code_bytes + 15) / 16 * 4;
         a.lcode = lcode;
         a.lmax = lmax;
     }
@@ -893,7 +897,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     if (kv_dtype == HS2_F32)
         HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_rows_attn(a, H, d, kv_dtype, false, true, s)));
     else
-        HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_decode_split(a, H, d, kv_dtype, s)));
+        HS2_TRY(TIMED(KC_DECODE_ROWS, s, launch_decode_split(a, H, d, kv_dtype, code_bytes, s)));
     // the score histogram and the candidate counters (adjacent in the
     // workspace) start at zero: cleared by the combine kernel, else a fill
     const int64_t n_zero = (w.thr + 2 * B) - w.hist;
@@ -918,6 +922,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     sa.logits = kv_dtype == HS2_F32 ? w.logits : nullptr;
     sa.lcode = lcode;
     sa.lmax = lmax;
+    sa.code_bytes = code_bytes;
     sa.lse2 = w.lse2;
     sa.scores = sc;
     sa.hist = w.hist;
@@ -941,7 +946,25 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     se.out = indices;
     se.out_stride = n_sel;
     se.out_offset = window;
-    if (k_global > 0 && n_cand > 0) HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
+    const bool rescore = kv_dtype != HS2_F32 && code_bytes == 1;
+    se.exact_kth = rescore ? 1 : 0;
+    if (k_global > 0 && n_cand > 0) {
+        HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
+        if (rescore) {
+            RescoreArgs ra{};
+            ra.q = q_full;
+            ra.k = k;
+            ra.ks = k_scale;
+            ra.lse2 = w.lse2;
+            ra.thr = w.thr;
+            ra.cand = w.cand;
+            ra.scores = sc;
+            ra.n_ctx = n_ctx;
+            ra.n_cand = n_cand;
+            ra.scale_log2 = sm_scale * kLog2eF;
+            HS2_TRY(TIMED(KC_RESCORE, s, launch_decode_rescore(ra, B, H, d, kv_dtype, s)));
+        }
+    }
     HS2_TRY(TIMED(KC_SEL_FINAL, s, launch_select_final_w(se, window, n_ctx - 1, s)));
     // 4. sparse layers reuse the indices and the cache
     if (n_sparse > 0)

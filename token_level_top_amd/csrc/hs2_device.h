@@ -58,6 +58,9 @@ constexpr float kScoreUnshift = 5.421010862427522e-20f;  // 2^-64
 // (resolution 2^-10, range 64).
 constexpr float kCodeScale = 1024.0f;
 constexpr float kCodeUnscale = 1.0f / 1024.0f;
+// 8-bit codes: c = round(16 (M - x)) in [0, 255] (resolution 1/16, range 16)
+constexpr float kCode8Scale = 16.0f;
+constexpr float kCode8Unscale = 1.0f / 16.0f;
 
 // Four OCP E4M3FN codes (one dword) -> four floats, exact (hardware convert).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {

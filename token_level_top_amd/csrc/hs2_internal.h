@@ -25,7 +25,7 @@ struct RowsArgs {
     float* logits;          // contiguous + store (fp32 cache): [B][n_ctx][H] base-2 logits
     // decode split kernel (bf16 / FP8 cache): the logits as 16-bit codes below
     // the maximum of their 32-key block and head, and those maxima
-    uint16_t* lcode;        // [B][n_ctx][H]
+    void* lcode;            // [B][n_ctx][H] codes of code_bytes each (16- or 8-bit)
     float* lmax;            // [B][ceil(n_ctx / 32)][H] base 2
     float* part;            // n_split > 1: [n_tok][n_split][H*(D+2)] = m[H], l[H], O[H][D]
     void* out;              // n_split == 1: [n_tok][H][D] in the query type
@@ -68,7 +68,7 @@ hipError_t launch_combine(const CombineArgs& a, int H, int D, int qt, hipStream_
 // token; n_rows, n_split and rows_per_split are set by the launcher)
 hipError_t launch_block_branches(const RowsArgs& a, int H, int D, int kv, hipStream_t st);
 // decode full layer over a contiguous cache range, bf16 or FP8 cache (logits always stored)
-hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStream_t st);
+hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, int code_bytes, hipStream_t st);
 
 // ---- selection ------------------------------------------------------------
 constexpr int kHistBins = 4096;      // top 12 bits of a non-negative fp32 (bits 30..19)
@@ -79,7 +79,7 @@ constexpr int kSelChunk = 8192;      // scores per workgroup in the histogram an
 // scores [B][n_ctx] and the histogram of candidates j < n_cand.
 struct ScoreArgs {
     const float* logits;    // [B][n_ctx][H] base 2 (fp32 cache), or NULL:
-    const uint16_t* lcode;  // [B][n_ctx][H] codes below the block maxima
+    const void* lcode;      // [B][n_ctx][H] codes below the block maxima (code_bytes each)
     const float* lmax;      // [B][ceil(n_ctx / 32)][H] block maxima, base 2
     const float* lse2;      // [B][H]
     float* scores;          // [B][n_ctx]
@@ -87,8 +87,24 @@ struct ScoreArgs {
     int64_t n_ctx;
     int64_t n_cand;         // candidates per row (n_ctx - window, >= 0)
     int H;
+    int code_bytes;         // 2: scores from 16-bit codes; 1: 8-bit codes, scores = upper bounds, histogram of lower bounds
 };
 hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st);
+
+// Exact scores of the collected candidates (8-bit-code form of the decode step).
+struct RescoreArgs {
+    const void* q;          // [B][H][D] bf16 full-layer query
+    const void* k;          // [B][n_ctx][D] bf16 or FP8 codes
+    const float* ks;        // [B][n_ctx] FP8 key scales (else unused)
+    const float* lse2;      // [B][H] base 2
+    const uint32_t* thr;    // [B][2]: candidate count at [2b+1]
+    uint64_t* cand;         // [B][kCandCap] rank keys, rewritten with exact scores
+    float* scores;          // [B][n_ctx]: exact scores written here for a row whose candidates overflowed
+    int64_t n_ctx;
+    int64_t n_cand;         // candidate positions per row (n_ctx - window)
+    float scale_log2;       // sm_scale * log2(e)
+};
+hipError_t launch_decode_rescore(const RescoreArgs& a, int B, int H, int D, int kv, hipStream_t st);
 
 // Top-k of rows of non-negative fp32 scores.
 struct SelectArgs {
@@ -107,6 +123,7 @@ struct SelectArgs {
     int64_t out_stride;
     int out_offset;         // first column written in each out row
     int rev;                // test hook: deal the grid in reverse order (0: normal)
+    int exact_kth;          // final step: rank the candidates by their keys alone (no threshold bin)
 };
 // hist zeroed; fills hist
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);

@@ -44,7 +44,11 @@ namespace hs2 {
 constexpr int kDecThreads = 256;
 constexpr int kDecBlock = 32;  // keys per wave per step
 
-template <int H, int D, int KV>
+// CB: bytes per logit code, 2 (the 16-bit codes above) or 1 (8-bit codes
+// c = round(16 (M - x)), clamped to 255: resolution 1/16 in the exponent, a
+// factor 2^(+-1/32) per term; the selection then bounds every score from them
+// and recomputes the exact scores of the keys it cannot decide).
+template <int H, int D, int KV, int CB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a) {
     static_assert(KV == DT_BF16 || KV == DT_FP8, "bf16 or FP8 cache");
     static_assert(H <= 16 && (H == 4 || H == 8 || H == 16), "heads on the 16 MFMA columns");
@@ -62,7 +66,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     using KPiece = typename std::conditional<KV == DT_FP8, u32x2, u32x4>::type;
 
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][kDecBlock * VLD];
-    __shared__ __attribute__((aligned(16))) uint16_t lg_lds[4][kDecBlock * H];
+    using Code = typename std::conditional<CB == 1, uint8_t, uint16_t>::type;
+    constexpr float kCS = CB == 1 ? kCode8Scale : kCodeScale;
+    constexpr float kCMax = CB == 1 ? 255.f : 65535.f;
+    __shared__ __attribute__((aligned(16))) Code lg_lds[4][kDecBlock * H];
     __shared__ float vs_lds[4][kDecBlock];
     __shared__ float ks_lds[4][kDecBlock];
 
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + kv_base * RB;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + kv_base * RB;
     uint16_t* vl = v_lds[w];
-    uint16_t* lgl = lg_lds[w];
+    Code* lgl = lg_lds[w];
 
     // query fragment (B operand): head hl, k-step c, slots d = 32c + 8g .. +7
     u32x4 qf[NC];
@@ -187,12 +194,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     const int64_t n_blk = (a.n_ctx + kDecBlock - 1) / kDecBlock;  // code blocks per sequence
     auto flush_logits = [&]() {
         const bool any = pend_j < r_end;
-        const auto rl = raw_buffer(a.lcode + (kv_base + (size_t)pend_j) * H,
-                                   (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * 2));
-        constexpr int NP = kDecBlock * H * 2 / 16;  // 16-byte pieces of a block's codes
+        const auto rl = raw_buffer(reinterpret_cast<Code*>(a.lcode) + (kv_base + (size_t)pend_j) * H,
+                                   (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * CB));
+        constexpr int NP = kDecBlock * H * CB / 16;  // 16-byte pieces of a block's codes
 #pragma unroll
         for (int p = lane; p < NP; p += 64)
-            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lgl + 8 * p), rl, 16 * p, 0, 2);
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lgl + 16 / CB * p), rl, 16 * p, 0, 2);
         const auto rm = raw_buffer(a.lmax + ((size_t)seq * n_blk + (size_t)(any ? pend_j / kDecBlock : 0)) * H,
                                    any ? (uint32_t)(H * 4) : 0u);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pend_mx), rm, 4 * hl, 0, 2);
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     lgl[(16 * grp + 4 * g + i) * H + hl] =
-                        (uint16_t)(uint32_t)fminf((mx - x[grp][i]) * kCodeScale + 0.5f, 65535.f);
+                        (Code)(uint32_t)fminf((mx - x[grp][i]) * kCS + 0.5f, kCMax);
         }
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
@@ -383,25 +390,29 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     }
 }
 
-template <int H, int D>
+template <int H, int D, int CB>
 static hipError_t launch_dec_hd(const RowsArgs& a, int kv, hipStream_t st) {
     const dim3 grid((unsigned)a.n_split, (unsigned)a.n_tok);
     if (kv == DT_FP8)
-        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_FP8>), grid, dim3(kDecThreads), 0, st, a);
+        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_FP8, CB>), grid, dim3(kDecThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_BF16>), grid, dim3(kDecThreads), 0, st, a);
+        hipLaunchKernelGGL((decode_split_kernel<H, D, DT_BF16, CB>), grid, dim3(kDecThreads), 0, st, a);
     return hipGetLastError();
 }
-
-hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, hipStream_t st) {
+template <int CB>
+static hipError_t launch_dec_cb(const RowsArgs& a, int H, int D, int kv, hipStream_t st) {
     if (D == 64) {
-        if (H == 4) return launch_dec_hd<4, 64>(a, kv, st);
-        if (H == 8) return launch_dec_hd<8, 64>(a, kv, st);
-        return launch_dec_hd<16, 64>(a, kv, st);
+        if (H == 4) return launch_dec_hd<4, 64, CB>(a, kv, st);
+        if (H == 8) return launch_dec_hd<8, 64, CB>(a, kv, st);
+        return launch_dec_hd<16, 64, CB>(a, kv, st);
     }
-    if (H == 4) return launch_dec_hd<4, 128>(a, kv, st);
-    if (H == 8) return launch_dec_hd<8, 128>(a, kv, st);
-    return launch_dec_hd<16, 128>(a, kv, st);
+    if (H == 4) return launch_dec_hd<4, 128, CB>(a, kv, st);
+    if (H == 8) return launch_dec_hd<8, 128, CB>(a, kv, st);
+    return launch_dec_hd<16, 128, CB>(a, kv, st);
+}
+
+hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, int code_bytes, hipStream_t st) {
+    return code_bytes == 1 ? launch_dec_cb<1>(a, H, D, kv, st) : launch_dec_cb<2>(a, H, D, kv, st);
 }
 
 }  // namespace hs2

@@ -139,13 +139,21 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
     flush_hist(hist, a.hist + (size_t)b * kHistBins);
 }
 
-// The same from the 16-bit logit codes of the bf16 / FP8 split kernel: term h
-// of key j is 2^(M_h - c_hj / 1024 - LSE_h) with M_h the maximum of head h over
-// the 32-key block of j. The chunk's block maxima, less the LSE, are staged in
-// LDS first; then every thread takes keys j0 + 256 i + t, loading the 2H code
-// bytes of kBatch keys before it forms their scores (consecutive threads read
+// The same from the logit codes of the bf16 / FP8 split kernel: term h of key
+// j is 2^(M_h - c_hj / 1024 - LSE_h) with M_h the maximum of head h over the
+// 32-key block of j. The chunk's block maxima, less the LSE, are staged in LDS
+// first; then every thread takes keys j0 + 256 i + t, loading the code bytes
+// of kBatch keys before it forms their scores (consecutive threads read
 // consecutive keys).
-template <int H>
+// CB = 1 (8-bit codes c = round(16 (M - x)), clamped at 255): a term lies in
+// [m / r, m r], m = 2^(M - c/16 - LSE), r = 2^(1/32 + 2^-12) (the code's half
+// step plus a margin far above the fp32 rounding of the sums), or in
+// [0, 2^(M - 254.5/16 - LSE)] where clamped. The kernel stores the upper
+// bound of every score and histograms the lower bounds: the collect step then
+// keeps every key whose upper bound reaches the bin of the k-th largest lower
+// bound -- a superset of the top k -- and the rescore step replaces their
+// bounds by exact scores.
+template <int H, int CB>
 __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArgs a) {
     constexpr int kBatch = 8;
     constexpr int NBLK = kSelChunk / 32;  // 32-key blocks of a chunk
@@ -169,37 +177,72 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArg
         }
     }
     __syncthreads();
-    const uint16_t* lc = a.lcode + (size_t)b * (size_t)a.n_ctx * H;
-    using Piece = typename std::conditional<H == 4, u32x2, u32x4>::type;
-    constexpr int NPC = H == 4 ? 1 : H / 8;  // pieces per key
+    constexpr int KB = H * CB;  // code bytes per key
+    const uint8_t* lc = reinterpret_cast<const uint8_t*>(a.lcode) + (size_t)b * (size_t)a.n_ctx * KB;
+    using Piece = typename std::conditional<KB == 4, uint32_t,
+                                            typename std::conditional<KB == 8, u32x2, u32x4>::type>::type;
+    constexpr int WPP = sizeof(Piece) / 4;              // 32-bit words per piece
+    constexpr int NPC = KB <= 16 ? 1 : KB / 16;        // pieces per key
+    constexpr float kR = 1.0221235f, kRInv = 0.9783545f;  // 2^(+-(1/32 + 2^-12)) = 1.0220701, 0.9784065, widened
     for (int64_t jb = j0; jb < j1; jb += (int64_t)kBatch * kSelThreads) {
         Piece cw[kBatch][NPC];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int64_t j = min<int64_t>(jb + (int64_t)i * kSelThreads + tid, j1 - 1);
 #pragma unroll
-            for (int c = 0; c < NPC; ++c) cw[i][c] = reinterpret_cast<const Piece*>(lc + (size_t)j * H)[c];
+            for (int c = 0; c < NPC; ++c) cw[i][c] = reinterpret_cast<const Piece*>(lc + (size_t)j * KB)[c];
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int64_t j = jb + (int64_t)i * kSelThreads + tid;
             if (j >= j1) break;
             const float* mrow = ml + (int)((j - j0) >> 5) * H;
-            float s = 0.f;
+            float s = 0.f, s_cl = 0.f;
 #pragma unroll
             for (int h = 0; h < H; ++h) {
-                constexpr int WPP = sizeof(Piece) / 4;  // 32-bit words per piece
-                const uint32_t word = cw[i][(h / 2) / WPP][(h / 2) % WPP];
-                const uint32_t code = (word >> (16 * (h & 1))) & 0xffffu;
-                s += fast_exp2(fmaf((float)code, -kCodeUnscale, mrow[h]));
+                constexpr int PER_WORD = 4 / CB;  // codes per 32-bit word
+                const int wi = h / PER_WORD;
+                uint32_t word;
+                if constexpr (WPP == 1)
+                    word = reinterpret_cast<const uint32_t*>(&cw[i][0])[wi];
+                else
+                    word = cw[i][wi / WPP][wi % WPP];
+                if constexpr (CB == 2) {
+                    const uint32_t code = (word >> (16 * (h & 1))) & 0xffffu;
+                    s += fast_exp2(fmaf((float)code, -kCodeUnscale, mrow[h]));
+                } else {
+                    // a clamped code (255) bounds its term by the value at 254.5
+                    const uint32_t code = (word >> (8 * (h & 3))) & 0xffu;
+                    const bool cl = code == 255u;
+                    const float e = fast_exp2(fmaf(cl ? 254.5f : (float)code, -kCode8Unscale, mrow[h]));
+                    s += cl ? 0.f : e;
+                    s_cl += cl ? e : 0.f;
+                }
             }
-            s *= kScoreUnshift;  // exact power-of-two rescale to the true score
+            float hist_s;
+            if constexpr (CB == 2) {
+                s *= kScoreUnshift;  // exact power-of-two rescale to the true score
+                hist_s = s;
+            } else {
+                hist_s = s * kRInv * kScoreUnshift;       // lower bound
+                s = (s * kR + s_cl) * kScoreUnshift;      // upper bound
+            }
             a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
-            if (j < a.n_cand) atomicAdd(&hist[score_bin(s)], 1u);
+            if (j < a.n_cand) atomicAdd(&hist[score_bin(hist_s)], 1u);
         }
     }
     __syncthreads();
     flush_hist(hist, a.hist + (size_t)b * kHistBins);
+}
+
+template <int CB>
+static void launch_score_code(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+    if (a.H == 4)
+        hipLaunchKernelGGL((decode_score_code_kernel<4, CB>), grid, dim3(kSelThreads), 0, st, a);
+    else if (a.H == 8)
+        hipLaunchKernelGGL((decode_score_code_kernel<8, CB>), grid, dim3(kSelThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_score_code_kernel<16, CB>), grid, dim3(kSelThreads), 0, st, a);
 }
 
 hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st) {
@@ -211,13 +254,113 @@ hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st) {
             hipLaunchKernelGGL(decode_score_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
         else
             hipLaunchKernelGGL(decode_score_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
+    } else if (a.code_bytes == 1) {
+        launch_score_code<1>(a, grid, st);
     } else {
-        if (a.H == 4)
-            hipLaunchKernelGGL(decode_score_code_kernel<4>, grid, dim3(kSelThreads), 0, st, a);
-        else if (a.H == 8)
-            hipLaunchKernelGGL(decode_score_code_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL(decode_score_code_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
+        launch_score_code<2>(a, grid, st);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ decode rescore
+// After the collect step of the 8-bit-code form: the exact score of every
+// candidate, recomputed from its key row and the row's query with the split
+// kernel's own arithmetic (S^T = K Q^T on v_mfma_f32_16x16x32_bf16, 16 keys
+// on M and the heads on N, the same operand layout, so the logits are the
+// ones the split kernel formed), then sum_h 2^(x_h - LSE_h), written back into
+// the candidate's rank key in place. Each wave takes 16 candidates at a time;
+// workgroups past the row's candidate count leave at once. A row whose
+// candidates overflowed the list (the final step then ranks its whole score
+// row) gets exact scores for all its keys instead, written over the upper
+// bounds in the score row.
+template <int H, int D, int KV>
+__global__ __launch_bounds__(kSelThreads) void decode_rescore_kernel(RescoreArgs a) {
+    constexpr int NC = D / 32;  // MFMA k-steps over d
+    constexpr int ESZ = KV == DT_FP8 ? 1 : 2;
+    constexpr int RB = D * ESZ;
+    constexpr int kPerWg = kSelThreads / 64 * 16;  // candidates per workgroup pass
+    const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hl = lane & 15, g = lane >> 4;
+    const uint32_t nc = a.thr[2 * r + 1];
+    const bool overflow = nc > (uint32_t)kCandCap;
+    const int64_t n = overflow ? a.n_cand : (int64_t)nc;
+    const int64_t stride = (int64_t)gridDim.x * kPerWg;
+    if ((int64_t)blockIdx.x * kPerWg >= n) return;  // uniform over the workgroup
+    // query fragment (B operand): head hl, k-step c, d = 32c + 8g .. +7
+    u32x4 qf[NC];
+    {
+        const bool hv = hl < H;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)r * H + (hv ? hl : 0)) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 v4 = *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * g);
+            qf[c] = hv ? v4 : u32x4{0, 0, 0, 0};
+        }
+    }
+    const float l2 = hl < H ? a.lse2[(size_t)r * H + hl] - kScoreShift : 0.f;
+    const size_t kv_base = (size_t)r * (size_t)a.n_ctx;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + kv_base * RB;
+    uint64_t* cand = a.cand + (size_t)r * kCandCap;
+    for (int64_t i0 = (int64_t)blockIdx.x * kPerWg + 16 * w; i0 < n; i0 += stride) {
+        // A operand: candidate i0 + hl, d = 32c + 8g .. +7
+        const int64_t i = i0 + hl;
+        const bool live = i < n;
+        const uint32_t pos = live ? (overflow ? (uint32_t)i : key_pos(cand[i])) : 0u;
+        const uint8_t* kp = kb + (size_t)pos * RB + 8 * g * ESZ;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            u32x4 kk;
+            if constexpr (KV == DT_FP8) {
+                const u32x2 raw = *reinterpret_cast<const u32x2*>(kp + 32 * c);
+                const u32x2 lo = fp8x4_to_bf16x4(raw[0]), hi = fp8x4_to_bf16x4(raw[1]);
+                kk = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                kk = *reinterpret_cast<const u32x4*>(kp + 64 * c);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk), as_bf16x8(qf[c]), acc, 0, 0, 0);
+        }
+        // acc[e]: candidate 4g + e, head hl
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int src = 4 * g + e;  // the lane that loaded this candidate's row
+            const uint32_t pe = __shfl(pos, src);
+            const bool le = i0 + src < n;
+            float x = acc[e] * a.scale_log2;
+            if constexpr (KV == DT_FP8) x *= le ? a.ks[kv_base + pe] : 0.f;
+            float t = (le && hl < H) ? fast_exp2(x - l2) : 0.f;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
+            if (le && hl == 0) {
+                const float sc = t * kScoreUnshift;
+                if (overflow)
+                    a.scores[(size_t)r * (size_t)a.n_ctx + pe] = sc;
+                else
+                    cand[i0 + src] = rank_key(sc, pe);
+            }
+        }
+    }
+}
+
+template <int H, int D>
+static void launch_rescore_hd(const RescoreArgs& a, int kv, dim3 grid, hipStream_t st) {
+    if (kv == DT_FP8)
+        hipLaunchKernelGGL((decode_rescore_kernel<H, D, DT_FP8>), grid, dim3(kSelThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_rescore_kernel<H, D, DT_BF16>), grid, dim3(kSelThreads), 0, st, a);
+}
+
+hipError_t launch_decode_rescore(const RescoreArgs& a, int B, int H, int D, int kv, hipStream_t st) {
+    // one pass over a full candidate list (kCandCap keys) per row
+    const dim3 grid((unsigned)(kCandCap / (kSelThreads / 64 * 16)), (unsigned)B);
+    if (D == 64) {
+        if (H == 4) launch_rescore_hd<4, 64>(a, kv, grid, st);
+        else if (H == 8) launch_rescore_hd<8, 64>(a, kv, grid, st);
+        else launch_rescore_hd<16, 64>(a, kv, grid, st);
+    } else {
+        if (H == 4) launch_rescore_hd<4, 128>(a, kv, grid, st);
+        else if (H == 8) launch_rescore_hd<8, 128>(a, kv, grid, st);
+        else launch_rescore_hd<16, 128>(a, kv, grid, st);
     }
     return hipGetLastError();
 }
@@ -703,12 +846,14 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
         return;
     }
     // Keys above the threshold bin are all kept (fewer than kk of them); of the
-    // nb keys in the bin the need = kk - (nc - nb) largest are kept.
+    // nb keys in the bin the need = kk - (nc - nb) largest are kept. With
+    // exact_kth the candidates' keys carry scores the threshold bin was not
+    // taken from (the decode rescore step), so the k-th key is searched for.
     const uint32_t tbin = a.thr[2 * r];
     uint64_t* inb_key = reinterpret_cast<uint64_t*>(pos);  // pos[0, 1024): kRankMax keys
     uint32_t* inb_idx = reinterpret_cast<uint32_t*>(pos + 1024);
     __syncthreads();
-    for (uint32_t ib = 0; ib < nc; ib += blockDim.x) {
+    for (uint32_t ib = 0; !a.exact_kth && ib < nc; ib += blockDim.x) {
         const uint32_t i = ib + tid;
         const uint64_t k = i < nc ? keys[i] : 0ull;
         const bool in_bin = i < nc && (uint32_t)(k >> 51) == tbin;
@@ -725,7 +870,7 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     __syncthreads();
     const uint32_t nb = ctl[4];
     // flags in hist[0, nc): 1 = kept
-    if (nb <= (uint32_t)kRankMax) {
+    if (!a.exact_kth && nb <= (uint32_t)kRankMax) {
         const uint32_t need = kk - (nc - nb);
         bool kept = false;
         if (tid < (int)nb) {
