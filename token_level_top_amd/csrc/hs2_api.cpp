@@ -90,6 +90,12 @@ int decode_splits(int B, int64_t n_ctx) {
     const int rps = decode_rows_per_split(B, n_ctx);
     return (int)((n_ctx + rps - 1) / rps);
 }
+// 128-key chunks a split of the bf16 / FP8 split kernel takes, at most (<= rows_per_split / 128)
+int decode_max_chunks(int B, int64_t n_ctx) {
+    const int64_t chunks = (n_ctx + kTile - 1) / kTile;
+    const int ns = decode_splits(B, n_ctx);
+    return (int)((chunks + ns - 1) / ns);
+}
 // sparse layers: with few tokens a token's index row is split over
 // workgroups, as evenly as whole 128-row tiles allow, so that one round of
 // the sparse kernel (2 workgroups per CU) covers the grid and every split
@@ -120,9 +126,11 @@ DecodeWs decode_ws(void* base, int B, int64_t n_ctx, int H, int d, int window, i
     Carver c(base);
     DecodeWs w;
     const int ns = decode_splits(B, n_ctx);
-    // fp32 logits, or (bf16 / FP8 caches) the 16-bit codes followed by the
-    // 32-key block maxima: 2 n_ctx H bytes + 4 ceil(n_ctx / 32) H, never more
-    w.logits = c.take<float>(sizeof(float) * (size_t)B * n_ctx * H + 64 * (size_t)B * H);
+    // fp32 logits, or (bf16 / FP8 caches) the codes (at most 2 n_ctx H bytes a
+    // sequence) followed by the block maxima by (split, chunk, wave): 16 H
+    // bytes per chunk slot, n_split * max_chunks slots, at most
+    // ceil(n_ctx / 128) + n_split; together never more
+    w.logits = c.take<float>(sizeof(float) * (size_t)B * n_ctx * H + 512 * (size_t)B * H);
     w.part = ns > 1 ? c.take<float>(sizeof(float) * (size_t)B * ns * H * (d + 2)) : nullptr;
     w.lse2 = c.take<float>(sizeof(float) * (size_t)B * H);
     w.scores = c.take<float>(sizeof(float) * (size_t)B * n_ctx);
@@ -886,6 +894,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
         lmax = reinterpret_cast<float*>(w.logits) + ((size_t)B * n_ctx * H * code_bytes + 15) / 16 * 4;
         a.lcode = lcode;
         a.lmax = lmax;
+        a.max_chunks = decode_max_chunks(B, n_ctx);
     }
     if (ns > 1) {
         a.part = w.part;
@@ -922,6 +931,8 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     sa.logits = kv_dtype == HS2_F32 ? w.logits : nullptr;
     sa.lcode = lcode;
     sa.lmax = lmax;
+    sa.n_split = ns;
+    sa.max_chunks = decode_max_chunks(B, n_ctx);
     sa.code_bytes = code_bytes;
     sa.lse2 = w.lse2;
     sa.scores = sc;

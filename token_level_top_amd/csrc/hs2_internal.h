@@ -26,7 +26,8 @@ struct RowsArgs {
     // decode split kernel (bf16 / FP8 cache): the logits as 16-bit codes below
     // the maximum of their 32-key block and head, and those maxima
     void* lcode;            // [B][n_ctx][H] codes of code_bytes each (16- or 8-bit)
-    float* lmax;            // [B][ceil(n_ctx / 32)][H] base 2
+    float* lmax;            // [B][n_split][max_chunks][4][H] base 2: block maxima by (split, chunk, wave)
+    int max_chunks;         // 128-key chunks per split, at most (ceil(ceil(n_ctx / 128) / n_split))
     float* part;            // n_split > 1: [n_tok][n_split][H*(D+2)] = m[H], l[H], O[H][D]
     void* out;              // n_split == 1: [n_tok][H][D] in the query type
     float* lse;             // n_split == 1: [n_tok][H] natural log, nullable
@@ -80,7 +81,8 @@ constexpr int kSelChunk = 8192;      // scores per workgroup in the histogram an
 struct ScoreArgs {
     const float* logits;    // [B][n_ctx][H] base 2 (fp32 cache), or NULL:
     const void* lcode;      // [B][n_ctx][H] codes below the block maxima (code_bytes each)
-    const float* lmax;      // [B][ceil(n_ctx / 32)][H] block maxima, base 2
+    const float* lmax;      // [B][n_split][max_chunks][4][H] block maxima, base 2 (the split kernel's layout)
+    int n_split, max_chunks;
     const float* lse2;      // [B][H]
     float* scores;          // [B][n_ctx]
     uint32_t* hist;         // [B][kHistBins], zeroed by the caller

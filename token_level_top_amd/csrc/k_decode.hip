@@ -43,6 +43,8 @@ namespace hs2 {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecBlock = 32;  // keys per wave per step
+// 128-key chunks a split takes at most (rows_per_split <= 8192, checked by the launcher)
+constexpr int kDecMaxChunks = 64;
 
 // CB: bytes per logit code, 2 (the 16-bit codes above) or 1 (8-bit codes
 // c = round(16 (M - x)), clamped to 255: resolution 1/16 in the exponent, a
@@ -70,6 +72,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     constexpr float kCS = CB == 1 ? kCode8Scale : kCodeScale;
     constexpr float kCMax = CB == 1 ? 255.f : 65535.f;
     __shared__ __attribute__((aligned(16))) Code lg_lds[4][kDecBlock * H];
+    // block maxima of the whole split, written in one run at the end (one
+    // 64-byte store per block measured 23 us of this kernel at 64 x 128k)
+    // (+1: with an odd block count a wave's last trip runs one masked block more)
+    __shared__ __attribute__((aligned(16))) float mx_lds[kDecMaxChunks + 1][4][H];
     __shared__ float vs_lds[4][kDecBlock];
     __shared__ float ks_lds[4][kDecBlock];
 
@@ -184,25 +190,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     };
     // logit codes of the previous block: staged [32][H] in LDS, written as
     // 16-B streaming stores through a descriptor ending at the block's last row
-    // inside the sequence (before the first block its range is empty), and the
-    // block's H maxima (every lane stores its head's; lanes of one head store
-    // the same value, heads >= H fall outside the range). Every load and store
-    // of the loop is issued unconditionally, so the compiler's waits on the
-    // loads of the next block count exactly the operations issued after them.
+    // inside the sequence (before the first block its range is empty). Every
+    // load and store of the loop is issued unconditionally, so the compiler's
+    // waits on the loads of the next block count exactly the operations issued
+    // after them.
     int64_t pend_j = r_end;
-    float pend_mx = 0.f;
-    const int64_t n_blk = (a.n_ctx + kDecBlock - 1) / kDecBlock;  // code blocks per sequence
     auto flush_logits = [&]() {
-        const bool any = pend_j < r_end;
         const auto rl = raw_buffer(reinterpret_cast<Code*>(a.lcode) + (kv_base + (size_t)pend_j) * H,
                                    (uint32_t)min<int64_t>(kDecBlock, max<int64_t>(0, r_end - pend_j)) * (uint32_t)(H * CB));
         constexpr int NP = kDecBlock * H * CB / 16;  // 16-byte pieces of a block's codes
 #pragma unroll
         for (int p = lane; p < NP; p += 64)
             __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lgl + 16 / CB * p), rl, 16 * p, 0, 2);
-        const auto rm = raw_buffer(a.lmax + ((size_t)seq * n_blk + (size_t)(any ? pend_j / kDecBlock : 0)) * H,
-                                   any ? (uint32_t)(H * 4) : 0u);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pend_mx), rm, 4 * hl, 0, 2);
     };
 
     // S^T for the two 16-key groups of a block
@@ -226,7 +225,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         }
     };
     // logits, online softmax and O^T += V^T P^T for the block at j (V in LDS)
-    auto finish = [&](const f32x4* sacc, int64_t j) {
+    auto finish = [&](const f32x4* sacc, int64_t j, int n) {
         // base-2 logits; lane holds head hl of block keys 16*grp + 4g + i
         float x[2][4];
         float mx = -INFINITY;
@@ -247,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         mx = fmaxf(mx, xor32(mx));
         // codes below the block maximum of head hl (a masked key, or a block
         // with every key masked, gives NaN or +inf, and fminf then the clamp)
-        pend_mx = mx;
+        if (hl < H && g == 0) mx_lds[n][w][hl] = mx;
         if (hl < H) {
 #pragma unroll
             for (int grp = 0; grp < 2; ++grp)
@@ -305,7 +304,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
         f32x4 sacc[2];
         scores(buf, sacc);
         load_block(buf, blk_j(n + 2));
-        finish(sacc, j);
+        finish(sacc, j, n);
         stage_v(buf ^ 1);
     };
     load_block(0, blk_j(0));
@@ -321,6 +320,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(RowsArgs a
     l_run += __shfl_xor(l_run, 16);
     l_run += xor32(l_run);
     __syncthreads();
+    // the split's block maxima, [chunk][wave][H] = the layout of its region
+    // [seq][split][chunks of a split][4][H] (blocks past the sequence are
+    // written too and never read)
+    {
+        const int n_chk = s0 < r_end ? (int)((r_end - s0 + c_stride - 1) / c_stride) : 0;  // chunks of the split
+        float* mdst = a.lmax + ((size_t)seq * a.n_split + (size_t)split) * (size_t)a.max_chunks * 4 * H;
+        for (int e = tid; e < n_chk * H; e += kDecThreads)
+            reinterpret_cast<f32x4*>(mdst)[e] = reinterpret_cast<const f32x4*>(&mx_lds[0][0][0])[e];
+    }
     // [4 waves][16][RS], then m, l; rows of RS = D + 4 floats (an odd number of
     // 16-byte units), so the 16 head lanes of one 16-byte store hit 16 bank quads
     constexpr int RS = D + 4;
@@ -412,6 +420,7 @@ static hipError_t launch_dec_cb(const RowsArgs& a, int H, int D, int kv, hipStre
 }
 
 hipError_t launch_decode_split(const RowsArgs& a, int H, int D, int kv, int code_bytes, hipStream_t st) {
+    if (a.max_chunks > kDecMaxChunks) return hipErrorInvalidValue;
     return code_bytes == 1 ? launch_dec_cb<1>(a, H, D, kv, st) : launch_dec_cb<2>(a, H, D, kv, st);
 }
 

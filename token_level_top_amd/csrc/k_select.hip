@@ -163,16 +163,20 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArg
     for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
     const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
     const int64_t j1 = min<int64_t>(j0 + kSelChunk, a.n_ctx);
-    const int64_t n_blk = (a.n_ctx + 31) / 32;
     const int nb = (int)((j1 - j0 + 31) / 32);
     {
-        const float* lm = a.lmax + ((size_t)b * (size_t)n_blk + (size_t)(j0 / 32)) * H;
+        // block bg = j / 32 lies in 128-key chunk c = bg / 4, taken by wave bg % 4
+        // of split c % n_split as its chunk c / n_split
         const float* l2 = a.lse2 + (size_t)b * H;
         for (int e = tid; e < nb * H / 4; e += kSelThreads) {
-            const f32x4 m = reinterpret_cast<const f32x4*>(lm)[e];
+            const int bl = e / (H / 4), qd = e % (H / 4);
+            const int64_t bg = j0 / 32 + bl, c = bg >> 2;
+            const size_t rec = (((size_t)b * a.n_split + (size_t)(c % a.n_split)) * (size_t)a.max_chunks +
+                                (size_t)(c / a.n_split)) * 4 + (size_t)(bg & 3);
+            const f32x4 m = *reinterpret_cast<const f32x4*>(a.lmax + rec * H + 4 * qd);
             f32x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = m[i] - (l2[(4 * e + i) % H] - kScoreShift);
+            for (int i = 0; i < 4; ++i) v[i] = m[i] - (l2[4 * qd + i] - kScoreShift);
             reinterpret_cast<f32x4*>(ml)[e] = v;
         }
     }
