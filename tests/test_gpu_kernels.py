@@ -334,6 +334,33 @@ def test_prefill_all_tied_scores(hs2, orc):
     rows_close(out[0], ref["out"], 1e-2)
 
 
+@pytest.mark.parametrize("cfg", [3, 5])
+@pytest.mark.parametrize("want_scores", [True, False])
+def test_decode_all_tied_scores(hs2, orc, cfg, want_scores):
+    """A zero query gives every key of its sequence the same score, so every
+    candidate ties: the lowest positions win. Without the score vector the
+    collect step then keeps more candidates than its list holds, and the
+    overflow path runs (exact scores for the whole row, whole-row selection);
+    the other sequence takes the ordinary path in the same launch."""
+    wl = workload(cfg).with_(B=2, n_q=1, q_pos0=8999, n_ctx=9000, n_sparse=1, needles="none", n_needles=0,
+                             decode=True)
+    x = make_inputs(wl)
+    x.q[0] = 0
+    say("decode all tied", wl.name, "with" if want_scores else "without", "the score vector")
+    r = hs2.decode_step(dev(x.q[:, 0]).contiguous(), dev(x.q_sparse[:, :, 0]).contiguous(), dev(x.k), dev(x.v),
+                        dev(x.k_scale), dev(x.v_scale), window=128, k_global=1024, sm_scale=x.sm_scale,
+                        want_scores=want_scores)
+    torch.cuda.synchronize()
+    g = to_np(r["indices"])
+    assert g[0, 128:].tolist() == list(range(1024))
+    assert g[0, :128].tolist() == list(range(9000 - 128, 9000))
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, 128, 1024, x.sm_scale, [0, 1],
+                          want_scores=True)
+    ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], 128)
+    say(f"  overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
+    rows_close(r["out_full"], ref["out"], RTOL[wl.kv_dtype], "tied decode out")
+
+
 @pytest.mark.parametrize("cfg,B,H,d,n_q,q_pos0,n_ctx", [
     (2, 2, 16, 128, 200, 300, 500),     # two sequences in one launch
     (2, 1, 8, 64, 500, 4000, 4500),     # bf16, H=8, d=64 instantiations
