@@ -1407,9 +1407,10 @@ void block_score_kernel(PrefillArgs a) {
 #endif
 enum PfKernel { PF_FWD, PF_STREAM, PF_BLOCKS };
 // Threshold histograms in the streaming top-K (measured): the pass at 32 Ki keys
-// per row drops 11-14 % with fewer than 16 heads or in the indexer form, while on
-// 256 Ki rows it costs more than it saves, and the 16-head forms (4 waves per
-// SIMD in 128 registers) spill with it. Used where no row has 64 Ki candidates.
+// per row drops 11-14 % with fewer than 16 heads or in the indexer form and 2 %
+// with 16 heads (whose form, 4 waves per SIMD in 128 registers, spills 7
+// registers with them against 5 without), while on 256 Ki rows it costs more
+// than it saves. Used where no row has 64 Ki candidates.
 static bool hist_pays(const PrefillArgs& a) { return a.q_pos0 + a.n_q - a.window < 65536; }
 template <int H, int D, int KV>
 static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st) {
@@ -1425,14 +1426,10 @@ static hipError_t launch_pf(const PrefillArgs& a, PfKernel which, hipStream_t st
                                st, a);
     }
     else if (which == PF_STREAM) {
-        if constexpr (H < 16) {
-            if (hist_pays(a))
-                hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, true>), grid, dim3(kPfThreads), 0, st, a);
-            else
-                hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, false>), grid, dim3(kPfThreads), 0, st, a);
-        } else {
+        if (hist_pays(a))
+            hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, true>), grid, dim3(kPfThreads), 0, st, a);
+        else
             hipLaunchKernelGGL((score_stream_kernel<H, D, KV, false, false>), grid, dim3(kPfThreads), 0, st, a);
-        }
     }
     else
         hipLaunchKernelGGL((block_score_kernel<H, D, KV>), grid, dim3(kPfThreads), 0, st, a);
