@@ -78,3 +78,48 @@ def test_peaked_attention_clamps_and_the_narrow_range_would_not_hold():
     allow = 4e-4 * exact + 1e-17 * exact.max()
     assert (np.abs(coded - exact) <= allow).all()
     assert (np.abs(narrow - exact) > 1e3 * allow).any()
+
+
+# The 8-bit form of the timed decode step: codes c = min(round(16 (M - x)), 255)
+# give bounds, the collect step keeps every key whose upper bound reaches the
+# bin of the K-th largest lower bound, and only those are rescored exactly.
+KR, KR_INV = np.float32(1.0221235), np.float32(0.9783545)  # the kernel's 2^(+-(1/32 + 2^-12)), widened
+
+
+def score_bin(x):
+    """The selection's histogram bin: bits 30..19 of the fp32 value."""
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 19) & 0xFFF
+
+
+def bounds8(x2):
+    """x2 [n][H] base-2 logits -> (exact, lower, upper) scores as the score kernel forms them."""
+    n, H = x2.shape
+    mx = x2.max(axis=0)
+    lse2 = np.log2(np.exp2(x2 - mx).sum(axis=0)) + mx
+    exact = np.exp2(x2 - lse2).sum(axis=1)
+    nb = (n + 31) // 32
+    pad = np.full((nb * 32, H), -np.inf)
+    pad[:n] = x2
+    M = np.repeat(pad.reshape(nb, 32, H).max(axis=1), 32, axis=0)[:n]
+    c = np.minimum(np.floor((M - x2) * 16 + 0.5), 255)
+    e = np.exp2(M - c / 16 - lse2)
+    upper = e.sum(axis=1) * KR
+    lower = np.where(c == 255, 0.0, e).sum(axis=1) * KR_INV
+    return exact, lower, upper
+
+
+@pytest.mark.parametrize("B,n_ctx,scale_mult", [(2, 5003, 1.0), (1, 20000, 1.0), (1, 20000, 12.0)])
+def test_eight_bit_bounds_hold_and_keep_the_top_k(B, n_ctx, scale_mult):
+    lg, wl = base2_logits(B, n_ctx, scale_mult)
+    K = wl.k_global
+    for b in range(B):
+        exact, lower, upper = bounds8(lg[b])
+        assert (lower <= exact * (1 + 1e-9)).all() and (exact <= upper * (1 + 1e-9)).all()
+        n_cand = n_ctx - wl.window
+        lo, up, ex = lower[:n_cand], upper[:n_cand], exact[:n_cand]
+        tbin = score_bin(np.sort(lo)[::-1][K - 1])
+        kept = score_bin(up) >= tbin
+        top = np.lexsort((np.arange(n_cand), -ex))[:K]
+        assert kept[top].all()
+        if scale_mult == 1.0:
+            assert kept.sum() <= 4096  # the candidate list holds them

@@ -201,26 +201,23 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArg
             const int64_t j = jb + (int64_t)i * kSelThreads + tid;
             if (j >= j1) break;
             const float* mrow = ml + (int)((j - j0) >> 5) * H;
-            float s = 0.f, s_cl = 0.f;
+            constexpr int PER_WORD = 4 / CB;  // codes per 32-bit word
+            auto word_of = [&](int wi) -> uint32_t {
+                if constexpr (WPP == 1)
+                    return reinterpret_cast<const uint32_t*>(&cw[i][0])[wi];
+                else
+                    return cw[i][wi / WPP][wi % WPP];
+            };
+            float s = 0.f;
 #pragma unroll
             for (int h = 0; h < H; ++h) {
-                constexpr int PER_WORD = 4 / CB;  // codes per 32-bit word
-                const int wi = h / PER_WORD;
-                uint32_t word;
-                if constexpr (WPP == 1)
-                    word = reinterpret_cast<const uint32_t*>(&cw[i][0])[wi];
-                else
-                    word = cw[i][wi / WPP][wi % WPP];
+                const uint32_t word = word_of(h / PER_WORD);
                 if constexpr (CB == 2) {
                     const uint32_t code = (word >> (16 * (h & 1))) & 0xffffu;
                     s += fast_exp2(fmaf((float)code, -kCodeUnscale, mrow[h]));
                 } else {
-                    // a clamped code (255) bounds its term by the value at 254.5
                     const uint32_t code = (word >> (8 * (h & 3))) & 0xffu;
-                    const bool cl = code == 255u;
-                    const float e = fast_exp2(fmaf(cl ? 254.5f : (float)code, -kCode8Unscale, mrow[h]));
-                    s += cl ? 0.f : e;
-                    s_cl += cl ? e : 0.f;
+                    s += fast_exp2(fmaf((float)code, -kCode8Unscale, mrow[h]));
                 }
             }
             float hist_s;
@@ -228,8 +225,28 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArg
                 s *= kScoreUnshift;  // exact power-of-two rescale to the true score
                 hist_s = s;
             } else {
-                hist_s = s * kRInv * kScoreUnshift;       // lower bound
-                s = (s * kR + s_cl) * kScoreUnshift;      // upper bound
+                // Upper bound: s r, also for a clamped code (255), whose term lies in
+                // [0, its value at 254.5] = [0, its value at 255 times 2^(1/32)].
+                // Lower bound: s / r, without the clamped terms; a key with one
+                // (a byte 0xff among its codes: a zero byte of the complement) is
+                // summed again without them.
+                uint32_t ff = 0;
+#pragma unroll
+                for (int wi = 0; wi < H / 4; ++wi) {
+                    const uint32_t x = ~word_of(wi);
+                    ff |= (x - 0x01010101u) & ~x & 0x80808080u;
+                }
+                float s_lo = s;
+                if (ff) {
+                    s_lo = 0.f;
+#pragma unroll
+                    for (int h = 0; h < H; ++h) {
+                        const uint32_t code = (word_of(h / 4) >> (8 * (h & 3))) & 0xffu;
+                        if (code != 255u) s_lo += fast_exp2(fmaf((float)code, -kCode8Unscale, mrow[h]));
+                    }
+                }
+                hist_s = s_lo * kRInv * kScoreUnshift;  // lower bound
+                s = s * kR * kScoreUnshift;             // upper bound
             }
             a.scores[(size_t)b * (size_t)a.n_ctx + j] = s;
             if (j < a.n_cand) atomicAdd(&hist[score_bin(hist_s)], 1u);
