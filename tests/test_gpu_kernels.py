@@ -390,6 +390,40 @@ def test_prefill_batched_and_head_shapes(hs2, orc, cfg, B, H, d, n_q, q_pos0, n_
     lse_close(sl[0].reshape(B * n_q, H), s["lse"], tol)
 
 
+@pytest.mark.parametrize("want_scores", [True, False])
+@pytest.mark.parametrize("cfg,B,H,d,n_ctx", [
+    (3, 3, 8, 64, 6000),     # bf16, H=8, d=64 instantiations of the split, score and rescore kernels
+    (5, 2, 4, 128, 7001),    # FP8, H=4, ragged last block
+    (3, 2, 16, 64, 4500),    # bf16, H=16, d=64
+    (5, 2, 8, 128, 5100),    # FP8, H=8
+])
+def test_decode_head_shapes(hs2, orc, cfg, B, H, d, n_ctx, want_scores):
+    """Every (H, d) form of the bf16 / FP8 decode step, with the score vector
+    (16-bit logit codes) and without it (8-bit codes, bounds, exact rescoring)."""
+    wl = workload(cfg).with_(B=B, H=H, d=d, n_q=1, q_pos0=n_ctx - 1, n_ctx=n_ctx, n_sparse=1, needles="decode",
+                             n_needles=4, decode=True)
+    x = make_inputs(wl)
+    say("decode shapes", wl.name, B, H, d, n_ctx, "with" if want_scores else "without", "the score vector")
+    r = hs2.decode_step(dev(x.q[:, 0]).contiguous(), dev(x.q_sparse[:, :, 0]).contiguous(), dev(x.k), dev(x.v),
+                        dev(x.k_scale), dev(x.v_scale), window=wl.window, k_global=wl.k_global,
+                        sm_scale=x.sm_scale, want_scores=want_scores)
+    torch.cuda.synchronize()
+    rows = list(range(B))
+    ref = orc.full_select(x.q, x.k, x.v, x.k_scale, x.v_scale, wl.q_pos0, wl.window, wl.k_global, x.sm_scale,
+                          rows, want_scores=True)
+    tol = RTOL[wl.kv_dtype]
+    rows_close(r["out_full"], ref["out"], tol, "decode out")
+    lse_close(r["lse_full"], ref["lse"], tol)
+    if want_scores:
+        decode_scores_close(r["scores"], ref["scores"], wl.kv_dtype)
+    ov, mn, sw = check_index_rows(r["indices"], ref["idx"], ref["scores"], ref["kth"], wl.window)
+    say(f"  overlap mean {ov:.4f} min {mn:.4f} swaps {sw}")
+    gidx = to_np(r["indices"]).astype(np.int32)
+    s = orc.sparse(x.q_sparse[0].contiguous(), x.k, x.v, x.k_scale, x.v_scale, gidx, x.sm_scale, rows)
+    rows_close(r["out_sparse"][0], s["out"], tol, "decode sparse out")
+    lse_close(r["lse_sparse"][0], s["lse"], tol)
+
+
 def test_sparse_attn_beyond_65535_tokens(hs2, orc):
     """More query tokens in one call than a grid's y dimension holds (65535):
     the sparse layer's 1-D grid covers them all; sampled rows against the
