@@ -958,7 +958,7 @@ int hs2_decode_step(const void* q_full, const void* q_sparse, int q_dtype, int n
     se.out_stride = n_sel;
     se.out_offset = window;
     const bool rescore = kv_dtype != HS2_F32 && code_bytes == 1;
-    se.exact_kth = rescore ? 1 : 0;
+    se.exact_scores = rescore ? 1 : 0;
     if (k_global > 0 && n_cand > 0) {
         HS2_TRY(TIMED(KC_SEL_COLLECT, s, launch_select_collect(se, s)));
         if (rescore) {

@@ -125,7 +125,10 @@ struct SelectArgs {
     int64_t out_stride;
     int out_offset;         // first column written in each out row
     int rev;                // test hook: deal the grid in reverse order (0: normal)
-    int exact_kth;          // final step: rank the candidates by their keys alone (no threshold bin)
+    // decode rescore form: the candidates' keys carry exact scores, not the
+    // scores they were collected by; the final step forms their histogram
+    // itself (candidates may also lie below its threshold bin)
+    int exact_scores;
 };
 // hist zeroed; fills hist
 hipError_t launch_select_hist(const SelectArgs& a, hipStream_t st);

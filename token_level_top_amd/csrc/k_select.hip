@@ -354,10 +354,11 @@ __global__ __launch_bounds__(kSelThreads) void decode_rescore_kernel(RescoreArgs
             for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
             if (le && hl == 0) {
                 const float sc = t * kScoreUnshift;
-                if (overflow)
+                if (overflow) {
                     a.scores[(size_t)r * (size_t)a.n_ctx + pe] = sc;
-                else
+                } else {
                     cand[i0 + src] = rank_key(sc, pe);
+                }
             }
         }
     }
@@ -806,6 +807,48 @@ __device__ void block_sort_positions(int32_t* v, int32_t* tmp, int n) {
 // In-bin ranking: keys in the threshold bin are ranked among themselves by
 // direct comparison when there are at most this many (else the digit search).
 constexpr int kRankMax = 512;
+
+// Threshold bin of a row's 4096-bin histogram for a kFinThreads block: the
+// largest bin b with (count of bins >= b) >= kk (1 <= kk <= the total), and
+// the count strictly above it. Thread t owns bins 4095 - 4t .. 4092 - 4t; a
+// wave scan of their sums and a scan over the 16 wave totals (in sh[0, 32))
+// find the bin; two barriers.
+__device__ uint2 block_threshold_bin(const uint32_t* hrow, uint32_t kk, uint32_t* sh) {
+    static_assert(kHistBins == 4 * kFinThreads, "four bins per thread");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        c[e] = hrow[kHistBins - 1 - 4 * t - e];
+        sum += c[e];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int q = 0; q < w; ++q) before += sh[q];
+    uint32_t acc = before + incl - sum;  // count in the bins above this thread's four
+    if (acc < kk && acc + sum >= kk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (acc + c[e] >= kk) {
+                sh[16] = (uint32_t)(kHistBins - 1 - 4 * t - e);
+                sh[17] = acc;
+                break;
+            }
+            acc += c[e];
+        }
+    }
+    __syncthreads();
+    const uint2 res = make_uint2(sh[16], sh[17]);
+    __syncthreads();
+    return res;
+}
 static_assert(kRankMax <= kFinThreads, "one in-bin key per thread");
 
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a, int window, int64_t p_last) {
@@ -867,14 +910,27 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
         return;
     }
     // Keys above the threshold bin are all kept (fewer than kk of them); of the
-    // nb keys in the bin the need = kk - (nc - nb) largest are kept. With
-    // exact_kth the candidates' keys carry scores the threshold bin was not
-    // taken from (the decode rescore step), so the k-th key is searched for.
-    const uint32_t tbin = a.thr[2 * r];
+    // nb keys in the bin the need = kk - above largest are kept. The bin comes
+    // from the histogram the candidates were collected by (then every
+    // candidate is in the bin or above it: above = nc - nb) or, in the decode
+    // rescore form, from a histogram of the candidates' exact scores built
+    // here in LDS (then candidates below the bin are dropped).
+    uint32_t tbin, above_exact = 0;
+    if (a.exact_scores) {
+        for (int i = tid; i < kHistBins; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < nc; i += blockDim.x) atomicAdd(&hist[(uint32_t)(keys[i] >> 51)], 1u);
+        __syncthreads();
+        const uint2 ta = block_threshold_bin(hist, kk, scratch);
+        tbin = ta.x;
+        above_exact = ta.y;
+    } else {
+        tbin = a.thr[2 * r];
+    }
     uint64_t* inb_key = reinterpret_cast<uint64_t*>(pos);  // pos[0, 1024): kRankMax keys
     uint32_t* inb_idx = reinterpret_cast<uint32_t*>(pos + 1024);
     __syncthreads();
-    for (uint32_t ib = 0; !a.exact_kth && ib < nc; ib += blockDim.x) {
+    for (uint32_t ib = 0; ib < nc; ib += blockDim.x) {
         const uint32_t i = ib + tid;
         const uint64_t k = i < nc ? keys[i] : 0ull;
         const bool in_bin = i < nc && (uint32_t)(k >> 51) == tbin;
@@ -891,8 +947,8 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelectArgs a,
     __syncthreads();
     const uint32_t nb = ctl[4];
     // flags in hist[0, nc): 1 = kept
-    if (!a.exact_kth && nb <= (uint32_t)kRankMax) {
-        const uint32_t need = kk - (nc - nb);
+    if (nb <= (uint32_t)kRankMax) {
+        const uint32_t need = kk - (a.exact_scores ? above_exact : nc - nb);
         bool kept = false;
         if (tid < (int)nb) {
             const uint64_t kq = inb_key[tid];
