@@ -23,8 +23,8 @@ struct RowsArgs {
     int n_split;            // workgroups per token
     float scale_log2;       // sm_scale * log2(e)
     float* logits;          // contiguous + store (fp32 cache): [B][n_ctx][H] base-2 logits
-    // decode split kernel (bf16 / FP8 cache): the logits as 16-bit codes below
-    // the maximum of their 32-key block and head, and those maxima
+    // decode split kernel (bf16 / FP8 cache): the logits as 8- or 16-bit codes
+    // below the maximum of their 32-key block and head, and those maxima
     void* lcode;            // [B][n_ctx][H] codes of code_bytes each (16- or 8-bit)
     float* lmax;            // [B][n_split][max_chunks][4][H] base 2: block maxima by (split, chunk, wave)
     int max_chunks;         // 128-key chunks per split, at most (ceil(ceil(n_ctx / 128) / n_split))

@@ -8,14 +8,17 @@
 // read each key and value row once, form the H logits of the key, keep an online
 // softmax per head, accumulate P V, and keep the base-2 logits for the token
 // score, which needs the final LSE (only known once every split is done).
-// The logits are kept as 16-bit codes: for each 32-key block and head the
-// block maximum M (fp32) and per key c = round(1024 (M - x)), clamped to
-// 65535 (64 below M); the score kernel forms 2^(M - c/1024 - LSE), within a
-// factor 2^(+-1/2048) (relative 3.4e-4) of the exact term, or below 2^-64 of
-// the block's largest term where clamped. The wide range keeps a clamped term
+// The logits are kept as codes below the maximum M (fp32) of their 32-key
+// block and head. With 16-bit codes, c = round(1024 (M - x)) clamped to 65535
+// (64 below M), the score kernel forms 2^(M - c/1024 - LSE) within a factor
+// 2^(+-1/2048) (relative 3.4e-4) of the exact term, or below 2^-64 of the
+// block's largest term where clamped; the wide range keeps a clamped term
 // negligible against any score fp32 can rank, also when a block holds a term
-// many orders of magnitude above its neighbours (peaked attention). That is 2.125 H bytes a key instead of
-// 4 H, written once and read once.
+// many orders of magnitude above its neighbours (peaked attention). With 8-bit
+// codes (see CB below) the codes only bound the scores and the selection
+// recomputes the exact scores of its candidates. That is 2.125 H or 1.125 H
+// bytes a key instead of 4 H, written once and read once; the block maxima
+// stay in LDS for the whole split and are written in one run at its end.
 //
 // Layout of the work: the n_split workgroups of a sequence deal its keys out
 // in 128-key chunks, split s taking chunks s, s + n_split, s + 2 n_split, ...,
