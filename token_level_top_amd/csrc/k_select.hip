@@ -153,16 +153,17 @@ __global__ __launch_bounds__(kSelThreads) void decode_score_kernel(ScoreArgs a) 
 // keeps every key whose upper bound reaches the bin of the k-th largest lower
 // bound -- a superset of the top k -- and the rescore step replaces their
 // bounds by exact scores.
+constexpr int kScoreChunk = 4096;  // keys per workgroup of the code-form score kernel
 template <int H, int CB>
 __global__ __launch_bounds__(kSelThreads) void decode_score_code_kernel(ScoreArgs a) {
     constexpr int kBatch = 8;
-    constexpr int NBLK = kSelChunk / 32;  // 32-key blocks of a chunk
+    constexpr int NBLK = kScoreChunk / 32;  // 32-key blocks of a chunk
     __shared__ uint32_t hist[kHistBins];
     __shared__ __attribute__((aligned(16))) float ml[NBLK * H];  // M_h - LSE_h + kScoreShift per block
     const int b = blockIdx.y, tid = threadIdx.x;
     for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
-    const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
-    const int64_t j1 = min<int64_t>(j0 + kSelChunk, a.n_ctx);
+    const int64_t j0 = (int64_t)blockIdx.x * kScoreChunk;
+    const int64_t j1 = min<int64_t>(j0 + kScoreChunk, a.n_ctx);
     const int nb = (int)((j1 - j0 + 31) / 32);
     {
         // block bg = j / 32 lies in 128-key chunk c = bg / 4, taken by wave bg % 4
@@ -275,10 +276,12 @@ hipError_t launch_decode_score(const ScoreArgs& a, int B, hipStream_t st) {
             hipLaunchKernelGGL(decode_score_kernel<8>, grid, dim3(kSelThreads), 0, st, a);
         else
             hipLaunchKernelGGL(decode_score_kernel<16>, grid, dim3(kSelThreads), 0, st, a);
-    } else if (a.code_bytes == 1) {
-        launch_score_code<1>(a, grid, st);
     } else {
-        launch_score_code<2>(a, grid, st);
+        const dim3 cgrid((unsigned)((a.n_ctx + kScoreChunk - 1) / kScoreChunk), (unsigned)B);
+        if (a.code_bytes == 1)
+            launch_score_code<1>(a, cgrid, st);
+        else
+            launch_score_code<2>(a, cgrid, st);
     }
     return hipGetLastError();
 }
