@@ -258,10 +258,15 @@ constexpr int kCompactScratchMem = 256;  // uint32 per wave: one bin per value o
 // the keys above the current digit bin plus the bin itself number at most
 // max_keep, T is the bin's lower edge and all of them are kept (a superset of
 // the top kk, still in list order). *kept (if given) receives the number kept.
+// A caller that already knows the digit bin of the kk-th key over the top
+// 64 - seed_hi bits (seed_hi < 64: keys under seed_prefix on those bits hold
+// the kk-th, and seed_need of them are needed, kk < cnt) starts the search
+// there, without the min/max pass and the passes above seed_hi.
 template <int U>
 __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t cnt, uint32_t kk, uint32_t* hist,
                                                   int32_t* pos_out, uint64_t* buf, uint32_t max_keep = 0,
-                                                  uint32_t* kept = nullptr) {
+                                                  uint32_t* kept = nullptr, int seed_hi = 64,
+                                                  uint64_t seed_prefix = 0, uint32_t seed_need = 0) {
     const uint32_t lane = lane_id();
     // every store this wave issued to the list (appends, an earlier compaction)
     // has completed before the first key is read back
@@ -288,19 +293,29 @@ __device__ __forceinline__ uint64_t wave_topk_mem(const uint64_t* keys, uint32_t
         });
         T = wave_min_u64(m);
     } else {
-        uint64_t kmax = 0, kmin = ~0ull;
-        each([&](uint64_t k, bool ok) {
-            if (ok) {
-                kmax = k > kmax ? k : kmax;
-                kmin = k < kmin ? k : kmin;
-            }
-        });
-        kmax = wave_max_u64(kmax);
-        kmin = wave_min_u64(kmin);
-        int hi = 64 - __clzll((long long)(kmax ^ kmin));  // bits [hi, 64) are shared by every key
-        uint64_t pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
-        uint64_t prefix = kmax & pmask;
-        uint32_t need = kk;
+        int hi;
+        uint64_t pmask, prefix;
+        uint32_t need;
+        if (seed_hi < 64) {
+            hi = seed_hi;
+            pmask = ~((1ull << hi) - 1ull);
+            prefix = seed_prefix & pmask;
+            need = seed_need;
+        } else {
+            uint64_t kmax = 0, kmin = ~0ull;
+            each([&](uint64_t k, bool ok) {
+                if (ok) {
+                    kmax = k > kmax ? k : kmax;
+                    kmin = k < kmin ? k : kmin;
+                }
+            });
+            kmax = wave_max_u64(kmax);
+            kmin = wave_min_u64(kmin);
+            hi = 64 - __clzll((long long)(kmax ^ kmin));  // bits [hi, 64) are shared by every key
+            pmask = hi >= 64 ? 0ull : ~((1ull << hi) - 1ull);
+            prefix = kmax & pmask;
+            need = kk;
+        }
         bool found = false;
         T = 0;
         while (hi > 0 && !found) {

@@ -808,8 +808,9 @@ __device__ __forceinline__ uint64_t trim_candidates(uint64_t* buf, uint32_t cnt,
 // exact top-kk of a token's candidate buffer, written as positions (after the
 // scan: registers are free, so more keys per lane are in flight)
 __device__ __forceinline__ void final_topk(uint64_t* buf, uint32_t cnt, uint32_t kk, uint32_t* hist,
-                                           int32_t* pos_out) {
-    wave_topk_mem<HS2_FINAL_U>(buf, cnt, kk, hist, pos_out, buf);
+                                           int32_t* pos_out, int seed_hi = 64, uint64_t seed_prefix = 0,
+                                           uint32_t seed_need = 0) {
+    wave_topk_mem<HS2_FINAL_U>(buf, cnt, kk, hist, pos_out, buf, 0, nullptr, seed_hi, seed_prefix, seed_need);
 }
 
 // Waves per SIMD for pass 2. The tile loop is VALU-issue bound, so four waves
@@ -1205,7 +1206,33 @@ void score_stream_kernel(PrefillArgs a) {
             uint32_t cs = cnt[u][side];
             uint64_t* buf = a.cand + row * (size_t)cap;
             if (kk == 0) cs = 0;
-            if (cs > 0) final_topk(buf, cs, kk, whist[w], out);   // writes min(kk, cs) positions
+            // with the threshold histograms (after a first trim) the bin of the
+            // kk-th key is known: bins > bb hold `above` keys, bin bb the
+            // kk-th; the exact search starts below the bin's 12 rank-word bits
+            // (bins 0 and 63 also hold keys beyond their edges: not used)
+            int seed_hi = 64;
+            uint64_t seed_prefix = 0;
+            uint32_t seed_need = 0;
+            if (THR_HIST && kk > 0 && kk < cs && tbase[u][side] >= 0) {
+                const int tb = tbase[u][side];
+                uint32_t v = thist[w][slot_token(u, side)][lane];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = __shfl_down(v, off);
+                    if (lane + off < 64) v += o;
+                }
+                const uint64_t ok = __ballot(v >= kk);
+                if (ok) {
+                    const int bb = 63 - __clzll((long long)ok);
+                    const uint32_t above = bb < 63 ? (uint32_t)__shfl(v, bb + 1) : 0u;
+                    if (bb >= 1 && bb <= 62 && tb + bb >= 0 && tb + bb + 1 < (1 << (32 - kThrShift))) {
+                        seed_hi = 32 + kThrShift;
+                        seed_prefix = (uint64_t)(uint32_t)(tb + bb) << (32 + kThrShift);
+                        seed_need = kk - above;
+                    }
+                }
+            }
+            if (cs > 0) final_topk(buf, cs, kk, whist[w], out, seed_hi, seed_prefix, seed_need);  // min(kk, cs) positions
             const uint32_t wrote = cs < kk ? cs : kk;
             for (uint32_t t = wrote + lane; t < (uint32_t)a.k_global; t += 64) out[t] = -1;
         }
